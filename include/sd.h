@@ -1,0 +1,185 @@
+/*
+ * sd.h -- C ABI of the MI355X (gfx950) sparse decode-attention library
+ * (libsdkv.so).
+ *
+ * One decode step of grouped-query attention for B sequences, each with ONE
+ * query token, over a paged KV cache, in two stages:
+ *
+ *   1. query-aware selection: every KV unit (a token, or a page of P tokens)
+ *      is scored against the query -- by the exact logits q.K, or by a bound
+ *      computed from per-page key minima and maxima -- and the top r_KV of
+ *      the units are kept per (sequence, KV head);
+ *   2. split-K attention over the kept units only: each split runs an online
+ *      softmax over its share of the kept tokens, and the splits are merged
+ *      by log-sum-exp.  Dense decoding is the same attention kernel with
+ *      every unit kept.
+ *
+ * Sources (page title, then the part of the page):
+ *   [Cross/cards] "Where Activation Sparsity and KV-Cache Sparsity Cross in
+ *     LLM Decoding", cards view, EntmaxKV abstract: pages are scored against
+ *     the query from light per-page statistics before they are loaded, then
+ *     candidates are selected and attention runs on them; pre-hoc sparsity
+ *     abstract: the dropped mass delta governs the error.
+ *   [Cross/list] same title, list view, Abstract: attention-scored KV
+ *     selection; dense and sparse decoding read the cache through one
+ *     split-K attention kernel.  Tables 4 and 16: a keep ratio of 1 turns
+ *     selection off.
+ *   [SparDA] "SparDA: Sparse Decoupled Attention for Efficient Long-Context
+ *     LLM Inference" summary page, Section 3.1: attention is computed over
+ *     the attended blocks only; the query heads of a GQA group share one KV
+ *     head and one block choice.  Appendix C: 64-token blocks.
+ *
+ * Conventions for every entry point
+ *   - Pointers named *_host or the shape struct are host memory; every other
+ *     pointer is device memory on the current HIP device.
+ *   - The caller owns all buffers.  The library never allocates or frees
+ *     memory; scratch space comes from the caller's workspace (ws, ws_bytes).
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and runs asynchronously; nothing synchronises the host.
+ *   - Host-visible arguments are validated before anything is enqueued.  On
+ *     a non-OK status nothing has been enqueued or written, and
+ *     sd_last_error() describes the failure (thread-local text).
+ *   - Device-resident metadata is trusted only as far as memory safety goes:
+ *     seq_lens[b] is clamped to [0, max_seq_len]; a block-table entry outside
+ *     [0, num_pages) makes the kernels skip that page.  A sequence with no
+ *     valid token yields out = 0 and lse = -inf.
+ *
+ * Layouts (row-major, innermost last)
+ *   q            [B][H_q][d]              dtype
+ *   k_pages      [num_pages][H_kv][P][d]  dtype  (one contiguous tile per
+ *   v_pages      [num_pages][H_kv][P][d]  dtype   page and KV head)
+ *   page_bounds  [num_pages][H_kv][2][d]  dtype  (row 0: channel minima,
+ *                                                  row 1: channel maxima)
+ *   block_table  [B][max_pages_per_seq]   int32  physical page of logical page u
+ *   seq_lens     [B]                      int32  valid tokens n_b
+ *   unit_scores  [B][H_kv][U_max]         fp32   U_max = max_pages_per_seq
+ *                                                 (page unit) or max_seq_len
+ *                                                 (token unit)
+ *   token_logits [B][H_q][max_seq_len]    fp32   (token unit only)
+ *   sel_idx      [B][H_kv][k_max]         int32  kept unit ids, ascending
+ *   sel_count    [B][H_kv]                int32  k_b per sequence
+ *   out          [B][H_q][d]              fp32
+ *   lse          [B][H_q]                 fp32   natural-log sum of exp(logits)
+ * Query head h reads KV head h / G, G = H_q / H_kv.  Logical token t of
+ * sequence b lives in page block_table[b][t / P], row t % P.
+ */
+#ifndef SPARSE_KV_SD_H
+#define SPARSE_KV_SD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sd_status {
+  SD_OK = 0,
+  SD_E_NULL = 1,         /* a required pointer is NULL */
+  SD_E_SHAPE = 2,        /* inconsistent sizes */
+  SD_E_DTYPE = 3,        /* unknown dtype */
+  SD_E_RATIO = 4,        /* r_KV not finite or <= 0 */
+  SD_E_WORKSPACE = 5,    /* ws too small or misaligned */
+  SD_E_UNSUPPORTED = 6,  /* valid, but not built: d, P or G outside the supported set */
+  SD_E_DEVICE = 7        /* the HIP runtime reported an error while enqueueing */
+} sd_status;
+
+typedef enum sd_dtype { SD_F32 = 0, SD_BF16 = 1 } sd_dtype;  /* q, K, V and page bounds */
+typedef enum sd_unit { SD_UNIT_TOKEN = 0, SD_UNIT_PAGE = 1 } sd_unit;
+
+/* Problem sizes (host struct). Supported: head_dim in {64, 128};
+ * page_size in {16, 64}; G = num_q_heads / num_kv_heads in {1, 2, 4, 8}. */
+typedef struct sd_shape {
+  int32_t batch;              /* B >= 1 sequences, one query token each */
+  int32_t num_q_heads;        /* H_q, a multiple of num_kv_heads */
+  int32_t num_kv_heads;       /* H_kv >= 1 */
+  int32_t head_dim;           /* d */
+  int32_t page_size;          /* P tokens per page */
+  int32_t max_pages_per_seq;  /* row length of block_table */
+  int32_t max_seq_len;        /* >= every seq_lens[b]; <= max_pages_per_seq * P */
+  int32_t dtype;              /* sd_dtype */
+  int64_t num_pages;          /* physical pages in k_pages / v_pages / page_bounds */
+  float softmax_scale;        /* multiplies q.K; <= 0 selects 1 / sqrt(d) */
+} sd_shape;
+
+/* Keep count for U units at keep ratio r_KV (host, pure): r_KV >= 1 keeps all
+ * U; otherwise R = floor(r_KV * 1e6 + 0.5) parts per million and
+ * k = ceil(R * U / 1e6) in integer arithmetic, clamped to [1, U].  The
+ * kernels apply the same rule per sequence to U_b.  Returns -1 when r_KV is
+ * not finite or <= 0, or U < 1. */
+int32_t sd_keep_count(double r_kv, int32_t num_units);
+
+/* Workspace bytes that suffice for every call below made with this shape,
+ * unit and r_KV (sd_decode_step included).  Host only; needs no GPU. */
+sd_status sd_workspace_bytes(const sd_shape* shape, int32_t unit, double r_kv, size_t* bytes_host);
+
+/* Setup step, not part of the decode step: channel-wise min and max of the
+ * keys of every page referenced by block_table[b][0 .. ceil(n_b / P) - 1],
+ * over the page's VALID tokens only, written to page_bounds.  These are the
+ * light per-page statistics of [Cross/cards] (EntmaxKV abstract).  A
+ * physical page is assumed to belong to one sequence. */
+sd_status sd_update_page_bounds(const sd_shape* shape, const void* k_pages,
+                                const int32_t* block_table, const int32_t* seq_lens,
+                                void* page_bounds, void* stream);
+
+/* Stage 1a, scoring ([Cross/cards] EntmaxKV abstract; [Cross/list] Abstract).
+ *   unit == SD_UNIT_PAGE: reads q and page_bounds;
+ *     unit_scores[b][g][u] = max over the G heads h of group g of
+ *       scale * sum_c max(q[b][h][c] * kmin[c], q[b][h][c] * kmax[c]),
+ *     an upper bound on every logit of page u; u < ceil(n_b / P).
+ *     token_logits is not used (may be NULL).
+ *   unit == SD_UNIT_TOKEN: reads q and every valid key;
+ *     token_logits[b][h][t] = scale * q[b][h] . K[b][h / G][t] and
+ *     unit_scores[b][g][t] = max over h in group g, for t < n_b.
+ * Entries past a sequence's units are left untouched. */
+sd_status sd_score_pages(const sd_shape* shape, const void* q, const void* k_pages,
+                         const void* page_bounds, const int32_t* block_table,
+                         const int32_t* seq_lens, int32_t unit, float* unit_scores,
+                         float* token_logits, void* stream);
+
+/* Stage 1b, exact top-k per (sequence b, KV head g): k_b = keep count of
+ * U_b units; keeps the k_b largest unit_scores[b][g][0 .. U_b - 1], equal
+ * scores going to the lower unit id (-0.0 equals +0.0), and writes them in
+ * ascending order to sel_idx[b][g][0 .. k_b - 1]; sel_count[b][g] = k_b.
+ * Scores must be finite.  k_max = sd_keep_count(r_kv, U_max) is the row
+ * length of sel_idx. */
+sd_status sd_select_topk(const sd_shape* shape, int32_t unit, const int32_t* seq_lens,
+                         const float* unit_scores, double r_kv, int32_t* sel_idx,
+                         int32_t* sel_count, void* ws, size_t ws_bytes, void* stream);
+
+/* Stage 2, split-K attention over the kept units ([Cross/list] Abstract;
+ * [SparDA] Section 3.1).  For each (b, g) the kept units
+ * sel_idx[b][g][0 .. sel_count[b][g] - 1] are cut into splits; each split
+ * keeps a running max, sum and weighted value sum over its tokens; splits are
+ * merged by log-sum-exp into out[b][h] and lse[b][h].
+ *   sel_idx == NULL: dense -- every unit of every sequence (sel_count unused).
+ *   unit == SD_UNIT_PAGE: a kept page contributes its valid tokens.
+ *   unit == SD_UNIT_TOKEN: sel_idx holds token ids; with token_logits != NULL
+ *     the logits are read from there (written by sd_score_pages) and only V
+ *     rows of the kept tokens are read; with NULL, q.K is recomputed.
+ * k_max: row length of sel_idx (ignored when sel_idx == NULL). */
+sd_status sd_attend_splitk(const sd_shape* shape, const void* q, const void* k_pages,
+                           const void* v_pages, const int32_t* block_table,
+                           const int32_t* seq_lens, int32_t unit, const int32_t* sel_idx,
+                           const int32_t* sel_count, int32_t k_max, const float* token_logits,
+                           float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* The whole decode step: r_kv >= 1 runs dense attention only; otherwise
+ * scoring (by unit), top-k and attention over the kept units.  page_bounds
+ * is read in page unit (built beforehand by sd_update_page_bounds).
+ * sel_idx / sel_count may be NULL (then they live in ws); when given they
+ * receive the selection ([B][H_kv][k_max], [B][H_kv]). */
+sd_status sd_decode_step(const sd_shape* shape, const void* q, const void* k_pages,
+                         const void* v_pages, const void* page_bounds,
+                         const int32_t* block_table, const int32_t* seq_lens, int32_t unit,
+                         double r_kv, float* out, float* lse, int32_t* sel_idx,
+                         int32_t* sel_count, void* ws, size_t ws_bytes, void* stream);
+
+/* Text of the last non-OK status on this thread ("" if none). */
+const char* sd_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_KV_SD_H */

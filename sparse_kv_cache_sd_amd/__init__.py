@@ -1,0 +1,25 @@
+"""MI355X (gfx950) sparse decode attention: query-aware top-k selection of KV
+tokens or pages, then split-K attention over the kept entries.
+
+The work is done by hand-written HIP kernels in libsdkv.so behind the C ABI of
+include/sd.h; this package is its thin Python binding (argument marshalling
+only) plus the in-tree build script.
+"""
+
+from ._lib import (  # noqa: F401
+    EXPORTS,
+    LIB_PATH,
+    SdError,
+    Shape,
+    UNIT_PAGE,
+    UNIT_TOKEN,
+    alloc_workspace,
+    attend_splitk,
+    decode_step,
+    keep_count,
+    lib,
+    score_pages,
+    select_topk,
+    update_page_bounds,
+    workspace_bytes,
+)

@@ -1,0 +1,289 @@
+"""ctypes binding of libsdkv.so (include/sd.h): argument marshalling only.
+
+Every function below takes torch tensors, checks that each one lives on the
+GPU with the dtype, shape and contiguity the C ABI expects (so that no kernel
+is ever handed a host pointer or a short buffer), and calls the entry point
+of the same name.  All arithmetic happens in the HIP kernels.  A missing
+library raises at once; there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdkv.so")
+
+SD_F32, SD_BF16 = 0, 1
+UNIT_TOKEN, UNIT_PAGE = 0, 1
+_UNITS = {"token": UNIT_TOKEN, "page": UNIT_PAGE}
+_STATUS = {0: "SD_OK", 1: "SD_E_NULL", 2: "SD_E_SHAPE", 3: "SD_E_DTYPE", 4: "SD_E_RATIO",
+           5: "SD_E_WORKSPACE", 6: "SD_E_UNSUPPORTED", 7: "SD_E_DEVICE"}
+WS_ALIGN = 256
+
+
+class SdError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class SdShape(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32),
+        ("max_seq_len", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("num_pages", ctypes.c_int64),
+        ("softmax_scale", ctypes.c_float),
+    ]
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_SIGS = {
+    "sd_keep_count": (ctypes.c_int32, [ctypes.c_double, _I32]),
+    "sd_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(SdShape), _I32, ctypes.c_double,
+                                          ctypes.POINTER(ctypes.c_size_t)]),
+    "sd_update_page_bounds": (ctypes.c_int, [ctypes.POINTER(SdShape), _P, _P, _P, _P, _P]),
+    "sd_score_pages": (ctypes.c_int, [ctypes.POINTER(SdShape), _P, _P, _P, _P, _P, _I32, _P,
+                                      _P, _P]),
+    "sd_select_topk": (ctypes.c_int, [ctypes.POINTER(SdShape), _I32, _P, _P, ctypes.c_double,
+                                      _P, _P, _P, ctypes.c_size_t, _P]),
+    "sd_attend_splitk": (ctypes.c_int, [ctypes.POINTER(SdShape), _P, _P, _P, _P, _P, _I32, _P,
+                                        _P, _I32, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "sd_decode_step": (ctypes.c_int, [ctypes.POINTER(SdShape), _P, _P, _P, _P, _P, _P, _I32,
+                                      ctypes.c_double, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "sd_last_error": (ctypes.c_char_p, []),
+}
+EXPORTS = tuple(_SIGS)
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m sparse_kv_cache_sd_amd.build`")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(h, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = h
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise SdError(status, lib().sd_last_error().decode())
+
+
+# ----------------------------------------------------------------------------
+# shape
+# ----------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class Shape:
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    page_size: int
+    max_pages_per_seq: int
+    max_seq_len: int
+    dtype: str             # "f32" | "bf16"
+    num_pages: int
+    softmax_scale: float = 0.0
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    def units_max(self, unit: str) -> int:
+        return self.max_pages_per_seq if unit == "page" else self.max_seq_len
+
+    def c(self) -> SdShape:
+        return SdShape(self.batch, self.num_q_heads, self.num_kv_heads, self.head_dim,
+                       self.page_size, self.max_pages_per_seq, self.max_seq_len,
+                       SD_F32 if self.dtype == "f32" else SD_BF16, self.num_pages,
+                       self.softmax_scale)
+
+
+def _unit(unit) -> int:
+    if isinstance(unit, str):
+        return _UNITS[unit]
+    return int(unit)
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t, name, dtype, shape=None, optional=False):
+    """Device pointer of a contiguous GPU tensor of the given dtype and shape."""
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _ws(ws, need):
+    if need == 0 and ws is None:
+        return None, 0
+    p = _dev(ws, "ws", torch.uint8)
+    if ws.data_ptr() % WS_ALIGN:
+        raise ValueError(f"ws must be {WS_ALIGN}-byte aligned")
+    return p, ws.numel()
+
+
+# ----------------------------------------------------------------------------
+# entry points
+# ----------------------------------------------------------------------------
+
+def keep_count(r_kv: float, num_units: int) -> int:
+    k = lib().sd_keep_count(float(r_kv), int(num_units))
+    if k < 0:
+        raise ValueError("r_kv must be finite and > 0, num_units >= 1")
+    return k
+
+
+def workspace_bytes(shape: Shape, unit, r_kv: float) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().sd_workspace_bytes(ctypes.byref(shape.c()), _unit(unit), float(r_kv),
+                                    ctypes.byref(out)))
+    return int(out.value)
+
+
+def alloc_workspace(shape: Shape, unit, r_kv: float, device="cuda") -> torch.Tensor:
+    n = max(1, workspace_bytes(shape, unit, r_kv))
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def _kv_shape(s: Shape):
+    return (s.num_pages, s.num_kv_heads, s.page_size, s.head_dim)
+
+
+def update_page_bounds(shape: Shape, k_pages, block_table, seq_lens, page_bounds, stream=None):
+    s = shape
+    _check(lib().sd_update_page_bounds(
+        ctypes.byref(s.c()),
+        _dev(k_pages, "k_pages", s.torch_dtype, _kv_shape(s)),
+        _dev(block_table, "block_table", torch.int32, (s.batch, s.max_pages_per_seq)),
+        _dev(seq_lens, "seq_lens", torch.int32, (s.batch,)),
+        _dev(page_bounds, "page_bounds", s.torch_dtype,
+             (s.num_pages, s.num_kv_heads, 2, s.head_dim)),
+        _stream(stream)))
+
+
+def score_pages(shape: Shape, q, k_pages, page_bounds, block_table, seq_lens, unit,
+                unit_scores, token_logits=None, stream=None):
+    s, u = shape, _unit(unit)
+    umax = s.max_pages_per_seq if u == UNIT_PAGE else s.max_seq_len
+    _check(lib().sd_score_pages(
+        ctypes.byref(s.c()),
+        _dev(q, "q", s.torch_dtype, (s.batch, s.num_q_heads, s.head_dim)),
+        _dev(k_pages, "k_pages", s.torch_dtype, _kv_shape(s), optional=u == UNIT_PAGE),
+        _dev(page_bounds, "page_bounds", s.torch_dtype,
+             (s.num_pages, s.num_kv_heads, 2, s.head_dim), optional=u == UNIT_TOKEN),
+        _dev(block_table, "block_table", torch.int32, (s.batch, s.max_pages_per_seq)),
+        _dev(seq_lens, "seq_lens", torch.int32, (s.batch,)),
+        u,
+        _dev(unit_scores, "unit_scores", torch.float32, (s.batch, s.num_kv_heads, umax)),
+        _dev(token_logits, "token_logits", torch.float32,
+             (s.batch, s.num_q_heads, s.max_seq_len), optional=u == UNIT_PAGE),
+        _stream(stream)))
+
+
+def select_topk(shape: Shape, unit, seq_lens, unit_scores, r_kv, sel_idx, sel_count,
+                ws=None, stream=None):
+    s, u = shape, _unit(unit)
+    umax = s.max_pages_per_seq if u == UNIT_PAGE else s.max_seq_len
+    k_max = keep_count(r_kv, umax)
+    wp, wn = _ws(ws, 0)
+    _check(lib().sd_select_topk(
+        ctypes.byref(s.c()), u,
+        _dev(seq_lens, "seq_lens", torch.int32, (s.batch,)),
+        _dev(unit_scores, "unit_scores", torch.float32, (s.batch, s.num_kv_heads, umax)),
+        float(r_kv),
+        _dev(sel_idx, "sel_idx", torch.int32, (s.batch, s.num_kv_heads, k_max)),
+        _dev(sel_count, "sel_count", torch.int32, (s.batch, s.num_kv_heads)),
+        wp, wn, _stream(stream)))
+
+
+def attend_splitk(shape: Shape, q, k_pages, v_pages, block_table, seq_lens, unit, sel_idx,
+                  sel_count, out, lse, ws, token_logits=None, stream=None):
+    s, u = shape, _unit(unit)
+    k_max = 0
+    if sel_idx is not None:
+        if sel_idx.dim() != 3 or tuple(sel_idx.shape[:2]) != (s.batch, s.num_kv_heads):
+            raise ValueError("sel_idx must have shape (B, H_kv, k_max)")
+        k_max = int(sel_idx.shape[2])
+    wp, wn = _ws(ws, 1)
+    _check(lib().sd_attend_splitk(
+        ctypes.byref(s.c()),
+        _dev(q, "q", s.torch_dtype, (s.batch, s.num_q_heads, s.head_dim)),
+        _dev(k_pages, "k_pages", s.torch_dtype, _kv_shape(s), optional=token_logits is not None),
+        _dev(v_pages, "v_pages", s.torch_dtype, _kv_shape(s)),
+        _dev(block_table, "block_table", torch.int32, (s.batch, s.max_pages_per_seq)),
+        _dev(seq_lens, "seq_lens", torch.int32, (s.batch,)),
+        u,
+        _dev(sel_idx, "sel_idx", torch.int32, optional=True),
+        _dev(sel_count, "sel_count", torch.int32, (s.batch, s.num_kv_heads),
+             optional=sel_idx is None),
+        k_max,
+        _dev(token_logits, "token_logits", torch.float32,
+             (s.batch, s.num_q_heads, s.max_seq_len), optional=True),
+        _dev(out, "out", torch.float32, (s.batch, s.num_q_heads, s.head_dim)),
+        _dev(lse, "lse", torch.float32, (s.batch, s.num_q_heads)),
+        wp, wn, _stream(stream)))
+
+
+def decode_step(shape: Shape, q, k_pages, v_pages, page_bounds, block_table, seq_lens, unit,
+                r_kv, out, lse, ws, sel_idx=None, sel_count=None, stream=None):
+    s, u = shape, _unit(unit)
+    umax = s.max_pages_per_seq if u == UNIT_PAGE else s.max_seq_len
+    dense = r_kv >= 1.0
+    wp, wn = _ws(ws, 1)
+    k_max = keep_count(r_kv, umax) if not (math.isnan(r_kv) or r_kv <= 0) else 0
+    _check(lib().sd_decode_step(
+        ctypes.byref(s.c()),
+        _dev(q, "q", s.torch_dtype, (s.batch, s.num_q_heads, s.head_dim)),
+        _dev(k_pages, "k_pages", s.torch_dtype, _kv_shape(s)),
+        _dev(v_pages, "v_pages", s.torch_dtype, _kv_shape(s)),
+        _dev(page_bounds, "page_bounds", s.torch_dtype,
+             (s.num_pages, s.num_kv_heads, 2, s.head_dim), optional=dense or u == UNIT_TOKEN),
+        _dev(block_table, "block_table", torch.int32, (s.batch, s.max_pages_per_seq)),
+        _dev(seq_lens, "seq_lens", torch.int32, (s.batch,)),
+        u, float(r_kv),
+        _dev(out, "out", torch.float32, (s.batch, s.num_q_heads, s.head_dim)),
+        _dev(lse, "lse", torch.float32, (s.batch, s.num_q_heads)),
+        _dev(sel_idx, "sel_idx", torch.int32, (s.batch, s.num_kv_heads, k_max), optional=True),
+        _dev(sel_count, "sel_count", torch.int32, (s.batch, s.num_kv_heads), optional=True),
+        wp, wn, _stream(stream)))

@@ -1,0 +1,359 @@
+// C ABI of libsdkv.so (declared in include/sd.h): argument validation, the
+// split plan, workspace carving and kernel launches.  Host code only.
+#include "sd.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+sd_status fail(sd_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+sd_status ok() {
+  g_err[0] = '\0';
+  return SD_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Blocks the attention pass aims for: four per CU on the 256 CUs of an MI355X.
+constexpr int64_t kTargetBlocks = 1024;
+// Fewest token rows one attention block should own.
+constexpr int64_t kMinRowsPerBlock = 64;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Parts-per-million keep ratio; -1 keeps everything (r >= 1).
+int ratio_ppm(double r) {
+  if (r >= 1.0) return -1;
+  return static_cast<int>(std::floor(r * 1e6 + 0.5));
+}
+
+int64_t keep_count_ppm(int R, int64_t U) {
+  if (U < 1) return 0;
+  if (R < 0) return U;
+  int64_t k = ceil_div(static_cast<int64_t>(R) * U, 1000000);
+  return k < 1 ? 1 : (k > U ? U : k);
+}
+
+sd_status check_shape(const sd_shape* s, sdkv::Dims* d) {
+  if (!s) return fail(SD_E_NULL, "shape is NULL");
+  if (s->batch < 1 || s->num_q_heads < 1 || s->num_kv_heads < 1 || s->head_dim < 1 ||
+      s->page_size < 1 || s->max_pages_per_seq < 1 || s->max_seq_len < 1 || s->num_pages < 1)
+    return fail(SD_E_SHAPE, "every size in the shape must be >= 1");
+  if (s->num_q_heads % s->num_kv_heads != 0)
+    return fail(SD_E_SHAPE, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)",
+                s->num_q_heads, s->num_kv_heads);
+  if (static_cast<int64_t>(s->max_seq_len) >
+      static_cast<int64_t>(s->max_pages_per_seq) * s->page_size)
+    return fail(SD_E_SHAPE, "max_seq_len (%d) exceeds max_pages_per_seq * page_size",
+                s->max_seq_len);
+  if (s->dtype != SD_F32 && s->dtype != SD_BF16)
+    return fail(SD_E_DTYPE, "dtype %d is neither SD_F32 nor SD_BF16", s->dtype);
+  const int G = s->num_q_heads / s->num_kv_heads;
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(SD_E_UNSUPPORTED, "head_dim %d not built (64 or 128)", s->head_dim);
+  if (s->page_size != 16 && s->page_size != 64)
+    return fail(SD_E_UNSUPPORTED, "page_size %d not built (16 or 64)", s->page_size);
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(SD_E_UNSUPPORTED, "group size %d not built (1, 2, 4 or 8)", G);
+  if (!std::isfinite(s->softmax_scale))
+    return fail(SD_E_SHAPE, "softmax_scale is not finite");
+  d->B = s->batch;
+  d->Hq = s->num_q_heads;
+  d->Hkv = s->num_kv_heads;
+  d->G = G;
+  d->D = s->head_dim;
+  d->P = s->page_size;
+  d->max_pages = s->max_pages_per_seq;
+  d->max_seq = s->max_seq_len;
+  d->dtype = s->dtype;
+  d->num_pages = s->num_pages;
+  d->scale = s->softmax_scale > 0.f ? s->softmax_scale
+                                    : 1.0f / std::sqrt(static_cast<float>(s->head_dim));
+  return SD_OK;
+}
+
+sd_status check_unit(int unit) {
+  if (unit != SD_UNIT_TOKEN && unit != SD_UNIT_PAGE)
+    return fail(SD_E_SHAPE, "unit %d is neither SD_UNIT_TOKEN nor SD_UNIT_PAGE", unit);
+  return SD_OK;
+}
+
+sd_status check_ratio(double r) {
+  if (!std::isfinite(r) || r <= 0.0) return fail(SD_E_RATIO, "r_kv must be finite and > 0");
+  return SD_OK;
+}
+
+int units_max(const sdkv::Dims& d, int unit) {
+  return unit == SD_UNIT_PAGE ? d.max_pages : d.max_seq;
+}
+
+// Split plan of the attention pass for lists of up to k_max units.
+struct Split {
+  int E;  // units per split
+  int S;  // splits per (sequence, KV head)
+};
+
+Split plan_split(const sdkv::Dims& d, int unit, int64_t k_max) {
+  const int64_t bg = static_cast<int64_t>(d.B) * d.Hkv;
+  const int64_t s_target = ceil_div(kTargetBlocks, bg) < 1 ? 1 : ceil_div(kTargetBlocks, bg);
+  const int64_t tpe = unit == SD_UNIT_PAGE ? d.P : 1;
+  int64_t E = ceil_div(k_max < 1 ? 1 : k_max, s_target);
+  const int64_t e_min = ceil_div(kMinRowsPerBlock, tpe);
+  if (E < e_min) E = e_min;
+  const int64_t S = ceil_div(k_max < 1 ? 1 : k_max, E);
+  return Split{static_cast<int>(E), static_cast<int>(S)};
+}
+
+// Most splits any k_max can produce: S <= s_target.
+int64_t max_splits(const sdkv::Dims& d) {
+  const int64_t bg = static_cast<int64_t>(d.B) * d.Hkv;
+  const int64_t s = ceil_div(kTargetBlocks, bg);
+  return s < 1 ? 1 : s;
+}
+
+// Workspace regions (offsets in bytes from ws).  The attention partials come
+// first so that sd_attend_splitk and sd_decode_step agree on where they live.
+struct Layout {
+  size_t part_o, part_lse, scores, logits, sel_idx, sel_count, total;
+};
+
+Layout layout(const sdkv::Dims& d, int unit, double r_kv) {
+  Layout L{};
+  const int64_t S = max_splits(d);
+  const int64_t bh = static_cast<int64_t>(d.B) * d.Hq;
+  const int64_t bg = static_cast<int64_t>(d.B) * d.Hkv;
+  const int64_t U = units_max(d, unit);
+  const int64_t k_max = keep_count_ppm(ratio_ppm(r_kv), U);
+  size_t off = 0;
+  L.part_o = off;     off = align_up(off + sizeof(float) * bh * S * d.D);
+  L.part_lse = off;   off = align_up(off + sizeof(float) * bh * S);
+  L.scores = off;     off = align_up(off + sizeof(float) * bg * U);
+  L.logits = off;
+  if (unit == SD_UNIT_TOKEN) off = align_up(off + sizeof(float) * bh * d.max_seq);
+  L.sel_idx = off;    off = align_up(off + sizeof(int32_t) * bg * k_max);
+  L.sel_count = off;  off = align_up(off + sizeof(int32_t) * bg);
+  L.total = off;
+  return L;
+}
+
+size_t attend_ws_bytes(const sdkv::Dims& d) {
+  const int64_t S = max_splits(d);
+  const int64_t bh = static_cast<int64_t>(d.B) * d.Hq;
+  return align_up(align_up(sizeof(float) * bh * S * d.D) + sizeof(float) * bh * S);
+}
+
+sd_status check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return SD_OK;
+  if (!ws) return fail(SD_E_NULL, "workspace is NULL (%zu bytes needed)", need);
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign != 0)
+    return fail(SD_E_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
+  if (ws_bytes < need)
+    return fail(SD_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                ws_bytes, need);
+  return SD_OK;
+}
+
+sd_status device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return SD_OK;
+  return fail(SD_E_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+
+// ---- validated launches (arguments already checked) ----
+
+sd_status do_score(const sdkv::Dims& d, const void* q, const void* k_pages, const void* bounds,
+                   const int32_t* bt, const int32_t* sl, int unit, float* scores, float* logits,
+                   hipStream_t st) {
+  sdkv::ScoreArgs a{d, unit, q, k_pages, bounds, bt, sl, scores, logits};
+  return device_status(sdkv::launch_score(a, st), "score kernel launch");
+}
+
+sd_status do_select(const sdkv::Dims& d, int unit, const int32_t* sl, const float* scores,
+                    double r_kv, int32_t* sel_idx, int32_t* sel_count, hipStream_t st) {
+  const int U = units_max(d, unit);
+  const int R = ratio_ppm(r_kv);
+  sdkv::SelectArgs a{d, unit, sl, scores, U, static_cast<int>(keep_count_ppm(R, U)), R,
+                     sel_idx, sel_count};
+  return device_status(sdkv::launch_select(a, st), "select kernel launch");
+}
+
+sd_status do_attend(const sdkv::Dims& d, const void* q, const void* kp, const void* vp,
+                    const int32_t* bt, const int32_t* sl, int unit, const int32_t* sel_idx,
+                    const int32_t* sel_count, int k_max, const float* logits, float* out,
+                    float* lse, void* ws, hipStream_t st) {
+  const int64_t kk = sel_idx ? k_max : units_max(d, unit);
+  const Split sp = plan_split(d, unit, kk);
+  const int64_t bh = static_cast<int64_t>(d.B) * d.Hq;
+  float* part_o = reinterpret_cast<float*>(at(ws, 0));
+  float* part_lse =
+      reinterpret_cast<float*>(at(ws, align_up(sizeof(float) * bh * max_splits(d) * d.D)));
+  sdkv::AttendArgs a{d,       unit,      q,      kp,   vp,   bt,      sl,
+                     sel_idx, sel_count, k_max,  logits, sp.E, sp.S, part_o,
+                     part_lse, out,      lse};
+  return device_status(sdkv::launch_attend(a, st), "attention kernel launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t sd_keep_count(double r_kv, int32_t num_units) {
+  if (!std::isfinite(r_kv) || r_kv <= 0.0 || num_units < 1) return -1;
+  return static_cast<int32_t>(keep_count_ppm(ratio_ppm(r_kv), num_units));
+}
+
+sd_status sd_workspace_bytes(const sd_shape* shape, int32_t unit, double r_kv,
+                             size_t* bytes_host) {
+  sdkv::Dims d;
+  sd_status st;
+  if ((st = check_shape(shape, &d)) != SD_OK) return st;
+  if ((st = check_unit(unit)) != SD_OK) return st;
+  if ((st = check_ratio(r_kv)) != SD_OK) return st;
+  if (!bytes_host) return fail(SD_E_NULL, "bytes_host is NULL");
+  *bytes_host = layout(d, unit, r_kv).total;
+  return ok();
+}
+
+sd_status sd_update_page_bounds(const sd_shape* shape, const void* k_pages,
+                                const int32_t* block_table, const int32_t* seq_lens,
+                                void* page_bounds, void* stream) {
+  sdkv::Dims d;
+  sd_status st;
+  if ((st = check_shape(shape, &d)) != SD_OK) return st;
+  if (!k_pages || !block_table || !seq_lens || !page_bounds)
+    return fail(SD_E_NULL, "k_pages, block_table, seq_lens and page_bounds are required");
+  sdkv::BoundsArgs a{d, k_pages, block_table, seq_lens, page_bounds};
+  if ((st = device_status(sdkv::launch_page_bounds(a, static_cast<hipStream_t>(stream)),
+                          "page bounds kernel launch")) != SD_OK)
+    return st;
+  return ok();
+}
+
+sd_status sd_score_pages(const sd_shape* shape, const void* q, const void* k_pages,
+                         const void* page_bounds, const int32_t* block_table,
+                         const int32_t* seq_lens, int32_t unit, float* unit_scores,
+                         float* token_logits, void* stream) {
+  sdkv::Dims d;
+  sd_status st;
+  if ((st = check_shape(shape, &d)) != SD_OK) return st;
+  if ((st = check_unit(unit)) != SD_OK) return st;
+  if (!q || !block_table || !seq_lens || !unit_scores)
+    return fail(SD_E_NULL, "q, block_table, seq_lens and unit_scores are required");
+  if (unit == SD_UNIT_PAGE && !page_bounds)
+    return fail(SD_E_NULL, "page unit scoring reads page_bounds");
+  if (unit == SD_UNIT_TOKEN && (!k_pages || !token_logits))
+    return fail(SD_E_NULL, "token unit scoring reads k_pages and writes token_logits");
+  if ((st = do_score(d, q, k_pages, page_bounds, block_table, seq_lens, unit, unit_scores,
+                     token_logits, static_cast<hipStream_t>(stream))) != SD_OK)
+    return st;
+  return ok();
+}
+
+sd_status sd_select_topk(const sd_shape* shape, int32_t unit, const int32_t* seq_lens,
+                         const float* unit_scores, double r_kv, int32_t* sel_idx,
+                         int32_t* sel_count, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  sdkv::Dims d;
+  sd_status st;
+  if ((st = check_shape(shape, &d)) != SD_OK) return st;
+  if ((st = check_unit(unit)) != SD_OK) return st;
+  if ((st = check_ratio(r_kv)) != SD_OK) return st;
+  if (!seq_lens || !unit_scores || !sel_idx || !sel_count)
+    return fail(SD_E_NULL, "seq_lens, unit_scores, sel_idx and sel_count are required");
+  if ((st = do_select(d, unit, seq_lens, unit_scores, r_kv, sel_idx, sel_count,
+                      static_cast<hipStream_t>(stream))) != SD_OK)
+    return st;
+  return ok();
+}
+
+sd_status sd_attend_splitk(const sd_shape* shape, const void* q, const void* k_pages,
+                           const void* v_pages, const int32_t* block_table,
+                           const int32_t* seq_lens, int32_t unit, const int32_t* sel_idx,
+                           const int32_t* sel_count, int32_t k_max, const float* token_logits,
+                           float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  sdkv::Dims d;
+  sd_status st;
+  if ((st = check_shape(shape, &d)) != SD_OK) return st;
+  if ((st = check_unit(unit)) != SD_OK) return st;
+  if (!q || !v_pages || !block_table || !seq_lens || !out || !lse)
+    return fail(SD_E_NULL, "q, v_pages, block_table, seq_lens, out and lse are required");
+  if (!token_logits && !k_pages) return fail(SD_E_NULL, "k_pages is required");
+  if (token_logits && unit != SD_UNIT_TOKEN)
+    return fail(SD_E_SHAPE, "token_logits is only read in token unit");
+  if (sel_idx) {
+    if (!sel_count) return fail(SD_E_NULL, "sel_count is required with sel_idx");
+    if (k_max < 1 || k_max > units_max(d, unit))
+      return fail(SD_E_SHAPE, "k_max %d outside [1, %d]", k_max, units_max(d, unit));
+  }
+  if ((st = check_ws(ws, ws_bytes, attend_ws_bytes(d))) != SD_OK) return st;
+  if ((st = do_attend(d, q, k_pages, v_pages, block_table, seq_lens, unit, sel_idx, sel_count,
+                      k_max, token_logits, out, lse, ws, static_cast<hipStream_t>(stream))) !=
+      SD_OK)
+    return st;
+  return ok();
+}
+
+sd_status sd_decode_step(const sd_shape* shape, const void* q, const void* k_pages,
+                         const void* v_pages, const void* page_bounds,
+                         const int32_t* block_table, const int32_t* seq_lens, int32_t unit,
+                         double r_kv, float* out, float* lse, int32_t* sel_idx,
+                         int32_t* sel_count, void* ws, size_t ws_bytes, void* stream) {
+  sdkv::Dims d;
+  sd_status st;
+  if ((st = check_shape(shape, &d)) != SD_OK) return st;
+  if ((st = check_unit(unit)) != SD_OK) return st;
+  if ((st = check_ratio(r_kv)) != SD_OK) return st;
+  if (!q || !k_pages || !v_pages || !block_table || !seq_lens || !out || !lse)
+    return fail(SD_E_NULL,
+                "q, k_pages, v_pages, block_table, seq_lens, out and lse are required");
+  const bool dense = r_kv >= 1.0;
+  if (!dense && unit == SD_UNIT_PAGE && !page_bounds)
+    return fail(SD_E_NULL, "page unit selection reads page_bounds");
+  if ((sel_idx == nullptr) != (sel_count == nullptr))
+    return fail(SD_E_NULL, "sel_idx and sel_count are given together or not at all");
+  const Layout L = layout(d, unit, r_kv);
+  if ((st = check_ws(ws, ws_bytes, L.total)) != SD_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dense) {
+    st = do_attend(d, q, k_pages, v_pages, block_table, seq_lens, unit, nullptr, nullptr, 0,
+                   nullptr, out, lse, ws, s);
+    return st != SD_OK ? st : ok();
+  }
+  const int U = units_max(d, unit);
+  const int k_max = static_cast<int>(keep_count_ppm(ratio_ppm(r_kv), U));
+  float* scores = reinterpret_cast<float*>(at(ws, L.scores));
+  float* logits = unit == SD_UNIT_TOKEN ? reinterpret_cast<float*>(at(ws, L.logits)) : nullptr;
+  int32_t* idx = sel_idx ? sel_idx : reinterpret_cast<int32_t*>(at(ws, L.sel_idx));
+  int32_t* cnt = sel_count ? sel_count : reinterpret_cast<int32_t*>(at(ws, L.sel_count));
+  if ((st = do_score(d, q, k_pages, page_bounds, block_table, seq_lens, unit, scores, logits,
+                     s)) != SD_OK)
+    return st;
+  if ((st = do_select(d, unit, seq_lens, scores, r_kv, idx, cnt, s)) != SD_OK) return st;
+  if ((st = do_attend(d, q, k_pages, v_pages, block_table, seq_lens, unit, idx, cnt, k_max,
+                      logits, out, lse, ws, s)) != SD_OK)
+    return st;
+  return ok();
+}
+
+const char* sd_last_error(void) { return g_err; }
+
+}  // extern "C"

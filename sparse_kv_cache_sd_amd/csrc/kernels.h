@@ -1,0 +1,79 @@
+// Internal interface between the C ABI (abi.cpp) and the HIP kernels.
+// Not installed; the public interface is include/sd.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdkv {
+
+enum Unit : int { kToken = 0, kPage = 1 };
+enum DType : int { kF32 = 0, kBF16 = 1 };
+
+// Problem sizes shared by every launch.
+struct Dims {
+  int B, Hq, Hkv, G, D, P;
+  int max_pages, max_seq;
+  int dtype;
+  int64_t num_pages;
+  float scale;  // softmax scale on q.K (natural-log domain)
+};
+
+struct BoundsArgs {
+  Dims d;
+  const void* k_pages;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  void* bounds;
+};
+
+struct ScoreArgs {
+  Dims d;
+  int unit;
+  const void* q;
+  const void* k_pages;
+  const void* bounds;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  float* unit_scores;   // [B][Hkv][U_max]
+  float* token_logits;  // [B][Hq][max_seq] (token unit)
+};
+
+struct SelectArgs {
+  Dims d;
+  int unit;
+  const int32_t* seq_lens;
+  const float* unit_scores;  // [B][Hkv][U_max]
+  int U_max;
+  int k_max;
+  int R_ppm;  // keep ratio in parts per million; < 0 keeps every unit
+  int32_t* sel_idx;    // [B][Hkv][k_max]
+  int32_t* sel_count;  // [B][Hkv]
+};
+
+struct AttendArgs {
+  Dims d;
+  int unit;
+  const void* q;
+  const void* k_pages;
+  const void* v_pages;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const int32_t* sel_idx;    // NULL: every unit
+  const int32_t* sel_count;
+  int k_max;
+  const float* token_logits;  // token unit: read logits instead of q.K
+  int E;                      // kept units per split
+  int S;                      // splits per (sequence, KV head)
+  float* part_o;              // [B][Hq][S][D]  split outputs, normalised
+  float* part_lse;            // [B][Hq][S]     split log-sum-exp (-inf: empty)
+  float* out;                 // [B][Hq][D]
+  float* lse;                 // [B][Hq]
+};
+
+hipError_t launch_page_bounds(const BoundsArgs& a, hipStream_t st);
+hipError_t launch_score(const ScoreArgs& a, hipStream_t st);
+hipError_t launch_select(const SelectArgs& a, hipStream_t st);
+hipError_t launch_attend(const AttendArgs& a, hipStream_t st);
+
+}  // namespace sdkv

@@ -1,0 +1,144 @@
+"""Helpers for the GPU parity tests: upload a kvsynth workload and compare the
+HIP path with the oracle under the stated rules.
+
+Comparison rules
+* integer and index outputs: bit-exact;
+* a selection instance (sequence b, KV head g) whose oracle score gap at the
+  k-th unit exceeds 1e-4 must select exactly the oracle's set; otherwise
+  every kept unit must score >= sigma_(k) - 1e-4 and every dropped unit
+  <= sigma_(k) + 1e-4, and the outputs are compared with the oracle rerun
+  on the GPU's own set;
+* outputs and lse: max-abs <= 1e-5 for fp32 data, <= 2e-2 for bf16 data;
+* scores: within the fp32 rounding bound (d + 4) * 2^-24 * scale * sum_c |q_c x_c|
+  of a d-term dot product accumulated in fp32.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+import kvsynth
+import sparse_kv_cache_sd_amd as sd
+from oracle import sdref
+
+GAP = 1e-4
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+
+
+def t_dev(a: np.ndarray, dtype: str) -> torch.Tensor:
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def host_f64(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        bits = t.cpu().view(torch.int16).numpy().view(np.uint16)
+        return sdref.widen(bits, "bf16")
+    return t.cpu().double().numpy()
+
+
+@dataclass
+class Dev:
+    w: kvsynth.Workload
+    shape: sd.Shape
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    bt: torch.Tensor
+    sl: torch.Tensor
+    bounds: torch.Tensor
+
+
+def upload(w: kvsynth.Workload, softmax_scale: float = 0.0) -> Dev:
+    r = w.recipe
+    pc = w.paged()
+    shape = sd.Shape(r.batch, r.num_q_heads, r.num_kv_heads, r.head_dim, r.page_size,
+                     w.max_pages(), w.n_alloc, r.dtype, pc.num_pages, softmax_scale)
+    dt = torch.float32 if r.dtype == "f32" else torch.bfloat16
+    bounds = torch.zeros((pc.num_pages, r.num_kv_heads, 2, r.head_dim), dtype=dt, device="cuda")
+    dev = Dev(w, shape, t_dev(w.q, r.dtype), t_dev(pc.k_pool, r.dtype), t_dev(pc.v_pool, r.dtype),
+              torch.from_numpy(pc.block_table).cuda(), torch.from_numpy(w.seq_lens).cuda(), bounds)
+    sd.update_page_bounds(shape, dev.k, dev.bt, dev.sl, dev.bounds)
+    return dev
+
+
+def run_decode(dev: Dev, unit: str, r_kv: float):
+    s = dev.shape
+    ws = sd.alloc_workspace(s, unit, r_kv)
+    out = torch.empty((s.batch, s.num_q_heads, s.head_dim), dtype=torch.float32, device="cuda")
+    lse = torch.empty((s.batch, s.num_q_heads), dtype=torch.float32, device="cuda")
+    sel = cnt = None
+    if r_kv < 1.0:
+        k_max = sd.keep_count(r_kv, s.units_max(unit))
+        sel = torch.full((s.batch, s.num_kv_heads, k_max), -7, dtype=torch.int32, device="cuda")
+        cnt = torch.full((s.batch, s.num_kv_heads), -7, dtype=torch.int32, device="cuda")
+    sd.decode_step(s, dev.q, dev.k, dev.v, dev.bounds, dev.bt, dev.sl, unit, r_kv, out, lse, ws,
+                   sel_idx=sel, sel_count=cnt)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lse.cpu().numpy(), (None if sel is None else sel.cpu().numpy()), \
+        (None if cnt is None else cnt.cpu().numpy())
+
+
+def oracle_group(w: kvsynth.Workload, b: int, g: int, unit: str, r_kv: float, scale: float,
+                 kept_override=None):
+    r = w.recipe
+    G = r.group
+    n = int(w.seq_lens[b])
+    qg = sdref.widen(w.q[b, g * G:(g + 1) * G], r.dtype)
+    Kg = sdref.widen(w.K[b, g, :n], r.dtype)
+    Vg = sdref.widen(w.V[b, g, :n], r.dtype)
+    return sdref.group_step(qg, Kg, Vg, unit=unit, page_size=r.page_size, r_kv=r_kv,
+                            scale=scale, kept_override=kept_override)
+
+
+def check_selection(gpu_kept: np.ndarray, orc: sdref.GroupResult) -> bool:
+    """Returns True when the sets must be (and are) identical; False when the
+    gap rule allowed a different valid set (asserted valid here)."""
+    if orc.gap > GAP:
+        np.testing.assert_array_equal(gpu_kept, orc.kept)
+        return True
+    k = orc.k
+    assert gpu_kept.size == k and np.all(np.diff(gpu_kept) > 0)
+    kth = np.sort(orc.sigma)[::-1][k - 1]
+    dropped = np.setdiff1d(np.arange(orc.sigma.size), gpu_kept)
+    assert np.all(orc.sigma[gpu_kept] >= kth - GAP)
+    assert np.all(orc.sigma[dropped] <= kth + GAP)
+    return False
+
+
+def compare_step(dev: Dev, unit: str, r_kv: float, groups=None, report=None):
+    """Run the whole decode step on the GPU and compare every (b, g) in
+    ``groups`` (default all) with the oracle.  Returns the max errors."""
+    w, s = dev.w, dev.shape
+    scale = 1.0 / math.sqrt(s.head_dim) if s.softmax_scale <= 0 else s.softmax_scale
+    out, lse, sel, cnt = run_decode(dev, unit, r_kv)
+    G, tol = s.group, TOL[s.dtype]
+    if groups is None:
+        groups = [(b, g) for b in range(s.batch) for g in range(s.num_kv_heads)]
+    err_o = err_l = 0.0
+    for b, g in groups:
+        orc = oracle_group(w, b, g, unit, r_kv, scale)
+        heads = slice(g * G, (g + 1) * G)
+        if r_kv >= 1.0:
+            ref_o, ref_l = orc.out_dense, orc.lse_dense
+        else:
+            assert int(cnt[b, g]) == orc.k
+            kept = sel[b, g, :orc.k].astype(np.int64)
+            if check_selection(kept, orc):
+                ref_o, ref_l = orc.out_sparse, orc.lse_sparse
+            else:
+                o2 = oracle_group(w, b, g, unit, r_kv, scale, kept_override=kept)
+                ref_o, ref_l = o2.out_sparse, o2.lse_sparse
+        e_o = float(np.abs(out[b, heads] - ref_o).max())
+        e_l = float(np.abs(lse[b, heads] - ref_l).max())
+        assert e_o <= tol, f"(b={b}, g={g}) out max-abs {e_o} > {tol}"
+        assert e_l <= tol, f"(b={b}, g={g}) lse max-abs {e_l} > {tol}"
+        err_o, err_l = max(err_o, e_o), max(err_l, e_l)
+    if report is not None:
+        report.append((unit, r_kv, err_o, err_l))
+    return err_o, err_l

@@ -1,0 +1,254 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle on
+seeded kvsynth inputs (reduced sizes spanning several tiles and ragged tails,
+plus edge cases).  Full-size configurations are in test_gpu_fullsize.py."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import kvsynth
+import sparse_kv_cache_sd_amd as sd
+from oracle import sdref
+
+from gpu_util import GAP, compare_step, host_f64, oracle_group, t_dev, upload
+
+pytestmark = pytest.mark.gpu
+
+R = kvsynth.RECIPES
+
+
+def _recipe(name, **kw):
+    return R[name].with_(**kw)
+
+
+# ------------------------------------------------------------- page bounds (setup)
+
+@pytest.mark.parametrize("name,kw", [
+    ("l8b", dict(seq_len=1000, num_q_heads=8, num_kv_heads=2)),
+    ("batch", dict(batch=3, seq_len=900, seq_len_min=1, num_q_heads=8, num_kv_heads=2)),
+    ("l70b", dict(seq_len=64 * 7 + 3, num_q_heads=16, num_kv_heads=2)),
+    ("tiny", dict(seq_len=333)),
+])
+def test_page_bounds_bitexact(name, kw):
+    dev = upload(kvsynth.generate(_recipe(name, **kw)))
+    w, s = dev.w, dev.shape
+    got = host_f64(dev.bounds)
+    for b in range(s.batch):
+        n = int(w.seq_lens[b])
+        for g in range(s.num_kv_heads):
+            kmin, kmax = sdref.page_bounds(sdref.widen(w.K[b, g, :n], s.dtype), s.page_size)
+            ids = dev.bt[b, :kmin.shape[0]].cpu().numpy()
+            np.testing.assert_array_equal(got[ids, g, 0], kmin)
+            np.testing.assert_array_equal(got[ids, g, 1], kmax)
+
+
+# ------------------------------------------------------------- scores
+
+def _score_tol(qg, X, scale, d):
+    """(d + 4) u scale sum_c |q_c x_c|, maximised over the group's heads."""
+    return (d + 4) * 2.0 ** -24 * scale * (np.abs(qg) @ np.abs(X).T).max(axis=0)
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("l8b", dict(seq_len=5000, num_q_heads=16, num_kv_heads=4)),
+    ("l70b", dict(seq_len=64 * 40 + 17)),
+    ("tiny", dict(unit="page")),
+])
+def test_page_scores(name, kw):
+    dev = upload(kvsynth.generate(_recipe(name, **kw)))
+    w, s = dev.w, dev.shape
+    scores = torch.full((s.batch, s.num_kv_heads, s.max_pages_per_seq), float("nan"), device="cuda")
+    sd.score_pages(s, dev.q, dev.k, dev.bounds, dev.bt, dev.sl, "page", scores)
+    got = scores.cpu().double().numpy()
+    scale = 1 / math.sqrt(s.head_dim)
+    G = s.group
+    for b in range(s.batch):
+        n = int(w.seq_lens[b])
+        for g in range(s.num_kv_heads):
+            qg = sdref.widen(w.q[b, g * G:(g + 1) * G], s.dtype)
+            kmin, kmax = sdref.page_bounds(sdref.widen(w.K[b, g, :n], s.dtype), s.page_size)
+            ref = sdref.page_scores(qg, kmin, kmax, scale)
+            tol = _score_tol(qg, np.maximum(np.abs(kmin), np.abs(kmax)), scale, s.head_dim)
+            assert np.all(np.abs(got[b, g, :ref.size] - ref) <= tol)
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("tiny", dict()),
+    ("sweep", dict(seq_len=3000, num_q_heads=16, num_kv_heads=4)),
+    ("l70b", dict(seq_len=64 * 20 + 5, unit="token")),
+])
+def test_token_scores_and_logits(name, kw):
+    dev = upload(kvsynth.generate(_recipe(name, **kw)))
+    w, s = dev.w, dev.shape
+    scores = torch.full((s.batch, s.num_kv_heads, s.max_seq_len), float("nan"), device="cuda")
+    logits = torch.full((s.batch, s.num_q_heads, s.max_seq_len), float("nan"), device="cuda")
+    sd.score_pages(s, dev.q, dev.k, None, dev.bt, dev.sl, "token", scores, logits)
+    got_s = scores.cpu().double().numpy()
+    got_l = logits.cpu().double().numpy()
+    scale = 1 / math.sqrt(s.head_dim)
+    G = s.group
+    for b in range(s.batch):
+        n = int(w.seq_lens[b])
+        for g in range(s.num_kv_heads):
+            qg = sdref.widen(w.q[b, g * G:(g + 1) * G], s.dtype)
+            Kg = sdref.widen(w.K[b, g, :n], s.dtype)
+            lg = sdref.group_logits(qg, Kg, scale)
+            tol_h = (s.head_dim + 4) * 2.0 ** -24 * scale * (np.abs(qg) @ np.abs(Kg).T)
+            assert np.all(np.abs(got_l[b, g * G:(g + 1) * G, :n] - lg) <= tol_h)
+            ref_s = sdref.token_scores(lg)
+            assert np.all(np.abs(got_s[b, g, :n] - ref_s) <= tol_h.max(axis=0))
+
+
+# ------------------------------------------------------------- top-k
+
+def _select_case(scores_np, seq_lens, unit, r_kv, shape):
+    s = shape
+    scores = torch.from_numpy(scores_np.astype(np.float32)).cuda()
+    umax = s.units_max(unit)
+    k_max = sd.keep_count(r_kv, umax)
+    sel = torch.full((s.batch, s.num_kv_heads, k_max), -1, dtype=torch.int32, device="cuda")
+    cnt = torch.full((s.batch, s.num_kv_heads), -1, dtype=torch.int32, device="cuda")
+    sd.select_topk(s, unit, torch.from_numpy(seq_lens).cuda(), scores, r_kv, sel, cnt)
+    torch.cuda.synchronize()
+    sel, cnt = sel.cpu().numpy(), cnt.cpu().numpy()
+    for b in range(s.batch):
+        n = int(seq_lens[b])
+        U = sdref.num_units(n, unit, s.page_size)
+        for g in range(s.num_kv_heads):
+            k = sdref.keep_count(r_kv, U)
+            assert cnt[b, g] == k
+            kept, _ = sdref.select_topk(sdref.widen(scores_np[b, g, :U].astype(np.float32), "f32"), k)
+            np.testing.assert_array_equal(sel[b, g, :k], kept)
+
+
+@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("U,unit,r", [(2048, "page", 0.3), (2048, "page", 0.05), (16384, "page", 0.05),
+                                      (1024, "token", 0.25), (131072, "token", 0.2), (37, "page", 0.5),
+                                      (5000, "token", 0.9999)])
+def test_select_bitexact_with_ties(seed, U, unit, r):
+    rng = np.random.default_rng(seed)
+    P = 16
+    shape = sd.Shape(2, 8, 2, 128, P, -(-U // P) if unit == "token" else U,
+                     U if unit == "token" else U * P, "bf16", 1)
+    umax = shape.units_max(unit)
+    if seed % 2 == 0:
+        sc = rng.integers(-6, 7, size=(2, 2, umax)).astype(np.float32) * 0.5   # heavy ties
+        sc[rng.random(sc.shape) < 0.1] = -0.0
+    else:
+        sc = rng.standard_normal((2, 2, umax)).astype(np.float32)
+    # sequence 1 is ragged: fewer units than the maximum
+    n1 = max(1, (umax * 3) // 5) * (P if unit == "page" else 1)
+    seq_lens = np.array([shape.max_seq_len, n1], dtype=np.int32)
+    _select_case(sc, seq_lens, unit, r, shape)
+
+
+# ------------------------------------------------------------- attention over a given set
+
+@pytest.mark.parametrize("name,kw,unit,r", [
+    ("tiny", dict(), "token", 0.25),
+    ("l8b", dict(seq_len=4000, num_q_heads=16, num_kv_heads=4), "page", 0.3),
+    ("l70b", dict(seq_len=64 * 33 + 9), "page", 0.05),
+])
+def test_attend_on_oracle_selection(name, kw, unit, r):
+    """a4 + a5 in isolation: the oracle's kept set is uploaded and attended."""
+    w = kvsynth.generate(_recipe(name, **kw))
+    dev = upload(w)
+    s = dev.shape
+    scale = 1 / math.sqrt(s.head_dim)
+    orcs = {(b, g): oracle_group(w, b, g, unit, r, scale)
+            for b in range(s.batch) for g in range(s.num_kv_heads)}
+    k_max = sd.keep_count(r, s.units_max(unit))
+    sel = np.zeros((s.batch, s.num_kv_heads, k_max), dtype=np.int32)
+    cnt = np.zeros((s.batch, s.num_kv_heads), dtype=np.int32)
+    for (b, g), o in orcs.items():
+        sel[b, g, :o.k] = o.kept
+        cnt[b, g] = o.k
+    out = torch.empty((s.batch, s.num_q_heads, s.head_dim), device="cuda")
+    lse = torch.empty((s.batch, s.num_q_heads), device="cuda")
+    ws = sd.alloc_workspace(s, unit, 1.0)
+    sd.attend_splitk(s, dev.q, dev.k, dev.v, dev.bt, dev.sl, unit, torch.from_numpy(sel).cuda(),
+                     torch.from_numpy(cnt).cuda(), out, lse, ws)
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    G = s.group
+    tol = 1e-5 if s.dtype == "f32" else 2e-2
+    for (b, g), o in orcs.items():
+        assert np.abs(out[b, g * G:(g + 1) * G] - o.out_sparse).max() <= tol
+        assert np.abs(lse[b, g * G:(g + 1) * G] - o.lse_sparse).max() <= tol
+
+
+# ------------------------------------------------------------- whole step
+
+STEP_CASES = [
+    ("tiny", dict(), "token", 0.25),
+    ("tiny", dict(), "token", 1.0),
+    ("tiny", dict(unit="page"), "page", 0.25),
+    ("l8b", dict(seq_len=4096 + 7, num_q_heads=32, num_kv_heads=8), "page", 0.3),
+    ("l8b", dict(seq_len=4096 + 7, num_q_heads=32, num_kv_heads=8), "page", 1.0),
+    ("sweep", dict(seq_len=2048 + 100), "token", 0.3),
+    ("sweep", dict(seq_len=2048 + 100), "token", 0.2),
+    ("sweep", dict(seq_len=2048 + 100), "token", 1.0),
+    ("batch", dict(batch=4, seq_len=3000, seq_len_min=100), "page", 0.2),
+    ("batch", dict(batch=4, seq_len=3000, seq_len_min=100), "token", 0.2),
+    ("l70b", dict(seq_len=64 * 50 + 31), "page", 0.05),
+    ("l70b", dict(seq_len=64 * 50 + 31), "page", 1.0),
+]
+
+
+@pytest.mark.parametrize("name,kw,unit,r", STEP_CASES,
+                         ids=[f"{c[0]}-{c[2]}-{c[3]}-{i}" for i, c in enumerate(STEP_CASES)])
+def test_decode_step(name, kw, unit, r):
+    dev = upload(kvsynth.generate(_recipe(name, **kw)))
+    compare_step(dev, unit, r)
+
+
+@pytest.mark.parametrize("G,d,dtype", [(1, 128, "bf16"), (2, 64, "bf16"), (8, 64, "f32"),
+                                       (4, 64, "bf16"), (1, 64, "f32")])
+def test_group_and_head_dim_variants(G, d, dtype):
+    rec = R["batch"].with_(batch=2, seq_len=1500, seq_len_min=700, num_kv_heads=2,
+                           num_q_heads=2 * G, head_dim=d, dtype=dtype)
+    dev = upload(kvsynth.generate(rec))
+    for unit, r in [("page", 0.3), ("token", 0.3), ("page", 1.0)]:
+        compare_step(dev, unit, r)
+
+
+@pytest.mark.parametrize("n", [1, 2, 15, 16, 17, 63, 64, 65])
+@pytest.mark.parametrize("P", [16, 64])
+def test_short_and_ragged_lengths(n, P):
+    rec = R["l8b"].with_(seq_len=n, page_size=P, num_q_heads=8, num_kv_heads=2)
+    dev = upload(kvsynth.generate(rec))
+    for unit, r in [("page", 0.3), ("token", 0.3), ("page", 1.0), ("token", 0.01)]:
+        compare_step(dev, unit, r)
+
+
+def test_custom_softmax_scale():
+    rec = R["l8b"].with_(seq_len=700, num_q_heads=8, num_kv_heads=2)
+    dev = upload(kvsynth.generate(rec), softmax_scale=0.03)
+    compare_step(dev, "page", 0.3)
+    compare_step(dev, "token", 0.3)
+
+
+def test_empty_sequence_gives_zero_and_neg_inf():
+    rec = R["batch"].with_(batch=2, seq_len=300, seq_len_min=300, num_q_heads=8, num_kv_heads=2)
+    dev = upload(kvsynth.generate(rec))
+    dev.sl[1] = 0
+    s = dev.shape
+    for unit, r in [("page", 0.3), ("token", 0.3), ("page", 1.0)]:
+        ws = sd.alloc_workspace(s, unit, r)
+        out = torch.full((s.batch, s.num_q_heads, s.head_dim), 5.0, device="cuda")
+        lse = torch.full((s.batch, s.num_q_heads), 5.0, device="cuda")
+        sd.decode_step(s, dev.q, dev.k, dev.v, dev.bounds, dev.bt, dev.sl, unit, r, out, lse, ws)
+        torch.cuda.synchronize()
+        assert torch.all(out[1] == 0) and torch.all(torch.isneginf(lse[1]))
+        assert torch.all(torch.isfinite(out[0])) and torch.all(torch.isfinite(lse[0]))
+
+
+def test_deterministic_repeat():
+    rec = R["l8b"].with_(seq_len=5000, num_q_heads=16, num_kv_heads=4)
+    dev = upload(kvsynth.generate(rec))
+    from gpu_util import run_decode
+    a = run_decode(dev, "page", 0.3)
+    b = run_decode(dev, "page", 0.3)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
