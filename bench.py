@@ -1,0 +1,362 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload l8b]
+
+A step is one decode step of one attention layer: page-bound (or exact)
+scoring, top-k selection under r_KV and split-K attention over the kept
+units, merged by log-sum-exp.  Steps cycle over L distinct layer caches whose
+total size is at least 4x the 256 MB Infinity Cache, so the KV bytes come from
+HBM; the L-layer loop is captured in a HIP graph and replayed.  Inputs are
+resident in HBM before timing starts.
+
+Prints ONE JSON line: the metric (microseconds per decode-step-layer, lower
+is better), effective HBM GB/s on the algorithmic bytes, the roofline of the
+dominant kernel (the split-K attention kernel, timed alone with HIP events on
+its stream), the same-kernel dense step for comparison, and the fp64 CPU
+oracle timed on a bounded sample on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+MALL_BYTES = 256 * 2 ** 20      # Infinity Cache
+METRIC = "µs per decode-step-layer + effective HBM GB/s (% roofline) at 32K–1M, r_KV"
+
+WORKLOADS = {
+    # name: (recipe name, overrides, unit, r_kv, description)
+    "l8b": ("l8b", {}, "page", 0.3,
+            "Llama-3.1-8B-shaped layer, batch 1, 32 q / 8 kv heads, d 128, bf16 paged KV "
+            "(page 16), 32K context, page-bound top-k r_KV=0.3, split-K over kept pages"),
+    "sweep128k-0.3": ("sweep", {"seq_len": 131072, "seed": 7}, "token", 0.3,
+                      "8B-shaped, batch 1, 128K, exact q.K token top-k r_KV=0.3"),
+    "sweep128k-0.2": ("sweep", {"seq_len": 131072, "seed": 7}, "token", 0.2,
+                      "8B-shaped, batch 1, 128K, exact q.K token top-k r_KV=0.2"),
+    "sweep32k-0.2": ("sweep", {"seq_len": 32768, "seed": 5}, "token", 0.2,
+                     "8B-shaped, batch 1, 32K, exact q.K token top-k r_KV=0.2"),
+    "batch": ("batch", {}, "page", 0.2,
+              "16 sequences x U(48K,64K) context, 8B-shaped, page-bound top-k r_KV=0.2"),
+    "l70b-128k": ("l70b", {"seq_len": 131072, "seed": 5}, "page", 0.05,
+                  "Llama-3.1-70B-shaped layer on one GPU, 64 q / 8 kv heads, page 64, 128K, "
+                  "page-bound top-k r_KV=0.05"),
+    "l70b-1m": ("l70b", {"seq_len": 1048576, "seed": 6}, "page", 0.05,
+                "Llama-3.1-70B-shaped layer on one GPU, page 64, 1M context, r_KV=0.05"),
+}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------
+# algorithmic byte model (what the method must move per decode-step-layer)
+# ----------------------------------------------------------------------------
+
+def algorithmic_bytes(seq_lens, H_q, H_kv, d, P, elem, unit, r_kv, kept_tokens):
+    """Bytes per decode-step-layer.
+
+    dense:  every valid K and V row once.
+    page:   the page bounds of every page (2 d elements) + K and V of the kept
+            pages' valid tokens.
+    token:  every valid K row (scoring) + V of the kept tokens.
+    Plus q (read) and out/lse (written, fp32) in every mode.
+    kept_tokens: total valid tokens covered by the kept units over all (b, g).
+    """
+    qo = len(seq_lens) * H_q * (d * elem + d * 4 + 4)
+    n_tot = int(np.sum(seq_lens))
+    if r_kv >= 1.0:
+        return H_kv * n_tot * 2 * d * elem + qo
+    if unit == "page":
+        U_tot = int(np.sum([-(-int(n) // P) for n in seq_lens]))
+        return H_kv * U_tot * 2 * d * elem + kept_tokens * 2 * d * elem + qo
+    return H_kv * n_tot * d * elem + kept_tokens * d * elem + qo
+
+
+def attend_bytes(kept_tokens, d, elem, token_unit):
+    """Algorithmic bytes of one attention-kernel launch: K and V rows of the
+    kept tokens (V only in token unit, where logits are reused); the unit
+    scores and q / out are below 0.2% of it and left out."""
+    return kept_tokens * (1 if token_unit else 2) * d * elem
+
+
+def kept_token_count(sel, cnt, seq_lens, unit, P):
+    total = 0
+    for b in range(sel.shape[0]):
+        n = int(seq_lens[b])
+        for g in range(sel.shape[1]):
+            ids = sel[b, g, :cnt[b, g]]
+            if unit == "page":
+                total += int(np.sum(np.minimum(P, n - ids.astype(np.int64) * P)))
+            else:
+                total += ids.size
+    return total
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the oracle, as it stands, on a bounded sample
+# ----------------------------------------------------------------------------
+
+def cpu_baseline(w, unit, r_kv, budget_s=12.0):
+    from oracle import sdref
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    r = w.recipe
+    G = r.group
+    scale = 1.0 / math.sqrt(r.head_dim)
+    groups = [(b, g) for b in range(r.batch) for g in range(r.num_kv_heads)]
+    t0 = time.perf_counter()
+    done = 0
+    while True:
+        b, g = groups[done % len(groups)]
+        n = int(w.seq_lens[b])
+        qg = sdref.widen(w.q[b, g * G:(g + 1) * G], r.dtype)
+        Kg = sdref.widen(w.K[b, g, :n], r.dtype)
+        Vg = sdref.widen(w.V[b, g, :n], r.dtype)
+        sdref.group_step(qg, Kg, Vg, unit=unit, page_size=r.page_size, r_kv=r_kv, scale=scale)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or done >= 4 * len(groups):
+            break
+    per_group = el / done
+    us_per_step = per_group * len(groups) * 1e6
+    return {"value": round(us_per_step, 1), "unit": "us/step-layer", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{done} of the step's {len(groups)} (sequence, KV head) selection "
+                      f"instances of layer 0 run through oracle.sdref.group_step (fp64 numpy: "
+                      f"page bounds, scores, top-k, dense + sparse attention, delta) in "
+                      f"{el:.1f} s; value = mean time per instance x {len(groups)}"}
+
+
+# ----------------------------------------------------------------------------
+# main
+# ----------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=800, help="decode-step-layers timed")
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default="l8b", choices=sorted(WORKLOADS))
+    ap.add_argument("--layers", type=int, default=0, help="distinct layer caches (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this decode-attention path has no multi-GPU "
+              "mode (see DESIGN.md for how it would shard); use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import kvsynth
+    import sparse_kv_cache_sd_amd as sd
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    sd.lib()  # fail loudly if the HIP library is missing
+
+    rname, over, unit, r_kv, desc = WORKLOADS[args.workload]
+    rec = kvsynth.RECIPES[rname].with_(**over)
+    P, d, H_q, H_kv = rec.page_size, rec.head_dim, rec.num_q_heads, rec.num_kv_heads
+    elem = 2 if rec.dtype == "bf16" else 4
+
+    # ---- layer caches
+    w0 = kvsynth.generate(rec)
+    dense_layer = H_kv * int(np.sum(w0.seq_lens)) * 2 * d * elem
+    L = args.layers or max(1, math.ceil(4 * MALL_BYTES / dense_layer))
+    L = min(L, 16)
+    log(f"workload {args.workload}: {desc}; {L} layer caches of {dense_layer / 1e6:.1f} MB")
+    dt = torch.bfloat16 if rec.dtype == "bf16" else torch.float32
+
+    def dev(a):
+        if rec.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    # Every layer has its own K/V pool and query; the sequences' block table
+    # and lengths are shared by all layers, as in a serving engine.
+    layers = []
+    bt_host = None
+    for i in range(L):
+        w = w0 if i == 0 else kvsynth.generate(rec.with_(seed=rec.seed + 100 * i),
+                                               seq_lens=w0.seq_lens)
+        pc = w.paged(block_table=bt_host)
+        if bt_host is None:
+            bt_host = pc.block_table
+            bt_dev = torch.from_numpy(bt_host).cuda()
+            sl_dev = torch.from_numpy(w0.seq_lens).cuda()
+        lay = dict(q=dev(w.q), k=dev(pc.k_pool), v=dev(pc.v_pool), bt=bt_dev, sl=sl_dev,
+                   num_pages=pc.num_pages)
+        del pc
+        if i > 0:
+            del w
+        layers.append(lay)
+        log(f"layer {i} resident")
+    num_pages = layers[0]["num_pages"]
+    shape = sd.Shape(rec.batch, H_q, H_kv, d, P, w0.max_pages(), w0.n_alloc, rec.dtype, num_pages)
+    for lay in layers:
+        lay["bounds"] = torch.empty(sd.bounds_shape(shape), dtype=dt, device="cuda")
+        sd.update_page_bounds(shape, lay["k"], lay["bt"], lay["sl"], lay["bounds"])
+    torch.cuda.synchronize()
+
+    k_max = sd.keep_count(r_kv, shape.units_max(unit))
+    ws = sd.alloc_workspace(shape, unit, r_kv)
+    ws_dense = sd.alloc_workspace(shape, unit, 1.0)
+    out = torch.empty((rec.batch, H_q, d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((rec.batch, H_q), dtype=torch.float32, device="cuda")
+    sels = [torch.empty((rec.batch, H_kv, k_max), dtype=torch.int32, device="cuda") for _ in range(L)]
+    cnts = [torch.empty((rec.batch, H_kv), dtype=torch.int32, device="cuda") for _ in range(L)]
+    stream = torch.cuda.Stream()
+
+    def sparse_step(i):
+        lay = layers[i]
+        sd.decode_step(shape, lay["q"], lay["k"], lay["v"], lay["bounds"], lay["bt"], lay["sl"],
+                       unit, r_kv, out, lse, ws, sels[i], cnts[i], stream=stream)
+
+    def dense_step(i):
+        lay = layers[i]
+        sd.decode_step(shape, lay["q"], lay["k"], lay["v"], lay["bounds"], lay["bt"], lay["sl"],
+                       unit, 1.0, out, lse, ws_dense, stream=stream)
+
+    # scores of every layer, for timing the attention stage on its own
+    umax = shape.units_max(unit)
+    scores = [torch.empty((rec.batch, H_kv, umax), dtype=torch.float32, device="cuda")
+              for _ in range(L)]
+    logits = [torch.empty((rec.batch, H_q, shape.max_seq_len), dtype=torch.float32, device="cuda")
+              if unit == "token" else None for _ in range(L)]
+    for i, lay in enumerate(layers):
+        sd.score_pages(shape, lay["q"], lay["k"], lay["bounds"], lay["bt"], lay["sl"], unit,
+                       scores[i], logits[i], stream=stream)
+    torch.cuda.synchronize()
+
+    def attend_only(i):
+        """The split-K attention kernel alone (one launch), as the decode step
+        runs it: page unit selects inside the attention kernel; token unit
+        attends the stored selection with the stored logits."""
+        lay = layers[i]
+        if unit == "page":
+            sd.attend_partials(shape, lay["q"], lay["k"], lay["v"], lay["bt"], lay["sl"], unit, ws,
+                               unit_scores=scores[i], r_kv=r_kv, stream=stream)
+        else:
+            sd.attend_partials(shape, lay["q"], lay["k"], lay["v"], lay["bt"], lay["sl"], unit, ws,
+                               sel_idx=sels[i], sel_count=cnts[i], token_logits=logits[i],
+                               stream=stream)
+
+    def timed(fn, steps, warmup, graph):
+        """Mean microseconds per call of fn(layer) over `steps` calls cycling layers."""
+        with torch.cuda.stream(stream):
+            for i in range(warmup):
+                fn(i % L)
+            torch.cuda.synchronize()
+            reps = max(1, steps // L)
+            if graph:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    for i in range(L):
+                        fn(i)
+                g.replay()
+                torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(reps):
+                if graph:
+                    g.replay()
+                else:
+                    for i in range(L):
+                        fn(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / (reps * L), reps * L
+
+    graph = not args.no_graph
+    # warm selections so attend_only has valid inputs
+    with torch.cuda.stream(stream):
+        for i in range(L):
+            sparse_step(i)
+    torch.cuda.synchronize()
+
+    us_sparse, n_steps = timed(sparse_step, args.steps, args.warmup, graph)
+    log(f"sparse step: {us_sparse:.2f} us/step-layer over {n_steps} steps ({'graph' if graph else 'eager'})")
+    us_dense, _ = timed(dense_step, args.steps, args.warmup, graph)
+    log(f"dense step:  {us_dense:.2f} us/step-layer")
+    us_attend, n_att = timed(attend_only, args.steps, args.warmup, graph)
+    log(f"attend alone (HIP events on its stream): {us_attend:.2f} us/launch")
+    us_sparse_eager, _ = timed(sparse_step, min(args.steps, 400), 10, False)
+    log(f"sparse step eager: {us_sparse_eager:.2f} us/step-layer")
+
+    # bytes from the actual selections
+    kept = []
+    for i in range(L):
+        kept.append(kept_token_count(sels[i].cpu().numpy(), cnts[i].cpu().numpy(),
+                                     w0.seq_lens, unit, P))
+    kept_mean = float(np.mean(kept))
+    b_sparse = algorithmic_bytes(w0.seq_lens, H_q, H_kv, d, P, elem, unit, r_kv, kept_mean)
+    b_dense = algorithmic_bytes(w0.seq_lens, H_q, H_kv, d, P, elem, unit, 1.0, 0)
+    b_attend = attend_bytes(kept_mean, d, elem, unit == "token")
+    gbps = b_sparse / (us_sparse * 1e-6) / 1e9
+    gbps_dense = b_dense / (us_dense * 1e-6) / 1e9
+    gbps_att = b_attend / (us_attend * 1e-6) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(us_sparse, 3),
+        "unit": "us/step-layer",
+        "n_gpus": 1,
+        "steps": n_steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us_sparse / 1e3, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": rec.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": desc,
+            "batch": rec.batch, "num_q_heads": H_q, "num_kv_heads": H_kv, "head_dim": d,
+            "page_size": P, "context": int(w0.seq_lens.max()), "unit": unit, "r_kv": r_kv,
+            "k_per_kv_head": k_max, "layer_caches": L, "timing": "hip-graph" if graph else "eager",
+        },
+        "effective_gbps": round(gbps, 1),
+        "pct_hbm_roofline": round(100 * gbps / HBM_PEAK_GBPS, 1),
+        "algorithmic_bytes_per_step": int(b_sparse),
+        "dense": {"us_per_step_layer": round(us_dense, 3), "effective_gbps": round(gbps_dense, 1),
+                  "pct_hbm_roofline": round(100 * gbps_dense / HBM_PEAK_GBPS, 1),
+                  "bytes_per_step": int(b_dense)},
+        "speedup_vs_dense": round(us_dense / us_sparse, 3),
+        "byte_bound_speedup": round(b_dense / b_sparse, 3),
+        "eager_us_per_step_layer": round(us_sparse_eager, 3),
+        "roofline": {
+            "kernel": ("attend_mfma_kernel: in-kernel top-k + split-K attention partials over "
+                       "the kept pages" if unit == "page" else
+                       "attend_mfma_kernel: split-K attention partials over the kept tokens "
+                       "(stored logits)"),
+            "bound": "hbm", "achieved": round(gbps_att, 1), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(gbps_att / HBM_PEAK_GBPS, 4), "traffic": None,
+            "us_per_launch": round(us_attend, 3), "bytes_per_launch": int(b_attend),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        result["cpu_baseline"] = cpu_baseline(w0, unit, r_kv)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

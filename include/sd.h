@@ -33,7 +33,9 @@
  *   - Pointers named *_host or the shape struct are host memory; every other
  *     pointer is device memory on the current HIP device.
  *   - The caller owns all buffers.  The library never allocates or frees
- *     memory; scratch space comes from the caller's workspace (ws, ws_bytes).
+ *     memory; scratch space comes from the caller's workspace (ws, ws_bytes,
+ *     256-byte aligned, contents need not be initialised).  Calls that share
+ *     a workspace must not overlap in time (enqueue them on one stream).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
  *     and runs asynchronously; nothing synchronises the host.
  *   - Host-visible arguments are validated before anything is enqueued.  On
@@ -48,8 +50,9 @@
  *   q            [B][H_q][d]              dtype
  *   k_pages      [num_pages][H_kv][P][d]  dtype  (one contiguous tile per
  *   v_pages      [num_pages][H_kv][P][d]  dtype   page and KV head)
- *   page_bounds  [num_pages][H_kv][2][d]  dtype  (row 0: channel minima,
- *                                                  row 1: channel maxima)
+ *   page_bounds  [B][H_kv][max_pages_per_seq][2][d]  dtype  per sequence, in
+ *                logical page order (row 0: channel minima, row 1: maxima);
+ *                entries past a sequence's last page are not read
  *   block_table  [B][max_pages_per_seq]   int32  physical page of logical page u
  *   seq_lens     [B]                      int32  valid tokens n_b
  *   unit_scores  [B][H_kv][U_max]         fp32   U_max = max_pages_per_seq
@@ -72,6 +75,8 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+#define SD_API __attribute__((visibility("default")))
 
 typedef enum sd_status {
   SD_OK = 0,
@@ -107,18 +112,19 @@ typedef struct sd_shape {
  * k = ceil(R * U / 1e6) in integer arithmetic, clamped to [1, U].  The
  * kernels apply the same rule per sequence to U_b.  Returns -1 when r_KV is
  * not finite or <= 0, or U < 1. */
-int32_t sd_keep_count(double r_kv, int32_t num_units);
+SD_API int32_t sd_keep_count(double r_kv, int32_t num_units);
 
 /* Workspace bytes that suffice for every call below made with this shape,
  * unit and r_KV (sd_decode_step included).  Host only; needs no GPU. */
-sd_status sd_workspace_bytes(const sd_shape* shape, int32_t unit, double r_kv, size_t* bytes_host);
+SD_API sd_status sd_workspace_bytes(const sd_shape* shape, int32_t unit, double r_kv, size_t* bytes_host);
 
-/* Setup step, not part of the decode step: channel-wise min and max of the
- * keys of every page referenced by block_table[b][0 .. ceil(n_b / P) - 1],
- * over the page's VALID tokens only, written to page_bounds.  These are the
- * light per-page statistics of [Cross/cards] (EntmaxKV abstract).  A
- * physical page is assumed to belong to one sequence. */
-sd_status sd_update_page_bounds(const sd_shape* shape, const void* k_pages,
+/* Setup step, not part of the decode step: for every sequence b and logical
+ * page u < ceil(n_b / P), the channel-wise min and max of the keys of page
+ * block_table[b][u] over the page's VALID tokens only, written to
+ * page_bounds[b][g][u].  These are the light per-page statistics of
+ * [Cross/cards] (EntmaxKV abstract).  Kept in logical order so that scoring
+ * needs no block-table lookup. */
+SD_API sd_status sd_update_page_bounds(const sd_shape* shape, const void* k_pages,
                                 const int32_t* block_table, const int32_t* seq_lens,
                                 void* page_bounds, void* stream);
 
@@ -132,7 +138,7 @@ sd_status sd_update_page_bounds(const sd_shape* shape, const void* k_pages,
  *     token_logits[b][h][t] = scale * q[b][h] . K[b][h / G][t] and
  *     unit_scores[b][g][t] = max over h in group g, for t < n_b.
  * Entries past a sequence's units are left untouched. */
-sd_status sd_score_pages(const sd_shape* shape, const void* q, const void* k_pages,
+SD_API sd_status sd_score_pages(const sd_shape* shape, const void* q, const void* k_pages,
                          const void* page_bounds, const int32_t* block_table,
                          const int32_t* seq_lens, int32_t unit, float* unit_scores,
                          float* token_logits, void* stream);
@@ -143,7 +149,7 @@ sd_status sd_score_pages(const sd_shape* shape, const void* q, const void* k_pag
  * ascending order to sel_idx[b][g][0 .. k_b - 1]; sel_count[b][g] = k_b.
  * Scores must be finite.  k_max = sd_keep_count(r_kv, U_max) is the row
  * length of sel_idx. */
-sd_status sd_select_topk(const sd_shape* shape, int32_t unit, const int32_t* seq_lens,
+SD_API sd_status sd_select_topk(const sd_shape* shape, int32_t unit, const int32_t* seq_lens,
                          const float* unit_scores, double r_kv, int32_t* sel_idx,
                          int32_t* sel_count, void* ws, size_t ws_bytes, void* stream);
 
@@ -158,25 +164,66 @@ sd_status sd_select_topk(const sd_shape* shape, int32_t unit, const int32_t* seq
  *     the logits are read from there (written by sd_score_pages) and only V
  *     rows of the kept tokens are read; with NULL, q.K is recomputed.
  * k_max: row length of sel_idx (ignored when sel_idx == NULL). */
-sd_status sd_attend_splitk(const sd_shape* shape, const void* q, const void* k_pages,
+SD_API sd_status sd_attend_splitk(const sd_shape* shape, const void* q, const void* k_pages,
                            const void* v_pages, const int32_t* block_table,
                            const int32_t* seq_lens, int32_t unit, const int32_t* sel_idx,
                            const int32_t* sel_count, int32_t k_max, const float* token_logits,
                            float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Stage 2a alone: the split partials of the split-K attention, written to the
+ * workspace (per split j of (b, g): the normalised output and log-sum-exp of
+ * each head over the split's tokens).  The kept list comes from exactly one
+ * source:
+ *   sel_idx != NULL   the list ([B][H_kv][k_max], counts in sel_count);
+ *   unit_scores != NULL  (page unit, bf16, <= 16384 pages per sequence) every
+ *                     block runs the exact top-k of sd_select_topk on the page
+ *                     scores itself and attends its share of the kept pages;
+ *                     sel_out / sel_count_out, if given, receive the selection;
+ *                     SD_E_UNSUPPORTED outside that range;
+ *   neither           every unit (dense).
+ * token_logits as in sd_attend_splitk.  Follow with sd_merge_splits on the
+ * same workspace. */
+SD_API sd_status sd_attend_partials(const sd_shape* shape, const void* q, const void* k_pages,
+                             const void* v_pages, const int32_t* block_table,
+                             const int32_t* seq_lens, int32_t unit, const int32_t* sel_idx,
+                             const int32_t* sel_count, int32_t k_max, const float* token_logits,
+                             const float* unit_scores, double r_kv, int32_t* sel_out,
+                             int32_t* sel_count_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Stage 2b alone: log-sum-exp merge of the partials that the last
+ * sd_attend_partials call on this workspace wrote (the split count is kept
+ * in the workspace):  M = max_j lse_j, w_j = exp(lse_j - M),
+ * out = sum_j w_j o_j / sum_j w_j, lse = M + log sum_j w_j. */
+SD_API sd_status sd_merge_splits(const sd_shape* shape, float* out, float* lse, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/* Stages 1b and 2 together, page unit: from the page scores of
+ * sd_score_pages, the exact top-k (as sd_select_topk) and split-K attention
+ * over the kept pages (as sd_attend_splitk).  For bf16 data with at most
+ * 16384 pages per sequence, every attention block selects the pages of its
+ * (sequence, KV head) itself and attends its share of them (one kernel, then
+ * the merge); otherwise it runs top-k, attention and merge in turn.
+ * sel_idx / sel_count may be NULL; when given they receive the selection
+ * ([B][H_kv][k_max], [B][H_kv]).  ws as for sd_decode_step with page unit. */
+SD_API sd_status sd_select_attend(const sd_shape* shape, const void* q, const void* k_pages,
+                           const void* v_pages, const int32_t* block_table,
+                           const int32_t* seq_lens, const float* unit_scores, double r_kv,
+                           float* out, float* lse, int32_t* sel_idx, int32_t* sel_count,
+                           void* ws, size_t ws_bytes, void* stream);
 
 /* The whole decode step: r_kv >= 1 runs dense attention only; otherwise
  * scoring (by unit), top-k and attention over the kept units.  page_bounds
  * is read in page unit (built beforehand by sd_update_page_bounds).
  * sel_idx / sel_count may be NULL (then they live in ws); when given they
  * receive the selection ([B][H_kv][k_max], [B][H_kv]). */
-sd_status sd_decode_step(const sd_shape* shape, const void* q, const void* k_pages,
+SD_API sd_status sd_decode_step(const sd_shape* shape, const void* q, const void* k_pages,
                          const void* v_pages, const void* page_bounds,
                          const int32_t* block_table, const int32_t* seq_lens, int32_t unit,
                          double r_kv, float* out, float* lse, int32_t* sel_idx,
                          int32_t* sel_count, void* ws, size_t ws_bytes, void* stream);
 
 /* Text of the last non-OK status on this thread ("" if none). */
-const char* sd_last_error(void);
+SD_API const char* sd_last_error(void);
 
 #ifdef __cplusplus
 }

@@ -147,28 +147,32 @@ class Workload:
     def max_pages(self) -> int:
         return self.n_alloc // self.recipe.page_size
 
-    def paged(self, seed_offset: int = 0) -> "PagedCache":
+    def paged(self, seed_offset: int = 0, block_table=None) -> "PagedCache":
         """Scatter K and V into a shuffled physical page pool.
 
         Pages are numbered per sequence, u = 0 .. ceil(n_b / P) - 1; the pool
         holds sum_b ceil(n_b / P) pages in a random order, and block_table[b, u]
         names the physical page of logical page u.  Entries past a sequence's
-        last page hold -1.  Rows past n_b inside a last page are zeros.
+        last page hold -1.  Rows past n_b inside a last page are zeros.  A
+        given ``block_table`` (from another workload with the same lengths,
+        e.g. another layer of the same sequences) is reused as is.
         """
         r = self.recipe
         P, B, H_kv, d = r.page_size, r.batch, r.num_kv_heads, r.head_dim
         U = [-(-int(n) // P) for n in self.seq_lens]
         num_pages = int(sum(U))
-        rng = np.random.Generator(np.random.PCG64(r.seed * 1000 + 7 + seed_offset))
-        perm = rng.permutation(num_pages).astype(np.int32)
-        block_table = np.full((B, self.max_pages()), -1, dtype=np.int32)
+        if block_table is None:
+            rng = np.random.Generator(np.random.PCG64(r.seed * 1000 + 7 + seed_offset))
+            perm = rng.permutation(num_pages).astype(np.int32)
+            block_table = np.full((B, self.max_pages()), -1, dtype=np.int32)
+            off = 0
+            for b in range(B):
+                block_table[b, :U[b]] = perm[off:off + U[b]]
+                off += U[b]
         k_pool = np.zeros((num_pages, H_kv, P, d), dtype=self.K.dtype)
         v_pool = np.zeros((num_pages, H_kv, P, d), dtype=self.V.dtype)
-        off = 0
         for b in range(B):
-            ids = perm[off:off + U[b]]
-            off += U[b]
-            block_table[b, :U[b]] = ids
+            ids = block_table[b, :U[b]]
             kb = self.K[b, :, :U[b] * P].reshape(H_kv, U[b], P, d).transpose(1, 0, 2, 3)
             vb = self.V[b, :, :U[b] * P].reshape(H_kv, U[b], P, d).transpose(1, 0, 2, 3)
             k_pool[ids] = kb

@@ -14,11 +14,15 @@ from ._lib import (  # noqa: F401
     UNIT_PAGE,
     UNIT_TOKEN,
     alloc_workspace,
+    attend_partials,
     attend_splitk,
+    bounds_shape,
     decode_step,
     keep_count,
     lib,
+    merge_splits,
     score_pages,
+    select_attend,
     select_topk,
     update_page_bounds,
     workspace_bytes,

@@ -62,6 +62,12 @@ _SIGS = {
                                         _P, _I32, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "sd_decode_step": (ctypes.c_int, [ctypes.POINTER(SdShape), _P, _P, _P, _P, _P, _P, _I32,
                                       ctypes.c_double, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "sd_select_attend": (ctypes.c_int, [ctypes.POINTER(SdShape), _P, _P, _P, _P, _P, _P,
+                                        ctypes.c_double, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "sd_attend_partials": (ctypes.c_int, [ctypes.POINTER(SdShape), _P, _P, _P, _P, _P, _I32, _P,
+                                          _P, _I32, _P, _P, ctypes.c_double, _P, _P, _P,
+                                          ctypes.c_size_t, _P]),
+    "sd_merge_splits": (ctypes.c_int, [ctypes.POINTER(SdShape), _P, _P, _P, ctypes.c_size_t, _P]),
     "sd_last_error": (ctypes.c_char_p, []),
 }
 EXPORTS = tuple(_SIGS)
@@ -182,12 +188,22 @@ def workspace_bytes(shape: Shape, unit, r_kv: float) -> int:
 
 
 def alloc_workspace(shape: Shape, unit, r_kv: float, device="cuda") -> torch.Tensor:
+    """A workspace for calls with this shape, unit and keep ratio."""
     n = max(1, workspace_bytes(shape, unit, r_kv))
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
 def _kv_shape(s: Shape):
     return (s.num_pages, s.num_kv_heads, s.page_size, s.head_dim)
+
+
+def _bounds_shape(s: Shape):
+    return (s.batch, s.num_kv_heads, s.max_pages_per_seq, 2, s.head_dim)
+
+
+def bounds_shape(shape: Shape):
+    """Shape of the page-statistics tensor: [B, H_kv, max_pages_per_seq, 2, d]."""
+    return _bounds_shape(shape)
 
 
 def update_page_bounds(shape: Shape, k_pages, block_table, seq_lens, page_bounds, stream=None):
@@ -198,7 +214,7 @@ def update_page_bounds(shape: Shape, k_pages, block_table, seq_lens, page_bounds
         _dev(block_table, "block_table", torch.int32, (s.batch, s.max_pages_per_seq)),
         _dev(seq_lens, "seq_lens", torch.int32, (s.batch,)),
         _dev(page_bounds, "page_bounds", s.torch_dtype,
-             (s.num_pages, s.num_kv_heads, 2, s.head_dim)),
+             _bounds_shape(s)),
         _stream(stream)))
 
 
@@ -211,7 +227,7 @@ def score_pages(shape: Shape, q, k_pages, page_bounds, block_table, seq_lens, un
         _dev(q, "q", s.torch_dtype, (s.batch, s.num_q_heads, s.head_dim)),
         _dev(k_pages, "k_pages", s.torch_dtype, _kv_shape(s), optional=u == UNIT_PAGE),
         _dev(page_bounds, "page_bounds", s.torch_dtype,
-             (s.num_pages, s.num_kv_heads, 2, s.head_dim), optional=u == UNIT_TOKEN),
+             _bounds_shape(s), optional=u == UNIT_TOKEN),
         _dev(block_table, "block_table", torch.int32, (s.batch, s.max_pages_per_seq)),
         _dev(seq_lens, "seq_lens", torch.int32, (s.batch,)),
         u,
@@ -278,7 +294,7 @@ def decode_step(shape: Shape, q, k_pages, v_pages, page_bounds, block_table, seq
         _dev(k_pages, "k_pages", s.torch_dtype, _kv_shape(s)),
         _dev(v_pages, "v_pages", s.torch_dtype, _kv_shape(s)),
         _dev(page_bounds, "page_bounds", s.torch_dtype,
-             (s.num_pages, s.num_kv_heads, 2, s.head_dim), optional=dense or u == UNIT_TOKEN),
+             _bounds_shape(s), optional=dense or u == UNIT_TOKEN),
         _dev(block_table, "block_table", torch.int32, (s.batch, s.max_pages_per_seq)),
         _dev(seq_lens, "seq_lens", torch.int32, (s.batch,)),
         u, float(r_kv),
@@ -286,4 +302,70 @@ def decode_step(shape: Shape, q, k_pages, v_pages, page_bounds, block_table, seq
         _dev(lse, "lse", torch.float32, (s.batch, s.num_q_heads)),
         _dev(sel_idx, "sel_idx", torch.int32, (s.batch, s.num_kv_heads, k_max), optional=True),
         _dev(sel_count, "sel_count", torch.int32, (s.batch, s.num_kv_heads), optional=True),
+        wp, wn, _stream(stream)))
+
+
+def select_attend(shape: Shape, q, k_pages, v_pages, block_table, seq_lens, unit_scores, r_kv,
+                  out, lse, ws, sel_idx=None, sel_count=None, stream=None):
+    s = shape
+    k_max = keep_count(r_kv, s.max_pages_per_seq)
+    wp, wn = _ws(ws, 1)
+    _check(lib().sd_select_attend(
+        ctypes.byref(s.c()),
+        _dev(q, "q", s.torch_dtype, (s.batch, s.num_q_heads, s.head_dim)),
+        _dev(k_pages, "k_pages", s.torch_dtype, _kv_shape(s)),
+        _dev(v_pages, "v_pages", s.torch_dtype, _kv_shape(s)),
+        _dev(block_table, "block_table", torch.int32, (s.batch, s.max_pages_per_seq)),
+        _dev(seq_lens, "seq_lens", torch.int32, (s.batch,)),
+        _dev(unit_scores, "unit_scores", torch.float32,
+             (s.batch, s.num_kv_heads, s.max_pages_per_seq)),
+        float(r_kv),
+        _dev(out, "out", torch.float32, (s.batch, s.num_q_heads, s.head_dim)),
+        _dev(lse, "lse", torch.float32, (s.batch, s.num_q_heads)),
+        _dev(sel_idx, "sel_idx", torch.int32, (s.batch, s.num_kv_heads, k_max), optional=True),
+        _dev(sel_count, "sel_count", torch.int32, (s.batch, s.num_kv_heads), optional=True),
+        wp, wn, _stream(stream)))
+
+
+def attend_partials(shape: Shape, q, k_pages, v_pages, block_table, seq_lens, unit, ws,
+                    sel_idx=None, sel_count=None, token_logits=None, unit_scores=None,
+                    r_kv=1.0, sel_out=None, sel_count_out=None, stream=None):
+    s, u = shape, _unit(unit)
+    k_max = 0
+    if sel_idx is not None:
+        if sel_idx.dim() != 3 or tuple(sel_idx.shape[:2]) != (s.batch, s.num_kv_heads):
+            raise ValueError("sel_idx must have shape (B, H_kv, k_max)")
+        k_max = int(sel_idx.shape[2])
+    km_sel = keep_count(r_kv, s.max_pages_per_seq) if unit_scores is not None else 0
+    wp, wn = _ws(ws, 1)
+    _check(lib().sd_attend_partials(
+        ctypes.byref(s.c()),
+        _dev(q, "q", s.torch_dtype, (s.batch, s.num_q_heads, s.head_dim)),
+        _dev(k_pages, "k_pages", s.torch_dtype, _kv_shape(s), optional=token_logits is not None),
+        _dev(v_pages, "v_pages", s.torch_dtype, _kv_shape(s)),
+        _dev(block_table, "block_table", torch.int32, (s.batch, s.max_pages_per_seq)),
+        _dev(seq_lens, "seq_lens", torch.int32, (s.batch,)),
+        u,
+        _dev(sel_idx, "sel_idx", torch.int32, optional=True),
+        _dev(sel_count, "sel_count", torch.int32, (s.batch, s.num_kv_heads),
+             optional=sel_idx is None),
+        k_max,
+        _dev(token_logits, "token_logits", torch.float32,
+             (s.batch, s.num_q_heads, s.max_seq_len), optional=True),
+        _dev(unit_scores, "unit_scores", torch.float32,
+             (s.batch, s.num_kv_heads, s.max_pages_per_seq), optional=True),
+        float(r_kv),
+        _dev(sel_out, "sel_out", torch.int32, (s.batch, s.num_kv_heads, km_sel), optional=True),
+        _dev(sel_count_out, "sel_count_out", torch.int32, (s.batch, s.num_kv_heads),
+             optional=True),
+        wp, wn, _stream(stream)))
+
+
+def merge_splits(shape: Shape, out, lse, ws, stream=None):
+    s = shape
+    wp, wn = _ws(ws, 1)
+    _check(lib().sd_merge_splits(
+        ctypes.byref(s.c()),
+        _dev(out, "out", torch.float32, (s.batch, s.num_q_heads, s.head_dim)),
+        _dev(lse, "lse", torch.float32, (s.batch, s.num_q_heads)),
         wp, wn, _stream(stream)))

@@ -23,8 +23,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsdkv.so")
 
 ARCH = "gfx950"
-COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall",
-          "-Wno-unused-function"]
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", f"-I{INCLUDE}", f"-I{CSRC}",
+          "-Wall", "-Wno-unused-function"]
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "kernels.h"
@@ -31,10 +32,16 @@ sd_status ok() {
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// Blocks the attention pass aims for: four per CU on the 256 CUs of an MI355X.
-constexpr int64_t kTargetBlocks = 1024;
-// Fewest token rows one attention block should own.
-constexpr int64_t kMinRowsPerBlock = 64;
+// Attention blocks the split plan aims for: one 8-wave block per CU of an
+// MI355X (256 CUs).  SD_ATTEND_BLOCKS overrides it (read once).
+int64_t target_blocks() {
+  static const int64_t v = [] {
+    const char* e = std::getenv("SD_ATTEND_BLOCKS");
+    const long x = e ? std::strtol(e, nullptr, 10) : 0;
+    return static_cast<int64_t>(x > 0 ? x : 256);
+  }();
+  return v;
+}
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -104,34 +111,31 @@ int units_max(const sdkv::Dims& d, int unit) {
   return unit == SD_UNIT_PAGE ? d.max_pages : d.max_seq;
 }
 
-// Split plan of the attention pass for lists of up to k_max units.
+// Split plan of the attention pass for lists of up to k_max units: S splits
+// per (sequence, KV head), each of E units, so that B * H_kv * S is about the
+// block target; E is at least one 16-row chunk.
 struct Split {
-  int E;  // units per split
-  int S;  // splits per (sequence, KV head)
+  int E;
+  int S;
 };
 
-Split plan_split(const sdkv::Dims& d, int unit, int64_t k_max) {
-  const int64_t bg = static_cast<int64_t>(d.B) * d.Hkv;
-  const int64_t s_target = ceil_div(kTargetBlocks, bg) < 1 ? 1 : ceil_div(kTargetBlocks, bg);
-  const int64_t tpe = unit == SD_UNIT_PAGE ? d.P : 1;
-  int64_t E = ceil_div(k_max < 1 ? 1 : k_max, s_target);
-  const int64_t e_min = ceil_div(kMinRowsPerBlock, tpe);
-  if (E < e_min) E = e_min;
-  const int64_t S = ceil_div(k_max < 1 ? 1 : k_max, E);
-  return Split{static_cast<int>(E), static_cast<int>(S)};
-}
-
-// Most splits any k_max can produce: S <= s_target.
 int64_t max_splits(const sdkv::Dims& d) {
   const int64_t bg = static_cast<int64_t>(d.B) * d.Hkv;
-  const int64_t s = ceil_div(kTargetBlocks, bg);
-  return s < 1 ? 1 : s;
+  int64_t s = ceil_div(target_blocks(), bg);
+  return s < 1 ? 1 : (s > sdkv::kMaxSplits ? sdkv::kMaxSplits : s);
 }
 
-// Workspace regions (offsets in bytes from ws).  The attention partials come
-// first so that sd_attend_splitk and sd_decode_step agree on where they live.
+Split plan_split(const sdkv::Dims& d, int unit, int64_t k_max) {
+  const int64_t kk = k_max < 1 ? 1 : k_max;
+  int64_t E = ceil_div(kk, max_splits(d));
+  if (unit == SD_UNIT_TOKEN) E = ceil_div(E, 16) * 16;
+  return Split{static_cast<int>(E), static_cast<int>(ceil_div(kk, E))};
+}
+
+// Workspace regions (byte offsets).  The split count and the attention
+// partials come first so that every entry point agrees on where they live.
 struct Layout {
-  size_t part_o, part_lse, scores, logits, sel_idx, sel_count, total;
+  size_t split_count, part_o, part_lse, attend_end, scores, logits, sel_idx, sel_count, total;
 };
 
 Layout layout(const sdkv::Dims& d, int unit, double r_kv) {
@@ -142,22 +146,20 @@ Layout layout(const sdkv::Dims& d, int unit, double r_kv) {
   const int64_t U = units_max(d, unit);
   const int64_t k_max = keep_count_ppm(ratio_ppm(r_kv), U);
   size_t off = 0;
-  L.part_o = off;     off = align_up(off + sizeof(float) * bh * S * d.D);
-  L.part_lse = off;   off = align_up(off + sizeof(float) * bh * S);
-  L.scores = off;     off = align_up(off + sizeof(float) * bg * U);
+  L.split_count = off; off = align_up(off + sizeof(int32_t));
+  L.part_o = off;      off = align_up(off + sizeof(float) * bh * S * d.D);
+  L.part_lse = off;    off = align_up(off + sizeof(float) * bh * S);
+  L.attend_end = off;
+  L.scores = off;      off = align_up(off + sizeof(float) * bg * U);
   L.logits = off;
   if (unit == SD_UNIT_TOKEN) off = align_up(off + sizeof(float) * bh * d.max_seq);
-  L.sel_idx = off;    off = align_up(off + sizeof(int32_t) * bg * k_max);
-  L.sel_count = off;  off = align_up(off + sizeof(int32_t) * bg);
+  L.sel_idx = off;     off = align_up(off + sizeof(int32_t) * bg * k_max);
+  L.sel_count = off;   off = align_up(off + sizeof(int32_t) * bg);
   L.total = off;
   return L;
 }
 
-size_t attend_ws_bytes(const sdkv::Dims& d) {
-  const int64_t S = max_splits(d);
-  const int64_t bh = static_cast<int64_t>(d.B) * d.Hq;
-  return align_up(align_up(sizeof(float) * bh * S * d.D) + sizeof(float) * bh * S);
-}
+size_t attend_ws_bytes(const sdkv::Dims& d) { return layout(d, SD_UNIT_PAGE, 1.0).attend_end; }
 
 sd_status check_ws(void* ws, size_t ws_bytes, size_t need) {
   if (need == 0) return SD_OK;
@@ -195,20 +197,105 @@ sd_status do_select(const sdkv::Dims& d, int unit, const int32_t* sl, const floa
   return device_status(sdkv::launch_select(a, st), "select kernel launch");
 }
 
-sd_status do_attend(const sdkv::Dims& d, const void* q, const void* kp, const void* vp,
-                    const int32_t* bt, const int32_t* sl, int unit, const int32_t* sel_idx,
-                    const int32_t* sel_count, int k_max, const float* logits, float* out,
-                    float* lse, void* ws, hipStream_t st) {
-  const int64_t kk = sel_idx ? k_max : units_max(d, unit);
+// Split-K attention partials.  Exactly one list source: sel_idx (list),
+// unit_scores (top-k inside the kernel) or neither (identity).
+sd_status do_partials(const sdkv::Dims& d, const void* q, const void* kp, const void* vp,
+                      const int32_t* bt, const int32_t* sl, int unit, const int32_t* sel_idx,
+                      const int32_t* sel_count, int k_max, const float* logits, void* ws,
+                      hipStream_t st, const float* unit_scores = nullptr, int R_ppm = -1,
+                      int32_t* sel_out = nullptr, int32_t* sel_count_out = nullptr) {
+  const bool listed = sel_idx != nullptr || unit_scores != nullptr;
+  const int64_t kk = listed ? k_max : units_max(d, unit);
   const Split sp = plan_split(d, unit, kk);
-  const int64_t bh = static_cast<int64_t>(d.B) * d.Hq;
-  float* part_o = reinterpret_cast<float*>(at(ws, 0));
-  float* part_lse =
-      reinterpret_cast<float*>(at(ws, align_up(sizeof(float) * bh * max_splits(d) * d.D)));
-  sdkv::AttendArgs a{d,       unit,      q,      kp,   vp,   bt,      sl,
-                     sel_idx, sel_count, k_max,  logits, sp.E, sp.S, part_o,
-                     part_lse, out,      lse};
+  const Layout L = layout(d, unit, 1.0);
+  sdkv::AttendArgs a{};
+  a.d = d;
+  a.unit = unit;
+  a.q = q;
+  a.k_pages = kp;
+  a.v_pages = vp;
+  a.block_table = bt;
+  a.seq_lens = sl;
+  a.sel_idx = sel_idx;
+  a.sel_count = sel_count;
+  a.k_max = listed ? k_max : 0;
+  a.token_logits = logits;
+  a.E = sp.E;
+  a.S = sp.S;
+  a.part_o = reinterpret_cast<float*>(at(ws, L.part_o));
+  a.part_lse = reinterpret_cast<float*>(at(ws, L.part_lse));
+  a.split_count = reinterpret_cast<int32_t*>(at(ws, L.split_count));
+  a.unit_scores = unit_scores;
+  a.R_ppm = R_ppm;
+  a.sel_out = sel_out;
+  a.sel_count_out = sel_count_out;
   return device_status(sdkv::launch_attend(a, st), "attention kernel launch");
+}
+
+sd_status do_merge(const sdkv::Dims& d, float* out, float* lse, void* ws, hipStream_t st) {
+  const Layout L = layout(d, SD_UNIT_PAGE, 1.0);
+  sdkv::MergeArgs a{};
+  a.d = d;
+  a.part_o = reinterpret_cast<const float*>(at(ws, L.part_o));
+  a.part_lse = reinterpret_cast<const float*>(at(ws, L.part_lse));
+  a.split_count = reinterpret_cast<const int32_t*>(at(ws, L.split_count));
+  a.S_max = static_cast<int>(max_splits(d));
+  a.out = out;
+  a.lse = lse;
+  return device_status(sdkv::launch_merge(a, st), "merge kernel launch");
+}
+
+// Whether the top-k can run inside the attention kernel: page unit, bf16, at
+// most kMaxSelectU pages per sequence, and a split slice that fits the
+// kernel's LDS list.
+bool fused_select(const sdkv::Dims& d, int unit, int k_max) {
+  if (unit != SD_UNIT_PAGE || d.dtype != SD_BF16 || d.max_pages > sdkv::kMaxSelectU) return false;
+  return plan_split(d, unit, k_max).E <= sdkv::kMaxSelectE;
+}
+
+// Page-unit selection + attention: fused when possible, else top-k then a
+// listed attention.
+sd_status do_select_attend(const sdkv::Dims& d, const void* q, const void* kp, const void* vp,
+                           const int32_t* bt, const int32_t* sl, const float* scores,
+                           double r_kv, float* out, float* lse, int32_t* sel_idx,
+                           int32_t* sel_count, void* ws, hipStream_t s) {
+  const int unit = SD_UNIT_PAGE;
+  const Layout L = layout(d, unit, r_kv);
+  const int k_max = static_cast<int>(keep_count_ppm(ratio_ppm(r_kv), units_max(d, unit)));
+  sd_status st;
+  if (fused_select(d, unit, k_max)) {
+    if ((st = do_partials(d, q, kp, vp, bt, sl, unit, nullptr, nullptr, k_max, nullptr, ws, s,
+                          scores, ratio_ppm(r_kv), sel_idx, sel_count)) != SD_OK)
+      return st;
+    return do_merge(d, out, lse, ws, s);
+  }
+  int32_t* idx = sel_idx ? sel_idx : reinterpret_cast<int32_t*>(at(ws, L.sel_idx));
+  int32_t* cnt = sel_count ? sel_count : reinterpret_cast<int32_t*>(at(ws, L.sel_count));
+  if ((st = do_select(d, unit, sl, scores, r_kv, idx, cnt, s)) != SD_OK) return st;
+  if ((st = do_partials(d, q, kp, vp, bt, sl, unit, idx, cnt, k_max, nullptr, ws, s)) != SD_OK)
+    return st;
+  return do_merge(d, out, lse, ws, s);
+}
+
+// Shared checks of the attention entry points.
+sd_status check_attend_args(const sdkv::Dims& d, int32_t unit, const void* q, const void* k_pages,
+                            const void* v_pages, const int32_t* block_table,
+                            const int32_t* seq_lens, const int32_t* sel_idx,
+                            const int32_t* sel_count, int32_t k_max,
+                            const float* token_logits) {
+  sd_status st;
+  if ((st = check_unit(unit)) != SD_OK) return st;
+  if (!q || !v_pages || !block_table || !seq_lens)
+    return fail(SD_E_NULL, "q, v_pages, block_table and seq_lens are required");
+  if (!token_logits && !k_pages) return fail(SD_E_NULL, "k_pages is required");
+  if (token_logits && unit != SD_UNIT_TOKEN)
+    return fail(SD_E_SHAPE, "token_logits is only read in token unit");
+  if (sel_idx) {
+    if (!sel_count) return fail(SD_E_NULL, "sel_count is required with sel_idx");
+    if (k_max < 1 || k_max > units_max(d, unit))
+      return fail(SD_E_SHAPE, "k_max %d outside [1, %d]", k_max, units_max(d, unit));
+  }
+  return SD_OK;
 }
 
 }  // namespace
@@ -285,6 +372,57 @@ sd_status sd_select_topk(const sd_shape* shape, int32_t unit, const int32_t* seq
   return ok();
 }
 
+sd_status sd_attend_partials(const sd_shape* shape, const void* q, const void* k_pages,
+                             const void* v_pages, const int32_t* block_table,
+                             const int32_t* seq_lens, int32_t unit, const int32_t* sel_idx,
+                             const int32_t* sel_count, int32_t k_max, const float* token_logits,
+                             const float* unit_scores, double r_kv, int32_t* sel_out,
+                             int32_t* sel_count_out, void* ws, size_t ws_bytes, void* stream) {
+  sdkv::Dims d;
+  sd_status st;
+  if ((st = check_shape(shape, &d)) != SD_OK) return st;
+  if ((st = check_attend_args(d, unit, q, k_pages, v_pages, block_table, seq_lens, sel_idx,
+                              sel_count, k_max, token_logits)) != SD_OK)
+    return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (unit_scores) {
+    if (sel_idx) return fail(SD_E_SHAPE, "give either sel_idx or unit_scores, not both");
+    if (unit != SD_UNIT_PAGE) return fail(SD_E_SHAPE, "in-kernel top-k is page unit only");
+    if ((st = check_ratio(r_kv)) != SD_OK) return st;
+    if ((sel_out == nullptr) != (sel_count_out == nullptr))
+      return fail(SD_E_NULL, "sel_out and sel_count_out are given together or not at all");
+    const int km = static_cast<int>(keep_count_ppm(ratio_ppm(r_kv), units_max(d, unit)));
+    if (!fused_select(d, unit, km))
+      return fail(SD_E_UNSUPPORTED,
+                  "in-kernel top-k needs bf16 data, <= %d pages per sequence and <= %d kept "
+                  "pages per split",
+                  sdkv::kMaxSelectU, sdkv::kMaxSelectE);
+    if ((st = check_ws(ws, ws_bytes, attend_ws_bytes(d))) != SD_OK) return st;
+    if ((st = do_partials(d, q, k_pages, v_pages, block_table, seq_lens, unit, nullptr, nullptr,
+                          km, nullptr, ws, s, unit_scores, ratio_ppm(r_kv), sel_out,
+                          sel_count_out)) != SD_OK)
+      return st;
+    return ok();
+  }
+  if (sel_out || sel_count_out) return fail(SD_E_SHAPE, "sel_out is written by in-kernel top-k only");
+  if ((st = check_ws(ws, ws_bytes, attend_ws_bytes(d))) != SD_OK) return st;
+  if ((st = do_partials(d, q, k_pages, v_pages, block_table, seq_lens, unit, sel_idx, sel_count,
+                        k_max, token_logits, ws, s)) != SD_OK)
+    return st;
+  return ok();
+}
+
+sd_status sd_merge_splits(const sd_shape* shape, float* out, float* lse, void* ws,
+                          size_t ws_bytes, void* stream) {
+  sdkv::Dims d;
+  sd_status st;
+  if ((st = check_shape(shape, &d)) != SD_OK) return st;
+  if (!out || !lse) return fail(SD_E_NULL, "out and lse are required");
+  if ((st = check_ws(ws, ws_bytes, attend_ws_bytes(d))) != SD_OK) return st;
+  if ((st = do_merge(d, out, lse, ws, static_cast<hipStream_t>(stream))) != SD_OK) return st;
+  return ok();
+}
+
 sd_status sd_attend_splitk(const sd_shape* shape, const void* q, const void* k_pages,
                            const void* v_pages, const int32_t* block_table,
                            const int32_t* seq_lens, int32_t unit, const int32_t* sel_idx,
@@ -293,21 +431,37 @@ sd_status sd_attend_splitk(const sd_shape* shape, const void* q, const void* k_p
   sdkv::Dims d;
   sd_status st;
   if ((st = check_shape(shape, &d)) != SD_OK) return st;
-  if ((st = check_unit(unit)) != SD_OK) return st;
-  if (!q || !v_pages || !block_table || !seq_lens || !out || !lse)
-    return fail(SD_E_NULL, "q, v_pages, block_table, seq_lens, out and lse are required");
-  if (!token_logits && !k_pages) return fail(SD_E_NULL, "k_pages is required");
-  if (token_logits && unit != SD_UNIT_TOKEN)
-    return fail(SD_E_SHAPE, "token_logits is only read in token unit");
-  if (sel_idx) {
-    if (!sel_count) return fail(SD_E_NULL, "sel_count is required with sel_idx");
-    if (k_max < 1 || k_max > units_max(d, unit))
-      return fail(SD_E_SHAPE, "k_max %d outside [1, %d]", k_max, units_max(d, unit));
-  }
+  if ((st = check_attend_args(d, unit, q, k_pages, v_pages, block_table, seq_lens, sel_idx,
+                              sel_count, k_max, token_logits)) != SD_OK)
+    return st;
+  if (!out || !lse) return fail(SD_E_NULL, "out and lse are required");
   if ((st = check_ws(ws, ws_bytes, attend_ws_bytes(d))) != SD_OK) return st;
-  if ((st = do_attend(d, q, k_pages, v_pages, block_table, seq_lens, unit, sel_idx, sel_count,
-                      k_max, token_logits, out, lse, ws, static_cast<hipStream_t>(stream))) !=
-      SD_OK)
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = do_partials(d, q, k_pages, v_pages, block_table, seq_lens, unit, sel_idx, sel_count,
+                        k_max, token_logits, ws, s)) != SD_OK)
+    return st;
+  if ((st = do_merge(d, out, lse, ws, s)) != SD_OK) return st;
+  return ok();
+}
+
+sd_status sd_select_attend(const sd_shape* shape, const void* q, const void* k_pages,
+                           const void* v_pages, const int32_t* block_table,
+                           const int32_t* seq_lens, const float* unit_scores, double r_kv,
+                           float* out, float* lse, int32_t* sel_idx, int32_t* sel_count,
+                           void* ws, size_t ws_bytes, void* stream) {
+  sdkv::Dims d;
+  sd_status st;
+  if ((st = check_shape(shape, &d)) != SD_OK) return st;
+  if ((st = check_ratio(r_kv)) != SD_OK) return st;
+  if (!q || !k_pages || !v_pages || !block_table || !seq_lens || !unit_scores || !out || !lse)
+    return fail(SD_E_NULL,
+                "q, k_pages, v_pages, block_table, seq_lens, unit_scores, out and lse are required");
+  if ((sel_idx == nullptr) != (sel_count == nullptr))
+    return fail(SD_E_NULL, "sel_idx and sel_count are given together or not at all");
+  if ((st = check_ws(ws, ws_bytes, layout(d, SD_UNIT_PAGE, r_kv).total)) != SD_OK) return st;
+  if ((st = do_select_attend(d, q, k_pages, v_pages, block_table, seq_lens, unit_scores, r_kv,
+                             out, lse, sel_idx, sel_count, ws,
+                             static_cast<hipStream_t>(stream))) != SD_OK)
     return st;
   return ok();
 }
@@ -334,23 +488,32 @@ sd_status sd_decode_step(const sd_shape* shape, const void* q, const void* k_pag
   if ((st = check_ws(ws, ws_bytes, L.total)) != SD_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dense) {
-    st = do_attend(d, q, k_pages, v_pages, block_table, seq_lens, unit, nullptr, nullptr, 0,
-                   nullptr, out, lse, ws, s);
-    return st != SD_OK ? st : ok();
+    if ((st = do_partials(d, q, k_pages, v_pages, block_table, seq_lens, unit, nullptr, nullptr,
+                          0, nullptr, ws, s)) != SD_OK)
+      return st;
+    if ((st = do_merge(d, out, lse, ws, s)) != SD_OK) return st;
+    return ok();
   }
   const int U = units_max(d, unit);
   const int k_max = static_cast<int>(keep_count_ppm(ratio_ppm(r_kv), U));
   float* scores = reinterpret_cast<float*>(at(ws, L.scores));
   float* logits = unit == SD_UNIT_TOKEN ? reinterpret_cast<float*>(at(ws, L.logits)) : nullptr;
-  int32_t* idx = sel_idx ? sel_idx : reinterpret_cast<int32_t*>(at(ws, L.sel_idx));
-  int32_t* cnt = sel_count ? sel_count : reinterpret_cast<int32_t*>(at(ws, L.sel_count));
   if ((st = do_score(d, q, k_pages, page_bounds, block_table, seq_lens, unit, scores, logits,
                      s)) != SD_OK)
     return st;
+  if (unit == SD_UNIT_PAGE) {
+    if ((st = do_select_attend(d, q, k_pages, v_pages, block_table, seq_lens, scores, r_kv, out,
+                               lse, sel_idx, sel_count, ws, s)) != SD_OK)
+      return st;
+    return ok();
+  }
+  int32_t* idx = sel_idx ? sel_idx : reinterpret_cast<int32_t*>(at(ws, L.sel_idx));
+  int32_t* cnt = sel_count ? sel_count : reinterpret_cast<int32_t*>(at(ws, L.sel_count));
   if ((st = do_select(d, unit, seq_lens, scores, r_kv, idx, cnt, s)) != SD_OK) return st;
-  if ((st = do_attend(d, q, k_pages, v_pages, block_table, seq_lens, unit, idx, cnt, k_max,
-                      logits, out, lse, ws, s)) != SD_OK)
+  if ((st = do_partials(d, q, k_pages, v_pages, block_table, seq_lens, unit, idx, cnt, k_max,
+                        logits, ws, s)) != SD_OK)
     return st;
+  if ((st = do_merge(d, out, lse, ws, s)) != SD_OK) return st;
   return ok();
 }
 

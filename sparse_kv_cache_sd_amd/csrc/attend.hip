@@ -1,63 +1,484 @@
-// Stage 2: split-K attention over the kept units, then the log-sum-exp merge.
+// Stage 2: split-K attention over the kept units, and the log-sum-exp merge
+// of the splits.
 //
-// Dense and sparse decoding share this kernel ("Where Activation Sparsity and
-// KV-Cache Sparsity Cross in LLM Decoding", list view, Abstract); a dense call
-// is the same kernel with every unit kept.  Attention runs over the tokens of
-// the kept blocks only ("SparDA ..." summary, Section 3.1).
+// Dense and sparse decoding share these kernels ("Where Activation Sparsity
+// and KV-Cache Sparsity Cross in LLM Decoding", list view, Abstract): a dense
+// call is the same kernel with every unit kept.  Attention runs over the
+// tokens of the kept blocks only ("SparDA ..." summary, Section 3.1).
 //
-// Work: block (split j, KV head g, sequence b) takes kept units
-// [j*E, min((j+1)*E, count)) of its list; a page unit expands to its P rows
-// (rows past n_b are skipped), a token unit is one row.  Each row is read by
-// LPR = d/8 lanes, 8 channels each, so one wave covers RPW = 64/LPR rows per
-// step and four waves interleave.  Every lane-row keeps its own online
-// softmax state (running max m, sum l, weighted sum acc) per query head of
-// the group, in the base-2 domain (q is pre-scaled by scale * log2 e).  At
-// the end the RPW lane-rows of a wave merge by shuffles, the four waves merge
-// through LDS, and the block writes one normalised partial output and its
-// log-sum-exp per head; a split with no valid row writes lse = -inf.
-// The merge kernel combines the S partials of each head by log-sum-exp.
-#include "device.h"
+// Work split: block (j, g, b) owns kept-list entries [j*E, (j+1)*E) of the
+// (sequence b, KV head g) list.  Its tokens are cut into chunks of 16 rows: a
+// 16-token page is one chunk, a 64-token page four, and in token unit a chunk
+// is 16 consecutive list entries.  Each split keeps an online softmax (running
+// max m, sum l, weighted value sum) per query head of the group and writes
+// its normalised output and log-sum-exp; a second kernel merges the splits of
+// every head by log-sum-exp.  (A merge inside the last block to finish would
+// need an agent-scope release per block, which on gfx950 writes back the
+// XCD's L2 each time and costs more than the kernel boundary.)
+//
+// The kept list comes from memory (a selection computed before), is the
+// identity (dense), or is computed by the block itself from the page scores:
+// every split of (b, g) runs the same exact top-k (topk.h, all eight waves)
+// and keeps its slice, which saves a kernel launch and a round trip through
+// memory.
+//
+// bf16 kernel (matrix cores).  Per chunk and wave:
+//   S^T[t][h] = sum_c K[t][c] Q[h][c]   4 x mfma 16x16x32 bf16 (d = 128): K rows
+//                                       are the A operand straight from HBM, the
+//                                       group's queries (padded to 16 heads) the
+//                                       B operand kept in registers;
+//   p = exp2(S^T * scale * log2 e - m)  in the MFMA result layout (lane holds 4
+//                                       tokens of one head); the chunk max over
+//                                       16 tokens uses two gfx950 permlane swaps;
+//   O^T[c][h] += sum_t V^T[c][t] P^T[t][h]   mfma 16x16x16 bf16 per 16 channels,
+//                                       P split into bf16 hi + lo parts so the
+//                                       weights keep ~16 significant bits; V^T
+//                                       comes from V rows staged in LDS through
+//                                       the gfx950 transposing LDS read.
+// Row addresses of up to 16 chunks per wave are resolved first (list entry,
+// then block table) into LDS, then K/V loads run two chunks at a time,
+// double-buffered.  The fp32 kernel keeps the same split structure with
+// vector FMAs.
+#include "topk.h"
 
 namespace sdkv {
 
-constexpr int kAttendThreads = 256;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
 
-template <typename T, int D, int G>
-__global__ __launch_bounds__(kAttendThreads) void attend_splitk_kernel(AttendArgs a) {
-  constexpr int LPR = D / 8;
+constexpr int kAttendWaves = 8;     // waves per block
+constexpr int kResolveWindow = 16;  // chunks a wave resolves per round
+
+// How a block obtains its kept list.
+enum SelMode : int {
+  kListed = 0,     // from memory (sel_idx) or the identity
+  kBlock4 = 4,     // in-kernel top-k by the whole block, 4 / 8 / 32 keys per thread
+  kBlock8 = 8,
+  kBlock32 = 32
+};
+
+// A block's slice of the list, known without device loads: entries
+// [e0, e_hi) may be read (e_hi <= list length); chunks past the loaded
+// count are masked later.
+struct Span {
+  int e0, e_hi;
+  int nch;  // chunks the slice can hold
+};
+
+__device__ __forceinline__ Span span_of(const AttendArgs& a, int j, int list_len) {
+  Span sp;
+  sp.e0 = j * a.E;
+  sp.e_hi = min(sp.e0 + a.E, list_len);
+  const int ne = max(0, sp.e_hi - sp.e0);
+  sp.nch = a.unit == kPage ? ne * (a.d.P / 16) : (ne + 15) / 16;
+  return sp;
+}
+
+// Pool row (row-major [num_pages * H_kv * P] index) of row `row` of chunk `c`,
+// or -1 when that row is not attended; *tok receives its token id.
+// unit_at(e) returns list entry e (called for e < sp.e_hi).
+template <typename UnitAt>
+__device__ __forceinline__ int resolve_row(const AttendArgs& a, const Span& sp, UnitAt&& unit_at,
+                                           int cnt, int n, int U, int b, int g, int c, int row,
+                                           int* tok) {
+  const Dims& d = a.d;
+  int e, t;
+  bool ok;
+  if (a.unit == kPage) {
+    const int cpu = d.P / 16;
+    e = sp.e0 + c / cpu;
+    const int u = e < sp.e_hi ? unit_at(e) : -1;
+    t = u * d.P + (c - (c / cpu) * cpu) * 16 + row;
+    ok = e < sp.e_hi && e < cnt && u >= 0 && u < U && t < n;
+  } else {
+    e = sp.e0 + c * 16 + row;
+    t = e < sp.e_hi ? unit_at(e) : -1;
+    ok = e < sp.e_hi && e < cnt && t >= 0 && t < n;
+  }
+  // the block-table read is clamped so it can issue before `ok` is known
+  int lp = t / d.P;
+  lp = lp < 0 ? 0 : (lp >= d.max_pages ? d.max_pages - 1 : lp);
+  const int phys = a.block_table[(int64_t)b * d.max_pages + lp];
+  ok = ok && phys >= 0 && phys < d.num_pages;
+  *tok = t;
+  return ok ? (int)(((int64_t)phys * d.Hkv + g) * d.P + (t - lp * d.P)) : -1;
+}
+
+// Writes a block's partial (s_po [G][D], s_plse [G] in LDS); split 0 of
+// (0, 0) also records the split count for the merge kernel.
+template <int D, int G, int NT>
+__device__ __forceinline__ void write_partial(const AttendArgs& a, int b, int g, int j,
+                                              const float* s_po, const float* s_plse) {
+  const int tid = threadIdx.x;
+  const int64_t bh0 = (int64_t)b * a.d.Hq + g * G;
+  for (int i = tid * 4; i < G * D; i += NT * 4) {
+    const int h = i / D, c = i - h * D;
+    *reinterpret_cast<float4*>(&a.part_o[((bh0 + h) * a.S + j) * D + c]) =
+        *reinterpret_cast<const float4*>(&s_po[i]);
+  }
+  if (tid < G) a.part_lse[(bh0 + tid) * a.S + j] = s_plse[tid];
+  if (tid == 0 && j == 0 && g == 0 && b == 0) *a.split_count = a.S;
+}
+
+// Log-sum-exp merge of the S split partials of one (sequence, query head):
+// M = max_j lse_j, w_j = exp(lse_j - M), out = sum_j w_j o_j / sum_j w_j,
+// lse = M + log sum_j w_j; splits with lse = -inf weigh nothing.  One block
+// of 256 threads per (sequence, query head): thread (slice, c4) sums float4
+// column c4 over the splits j = slice (mod SLICES), issuing the loads of its
+// first splits before the weights are known; the slices add up in LDS.
+template <int D>
+__global__ __launch_bounds__(256) void merge_splits_kernel(const float* __restrict__ part_o,
+                                                           const float* __restrict__ part_lse,
+                                                           const int32_t* __restrict__ split_count,
+                                                           float* __restrict__ out,
+                                                           float* __restrict__ lse, int S_max) {
+  constexpr int NT = 256, C4 = D / 4, SLICES = NT / C4, PRE = 8;
+  __shared__ float s_w[kMaxSplits];
+  __shared__ float s_ML[2];
+  __shared__ float4 s_red[SLICES][C4];
+  const int64_t bh = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int S = min(max(*split_count, 1), S_max);
+  const float* pl = part_lse + bh * S;
+  const int c4 = tid % C4, slice = tid / C4;
+  const float4* po = reinterpret_cast<const float4*>(part_o + bh * S * D) + c4;
+  float4 pre[PRE];
+#pragma unroll
+  for (int i = 0; i < PRE; ++i) {
+    const int j = slice + i * SLICES;
+    pre[i] = j < S ? po[(int64_t)j * C4] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  if (tid < 64) {
+    float M = -INFINITY;
+    for (int j = lane; j < S; j += 64) M = fmaxf(M, pl[j]);
+    M = wave_max(M);
+    float L = 0.f;
+    for (int j = lane; j < S; j += 64) {
+      const float w = M == -INFINITY ? 0.f : expf(pl[j] - M);
+      s_w[j] = w;
+      L += w;
+    }
+    L = wave_sum(L);
+    if (lane == 0) { s_ML[0] = M; s_ML[1] = L; }
+  }
+  __syncthreads();
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int i = 0; i < PRE; ++i) {
+    const int j = slice + i * SLICES;
+    const float w = j < S ? s_w[j] : 0.f;
+    acc.x = fmaf(w, pre[i].x, acc.x);
+    acc.y = fmaf(w, pre[i].y, acc.y);
+    acc.z = fmaf(w, pre[i].z, acc.z);
+    acc.w = fmaf(w, pre[i].w, acc.w);
+  }
+#pragma unroll 4
+  for (int j = slice + PRE * SLICES; j < S; j += SLICES) {
+    const float w = s_w[j];
+    const float4 v = po[(int64_t)j * C4];
+    acc.x = fmaf(w, v.x, acc.x);
+    acc.y = fmaf(w, v.y, acc.y);
+    acc.z = fmaf(w, v.z, acc.z);
+    acc.w = fmaf(w, v.w, acc.w);
+  }
+  s_red[slice][c4] = acc;
+  __syncthreads();
+  if (tid < C4) {
+    float4 sum = s_red[0][tid];
+#pragma unroll
+    for (int s = 1; s < SLICES; ++s) {
+      const float4 v = s_red[s][tid];
+      sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+    }
+    const float L = s_ML[1];
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    reinterpret_cast<float4*>(out + bh * D)[tid] =
+        make_float4(sum.x * inv, sum.y * inv, sum.z * inv, sum.w * inv);
+    if (tid == 0) lse[bh] = L > 0.f ? s_ML[0] + logf(L) : -INFINITY;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// bf16: matrix-core kernel
+// ----------------------------------------------------------------------------
+
+template <int D, int G, bool LOGITS, int SEL>
+__global__ __launch_bounds__(kAttendWaves * 64) void attend_mfma_kernel(AttendArgs a) {
+  constexpr int NW = kAttendWaves, NT = NW * 64, RW = kResolveWindow;
+  constexpr int KS = D / 32;        // 16x16x32 steps over the channels
+  constexpr int CT = D / 16;        // 16-channel output tiles
+  constexpr int VROW = D + 8;       // staged V row, bf16 elements (16-byte aligned rows)
+  constexpr bool SELECTS = SEL != kListed;
+  constexpr int KEYS = SELECTS ? SEL : 1;
+  // The V staging area is reused after the chunk loop for the per-wave outputs.
+  constexpr int kStage = NW * 16 * VROW * 2;
+  constexpr int kAfter = NW * G * D * 4;
+  __shared__ __align__(16) unsigned char s_raw[kStage > kAfter ? kStage : kAfter];
+  __shared__ int s_rows[NW][RW][16];
+  __shared__ int s_tok[LOGITS ? NW : 1][RW][16];
+  __shared__ float s_m[NW][16], s_l[NW][16];
+  __shared__ __align__(16) float s_po[G * D];
+  __shared__ float s_plse[G];
+  __shared__ int s_list[SELECTS ? kMaxSelectE : 1];
+  __shared__ RadixState s_rs;
+  __shared__ uint32_t s_rcnt[SELECTS ? 2 * KEYS * NW : 1];
+  auto s_v = reinterpret_cast<bf16_t(*)[16 * VROW]>(s_raw);
+  auto s_o = reinterpret_cast<float(*)[G][D]>(s_raw);
+
+  const Dims& d = a.d;
+  const int j = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = lane & 15, quad = lane >> 4;
+  const int64_t bg = (int64_t)b * d.Hkv + g;
+  const bf16_t* kp = static_cast<const bf16_t*>(a.k_pages);
+  const bf16_t* vp = static_cast<const bf16_t*>(a.v_pages);
+  const int32_t* list = a.sel_idx ? a.sel_idx + bg * a.k_max : nullptr;
+  const int units_cap = a.unit == kPage ? d.max_pages : d.max_seq;
+  const Span sp = span_of(a, j, (list || SELECTS) ? a.k_max : units_cap);
+  // chunks [w_lo, w_hi) of this block belong to this wave
+  const int cpw = (sp.nch + NW - 1) / NW;
+  const int w_lo = min(sp.nch, wave * cpw), w_hi = min(sp.nch, w_lo + cpw);
+
+  // In-kernel selection: the scores of (b, g) are read before the sequence
+  // length is known (a row holds max_pages of them).
+  uint32_t key[KEYS];
+  if constexpr (SELECTS) {
+    // interleaved: key[i] of thread t is unit t + NT*i
+    const float* sc = a.unit_scores + bg * d.max_pages;
+#pragma unroll
+    for (int i = 0; i < KEYS; ++i)
+      key[i] = order_key(sc[min((int)threadIdx.x + NT * i, d.max_pages - 1)]);
+  }
+  const int n = clamp_len(a.seq_lens[b], d.max_seq);
+  const int U = a.unit == kPage ? (n + d.P - 1) / d.P : n;
+  int cnt;
+  if constexpr (SELECTS) {
+    const int k = min(keep_count_dev(U, a.R_ppm), a.k_max);
+    int32_t* full = (j == 0 && a.sel_out) ? a.sel_out + bg * a.k_max : nullptr;
+    auto emit = [&](int pos, int unit_id) {
+      if (pos >= sp.e0 && pos < sp.e_hi) s_list[pos - sp.e0] = unit_id;
+      if (full) full[pos] = unit_id;
+    };
+    if (k == U) {
+      for (int e = threadIdx.x; e < U; e += NT) emit(e, e);
+    } else if (k > 0) {
+      topk_regs<KEYS, NW>(s_rs, s_rcnt, key, U, k, emit);
+    }
+    if (j == 0 && a.sel_count_out && threadIdx.x == 0) a.sel_count_out[bg] = k;
+    cnt = k;
+    __syncthreads();
+  } else {
+    cnt = list ? min(a.sel_count[bg], a.k_max) : U;
+  }
+  auto unit_at = [&](int e) -> int {
+    if constexpr (SELECTS) return e < cnt ? s_list[e - sp.e0] : -1;
+    else return list ? list[e] : e;
+  };
+
+  // B operand of the score product: lane holds Q[h = row][32 s + 8 quad .. +7].
+  bf16x8_t qop[KS];
+  {
+    const bf16_t* qrow = static_cast<const bf16_t*>(a.q) + ((int64_t)b * d.Hq + g * G + row) * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      uint4 w = make_uint4(0u, 0u, 0u, 0u);
+      if (!LOGITS && row < G) w = *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * quad);
+      qop[s] = __builtin_bit_cast(bf16x8_t, w);
+    }
+  }
+  const float qs = d.scale * kLog2e;
+
+  float4_t acc[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) acc[ct] = float4_t{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;
+  bf16_t* sv = &s_v[wave][0];
+
+  // One 16-row chunk: scores, online softmax, value accumulation.
+  auto process = [&](const uint4 (&kv)[KS], const uint4 (&vv)[KS], uint32_t vmask, int cl) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      *reinterpret_cast<uint4*>(sv + row * VROW + 32 * s + 8 * quad) = vv[s];
+    float x[4];
+    if constexpr (!LOGITS) {
+      float4_t st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv[s]), qop[s],
+                                                      st, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[r] = st[r] * qs;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int rr = 4 * quad + r;
+        x[r] = 0.f;
+        if (row < G && ((vmask >> rr) & 1u))
+          x[r] = a.token_logits[((int64_t)b * d.Hq + g * G + row) * d.max_seq +
+                                s_tok[LOGITS ? wave : 0][cl][rr]] * kLog2e;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (!((vmask >> (4 * quad + r)) & 1u)) x[r] = -INFINITY;
+    float cm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    cm = max_xor32(cm);
+    cm = max_xor16(cm);
+    const float mn = fmaxf(m, cm);
+    const float alpha = exp2f(m - mn);
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r] = exp2f(x[r] - mn);
+    l = fmaf(l, alpha, (p[0] + p[1]) + (p[2] + p[3]));
+    if (alpha != 1.f) {
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) acc[ct] *= alpha;
+    }
+    m = mn;
+    short4_t phi, plo;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const __bf16 hi = (__bf16)p[r];
+      const __bf16 lo = (__bf16)(p[r] - (float)hi);
+      phi[r] = __builtin_bit_cast(short, hi);
+      plo[r] = __builtin_bit_cast(short, lo);
+    }
+    __builtin_amdgcn_wave_barrier();
+    // lane reads V[4 quad + row / 4][16 ct + 4 (row % 4) .. +3]; the transposing
+    // read hands it V[4 quad + r][16 ct + row] for r = 0..3 (the V^T operand).
+    const bf16_t* vsrc = sv + (4 * quad + (row >> 2)) * VROW + 4 * (row & 3);
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const short4_t vop = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) short4_t*)(vsrc + 16 * ct));
+      acc[ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, phi, acc[ct], 0, 0, 0);
+      acc[ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, plo, acc[ct], 0, 0, 0);
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
+
+  for (int r0 = w_lo; r0 < w_hi; r0 += RW) {
+    const int nc = min(RW, w_hi - r0);
+    // Resolve the rows of up to RW chunks: lane (row, quad) takes chunk it*4+quad.
+#pragma unroll
+    for (int it = 0; it < RW / 4; ++it) {
+      const int cl = it * 4 + quad;
+      int t = 0, pr = -1;
+      if (cl < nc) pr = resolve_row(a, sp, unit_at, cnt, n, U, b, g, r0 + cl, row, &t);
+      s_rows[wave][cl][row] = pr;
+      if constexpr (LOGITS) s_tok[wave][cl][row] = t;
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    // Two chunks per load batch, double-buffered: batch i+1 is in flight while
+    // batch i is processed.
+    uint4 kA[2][KS], vA[2][KS], kB[2][KS], vB[2][KS];
+    uint32_t mA[2], mB[2];
+    auto load2 = [&](uint4 (&kk)[2][KS], uint4 (&vv)[2][KS], uint32_t (&mm)[2], int c0) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int pr = c0 + i < nc ? s_rows[wave][c0 + i][row] : -1;
+        mm[i] = (uint32_t)(__ballot(pr >= 0) & 0xFFFFull);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          kk[i][s] = make_uint4(0u, 0u, 0u, 0u);
+          vv[i][s] = make_uint4(0u, 0u, 0u, 0u);
+          if (pr >= 0) {
+            const int64_t o = (int64_t)pr * D + 32 * s + 8 * quad;
+            if constexpr (!LOGITS) kk[i][s] = *reinterpret_cast<const uint4*>(kp + o);
+            vv[i][s] = *reinterpret_cast<const uint4*>(vp + o);
+          }
+        }
+      }
+    };
+    auto run2 = [&](uint4 (&kk)[2][KS], uint4 (&vv)[2][KS], uint32_t (&mm)[2], int c0) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        if (mm[i] != 0u) process(kk[i], vv[i], mm[i], c0 + i);
+    };
+    load2(kA, vA, mA, 0);
+    for (int c = 0; c < nc; c += 4) {
+      if (c + 2 < nc) load2(kB, vB, mB, c + 2);
+      run2(kA, vA, mA, c);
+      if (c + 2 >= nc) break;
+      if (c + 4 < nc) load2(kA, vA, mA, c + 4);
+      run2(kB, vB, mB, c + 2);
+    }
+  }
+
+  // lane (row, quad) holds head `row`: sum over the four quads of l; the
+  // running max is already shared by them.
+  l = sum_xor32(l);
+  l = sum_xor16(l);
+  __syncthreads();  // every wave is done with the staging area
+  if (quad == 0) { s_m[wave][row] = m; s_l[wave][row] = l; }
+  if (row < G) {
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s_o[wave][row][16 * ct + 4 * quad + r] = acc[ct][r];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < G * D; i += NT) {
+    const int h = i / D, c = i - h * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][h]);
+    float L = 0.f, A = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float f = s_m[w][h] == -INFINITY ? 0.f : exp2f(s_m[w][h] - M);
+        L = fmaf(s_l[w][h], f, L);
+        A = fmaf(s_o[w][h][c], f, A);
+      }
+    }
+    s_po[i] = L > 0.f ? A / L : 0.f;
+    if (c == 0) s_plse[h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+  }
+  __syncthreads();
+  write_partial<D, G, NT>(a, b, g, j, s_po, s_plse);
+}
+
+// ----------------------------------------------------------------------------
+// fp32: vector kernel (same split structure; list from memory or identity)
+// ----------------------------------------------------------------------------
+
+template <int D, int G>
+__global__ __launch_bounds__(kAttendWaves * 64) void attend_f32_kernel(AttendArgs a) {
+  constexpr int NW = kAttendWaves, NT = NW * 64;
+  constexpr int LPR = D / 8;   // lanes per row, 8 channels each
   constexpr int RPW = 64 / LPR;
-  constexpr int NW = kAttendThreads / 64;
+  __shared__ float s_m[NW][RPW][G], s_l[NW][RPW][G];
+  __shared__ __align__(16) float s_acc[NW][G][D];
+  __shared__ __align__(16) float s_po[G * D];
+  __shared__ float s_plse[G];
+
   const Dims& d = a.d;
   const int j = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane / LPR, cl = lane % LPR;
+  const int64_t bg = (int64_t)b * d.Hkv + g;
+  const float* kp = static_cast<const float*>(a.k_pages);
+  const float* vp = static_cast<const float*>(a.v_pages);
+  const bool use_logits = a.token_logits != nullptr;
+  const int32_t* list = a.sel_idx ? a.sel_idx + bg * a.k_max : nullptr;
+  const int units_cap = a.unit == kPage ? d.max_pages : d.max_seq;
+  const Span sp = span_of(a, j, list ? a.k_max : units_cap);
   const int n = clamp_len(a.seq_lens[b], d.max_seq);
   const int U = a.unit == kPage ? (n + d.P - 1) / d.P : n;
-  const int64_t bg = (int64_t)b * d.Hkv + g;
-  int cnt = U;
-  const int32_t* list = nullptr;
-  if (a.sel_idx != nullptr) {
-    cnt = min(min(a.sel_count[bg], a.k_max), U);
-    list = a.sel_idx + bg * a.k_max;
-  }
-  const int e0 = j * a.E;
-  const int e1 = min(cnt, e0 + a.E);
-  const int tpe = a.unit == kPage ? d.P : 1;
-  const int rows = e1 > e0 ? (e1 - e0) * tpe : 0;
-  const bool use_logits = a.token_logits != nullptr;
+  const int cnt = list ? min(a.sel_count[bg], a.k_max) : U;
+  auto unit_at = [&](int e) -> int { return list ? list[e] : e; };
 
-  const T* qb = static_cast<const T*>(a.q) + ((int64_t)b * d.Hq + g * G) * D + cl * 8;
-  const T* kp = static_cast<const T*>(a.k_pages);
-  const T* vp = static_cast<const T*>(a.v_pages);
   const float qs = d.scale * kLog2e;
   float qv[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    load8(qb + h * D, qv[h]);
+    load8(static_cast<const float*>(a.q) + ((int64_t)b * d.Hq + g * G + h) * D + cl * 8, qv[h]);
 #pragma unroll
     for (int c = 0; c < 8; ++c) qv[h][c] *= qs;
   }
-
   float m[G], l[G], acc[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -66,30 +487,13 @@ __global__ __launch_bounds__(kAttendThreads) void attend_splitk_kernel(AttendArg
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[h][c] = 0.f;
   }
-
+  const int rows = sp.nch * 16;
   for (int base = wave * RPW; base < rows; base += NW * RPW) {
     const int r = base + sub;
-    bool ok = r < rows;
-    int t = 0;
-    int64_t row_off = 0;
-    if (ok) {
-      const int e = e0 + r / tpe;
-      const int within = r - (r / tpe) * tpe;
-      const int uu = list ? list[e] : e;
-      if (a.unit == kPage) {
-        t = uu * d.P + within;
-        ok = uu >= 0 && uu < U && t < n;
-      } else {
-        t = uu;
-        ok = t >= 0 && t < n;
-      }
-      if (ok) {
-        const int lp = t / d.P;
-        const int phys = a.block_table[(int64_t)b * d.max_pages + lp];
-        ok = phys >= 0 && phys < d.num_pages;
-        row_off = (((int64_t)phys * d.Hkv + g) * d.P + (t - lp * d.P)) * D + cl * 8;
-      }
-    }
+    int t = 0, pr = -1;
+    if (r < rows) pr = resolve_row(a, sp, unit_at, cnt, n, U, b, g, r >> 4, r & 15, &t);
+    const bool ok = pr >= 0;
+    const int64_t off = (int64_t)pr * D + cl * 8;
     float s[G];
     if (use_logits) {
 #pragma unroll
@@ -98,7 +502,7 @@ __global__ __launch_bounds__(kAttendThreads) void attend_splitk_kernel(AttendArg
     } else {
       float kv[8];
       if (ok) {
-        load8(kp + row_off, kv);
+        load8(kp + off, kv);
       } else {
 #pragma unroll
         for (int c = 0; c < 8; ++c) kv[c] = 0.f;
@@ -108,14 +512,12 @@ __global__ __launch_bounds__(kAttendThreads) void attend_splitk_kernel(AttendArg
         float dot = 0.f;
 #pragma unroll
         for (int c = 0; c < 8; ++c) dot = fmaf(qv[h][c], kv[c], dot);
-#pragma unroll
-        for (int o = LPR / 2; o > 0; o >>= 1) dot += __shfl_xor(dot, o, LPR);
-        s[h] = dot;
+        s[h] = group_sum<LPR>(dot);
       }
     }
     if (ok) {
       float vv[8];
-      load8(vp + row_off, vv);
+      load8(vp + off, vv);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         const float mn = fmaxf(m[h], s[h]);
@@ -128,101 +530,102 @@ __global__ __launch_bounds__(kAttendThreads) void attend_splitk_kernel(AttendArg
       }
     }
   }
-
-  // Merge the RPW lane-rows of this wave (shuffles across rows of LPR lanes).
+  // per wave: lane-rows to LDS, merged below together with the other waves
+  if (cl == 0) {
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float M = m[h];
-#pragma unroll
-    for (int o = LPR; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
-    const float f = m[h] == -INFINITY ? 0.f : exp2f(m[h] - M);
-    l[h] *= f;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) acc[h][c] *= f;
-#pragma unroll
-    for (int o = LPR; o < 64; o <<= 1) {
-      l[h] += __shfl_xor(l[h], o);
-#pragma unroll
-      for (int c = 0; c < 8; ++c) acc[h][c] += __shfl_xor(acc[h][c], o);
-    }
-    m[h] = M;
-  }
-
-  // Merge the waves through LDS.
-  __shared__ float s_m[NW][G], s_l[NW][G];
-  __shared__ float s_acc[NW][G][D];
-  if (sub == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) s_acc[wave][h][cl * 8 + c] = acc[h][c];
-      if (cl == 0) { s_m[wave][h] = m[h]; s_l[wave][h] = l[h]; }
-    }
+    for (int h = 0; h < G; ++h) { s_m[wave][sub][h] = m[h]; s_l[wave][sub][h] = l[h]; }
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < G * D; idx += kAttendThreads) {
-    const int h = idx / D, c = idx - h * D;
-    float M = -INFINITY;
+  float M[G];
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][h]);
+  for (int h = 0; h < G; ++h) {
+    M[h] = -INFINITY;
+    for (int w = 0; w < NW; ++w)
+      for (int q = 0; q < RPW; ++q) M[h] = fmaxf(M[h], s_m[w][q][h]);
+  }
+  // each lane-row rescales to the block max, then rows of a wave add up in LDS
+  for (int h = 0; h < G; ++h) {
+    const float f = m[h] == -INFINITY ? 0.f : exp2f(m[h] - M[h]);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[h][c] *= f;
+  }
+  for (int q = 0; q < RPW; ++q) {
+    if (sub == q) {
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          float* dst = &s_acc[wave][h][cl * 8 + c];
+          *dst = (q == 0 ? 0.f : *dst) + acc[h][c];
+        }
+    }
+    __syncthreads();
+  }
+  for (int i = threadIdx.x; i < G * D; i += NT) {
+    const int h = i / D, c = i - h * D;
     float L = 0.f, A = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
+    if (M[h] != -INFINITY) {
       for (int w = 0; w < NW; ++w) {
-        const float f = s_m[w][h] == -INFINITY ? 0.f : exp2f(s_m[w][h] - M);
-        L = fmaf(s_l[w][h], f, L);
-        A = fmaf(s_acc[w][h][c], f, A);
+        A += s_acc[w][h][c];
+        for (int q = 0; q < RPW; ++q)
+          L += s_m[w][q][h] == -INFINITY ? 0.f : s_l[w][q][h] * exp2f(s_m[w][q][h] - M[h]);
       }
     }
-    const int64_t hs = ((int64_t)b * d.Hq + g * G + h) * a.S + j;
-    a.part_o[hs * D + c] = L > 0.f ? A / L : 0.f;
-    if (c == 0) a.part_lse[hs] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+    s_po[i] = L > 0.f ? A / L : 0.f;
+    if (c == 0) s_plse[h] = L > 0.f ? (M[h] + log2f(L)) * kLn2 : -INFINITY;
   }
+  __syncthreads();
+  write_partial<D, G, NT>(a, b, g, j, s_po, s_plse);
 }
 
-// One block per (sequence, query head), one thread per channel.
-template <int D>
-__global__ __launch_bounds__(D) void merge_lse_kernel(const float* __restrict__ part_o,
-                                                      const float* __restrict__ part_lse,
-                                                      float* __restrict__ out,
-                                                      float* __restrict__ lse, int S) {
-  const int64_t bh = blockIdx.x;
-  const int c = threadIdx.x;
-  const float* pl = part_lse + bh * S;
-  float M = -INFINITY;
-  for (int j = 0; j < S; ++j) M = fmaxf(M, pl[j]);
-  if (M == -INFINITY) {
-    out[bh * D + c] = 0.f;
-    if (c == 0) lse[bh] = -INFINITY;
-    return;
-  }
-  float L = 0.f, A = 0.f;
-  for (int j = 0; j < S; ++j) {
-    const float w = expf(pl[j] - M);
-    L += w;
-    A = fmaf(w, part_o[(bh * S + j) * D + c], A);
-  }
-  out[bh * D + c] = A / L;
-  if (c == 0) lse[bh] = M + logf(L);
+// Keys per thread the in-kernel selection uses for max_pages units: the whole
+// block selects (a single wave's dependent instruction chain is slower).
+static int select_mode(int max_pages) {
+  if (max_pages <= kAttendWaves * 64 * 4) return kBlock4;
+  if (max_pages <= kAttendWaves * 64 * 8) return kBlock8;
+  return kBlock32;
 }
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
   const Dims& d = a.d;
+  if (a.S < 1 || a.S > kMaxSplits) return hipErrorInvalidValue;
+  const bool selects = a.unit_scores != nullptr;
+  if (selects && (a.unit != kPage || a.sel_idx != nullptr || d.dtype != kBF16 ||
+                  a.E > kMaxSelectE || d.max_pages > kMaxSelectU))
+    return hipErrorInvalidValue;
   const dim3 grid(a.S, d.Hkv, d.B);
+  const bool logits = a.token_logits != nullptr;
   const bool ok = dispatch_tdg(d.dtype, d.D, d.G, [&](auto t, auto dd, auto gg) {
     using T = decltype(t);
     constexpr int D = decltype(dd)::value;
     constexpr int G = decltype(gg)::value;
-    attend_splitk_kernel<T, D, G><<<grid, kAttendThreads, 0, st>>>(a);
+    constexpr int NT = kAttendWaves * 64;
+    if constexpr (std::is_same<T, float>::value) {
+      attend_f32_kernel<D, G><<<grid, NT, 0, st>>>(a);
+    } else if (selects) {
+      switch (select_mode(d.max_pages)) {
+        case kBlock4: attend_mfma_kernel<D, G, false, kBlock4><<<grid, NT, 0, st>>>(a); break;
+        case kBlock8: attend_mfma_kernel<D, G, false, kBlock8><<<grid, NT, 0, st>>>(a); break;
+        default: attend_mfma_kernel<D, G, false, kBlock32><<<grid, NT, 0, st>>>(a); break;
+      }
+    } else if (logits) {
+      attend_mfma_kernel<D, G, true, kListed><<<grid, NT, 0, st>>>(a);
+    } else {
+      attend_mfma_kernel<D, G, false, kListed><<<grid, NT, 0, st>>>(a);
+    }
   });
   if (!ok) return hipErrorInvalidValue;
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int bh = d.B * d.Hq;
-  if (d.D == 64)
-    merge_lse_kernel<64><<<bh, 64, 0, st>>>(a.part_o, a.part_lse, a.out, a.lse, a.S);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const MergeArgs& a, hipStream_t st) {
+  const int bh = a.d.B * a.d.Hq;
+  if (a.d.D == 64)
+    merge_splits_kernel<64><<<bh, 256, 0, st>>>(a.part_o, a.part_lse, a.split_count, a.out,
+                                                a.lse, a.S_max);
   else
-    merge_lse_kernel<128><<<bh, 128, 0, st>>>(a.part_o, a.part_lse, a.out, a.lse, a.S);
+    merge_splits_kernel<128><<<bh, 256, 0, st>>>(a.part_o, a.part_lse, a.split_count, a.out,
+                                                 a.lse, a.S_max);
   return hipGetLastError();
 }
 

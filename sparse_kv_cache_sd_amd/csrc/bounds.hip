@@ -7,6 +7,8 @@
 
 namespace sdkv {
 
+// Layout of the result: [B][H_kv][max_pages][2][d] in logical page order, so
+// that scoring streams a sequence's statistics without the block table.
 // grid (max_pages, B), block 256: one block per logical page of a sequence,
 // one thread per (KV head, channel) pair, looping over the page's valid rows.
 template <typename T>
@@ -29,7 +31,7 @@ __global__ __launch_bounds__(256) void page_bounds_kernel(
       lo = fminf(lo, v);
       hi = fmaxf(hi, v);
     }
-    T* dst = bounds + ((int64_t)phys * d.Hkv + g) * 2 * d.D + c;
+    T* dst = bounds + (((int64_t)b * d.Hkv + g) * d.max_pages + u) * 2 * d.D + c;
     dst[0] = from_f<T>(lo);
     dst[d.D] = from_f<T>(hi);
   }

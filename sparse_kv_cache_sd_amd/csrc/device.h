@@ -50,6 +50,110 @@ __device__ __forceinline__ int clamp_len(int n, int max_seq) {
   return n < 0 ? 0 : (n > max_seq ? max_seq : n);
 }
 
+// ---- cross-lane exchange without the LDS crossbar ----
+// DPP moves within rows of 16 lanes: quad_perm xor 1 (0xB1), xor 2 (0x4E),
+// row_half_mirror (lane i reads 7 - i within 8, 0x141), row_mirror (lane i
+// reads 15 - i within 16, 0x140).  After the quad steps every lane of a quad
+// holds the quad total, so a mirror pairs each lane with the other half.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of W lanes (W = 4, 8 or 16); every lane gets its group's total.
+template <int W>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(W == 4 || W == 8 || W == 16, "group width");
+  x += dpp_mov<0xB1>(x);
+  x += dpp_mov<0x4E>(x);
+  if constexpr (W >= 8) x += dpp_mov<0x141>(x);
+  if constexpr (W >= 16) x += dpp_mov<0x140>(x);
+  return x;
+}
+
+// Max over aligned groups of W lanes (W = 4, 8 or 16), same pairing as group_sum.
+template <int W>
+__device__ __forceinline__ float group_max(float x) {
+  static_assert(W == 4 || W == 8 || W == 16, "group width");
+  x = fmaxf(x, dpp_mov<0xB1>(x));
+  x = fmaxf(x, dpp_mov<0x4E>(x));
+  if constexpr (W >= 8) x = fmaxf(x, dpp_mov<0x141>(x));
+  if constexpr (W >= 16) x = fmaxf(x, dpp_mov<0x140>(x));
+  return x;
+}
+
+// gfx950 permlane swaps with old == src == x: the two results hold x of this
+// lane and of lane ^ 32 (permlane32) or lane ^ 16 (permlane16), in an order
+// that depends on the lane, so only symmetric combinations are formed.
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Inclusive prefix sum over the 64 lanes with DPP: row shifts by 1, 2, 4, 8
+// (lanes without a source in their row add 0), then lane 15 of each row feeds
+// the next row and lane 31 the upper half.
+__device__ __forceinline__ uint32_t wave_scan_dpp(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);
+  return v;
+}
+
+// Value of lane 63 broadcast to the wave.
+__device__ __forceinline__ uint32_t wave_last(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Wave-wide unsigned min / max: DPP within rows of 16, permlane swaps across rows.
+__device__ __forceinline__ uint32_t wave_umin(uint32_t v) {
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xF, 0xF, false));
+  auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  v = min(r[0], r[1]);
+  r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return min(r[0], r[1]);
+}
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xF, 0xF, false));
+  auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  v = max(r[0], r[1]);
+  r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return max(r[0], r[1]);
+}
+
+// Wave-wide max and sum (64 lanes) through the LDS crossbar; used off the hot loop.
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
 // Inclusive prefix sum over the 64 lanes of a wavefront.
 template <typename V>
 __device__ __forceinline__ V wave_incl_scan(V v) {

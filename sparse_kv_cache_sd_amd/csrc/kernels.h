@@ -64,16 +64,41 @@ struct AttendArgs {
   int k_max;
   const float* token_logits;  // token unit: read logits instead of q.K
   int E;                      // kept units per split
-  int S;                      // splits per (sequence, KV head)
+  int S;                      // splits per (sequence, KV head), <= kMaxSplits
   float* part_o;              // [B][Hq][S][D]  split outputs, normalised
   float* part_lse;            // [B][Hq][S]     split log-sum-exp (-inf: empty)
-  float* out;                 // [B][Hq][D]
-  float* lse;                 // [B][Hq]
+  int32_t* split_count;       // S, written for the merge kernel
+  // In-kernel selection (page unit, bf16): when unit_scores is set, every
+  // block selects the top-k pages of its (sequence, KV head) itself and
+  // attends its slice of them; sel_idx must then be NULL.
+  const float* unit_scores;   // [B][Hkv][max_pages]
+  int R_ppm;                  // keep ratio in parts per million (< 0: all)
+  int32_t* sel_out;           // optional [B][Hkv][k_max]: kept list (split 0 writes it)
+  int32_t* sel_count_out;     // optional [B][Hkv]
 };
+
+// Most splits one (sequence, KV head) is cut into.
+constexpr int kMaxSplits = 256;
+// Largest slice of the kept list a selecting attention block may own, and
+// the most units it can select from.
+constexpr int kMaxSelectE = 2048;
+constexpr int kMaxSelectU = 16384;
 
 hipError_t launch_page_bounds(const BoundsArgs& a, hipStream_t st);
 hipError_t launch_score(const ScoreArgs& a, hipStream_t st);
 hipError_t launch_select(const SelectArgs& a, hipStream_t st);
+// Log-sum-exp merge of the split partials written by an attention launch.
+struct MergeArgs {
+  Dims d;
+  const float* part_o;
+  const float* part_lse;
+  const int32_t* split_count;
+  int S_max;
+  float* out;                 // [B][Hq][D]
+  float* lse;                 // [B][Hq]
+};
+
 hipError_t launch_attend(const AttendArgs& a, hipStream_t st);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t st);
 
 }  // namespace sdkv

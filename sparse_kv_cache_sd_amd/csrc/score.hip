@@ -7,145 +7,239 @@
 // sum_c max(q_c kmin_c, q_c kmax_c) = sum_c q_c * (q_c >= 0 ? kmax_c : kmin_c)
 // because kmin_c <= kmax_c, and rounding is monotone, so the selected product
 // is also the larger one in floating point.  The group's score is the max over
-// its G query heads.
+// its G query heads.  The statistics are kept per sequence in logical page
+// order, so scoring streams them without a block-table lookup.  A page's
+// bound pair is read by LPR = d/8 consecutive lanes, 8 channels (16 B of
+// bf16) each; partial sums are reduced with DPP row moves, and every lane
+// issues the loads of kScoreIters pages at once, before the sequence length
+// is known.
 //
 // Token unit: the exact logits scale * q.K of every valid key, kept for the
 // attention pass, and their max over the group ("... list view", Abstract:
-// attention-scored KV selection reads every key once).
-//
-// Layout of work: one row (a page's bound pair, or a token's key) is read by
-// LPR = d/8 consecutive lanes, 8 channels (16 B of bf16) each, so a wave
-// reads 64/LPR rows per load; each lane holds its 8 channels of the group's
-// G queries in registers, and partial sums are reduced across the LPR lanes.
+// attention-scored KV selection reads every key once).  For bf16 the 16-row
+// chunks go through the matrix cores exactly as in the attention kernel
+// (S^T = K Q^T with mfma 16x16x32); for fp32 the vector path is used.
 #include "device.h"
 
 namespace sdkv {
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
 constexpr int kScoreThreads = 256;
-constexpr int kScoreRowsPerBlock = 256;
+constexpr int kScoreIters = 4;
+
+template <typename T, int D>
+constexpr int score_rows_per_block() {
+  return (kScoreThreads / 64) * kScoreIters * (64 / (D / 8));
+}
 
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kScoreThreads) void score_pages_kernel(
     const T* __restrict__ q, const T* __restrict__ bounds,
-    const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
-    float* __restrict__ scores, Dims d) {
+    const int32_t* __restrict__ seq_lens, float* __restrict__ scores, Dims d) {
   constexpr int LPR = D / 8;
   constexpr int RPW = 64 / LPR;
-  constexpr int NW = kScoreThreads / 64;
+  constexpr int IT = kScoreIters;
+  constexpr int PPB = score_rows_per_block<T, D>();
   const int g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane / LPR, cl = lane % LPR;
-  const int n = clamp_len(seq_lens[b], d.max_seq);
-  const int U = (n + d.P - 1) / d.P;
-  const int u0 = blockIdx.x * kScoreRowsPerBlock;
-  if (u0 >= U) return;
-  const int u1 = min(U, u0 + kScoreRowsPerBlock);
-
+  const int u0 = blockIdx.x * PPB;
   float qv[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h)
     load8(q + ((int64_t)b * d.Hq + g * G + h) * D + cl * 8, qv[h]);
 
-  float* out = scores + ((int64_t)b * d.Hkv + g) * d.max_pages;
-  for (int base = u0 + wave * RPW; base < u1; base += NW * RPW) {
-    const int u = base + sub;
-    bool ok = u < u1;
-    int phys = ok ? block_table[(int64_t)b * d.max_pages + u] : -1;
-    ok = ok && phys >= 0 && phys < d.num_pages;
-    float lo[8], hi[8];
-    if (ok) {
-      const T* row = bounds + ((int64_t)phys * d.Hkv + g) * 2 * D + cl * 8;
-      load8(row, lo);
-      load8(row + D, hi);
+  // statistics are stored in logical page order: no block-table lookup
+  const T* bnd = bounds + ((int64_t)b * d.Hkv + g) * d.max_pages * 2 * D + cl * 8;
+  float lo[IT][8], hi[IT][8];
+  int uu[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    uu[it] = u0 + (wave * IT + it) * RPW + sub;
+    if (uu[it] < d.max_pages) {
+      load8(bnd + (int64_t)uu[it] * 2 * D, lo[it]);
+      load8(bnd + (int64_t)uu[it] * 2 * D + D, hi[it]);
     } else {
 #pragma unroll
-      for (int c = 0; c < 8; ++c) lo[c] = hi[c] = 0.f;
+      for (int c = 0; c < 8; ++c) lo[it][c] = hi[it][c] = 0.f;
     }
+  }
+  const int n = clamp_len(seq_lens[b], d.max_seq);
+  const int U = (n + d.P - 1) / d.P;
+  float* out = scores + ((int64_t)b * d.Hkv + g) * d.max_pages;
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
     float best = -INFINITY;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float acc = 0.f;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) acc = fmaf(qv[h][c], qv[h][c] >= 0.f ? hi[c] : lo[c], acc);
-#pragma unroll
-      for (int o = LPR / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, LPR);
+      for (int c = 0; c < 8; ++c) acc = fmaf(qv[h][c], qv[h][c] >= 0.f ? hi[it][c] : lo[it][c], acc);
+      acc = group_sum<LPR>(acc);
       best = fmaxf(best, acc * d.scale);
     }
-    // A page whose block-table entry is out of range ranks last.
-    if (u < u1 && cl == 0) out[u] = ok ? best : -3.0e38f;
+    if (uu[it] < U && cl == 0) out[uu[it]] = best;
   }
 }
 
-template <typename T, int D, int G>
-__global__ __launch_bounds__(kScoreThreads) void score_tokens_kernel(
-    const T* __restrict__ q, const T* __restrict__ k_pages,
+// fp32 token scorer (vector FMAs).
+template <int D, int G>
+__global__ __launch_bounds__(kScoreThreads) void score_tokens_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ k_pages,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
     float* __restrict__ scores, float* __restrict__ logits, Dims d) {
   constexpr int LPR = D / 8;
   constexpr int RPW = 64 / LPR;
-  constexpr int NW = kScoreThreads / 64;
+  constexpr int IT = kScoreIters;
+  constexpr int TPB = score_rows_per_block<float, D>();
   const int g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane / LPR, cl = lane % LPR;
   const int n = clamp_len(seq_lens[b], d.max_seq);
-  const int t0 = blockIdx.x * kScoreRowsPerBlock;
+  const int t0 = blockIdx.x * TPB;
   if (t0 >= n) return;
-  const int t1 = min(n, t0 + kScoreRowsPerBlock);
 
   float qv[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h)
     load8(q + ((int64_t)b * d.Hq + g * G + h) * D + cl * 8, qv[h]);
 
-  float* sc = scores + ((int64_t)b * d.Hkv + g) * d.max_seq;
-  for (int base = t0 + wave * RPW; base < t1; base += NW * RPW) {
-    const int t = base + sub;
-    bool ok = t < t1;
-    const int lp = t / d.P;
-    int phys = ok ? block_table[(int64_t)b * d.max_pages + lp] : -1;
-    ok = ok && phys >= 0 && phys < d.num_pages;
-    float kv[8];
-    if (ok) {
-      load8(k_pages + (((int64_t)phys * d.Hkv + g) * d.P + (t - lp * d.P)) * D + cl * 8, kv);
+  float kv[IT][8];
+  bool ok[IT];
+  int tt[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    tt[it] = t0 + (wave * IT + it) * RPW + sub;
+    ok[it] = tt[it] < n;
+    const int lp = tt[it] / d.P;
+    const int phys = ok[it] ? block_table[(int64_t)b * d.max_pages + lp] : -1;
+    ok[it] = ok[it] && phys >= 0 && phys < d.num_pages;
+    if (ok[it]) {
+      load8(k_pages + (((int64_t)phys * d.Hkv + g) * d.P + (tt[it] - lp * d.P)) * D + cl * 8, kv[it]);
     } else {
 #pragma unroll
-      for (int c = 0; c < 8; ++c) kv[c] = 0.f;
+      for (int c = 0; c < 8; ++c) kv[it][c] = 0.f;
     }
+  }
+  float* sc = scores + ((int64_t)b * d.Hkv + g) * d.max_seq;
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
     float best = -INFINITY, mine = 0.f;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float acc = 0.f;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) acc = fmaf(qv[h][c], kv[c], acc);
-#pragma unroll
-      for (int o = LPR / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, LPR);
-      const float s = acc * d.scale;
+      for (int c = 0; c < 8; ++c) acc = fmaf(qv[h][c], kv[it][c], acc);
+      const float s = group_sum<LPR>(acc) * d.scale;
       best = fmaxf(best, s);
       if (h == cl) mine = s;
     }
-    if (t < t1) {
-      if (!ok) { best = -3.0e38f; mine = -3.0e38f; }
+    const int t = tt[it];
+    if (t < n) {
+      if (!ok[it]) { best = -3.0e38f; mine = -3.0e38f; }
       if (cl < G) logits[((int64_t)b * d.Hq + g * G + cl) * d.max_seq + t] = mine;
       if (cl == 0) sc[t] = best;
     }
   }
 }
 
+// bf16 token scorer on the matrix cores: each wave scores kScoreIters chunks
+// of 16 consecutive tokens (16 | P, so a chunk lies in one page and its rows
+// are contiguous in the page tile).
+template <int D, int G>
+__global__ __launch_bounds__(kScoreThreads) void score_tokens_mfma_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_pages,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
+    float* __restrict__ scores, float* __restrict__ logits, Dims d) {
+  constexpr int KS = D / 32;
+  constexpr int IT = kScoreIters;
+  constexpr int NW = kScoreThreads / 64;
+  constexpr int TPB = NW * IT * 16;
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = lane & 15, quad = lane >> 4;
+  const int n = clamp_len(seq_lens[b], d.max_seq);
+  const int t0 = blockIdx.x * TPB;
+  if (t0 >= n) return;
+
+  bf16x8_t qop[KS];
+  {
+    const bf16_t* qrow = q + ((int64_t)b * d.Hq + g * G + row) * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      uint4 w = make_uint4(0u, 0u, 0u, 0u);
+      if (row < G) w = *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * quad);
+      qop[s] = __builtin_bit_cast(bf16x8_t, w);
+    }
+  }
+  uint4 kv[IT][KS];
+  bool page_ok[IT];
+  int tc[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    tc[it] = t0 + (wave * IT + it) * 16;
+    const int t = tc[it] + row;
+    const int lp = tc[it] / d.P;
+    const int phys = tc[it] < n ? block_table[(int64_t)b * d.max_pages + lp] : -1;
+    page_ok[it] = phys >= 0 && phys < d.num_pages;
+    const bool ok = page_ok[it] && t < n;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      kv[it][s] = make_uint4(0u, 0u, 0u, 0u);
+      if (ok)
+        kv[it][s] = *reinterpret_cast<const uint4*>(
+            k_pages + (((int64_t)phys * d.Hkv + g) * d.P + (t - lp * d.P)) * D + 32 * s + 8 * quad);
+    }
+  }
+  float* sc = scores + ((int64_t)b * d.Hkv + g) * d.max_seq;
+  float* lg = logits + ((int64_t)b * d.Hq + g * G + row) * d.max_seq;
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    if (tc[it] >= n) continue;
+    float4_t st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv[it][s]), qop[s],
+                                                    st, 0, 0, 0);
+    // lane (row = head, quad) holds tokens tc + 4 quad + r
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = tc[it] + 4 * quad + r;
+      const float x = page_ok[it] ? st[r] * d.scale : -3.0e38f;
+      const float best = group_max<16>(row < G ? x : -INFINITY);
+      if (t < n) {
+        if (row < G) lg[t] = x;
+        if (row == 0) sc[t] = best;
+      }
+    }
+  }
+}
+
 hipError_t launch_score(const ScoreArgs& a, hipStream_t st) {
   const Dims& d = a.d;
-  const int U_max = a.unit == kPage ? d.max_pages : d.max_seq;
-  const dim3 grid((U_max + kScoreRowsPerBlock - 1) / kScoreRowsPerBlock, d.Hkv, d.B);
   const bool ok = dispatch_tdg(d.dtype, d.D, d.G, [&](auto t, auto dd, auto gg) {
     using T = decltype(t);
     constexpr int D = decltype(dd)::value;
     constexpr int G = decltype(gg)::value;
     if (a.unit == kPage) {
+      constexpr int R = score_rows_per_block<T, D>();
+      const dim3 grid((d.max_pages + R - 1) / R, d.Hkv, d.B);
       score_pages_kernel<T, D, G><<<grid, kScoreThreads, 0, st>>>(
-          static_cast<const T*>(a.q), static_cast<const T*>(a.bounds), a.block_table,
-          a.seq_lens, a.unit_scores, d);
+          static_cast<const T*>(a.q), static_cast<const T*>(a.bounds), a.seq_lens,
+          a.unit_scores, d);
+    } else if constexpr (std::is_same<T, float>::value) {
+      constexpr int R = score_rows_per_block<T, D>();
+      const dim3 grid((d.max_seq + R - 1) / R, d.Hkv, d.B);
+      score_tokens_f32_kernel<D, G><<<grid, kScoreThreads, 0, st>>>(
+          static_cast<const float*>(a.q), static_cast<const float*>(a.k_pages), a.block_table,
+          a.seq_lens, a.unit_scores, a.token_logits, d);
     } else {
-      score_tokens_kernel<T, D, G><<<grid, kScoreThreads, 0, st>>>(
-          static_cast<const T*>(a.q), static_cast<const T*>(a.k_pages), a.block_table,
+      constexpr int R = (kScoreThreads / 64) * kScoreIters * 16;
+      const dim3 grid((d.max_seq + R - 1) / R, d.Hkv, d.B);
+      score_tokens_mfma_kernel<D, G><<<grid, kScoreThreads, 0, st>>>(
+          static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k_pages), a.block_table,
           a.seq_lens, a.unit_scores, a.token_logits, d);
     }
   });

@@ -60,7 +60,7 @@ def upload(w: kvsynth.Workload, softmax_scale: float = 0.0) -> Dev:
     shape = sd.Shape(r.batch, r.num_q_heads, r.num_kv_heads, r.head_dim, r.page_size,
                      w.max_pages(), w.n_alloc, r.dtype, pc.num_pages, softmax_scale)
     dt = torch.float32 if r.dtype == "f32" else torch.bfloat16
-    bounds = torch.zeros((pc.num_pages, r.num_kv_heads, 2, r.head_dim), dtype=dt, device="cuda")
+    bounds = torch.zeros(sd.bounds_shape(shape), dtype=dt, device="cuda")
     dev = Dev(w, shape, t_dev(w.q, r.dtype), t_dev(pc.k_pool, r.dtype), t_dev(pc.v_pool, r.dtype),
               torch.from_numpy(pc.block_table).cuda(), torch.from_numpy(w.seq_lens).cuda(), bounds)
     sd.update_page_bounds(shape, dev.k, dev.bt, dev.sl, dev.bounds)

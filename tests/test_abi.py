@@ -1,0 +1,102 @@
+"""The C ABI without a GPU: the library loads, exports every entry point
+include/sd.h declares, and rejects bad host-visible arguments with the
+documented status before touching the device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_kv_cache_sd_amd as sd
+from sparse_kv_cache_sd_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "sd.h")
+
+
+def declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"SD_API\s+[\w\s\*]+?\b(sd_\w+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    names = declared()
+    assert len(names) >= 10
+    assert sorted(_lib.EXPORTS) == names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(sd.LIB_PATH)
+    for name in declared():
+        assert hasattr(lib, name), name
+
+
+@pytest.mark.parametrize("r,U,k", [(0.3, 2048, 615), (0.07, 100, 7), (0.05, 16384, 820),
+                                   (1.0, 9, 9), (2.0, 9, 9), (1e-9, 50, 1)])
+def test_keep_count_matches_rule(r, U, k):
+    assert sd.keep_count(r, U) == k
+
+
+def test_keep_count_rejects():
+    assert sd.lib().sd_keep_count(0.0, 10) == -1
+    assert sd.lib().sd_keep_count(float("nan"), 10) == -1
+    assert sd.lib().sd_keep_count(0.5, 0) == -1
+
+
+def _shape(**kw):
+    base = dict(batch=1, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
+                max_pages_per_seq=2048, max_seq_len=32768, dtype="bf16", num_pages=2048)
+    base.update(kw)
+    return sd.Shape(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), 6), (dict(page_size=32), 6), (dict(num_q_heads=48), 6),
+    (dict(num_q_heads=30), 2), (dict(max_seq_len=40000), 2), (dict(batch=0), 2),
+    (dict(num_pages=0), 2),
+])
+def test_shape_validation(kw, status):
+    with pytest.raises(sd.SdError) as e:
+        sd.workspace_bytes(_shape(**kw), "page", 0.3)
+    assert e.value.status == status
+
+
+def test_ratio_and_unit_validation():
+    with pytest.raises(sd.SdError) as e:
+        sd.workspace_bytes(_shape(), "page", 0.0)
+    assert e.value.status == 4
+    n = ctypes.c_size_t()
+    st = sd.lib().sd_workspace_bytes(ctypes.byref(_shape().c()), 7, 0.3, ctypes.byref(n))
+    assert st == 2
+
+
+def test_workspace_grows_with_selection_buffers():
+    s = _shape()
+    page = sd.workspace_bytes(s, "page", 0.3)
+    tok = sd.workspace_bytes(s, "token", 0.3)
+    assert tok > page > 0
+
+
+def test_null_pointers_rejected_before_any_launch():
+    lib = sd.lib()
+    sh = ctypes.byref(_shape().c())
+    st = lib.sd_decode_step(sh, None, None, None, None, None, None, 1, 0.3, None, None, None,
+                            None, None, 0, None)
+    assert st == 1 and b"required" in lib.sd_last_error()
+    st = lib.sd_attend_splitk(sh, None, None, None, None, None, 1, None, None, 0, None, None,
+                              None, None, 0, None)
+    assert st == 1
+    st = lib.sd_select_topk(sh, 1, None, None, 0.3, None, None, None, 0, None)
+    assert st == 1
+    st = lib.sd_merge_splits(sh, None, None, None, 0, None)
+    assert st == 1
+
+
+def test_workspace_size_and_alignment_checked():
+    lib = sd.lib()
+    sh = ctypes.byref(_shape().c())
+    fake = ctypes.c_void_p(0x10000)       # never dereferenced: validation fails first
+    st = lib.sd_merge_splits(sh, fake, fake, ctypes.c_void_p(0x10010), 1 << 30, None)
+    assert st == 5 and b"aligned" in lib.sd_last_error()
+    st = lib.sd_merge_splits(sh, fake, fake, ctypes.c_void_p(0x10000), 16, None)
+    assert st == 5 and b"smaller" in lib.sd_last_error()

@@ -39,9 +39,9 @@ def test_page_bounds_bitexact(name, kw):
         n = int(w.seq_lens[b])
         for g in range(s.num_kv_heads):
             kmin, kmax = sdref.page_bounds(sdref.widen(w.K[b, g, :n], s.dtype), s.page_size)
-            ids = dev.bt[b, :kmin.shape[0]].cpu().numpy()
-            np.testing.assert_array_equal(got[ids, g, 0], kmin)
-            np.testing.assert_array_equal(got[ids, g, 1], kmax)
+            U = kmin.shape[0]
+            np.testing.assert_array_equal(got[b, g, :U, 0], kmin)
+            np.testing.assert_array_equal(got[b, g, :U, 1], kmax)
 
 
 # ------------------------------------------------------------- scores
@@ -252,3 +252,65 @@ def test_deterministic_repeat():
     b = run_decode(dev, "page", 0.3)
     for x, y in zip(a, b):
         np.testing.assert_array_equal(x, y)
+
+
+# ------------------------------------------------------------- fused selection + attention
+
+@pytest.mark.parametrize("name,kw,r", [
+    ("l8b", dict(seq_len=4096 + 7), 0.3),
+    ("l8b", dict(seq_len=4096 + 7, dtype="f32"), 0.3),          # two-stage path
+    ("l70b", dict(seq_len=64 * 90 + 11), 0.05),
+    ("batch", dict(batch=3, seq_len=5000, seq_len_min=900), 0.2),
+    ("l8b", dict(seq_len=700, num_q_heads=8, num_kv_heads=8), 0.5),
+])
+def test_select_attend_matches_oracle(name, kw, r):
+    """sd_select_attend: in-kernel top-k + split-K attention against the oracle,
+    and its selection outputs against sd_select_topk on the same scores."""
+    dev = upload(kvsynth.generate(_recipe(name, **kw)))
+    w, s = dev.w, dev.shape
+    scale = 1 / math.sqrt(s.head_dim)
+    scores = torch.empty((s.batch, s.num_kv_heads, s.max_pages_per_seq), device="cuda")
+    sd.score_pages(s, dev.q, dev.k, dev.bounds, dev.bt, dev.sl, "page", scores)
+    k_max = sd.keep_count(r, s.max_pages_per_seq)
+    ws = sd.alloc_workspace(s, "page", r)
+    out = torch.empty((s.batch, s.num_q_heads, s.head_dim), device="cuda")
+    lse = torch.empty((s.batch, s.num_q_heads), device="cuda")
+    sel = torch.full((s.batch, s.num_kv_heads, k_max), -1, dtype=torch.int32, device="cuda")
+    cnt = torch.full((s.batch, s.num_kv_heads), -1, dtype=torch.int32, device="cuda")
+    sd.select_attend(s, dev.q, dev.k, dev.v, dev.bt, dev.sl, scores, r, out, lse, ws, sel, cnt)
+    sel2 = torch.full_like(sel, -1)
+    cnt2 = torch.full_like(cnt, -1)
+    sd.select_topk(s, "page", dev.sl, scores, r, sel2, cnt2)
+    torch.cuda.synchronize()
+    cnt_h = cnt.cpu().numpy()
+    np.testing.assert_array_equal(cnt_h, cnt2.cpu().numpy())
+    for b in range(s.batch):
+        for g in range(s.num_kv_heads):
+            k = int(cnt_h[b, g])
+            np.testing.assert_array_equal(sel[b, g, :k].cpu().numpy(), sel2[b, g, :k].cpu().numpy())
+    out, lse, sel = out.cpu().numpy(), lse.cpu().numpy(), sel.cpu().numpy()
+    G, tol = s.group, (1e-5 if s.dtype == "f32" else 2e-2)
+    for b in range(s.batch):
+        for g in range(s.num_kv_heads):
+            kept = sel[b, g, :cnt_h[b, g]].astype(np.int64)
+            ref = oracle_group(w, b, g, "page", r, scale, kept_override=kept)
+            assert np.abs(out[b, g * G:(g + 1) * G] - ref.out_sparse).max() <= tol
+            assert np.abs(lse[b, g * G:(g + 1) * G] - ref.lse_sparse).max() <= tol
+
+
+def test_workspace_reuse_is_stable():
+    """Repeated steps on one workspace give identical results."""
+    rec = R["batch"].with_(batch=2, seq_len=3000, seq_len_min=2000)
+    dev = upload(kvsynth.generate(rec))
+    s = dev.shape
+    for unit, r in [("page", 0.3), ("token", 0.2), ("page", 1.0)]:
+        ws = sd.alloc_workspace(s, unit, r)
+        outs = []
+        for _ in range(3):
+            out = torch.empty((s.batch, s.num_q_heads, s.head_dim), device="cuda")
+            lse = torch.empty((s.batch, s.num_q_heads), device="cuda")
+            sd.decode_step(s, dev.q, dev.k, dev.v, dev.bounds, dev.bt, dev.sl, unit, r, out, lse, ws)
+            outs.append((out.cpu().numpy(), lse.cpu().numpy()))
+        for o, l in outs[1:]:
+            np.testing.assert_array_equal(o, outs[0][0])
+            np.testing.assert_array_equal(l, outs[0][1])
