@@ -20,6 +20,7 @@ oracle timed on a bounded sample on the host cores.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -105,6 +106,116 @@ def kept_token_count(sel, cnt, seq_lens, unit, P):
 
 
 # ----------------------------------------------------------------------------
+# HBM traffic of the dominant kernel from committed rocprofv3 counter passes
+# ----------------------------------------------------------------------------
+
+KERNEL_SOURCES = ["attend.hip", "topk.h", "device.h", "kernels.h"]
+COPY_BYTES = 1 << 30            # one plain copy: 1 GiB read + 1 GiB written
+
+
+def kernel_sources_sha():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "sparse_kv_cache_sd_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(workload):
+    return os.path.join(ROOT, "profiles", f"attend_mfma_{workload}_traffic.txt")
+
+
+def read_traffic(workload):
+    """HBM bytes per launch of the attention kernel: FETCH_SIZE and WRITE_SIZE
+    (KiB per dispatch, rocprofv3 --pmc, one pass each) scaled by what the same
+    counters read for a plain 1 GiB copy.  None when no summary exists or the
+    kernel sources changed since the counters were taken."""
+    path = traffic_file(workload)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if "=" in line and not line.lstrip().startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_sources_sha256_16") != kernel_sources_sha():
+        return None
+    f = float(kv["attend_fetch_kib_per_dispatch"]) * 1024 * float(kv["fetch_scale"])
+    w = float(kv["attend_write_kib_per_dispatch"]) * 1024 * float(kv["write_scale"])
+    return int(f + w)
+
+
+def copy_calibration():
+    """A plain device copy of COPY_BYTES, run a few times, so a counter pass
+    over this process also sees what the counters read for known traffic."""
+    import torch
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+
+
+def summarize_pmc(fetch_dir, write_dir, workload, out_path, cmd_fetch, cmd_write):
+    """Writes the traffic summary from the counter_collection.csv files of
+    the two passes (attention kernel of the page-unit step vs. the copy)."""
+    import csv
+    import glob
+
+    def rows(d):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        assert files, f"no counter_collection.csv under {d}"
+        out = []
+        for f in files:
+            with open(f) as fh:
+                out += [(r["Kernel_Name"], r["Grid_Size"], float(r["Counter_Value"]))
+                        for r in csv.DictReader(fh)]
+        return out
+
+    def mean(rs, pred):
+        v = [x for n, gsz, x in rs if pred(n, gsz)]
+        assert v, "kernel not found in the counter pass"
+        return sum(v) / len(v), len(v)
+
+    fr, wr = rows(fetch_dir), rows(write_dir)
+    # the in-kernel-selection attention instance (SEL != 0, no stored logits)
+    att = lambda n, gsz: ("attend_mfma_kernel" in n and "false, 0>" not in n
+                          and "true" not in n)
+    af, an = mean(fr, att)
+    aw, _ = mean(wr, att)
+    # the plain copy: the blit dispatches with the grid of the 1 GiB copy, whose
+    # write counter is the largest of the process
+    copy_grid = max((x, gsz) for n, gsz, x in wr if "copyBuffer" in n)[1]
+    cp = lambda n, gsz: "copyBuffer" in n and gsz == copy_grid
+    cf, _ = mean(fr, cp)
+    cw, _ = mean(wr, cp)
+    anames = [n for n, _, _ in fr if att(n, None)]
+    lines = [
+        f"# HBM traffic of the in-kernel-selection attention kernel, workload {workload}",
+        "# FETCH_SIZE / WRITE_SIZE are KiB per dispatch (rocprofv3 --pmc, one counter per pass);",
+        f"# the scales make a plain {COPY_BYTES} B device copy read and write exactly that.",
+        f"# fetch pass: {cmd_fetch}",
+        f"# write pass: {cmd_write}",
+        f"# kernels: {sorted(set(anames))[0][:120]}",
+        f"kernel_sources_sha256_16 = {kernel_sources_sha()}",
+        f"attend_dispatches = {an}",
+        f"attend_fetch_kib_per_dispatch = {af:.1f}",
+        f"attend_write_kib_per_dispatch = {aw:.1f}",
+        f"copy_bytes = {COPY_BYTES}",
+        f"copy_fetch_kib_per_dispatch = {cf:.1f}",
+        f"copy_write_kib_per_dispatch = {cw:.1f}",
+        f"fetch_scale = {COPY_BYTES / (cf * 1024):.4f}",
+        f"write_scale = {COPY_BYTES / (cw * 1024):.4f}",
+    ]
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+# ----------------------------------------------------------------------------
 # CPU baseline: the oracle, as it stands, on a bounded sample
 # ----------------------------------------------------------------------------
 
@@ -155,7 +266,19 @@ def main():
     ap.add_argument("--layers", type=int, default=0, help="distinct layer caches (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead")
+    ap.add_argument("--copy-calibrate", action="store_true",
+                    help="run a plain 1 GiB copy first (for counter passes)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/attend_mfma_<workload>_traffic.txt from two "
+                         "rocprofv3 --pmc passes and exit")
+    ap.add_argument("--pmc-commands", nargs=2, default=["?", "?"],
+                    help="the two rocprofv3 command lines, recorded in the summary")
     args = ap.parse_args()
+
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload,
+                      traffic_file(args.workload), *args.pmc_commands)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this decode-attention path has no multi-GPU "
@@ -169,6 +292,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     sd.lib()  # fail loudly if the HIP library is missing
+    if args.copy_calibrate:
+        copy_calibration()
 
     rname, over, unit, r_kv, desc = WORKLOADS[args.workload]
     rec = kvsynth.RECIPES[rname].with_(**over)
@@ -348,7 +473,8 @@ def main():
                        "attend_mfma_kernel: split-K attention partials over the kept tokens "
                        "(stored logits)"),
             "bound": "hbm", "achieved": round(gbps_att, 1), "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s", "frac": round(gbps_att / HBM_PEAK_GBPS, 4), "traffic": None,
+            "unit": "GB/s", "frac": round(gbps_att / HBM_PEAK_GBPS, 4),
+            "traffic": read_traffic(args.workload) if unit == "page" else None,
             "us_per_launch": round(us_attend, 3), "bytes_per_launch": int(b_attend),
         },
     }

@@ -47,8 +47,9 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
+
 constexpr int kAttendWaves = 8;     // waves per block
-constexpr int kResolveWindow = 16;  // chunks a wave resolves per round
+constexpr int kResolveWindow = 8;   // chunks a wave resolves per round
 
 // How a block obtains its kept list.
 enum SelMode : int {
@@ -75,34 +76,39 @@ __device__ __forceinline__ Span span_of(const AttendArgs& a, int j, int list_len
   return sp;
 }
 
-// Pool row (row-major [num_pages * H_kv * P] index) of row `row` of chunk `c`,
-// or -1 when that row is not attended; *tok receives its token id.
-// unit_at(e) returns list entry e (called for e < sp.e_hi).
-template <typename UnitAt>
-__device__ __forceinline__ int resolve_row(const AttendArgs& a, const Span& sp, UnitAt&& unit_at,
-                                           int cnt, int n, int U, int b, int g, int c, int row,
-                                           int* tok) {
+// Pool rows (row-major [num_pages * H_kv * P] index) of row `row` of N
+// chunks c[i] (or -1 where that row is not attended; tok[i] receives its
+// token id).  unit_at(e) returns list entry e for e < sp.e_hi.  Every read is
+// issued unconditionally with a clamped index, list entries first and block
+// table entries second, so the N lookups cost two memory round trips.
+template <int N, typename UnitAt>
+__device__ __forceinline__ void resolve_rows(const AttendArgs& a, const Span& sp,
+                                             UnitAt&& unit_at, int cnt, int n, int U, int b,
+                                             int g, const int (&c)[N], const bool (&live)[N],
+                                             int row, int (&pr)[N], int (&tok)[N]) {
   const Dims& d = a.d;
-  int e, t;
-  bool ok;
-  if (a.unit == kPage) {
-    const int cpu = d.P / 16;
-    e = sp.e0 + c / cpu;
-    const int u = e < sp.e_hi ? unit_at(e) : -1;
-    t = u * d.P + (c - (c / cpu) * cpu) * 16 + row;
-    ok = e < sp.e_hi && e < cnt && u >= 0 && u < U && t < n;
-  } else {
-    e = sp.e0 + c * 16 + row;
-    t = e < sp.e_hi ? unit_at(e) : -1;
-    ok = e < sp.e_hi && e < cnt && t >= 0 && t < n;
+  const bool pg = a.unit == kPage;
+  const int cpu = d.P / 16;
+  int e[N], v[N], phys[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    e[i] = pg ? sp.e0 + c[i] / cpu : sp.e0 + c[i] * 16 + row;
+    v[i] = unit_at(max(sp.e0, min(e[i], sp.e_hi - 1)));
   }
-  // the block-table read is clamped so it can issue before `ok` is known
-  int lp = t / d.P;
-  lp = lp < 0 ? 0 : (lp >= d.max_pages ? d.max_pages - 1 : lp);
-  const int phys = a.block_table[(int64_t)b * d.max_pages + lp];
-  ok = ok && phys >= 0 && phys < d.num_pages;
-  *tok = t;
-  return ok ? (int)(((int64_t)phys * d.Hkv + g) * d.P + (t - lp * d.P)) : -1;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    tok[i] = pg ? v[i] * d.P + (c[i] - (c[i] / cpu) * cpu) * 16 + row : v[i];
+    int lp = tok[i] / d.P;
+    lp = lp < 0 ? 0 : (lp >= d.max_pages ? d.max_pages - 1 : lp);
+    phys[i] = a.block_table[(int64_t)b * d.max_pages + lp];
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int lp = tok[i] / d.P;
+    const bool ok = live[i] && e[i] < sp.e_hi && e[i] < cnt && v[i] >= 0 && (!pg || v[i] < U) &&
+                    tok[i] < n && phys[i] >= 0 && phys[i] < d.num_pages;
+    pr[i] = ok ? (int)(((int64_t)phys[i] * d.Hkv + g) * d.P + (tok[i] - lp * d.P)) : -1;
+  }
 }
 
 // Writes a block's partial (s_po [G][D], s_plse [G] in LDS); split 0 of
@@ -273,21 +279,32 @@ __global__ __launch_bounds__(kAttendWaves * 64) void attend_mfma_kernel(AttendAr
   }
   auto unit_at = [&](int e) -> int {
     if constexpr (SELECTS) return e < cnt ? s_list[e - sp.e0] : -1;
-    else return list ? list[e] : e;
+    else {
+      // one unconditional load (a valid dummy address in identity mode)
+      const int v = *(list ? list + e : a.seq_lens + b);
+      return list ? v : e;
+    }
   };
 
   // B operand of the score product: lane holds Q[h = row][32 s + 8 quad .. +7].
   bf16x8_t qop[KS];
   {
-    const bf16_t* qrow = static_cast<const bf16_t*>(a.q) + ((int64_t)b * d.Hq + g * G + row) * D;
+    const bf16_t* qrow =
+        static_cast<const bf16_t*>(a.q) + ((int64_t)b * d.Hq + g * G + min(row, G - 1)) * D;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      uint4 w = make_uint4(0u, 0u, 0u, 0u);
-      if (!LOGITS && row < G) w = *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * quad);
+      u32x4_t w = *reinterpret_cast<const u32x4_t*>(qrow + 32 * s + 8 * quad);
+      if (LOGITS || row >= G) w = u32x4_t{0u, 0u, 0u, 0u};
       qop[s] = __builtin_bit_cast(bf16x8_t, w);
     }
   }
   const float qs = d.scale * kLog2e;
+  // a valid row-sized address for loads of rows that are not attended
+  const bf16_t* qrow0 = static_cast<const bf16_t*>(a.q) + ((int64_t)b * d.Hq + g * G) * D;
+  // stored logits of head `row` of the group (token unit)
+  const float* logit_row =
+      LOGITS ? a.token_logits + ((int64_t)b * d.Hq + g * G + min(row, G - 1)) * d.max_seq
+             : nullptr;
 
   float4_t acc[CT];
 #pragma unroll
@@ -295,11 +312,13 @@ __global__ __launch_bounds__(kAttendWaves * 64) void attend_mfma_kernel(AttendAr
   float m = -INFINITY, l = 0.f;
   bf16_t* sv = &s_v[wave][0];
 
-  // One 16-row chunk: scores, online softmax, value accumulation.
-  auto process = [&](const uint4 (&kv)[KS], const uint4 (&vv)[KS], uint32_t vmask, int cl) {
+  // One 16-row chunk: scores, online softmax, value accumulation.  lg holds
+  // the chunk's stored logits in token unit (rows 4 quad + r of head `row`).
+  auto process = [&](const u32x4_t (&kv)[KS], const u32x4_t (&vv)[KS], const float (&lg)[4],
+                     uint32_t vmask) {
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      *reinterpret_cast<uint4*>(sv + row * VROW + 32 * s + 8 * quad) = vv[s];
+      *reinterpret_cast<u32x4_t*>(sv + row * VROW + 32 * s + 8 * quad) = vv[s];
     float x[4];
     if constexpr (!LOGITS) {
       float4_t st = {0.f, 0.f, 0.f, 0.f};
@@ -311,13 +330,7 @@ __global__ __launch_bounds__(kAttendWaves * 64) void attend_mfma_kernel(AttendAr
       for (int r = 0; r < 4; ++r) x[r] = st[r] * qs;
     } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int rr = 4 * quad + r;
-        x[r] = 0.f;
-        if (row < G && ((vmask >> rr) & 1u))
-          x[r] = a.token_logits[((int64_t)b * d.Hq + g * G + row) * d.max_seq +
-                                s_tok[LOGITS ? wave : 0][cl][rr]] * kLog2e;
-      }
+      for (int r = 0; r < 4; ++r) x[r] = row < G ? lg[r] * kLog2e : 0.f;
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r)
@@ -361,49 +374,72 @@ __global__ __launch_bounds__(kAttendWaves * 64) void attend_mfma_kernel(AttendAr
   for (int r0 = w_lo; r0 < w_hi; r0 += RW) {
     const int nc = min(RW, w_hi - r0);
     // Resolve the rows of up to RW chunks: lane (row, quad) takes chunk it*4+quad.
+    {
+      constexpr int NR = RW / 4;
+      int cc[NR], pr[NR], tk[NR];
+      bool live[NR];
 #pragma unroll
-    for (int it = 0; it < RW / 4; ++it) {
-      const int cl = it * 4 + quad;
-      int t = 0, pr = -1;
-      if (cl < nc) pr = resolve_row(a, sp, unit_at, cnt, n, U, b, g, r0 + cl, row, &t);
-      s_rows[wave][cl][row] = pr;
-      if constexpr (LOGITS) s_tok[wave][cl][row] = t;
+      for (int it = 0; it < NR; ++it) {
+        cc[it] = r0 + it * 4 + quad;
+        live[it] = it * 4 + quad < nc;
+      }
+      resolve_rows<NR>(a, sp, unit_at, cnt, n, U, b, g, cc, live, row, pr, tk);
+#pragma unroll
+      for (int it = 0; it < NR; ++it) {
+        s_rows[wave][it * 4 + quad][row] = pr[it];
+        if constexpr (LOGITS) s_tok[wave][it * 4 + quad][row] = tk[it];
+      }
     }
     __builtin_amdgcn_wave_barrier();
 
     // Two chunks per load batch, double-buffered: batch i+1 is in flight while
-    // batch i is processed.
-    uint4 kA[2][KS], vA[2][KS], kB[2][KS], vB[2][KS];
+    // batch i is processed.  Every load is issued unconditionally (rows that
+    // are not attended read the group's query row, which is cached, and are
+    // masked), so the compiler can wait for one batch while the next stays in
+    // flight; a branch around a load would make it drain all of them.
+    u32x4_t kA[2][KS], vA[2][KS], kB[2][KS], vB[2][KS];
+    float lA[2][4], lB[2][4];
     uint32_t mA[2], mB[2];
-    auto load2 = [&](uint4 (&kk)[2][KS], uint4 (&vv)[2][KS], uint32_t (&mm)[2], int c0) {
+    auto load2 = [&](u32x4_t (&kk)[2][KS], u32x4_t (&vv)[2][KS], float (&ll)[2][4],
+                     uint32_t (&mm)[2], int c0) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const int pr = c0 + i < nc ? s_rows[wave][c0 + i][row] : -1;
+        const int c = c0 + i;
+        int pr = s_rows[wave][min(c, RW - 1)][row];
+        if (c >= nc) pr = -1;
         mm[i] = (uint32_t)(__ballot(pr >= 0) & 0xFFFFull);
+        const bf16_t* kr = pr >= 0 ? kp + (int64_t)pr * D : qrow0;
+        const bf16_t* vr = pr >= 0 ? vp + (int64_t)pr * D : qrow0;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-          kk[i][s] = make_uint4(0u, 0u, 0u, 0u);
-          vv[i][s] = make_uint4(0u, 0u, 0u, 0u);
-          if (pr >= 0) {
-            const int64_t o = (int64_t)pr * D + 32 * s + 8 * quad;
-            if constexpr (!LOGITS) kk[i][s] = *reinterpret_cast<const uint4*>(kp + o);
-            vv[i][s] = *reinterpret_cast<const uint4*>(vp + o);
+          if constexpr (!LOGITS) kk[i][s] = *reinterpret_cast<const u32x4_t*>(kr + 32 * s + 8 * quad);
+          else kk[i][s] = u32x4_t{0u, 0u, 0u, 0u};
+          vv[i][s] = *reinterpret_cast<const u32x4_t*>(vr + 32 * s + 8 * quad);
+        }
+        if constexpr (LOGITS) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            int t = s_tok[LOGITS ? wave : 0][min(c, RW - 1)][4 * quad + r];
+            t = t < 0 ? 0 : (t >= d.max_seq ? d.max_seq - 1 : t);
+            ll[i][r] = logit_row[t];
           }
         }
       }
     };
-    auto run2 = [&](uint4 (&kk)[2][KS], uint4 (&vv)[2][KS], uint32_t (&mm)[2], int c0) {
+    auto run2 = [&](u32x4_t (&kk)[2][KS], u32x4_t (&vv)[2][KS], float (&ll)[2][4],
+                    uint32_t (&mm)[2]) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        if (mm[i] != 0u) process(kk[i], vv[i], mm[i], c0 + i);
+        if (mm[i] != 0u) process(kk[i], vv[i], ll[i], mm[i]);
     };
-    load2(kA, vA, mA, 0);
-    for (int c = 0; c < nc; c += 4) {
-      if (c + 2 < nc) load2(kB, vB, mB, c + 2);
-      run2(kA, vA, mA, c);
+    load2(kA, vA, lA, mA, 0);
+    for (int c = 0;; c += 4) {
+      load2(kB, vB, lB, mB, c + 2);
+      run2(kA, vA, lA, mA);
       if (c + 2 >= nc) break;
-      if (c + 4 < nc) load2(kA, vA, mA, c + 4);
-      run2(kB, vB, mB, c + 2);
+      load2(kA, vA, lA, mA, c + 4);
+      run2(kB, vB, lB, mB);
+      if (c + 4 >= nc) break;
     }
   }
 
@@ -469,7 +505,10 @@ __global__ __launch_bounds__(kAttendWaves * 64) void attend_f32_kernel(AttendArg
   const int n = clamp_len(a.seq_lens[b], d.max_seq);
   const int U = a.unit == kPage ? (n + d.P - 1) / d.P : n;
   const int cnt = list ? min(a.sel_count[bg], a.k_max) : U;
-  auto unit_at = [&](int e) -> int { return list ? list[e] : e; };
+  auto unit_at = [&](int e) -> int {
+    const int v = *(list ? list + e : a.seq_lens + b);
+    return list ? v : e;
+  };
 
   const float qs = d.scale * kLog2e;
   float qv[G][8];
@@ -490,8 +529,10 @@ __global__ __launch_bounds__(kAttendWaves * 64) void attend_f32_kernel(AttendArg
   const int rows = sp.nch * 16;
   for (int base = wave * RPW; base < rows; base += NW * RPW) {
     const int r = base + sub;
-    int t = 0, pr = -1;
-    if (r < rows) pr = resolve_row(a, sp, unit_at, cnt, n, U, b, g, r >> 4, r & 15, &t);
+    int cc[1] = {r >> 4}, prr[1], tk[1];
+    const bool live[1] = {r < rows};
+    resolve_rows<1>(a, sp, unit_at, cnt, n, U, b, g, cc, live, r & 15, prr, tk);
+    const int pr = prr[0], t = tk[0];
     const bool ok = pr >= 0;
     const int64_t off = (int64_t)pr * D + cl * 8;
     float s[G];

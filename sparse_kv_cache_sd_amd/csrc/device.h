@@ -46,6 +46,27 @@ __device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
+// Eight elements as raw 16-byte words, loaded now and widened later: keeping
+// the load and the conversion apart lets a lane issue all of its loads before
+// the first one is needed.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+template <typename T> struct Raw8 { u32x4_t w[sizeof(T) / 2]; };
+template <typename T>
+__device__ __forceinline__ Raw8<T> load_raw8(const T* p) {
+  Raw8<T> r;
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(T) / 2); ++i) r.w[i] = reinterpret_cast<const u32x4_t*>(p)[i];
+  return r;
+}
+__device__ __forceinline__ void widen8(const Raw8<bf16_t>& r, float (&v)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { v[2 * i] = bf16_lo(r.w[0][i]); v[2 * i + 1] = bf16_hi(r.w[0][i]); }
+}
+__device__ __forceinline__ void widen8(const Raw8<float>& r, float (&v)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(r.w[i / 4][i % 4]);
+}
+
 __device__ __forceinline__ int clamp_len(int n, int max_seq) {
   return n < 0 ? 0 : (n > max_seq ? max_seq : n);
 }

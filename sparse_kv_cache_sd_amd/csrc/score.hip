@@ -14,6 +14,11 @@
 // issues the loads of kScoreIters pages at once, before the sequence length
 // is known.
 //
+// In every kernel here the loads are issued unconditionally (indexes clamped,
+// rows that do not count read a valid row and are masked afterwards): a load
+// under a branch makes the compiler wait for every outstanding load at the
+// join, which would serialise the memory round trips.
+//
 // Token unit: the exact logits scale * q.K of every valid key, kept for the
 // attention pass, and their max over the group ("... list view", Abstract:
 // attention-scored KV selection reads every key once).  For bf16 the 16-row
@@ -53,30 +58,30 @@ __global__ __launch_bounds__(kScoreThreads) void score_pages_kernel(
 
   // statistics are stored in logical page order: no block-table lookup
   const T* bnd = bounds + ((int64_t)b * d.Hkv + g) * d.max_pages * 2 * D + cl * 8;
-  float lo[IT][8], hi[IT][8];
+  Raw8<T> lo_w[IT], hi_w[IT];
   int uu[IT];
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     uu[it] = u0 + (wave * IT + it) * RPW + sub;
-    if (uu[it] < d.max_pages) {
-      load8(bnd + (int64_t)uu[it] * 2 * D, lo[it]);
-      load8(bnd + (int64_t)uu[it] * 2 * D + D, hi[it]);
-    } else {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) lo[it][c] = hi[it][c] = 0.f;
-    }
+    const int uc = min(uu[it], d.max_pages - 1);
+    lo_w[it] = load_raw8(bnd + (int64_t)uc * 2 * D);
+    hi_w[it] = load_raw8(bnd + (int64_t)uc * 2 * D + D);
   }
+  __builtin_amdgcn_sched_barrier(0);  // all loads issue before the first use
   const int n = clamp_len(seq_lens[b], d.max_seq);
   const int U = (n + d.P - 1) / d.P;
   float* out = scores + ((int64_t)b * d.Hkv + g) * d.max_pages;
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
+    float lo[8], hi[8];
+    widen8(lo_w[it], lo);
+    widen8(hi_w[it], hi);
     float best = -INFINITY;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float acc = 0.f;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) acc = fmaf(qv[h][c], qv[h][c] >= 0.f ? hi[it][c] : lo[it][c], acc);
+      for (int c = 0; c < 8; ++c) acc = fmaf(qv[h][c], qv[h][c] >= 0.f ? hi[c] : lo[c], acc);
       acc = group_sum<LPR>(acc);
       best = fmaxf(best, acc * d.scale);
     }
@@ -106,32 +111,36 @@ __global__ __launch_bounds__(kScoreThreads) void score_tokens_f32_kernel(
   for (int h = 0; h < G; ++h)
     load8(q + ((int64_t)b * d.Hq + g * G + h) * D + cl * 8, qv[h]);
 
-  float kv[IT][8];
+  Raw8<float> kw[IT];
   bool ok[IT];
-  int tt[IT];
+  int tt[IT], phys[IT];
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     tt[it] = t0 + (wave * IT + it) * RPW + sub;
-    ok[it] = tt[it] < n;
-    const int lp = tt[it] / d.P;
-    const int phys = ok[it] ? block_table[(int64_t)b * d.max_pages + lp] : -1;
-    ok[it] = ok[it] && phys >= 0 && phys < d.num_pages;
-    if (ok[it]) {
-      load8(k_pages + (((int64_t)phys * d.Hkv + g) * d.P + (tt[it] - lp * d.P)) * D + cl * 8, kv[it]);
-    } else {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) kv[it][c] = 0.f;
-    }
+    const int lp = min(tt[it] / d.P, d.max_pages - 1);
+    phys[it] = block_table[(int64_t)b * d.max_pages + lp];
   }
+  const float* qrow0 = q + ((int64_t)b * d.Hq + g * G) * D + cl * 8;
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    ok[it] = tt[it] < n && phys[it] >= 0 && phys[it] < d.num_pages;
+    const int lp = tt[it] / d.P;
+    kw[it] = load_raw8(ok[it] ? k_pages + (((int64_t)phys[it] * d.Hkv + g) * d.P +
+                                           (tt[it] - lp * d.P)) * D + cl * 8
+                              : qrow0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
   float* sc = scores + ((int64_t)b * d.Hkv + g) * d.max_seq;
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
+    float kv[8];
+    widen8(kw[it], kv);
     float best = -INFINITY, mine = 0.f;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float acc = 0.f;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) acc = fmaf(qv[h][c], kv[it][c], acc);
+      for (int c = 0; c < 8; ++c) acc = fmaf(qv[h][c], kv[c], acc);
       const float s = group_sum<LPR>(acc) * d.scale;
       best = fmaxf(best, s);
       if (h == cl) mine = s;
@@ -174,25 +183,29 @@ __global__ __launch_bounds__(kScoreThreads) void score_tokens_mfma_kernel(
       qop[s] = __builtin_bit_cast(bf16x8_t, w);
     }
   }
-  uint4 kv[IT][KS];
+  u32x4_t kv[IT][KS];
   bool page_ok[IT];
-  int tc[IT];
+  int tc[IT], phys[IT];
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     tc[it] = t0 + (wave * IT + it) * 16;
+    const int lp = min(tc[it] / d.P, d.max_pages - 1);
+    phys[it] = block_table[(int64_t)b * d.max_pages + lp];
+  }
+  const bf16_t* qrow0 = q + ((int64_t)b * d.Hq + g * G) * D;
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
     const int t = tc[it] + row;
     const int lp = tc[it] / d.P;
-    const int phys = tc[it] < n ? block_table[(int64_t)b * d.max_pages + lp] : -1;
-    page_ok[it] = phys >= 0 && phys < d.num_pages;
-    const bool ok = page_ok[it] && t < n;
+    page_ok[it] = tc[it] < n && phys[it] >= 0 && phys[it] < d.num_pages;
+    const bf16_t* kr = page_ok[it] && t < n
+                           ? k_pages + (((int64_t)phys[it] * d.Hkv + g) * d.P + (t - lp * d.P)) * D
+                           : qrow0;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      kv[it][s] = make_uint4(0u, 0u, 0u, 0u);
-      if (ok)
-        kv[it][s] = *reinterpret_cast<const uint4*>(
-            k_pages + (((int64_t)phys * d.Hkv + g) * d.P + (t - lp * d.P)) * D + 32 * s + 8 * quad);
-    }
+    for (int s = 0; s < KS; ++s)
+      kv[it][s] = *reinterpret_cast<const u32x4_t*>(kr + 32 * s + 8 * quad);
   }
+  __builtin_amdgcn_sched_barrier(0);
   float* sc = scores + ((int64_t)b * d.Hkv + g) * d.max_seq;
   float* lg = logits + ((int64_t)b * d.Hq + g * G + row) * d.max_seq;
 #pragma unroll
