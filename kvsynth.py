@@ -32,20 +32,26 @@ Workload recipes (one per decode-attention configuration):
               ``l8b`` plus 1% planted salient pages per KV head (every valid
               token of such a page is salient, round-robin over the group).
 
-Draw order per sequence: channel scales, q, K, V, then per KV head the
-salient positions followed by their noise; the physical page permutation
-comes from a second generator seeded from the recipe's seed.  "N(0, 0.5)" is
-read as standard deviation 0.5.
+Draw order per sequence, from the recipe's generator: channel scales, q, then
+per KV head the salient positions followed by their noise.  The bulk K and V
+draws of each (sequence, KV head) come from their own PCG64 streams keyed by
+(seed, sequence, KV head, K or V), so they can be drawn in parallel threads
+and do not depend on the thread count.  The physical page permutation comes
+from a second generator seeded from the recipe's seed.  "N(0, 0.5)" is read as
+standard deviation 0.5.
 """
 
 from __future__ import annotations
 
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field, replace
 
 import numpy as np
 
 KTOK = 1024  # "K" tokens
+_THREADS = max(1, min(16, os.cpu_count() or 1))
 
 
 # ----------------------------------------------------------------------------
@@ -171,12 +177,15 @@ class Workload:
                 off += U[b]
         k_pool = np.zeros((num_pages, H_kv, P, d), dtype=self.K.dtype)
         v_pool = np.zeros((num_pages, H_kv, P, d), dtype=self.V.dtype)
-        for b in range(B):
+
+        def scatter(job):
+            b, g = job
             ids = block_table[b, :U[b]]
-            kb = self.K[b, :, :U[b] * P].reshape(H_kv, U[b], P, d).transpose(1, 0, 2, 3)
-            vb = self.V[b, :, :U[b] * P].reshape(H_kv, U[b], P, d).transpose(1, 0, 2, 3)
-            k_pool[ids] = kb
-            v_pool[ids] = vb
+            k_pool[ids, g] = self.K[b, g, :U[b] * P].reshape(U[b], P, d)
+            v_pool[ids, g] = self.V[b, g, :U[b] * P].reshape(U[b], P, d)
+
+        with ThreadPoolExecutor(_THREADS) as ex:
+            list(ex.map(scatter, [(b, g) for b in range(B) for g in range(H_kv)]))
         return PagedCache(k_pool, v_pool, block_table, num_pages)
 
 
@@ -211,20 +220,32 @@ def generate(recipe: Recipe, *, seq_lens=None) -> Workload:
     K_all = np.zeros((B, H_kv, n_alloc, d), dtype=store_dt)
     V_all = np.zeros((B, H_kv, n_alloc, d), dtype=store_dt)
     salient, salient_pages = {}, {}
+    scales, qs = [], []
     for b in range(B):
-        n = int(seq_lens[b])
         if r.channel_scale is not None:
             lo, hi = r.channel_scale
             sk = rng.uniform(lo, hi, size=(H_kv, d)).astype(np.float32)
             sv = rng.uniform(lo, hi, size=(H_kv, d)).astype(np.float32)
         else:
             sk = sv = np.ones((H_kv, d), dtype=np.float32)
-        q = rng.standard_normal((H_q, d), dtype=np.float32)
+        scales.append((sk, sv))
+        qs.append(rng.standard_normal((H_q, d), dtype=np.float32))
+
+    def bulk(job):
+        b, g, which = job
+        n = int(seq_lens[b])
+        stream = np.random.Generator(np.random.PCG64(np.random.SeedSequence([r.seed, b, g, which])))
+        dst = K_all if which == 0 else V_all
+        dst[b, g, :n] = _store(stream.standard_normal((n, d), dtype=np.float32) * scales[b][which][g],
+                               r.dtype)
+
+    with ThreadPoolExecutor(_THREADS) as ex:
+        list(ex.map(bulk, [(b, g, w) for b in range(B) for g in range(H_kv) for w in (0, 1)]))
+
+    for b in range(B):
+        n = int(seq_lens[b])
+        q = qs[b]
         qhat = q / np.linalg.norm(q, axis=1, keepdims=True)
-        for g in range(H_kv):
-            K_all[b, g, :n] = _store(rng.standard_normal((n, d), dtype=np.float32) * sk[g], r.dtype)
-        for g in range(H_kv):
-            V_all[b, g, :n] = _store(rng.standard_normal((n, d), dtype=np.float32) * sv[g], r.dtype)
         # salient positions, then their noise
         for g in range(H_kv):
             heads = [g * G + i for i in range(G)]

@@ -1,0 +1,112 @@
+"""Full-size GPU parity: every decode configuration at its real size, through
+one ``sd.decode_step`` call in the launch configuration the benchmark times
+(default split plan and workspace).
+
+Two kinds of check:
+
+* sampled (sequence, KV head) instances against the fp64 oracle, under the
+  rules of ``gpu_util`` (selected sets bit-exact where the oracle's score gap
+  at k exceeds 1e-4, out / lse max-abs 2e-2 for bf16);
+* for every instance, properties that hold at any size: the count follows the
+  keep-count rule, and the kept ids are exactly the top-k of the library's own
+  fp32 unit scores (equal scores to the lower id, ascending), which is unique;
+  every output is finite.
+"""
+
+from __future__ import annotations
+
+import functools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import kvsynth
+import sparse_kv_cache_sd_amd as sd
+from oracle import sdref
+
+from gpu_util import compare_step, run_decode, upload
+
+pytestmark = pytest.mark.gpu
+
+K = kvsynth.KTOK
+
+
+@functools.lru_cache(maxsize=2)
+def _dev(name: str, context: int | None):
+    if name == "l8b":
+        rec = kvsynth.RECIPES["l8b"]
+    elif name == "sweep":
+        rec = kvsynth.sweep_recipe(context, 0.3)
+    elif name == "batch":
+        rec = kvsynth.RECIPES["batch"]
+    elif name == "l70b":
+        rec = kvsynth.l70b_recipe(context)
+    else:
+        raise ValueError(name)
+    print(f"[fullsize] generating {name} context={context}", flush=True)
+    return upload(kvsynth.generate(rec))
+
+
+def _own_topk_property(dev, unit: str, r_kv: float, sel: np.ndarray, cnt: np.ndarray):
+    """The kept set of every (b, g) is the top-k of the library's own unit
+    scores, ties to the lower id, in ascending order."""
+    s = dev.shape
+    umax = s.units_max(unit)
+    scores = torch.empty((s.batch, s.num_kv_heads, umax), dtype=torch.float32, device="cuda")
+    logits = (torch.empty((s.batch, s.num_q_heads, s.max_seq_len), dtype=torch.float32,
+                          device="cuda") if unit == "token" else None)
+    sd.score_pages(s, dev.q, dev.k, dev.bounds, dev.bt, dev.sl, unit, scores, logits)
+    torch.cuda.synchronize()
+    sc = scores.cpu().numpy()
+    P = s.page_size
+    for b in range(s.batch):
+        n = int(dev.w.seq_lens[b])
+        U = -(-n // P) if unit == "page" else n
+        k = sdref.keep_count(r_kv, U)
+        assert int(cnt[b].min()) == k and int(cnt[b].max()) == k, f"b={b}: count != {k}"
+        for g in range(s.num_kv_heads):
+            x = sc[b, g, :U].astype(np.float64)
+            assert np.all(np.isfinite(x))
+            ref = np.sort(np.lexsort((np.arange(U), -x))[:k])
+            np.testing.assert_array_equal(sel[b, g, :k], ref, err_msg=f"(b={b}, g={g})")
+
+
+def _finite(out, lse):
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+
+
+# (id, recipe name, context, unit, r_kv, sampled (b, g) instances or "all")
+CASES = [
+    ("l8b-32k-page-0.3", "l8b", None, "page", 0.3, "all"),
+    ("l8b-32k-dense", "l8b", None, "page", 1.0, [(0, 0), (0, 5)]),
+    ("sweep-128k-token-0.3", "sweep", 128 * K, "token", 0.3, [(0, 0), (0, 3), (0, 7)]),
+    ("sweep-128k-token-0.2", "sweep", 128 * K, "token", 0.2, [(0, 1), (0, 6)]),
+    ("sweep-128k-dense", "sweep", 128 * K, "token", 1.0, [(0, 2)]),
+    ("sweep-64k-token-0.2", "sweep", 64 * K, "token", 0.2, [(0, 4)]),
+    ("sweep-8k-token-0.3", "sweep", 8 * K, "token", 0.3, "all"),
+    ("sweep-2k-token-0.2", "sweep", 2 * K, "token", 0.2, "all"),
+    ("l70b-128k-page-0.05", "l70b", 128 * K, "page", 0.05, "all"),
+    ("batch-page-0.2", "batch", None, "page", 0.2, "extremes"),
+    ("l70b-1m-page-0.05", "l70b", 1024 * K, "page", 0.05, [(0, 0), (0, 7)]),
+]
+
+
+@pytest.mark.parametrize("cid,name,context,unit,r_kv,groups", CASES, ids=[c[0] for c in CASES])
+def test_full_size(cid, name, context, unit, r_kv, groups):
+    print(f"[fullsize] {cid}", flush=True)
+    dev = _dev(name, context)
+    s = dev.shape
+    if groups == "all":
+        groups = [(b, g) for b in range(s.batch) for g in range(s.num_kv_heads)]
+    elif groups == "extremes":
+        lens = dev.w.seq_lens
+        groups = [(int(np.argmin(lens)), 0), (int(np.argmax(lens)), 7), (3, 2), (11, 5)]
+    if r_kv < 1.0:
+        out, lse, sel, cnt = run_decode(dev, unit, r_kv)
+        _finite(out, lse)
+        _own_topk_property(dev, unit, r_kv, sel, cnt)
+    e_o, e_l = compare_step(dev, unit, r_kv, groups=groups)
+    print(f"[fullsize] {cid}: {len(groups)} instances vs oracle, max-abs out {e_o:.2e} "
+          f"lse {e_l:.2e}", flush=True)
