@@ -135,8 +135,22 @@ Split plan_split(const sdkv::Dims& d, int unit, int64_t k_max) {
 // Workspace regions (byte offsets).  The split count and the attention
 // partials come first so that every entry point agrees on where they live.
 struct Layout {
-  size_t split_count, part_o, part_lse, attend_end, scores, logits, sel_idx, sel_count, total;
+  size_t split_count, part_o, part_lse, attend_end, scores, logits, sel_idx, sel_count, msel,
+      score_mm, total;
 };
+
+// Scratch of the many-block top-k (units beyond one block's registers).
+bool multi_select(const sdkv::Dims& d, int unit) { return units_max(d, unit) > sdkv::kMaxSelectU; }
+
+size_t select_ws_bytes(const sdkv::Dims& d, int unit) {
+  return multi_select(d, unit) ? sdkv::msel_workspace_bytes(d.B, d.Hkv, units_max(d, unit)) : 0;
+}
+
+// Partial min / max keys written by the token scorer for the many-block top-k.
+int score_mm_parts(const sdkv::Dims& d) {
+  const int per = sdkv::score_units_per_block(d.dtype, d.D);
+  return (d.max_seq + per - 1) / per;
+}
 
 Layout layout(const sdkv::Dims& d, int unit, double r_kv) {
   Layout L{};
@@ -155,6 +169,10 @@ Layout layout(const sdkv::Dims& d, int unit, double r_kv) {
   if (unit == SD_UNIT_TOKEN) off = align_up(off + sizeof(float) * bh * d.max_seq);
   L.sel_idx = off;     off = align_up(off + sizeof(int32_t) * bg * k_max);
   L.sel_count = off;   off = align_up(off + sizeof(int32_t) * bg);
+  L.msel = off;        off = align_up(off + select_ws_bytes(d, unit));
+  L.score_mm = off;
+  if (unit == SD_UNIT_TOKEN && multi_select(d, unit))
+    off = align_up(off + sizeof(uint32_t) * 2 * bg * score_mm_parts(d));
   L.total = off;
   return L;
 }
@@ -183,17 +201,26 @@ char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 
 sd_status do_score(const sdkv::Dims& d, const void* q, const void* k_pages, const void* bounds,
                    const int32_t* bt, const int32_t* sl, int unit, float* scores, float* logits,
-                   hipStream_t st) {
-  sdkv::ScoreArgs a{d, unit, q, k_pages, bounds, bt, sl, scores, logits};
+                   hipStream_t st, uint32_t* score_mm = nullptr) {
+  sdkv::ScoreArgs a{d, unit, q, k_pages, bounds, bt, sl, scores, logits, score_mm};
   return device_status(sdkv::launch_score(a, st), "score kernel launch");
 }
 
+// msel_ws: select_ws_bytes(d, unit) bytes (unused below kMaxSelectU units);
+// score_mm: the token scorer's partial min / max keys, or NULL.
 sd_status do_select(const sdkv::Dims& d, int unit, const int32_t* sl, const float* scores,
-                    double r_kv, int32_t* sel_idx, int32_t* sel_count, hipStream_t st) {
+                    double r_kv, int32_t* sel_idx, int32_t* sel_count, void* msel_ws,
+                    hipStream_t st, const uint32_t* score_mm = nullptr) {
   const int U = units_max(d, unit);
   const int R = ratio_ppm(r_kv);
   sdkv::SelectArgs a{d, unit, sl, scores, U, static_cast<int>(keep_count_ppm(R, U)), R,
                      sel_idx, sel_count};
+  if (multi_select(d, unit))
+    return device_status(
+        sdkv::launch_select_multi(a, score_mm, score_mm ? score_mm_parts(d) : 0,
+                                  score_mm ? sdkv::score_units_per_block(d.dtype, d.D) : 0,
+                                  msel_ws, st),
+        "select kernels launch");
   return device_status(sdkv::launch_select(a, st), "select kernel launch");
 }
 
@@ -203,7 +230,8 @@ sd_status do_partials(const sdkv::Dims& d, const void* q, const void* kp, const 
                       const int32_t* bt, const int32_t* sl, int unit, const int32_t* sel_idx,
                       const int32_t* sel_count, int k_max, const float* logits, void* ws,
                       hipStream_t st, const float* unit_scores = nullptr, int R_ppm = -1,
-                      int32_t* sel_out = nullptr, int32_t* sel_count_out = nullptr) {
+                      int32_t* sel_out = nullptr, int32_t* sel_count_out = nullptr,
+                      int* S_out = nullptr) {
   const bool listed = sel_idx != nullptr || unit_scores != nullptr;
   const int64_t kk = listed ? k_max : units_max(d, unit);
   const Split sp = plan_split(d, unit, kk);
@@ -229,13 +257,18 @@ sd_status do_partials(const sdkv::Dims& d, const void* q, const void* kp, const 
   a.R_ppm = R_ppm;
   a.sel_out = sel_out;
   a.sel_count_out = sel_count_out;
+  if (S_out) *S_out = sp.S;
   return device_status(sdkv::launch_attend(a, st), "attention kernel launch");
 }
 
-sd_status do_merge(const sdkv::Dims& d, float* out, float* lse, void* ws, hipStream_t st) {
+// S_known > 0: the split count of the attention launch just enqueued (saves
+// the merge kernel a dependent read of the workspace header).
+sd_status do_merge(const sdkv::Dims& d, float* out, float* lse, void* ws, hipStream_t st,
+                   int S_known = 0) {
   const Layout L = layout(d, SD_UNIT_PAGE, 1.0);
   sdkv::MergeArgs a{};
   a.d = d;
+  a.S_known = S_known;
   a.part_o = reinterpret_cast<const float*>(at(ws, L.part_o));
   a.part_lse = reinterpret_cast<const float*>(at(ws, L.part_lse));
   a.split_count = reinterpret_cast<const int32_t*>(at(ws, L.split_count));
@@ -263,18 +296,20 @@ sd_status do_select_attend(const sdkv::Dims& d, const void* q, const void* kp, c
   const Layout L = layout(d, unit, r_kv);
   const int k_max = static_cast<int>(keep_count_ppm(ratio_ppm(r_kv), units_max(d, unit)));
   sd_status st;
+  int S = 0;
   if (fused_select(d, unit, k_max)) {
     if ((st = do_partials(d, q, kp, vp, bt, sl, unit, nullptr, nullptr, k_max, nullptr, ws, s,
-                          scores, ratio_ppm(r_kv), sel_idx, sel_count)) != SD_OK)
+                          scores, ratio_ppm(r_kv), sel_idx, sel_count, &S)) != SD_OK)
       return st;
-    return do_merge(d, out, lse, ws, s);
+    return do_merge(d, out, lse, ws, s, S);
   }
   int32_t* idx = sel_idx ? sel_idx : reinterpret_cast<int32_t*>(at(ws, L.sel_idx));
   int32_t* cnt = sel_count ? sel_count : reinterpret_cast<int32_t*>(at(ws, L.sel_count));
-  if ((st = do_select(d, unit, sl, scores, r_kv, idx, cnt, s)) != SD_OK) return st;
-  if ((st = do_partials(d, q, kp, vp, bt, sl, unit, idx, cnt, k_max, nullptr, ws, s)) != SD_OK)
+  if ((st = do_select(d, unit, sl, scores, r_kv, idx, cnt, at(ws, L.msel), s)) != SD_OK) return st;
+  if ((st = do_partials(d, q, kp, vp, bt, sl, unit, idx, cnt, k_max, nullptr, ws, s, nullptr, -1,
+                        nullptr, nullptr, &S)) != SD_OK)
     return st;
-  return do_merge(d, out, lse, ws, s);
+  return do_merge(d, out, lse, ws, s, S);
 }
 
 // Shared checks of the attention entry points.
@@ -357,8 +392,6 @@ sd_status sd_score_pages(const sd_shape* shape, const void* q, const void* k_pag
 sd_status sd_select_topk(const sd_shape* shape, int32_t unit, const int32_t* seq_lens,
                          const float* unit_scores, double r_kv, int32_t* sel_idx,
                          int32_t* sel_count, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   sdkv::Dims d;
   sd_status st;
   if ((st = check_shape(shape, &d)) != SD_OK) return st;
@@ -366,7 +399,8 @@ sd_status sd_select_topk(const sd_shape* shape, int32_t unit, const int32_t* seq
   if ((st = check_ratio(r_kv)) != SD_OK) return st;
   if (!seq_lens || !unit_scores || !sel_idx || !sel_count)
     return fail(SD_E_NULL, "seq_lens, unit_scores, sel_idx and sel_count are required");
-  if ((st = do_select(d, unit, seq_lens, unit_scores, r_kv, sel_idx, sel_count,
+  if ((st = check_ws(ws, ws_bytes, select_ws_bytes(d, unit))) != SD_OK) return st;
+  if ((st = do_select(d, unit, seq_lens, unit_scores, r_kv, sel_idx, sel_count, ws,
                       static_cast<hipStream_t>(stream))) != SD_OK)
     return st;
   return ok();
@@ -437,10 +471,11 @@ sd_status sd_attend_splitk(const sd_shape* shape, const void* q, const void* k_p
   if (!out || !lse) return fail(SD_E_NULL, "out and lse are required");
   if ((st = check_ws(ws, ws_bytes, attend_ws_bytes(d))) != SD_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  int S = 0;
   if ((st = do_partials(d, q, k_pages, v_pages, block_table, seq_lens, unit, sel_idx, sel_count,
-                        k_max, token_logits, ws, s)) != SD_OK)
+                        k_max, token_logits, ws, s, nullptr, -1, nullptr, nullptr, &S)) != SD_OK)
     return st;
-  if ((st = do_merge(d, out, lse, ws, s)) != SD_OK) return st;
+  if ((st = do_merge(d, out, lse, ws, s, S)) != SD_OK) return st;
   return ok();
 }
 
@@ -487,19 +522,23 @@ sd_status sd_decode_step(const sd_shape* shape, const void* q, const void* k_pag
   const Layout L = layout(d, unit, r_kv);
   if ((st = check_ws(ws, ws_bytes, L.total)) != SD_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  int S = 0;
   if (dense) {
     if ((st = do_partials(d, q, k_pages, v_pages, block_table, seq_lens, unit, nullptr, nullptr,
-                          0, nullptr, ws, s)) != SD_OK)
+                          0, nullptr, ws, s, nullptr, -1, nullptr, nullptr, &S)) != SD_OK)
       return st;
-    if ((st = do_merge(d, out, lse, ws, s)) != SD_OK) return st;
+    if ((st = do_merge(d, out, lse, ws, s, S)) != SD_OK) return st;
     return ok();
   }
   const int U = units_max(d, unit);
   const int k_max = static_cast<int>(keep_count_ppm(ratio_ppm(r_kv), U));
   float* scores = reinterpret_cast<float*>(at(ws, L.scores));
   float* logits = unit == SD_UNIT_TOKEN ? reinterpret_cast<float*>(at(ws, L.logits)) : nullptr;
+  uint32_t* smm = unit == SD_UNIT_TOKEN && multi_select(d, unit)
+                      ? reinterpret_cast<uint32_t*>(at(ws, L.score_mm))
+                      : nullptr;
   if ((st = do_score(d, q, k_pages, page_bounds, block_table, seq_lens, unit, scores, logits,
-                     s)) != SD_OK)
+                     s, smm)) != SD_OK)
     return st;
   if (unit == SD_UNIT_PAGE) {
     if ((st = do_select_attend(d, q, k_pages, v_pages, block_table, seq_lens, scores, r_kv, out,
@@ -509,11 +548,13 @@ sd_status sd_decode_step(const sd_shape* shape, const void* q, const void* k_pag
   }
   int32_t* idx = sel_idx ? sel_idx : reinterpret_cast<int32_t*>(at(ws, L.sel_idx));
   int32_t* cnt = sel_count ? sel_count : reinterpret_cast<int32_t*>(at(ws, L.sel_count));
-  if ((st = do_select(d, unit, seq_lens, scores, r_kv, idx, cnt, s)) != SD_OK) return st;
-  if ((st = do_partials(d, q, k_pages, v_pages, block_table, seq_lens, unit, idx, cnt, k_max,
-                        logits, ws, s)) != SD_OK)
+  if ((st = do_select(d, unit, seq_lens, scores, r_kv, idx, cnt, at(ws, L.msel), s, smm)) !=
+      SD_OK)
     return st;
-  if ((st = do_merge(d, out, lse, ws, s)) != SD_OK) return st;
+  if ((st = do_partials(d, q, k_pages, v_pages, block_table, seq_lens, unit, idx, cnt, k_max,
+                        logits, ws, s, nullptr, -1, nullptr, nullptr, &S)) != SD_OK)
+    return st;
+  if ((st = do_merge(d, out, lse, ws, s, S)) != SD_OK) return st;
   return ok();
 }
 

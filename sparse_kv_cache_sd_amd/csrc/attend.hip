@@ -134,18 +134,21 @@ __device__ __forceinline__ void write_partial(const AttendArgs& a, int b, int g,
 // column c4 over the splits j = slice (mod SLICES), issuing the loads of its
 // first splits before the weights are known; the slices add up in LDS.
 template <int D>
-__global__ __launch_bounds__(256) void merge_splits_kernel(const float* __restrict__ part_o,
-                                                           const float* __restrict__ part_lse,
-                                                           const int32_t* __restrict__ split_count,
-                                                           float* __restrict__ out,
-                                                           float* __restrict__ lse, int S_max) {
+__global__ __launch_bounds__(256) void merge_splits_kernel(MergeArgs a) {
   constexpr int NT = 256, C4 = D / 4, SLICES = NT / C4, PRE = 8;
   __shared__ float s_w[kMaxSplits];
   __shared__ float s_ML[2];
   __shared__ float4 s_red[SLICES][C4];
-  const int64_t bh = blockIdx.x;
+  // block id = bg + B*Hkv*i merges head i of group bg: on the XCD that wrote
+  // the group's partials
+  const GroupBlock gb = group_block(a.d.B * a.d.Hkv);
+  const int64_t bh = (int64_t)(gb.bg / a.d.Hkv) * a.d.Hq + (gb.bg % a.d.Hkv) * a.d.G + gb.j;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int S = min(max(*split_count, 1), S_max);
+  const float* __restrict__ part_o = a.part_o;
+  const float* __restrict__ part_lse = a.part_lse;
+  float* __restrict__ out = a.out;
+  float* __restrict__ lse = a.lse;
+  const int S = a.S_known > 0 ? a.S_known : min(max(*a.split_count, 1), a.S_max);
   const float* pl = part_lse + bh * S;
   const int c4 = tid % C4, slice = tid / C4;
   const float4* po = reinterpret_cast<const float4*>(part_o + bh * S * D) + c4;
@@ -233,7 +236,8 @@ __global__ __launch_bounds__(kAttendWaves * 64) void attend_mfma_kernel(AttendAr
   auto s_o = reinterpret_cast<float(*)[G][D]>(s_raw);
 
   const Dims& d = a.d;
-  const int j = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const GroupBlock gb = group_block(d.B * d.Hkv);
+  const int j = gb.j, g = gb.bg % d.Hkv, b = gb.bg / d.Hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = lane & 15, quad = lane >> 4;
   const int64_t bg = (int64_t)b * d.Hkv + g;
@@ -492,7 +496,8 @@ __global__ __launch_bounds__(kAttendWaves * 64) void attend_f32_kernel(AttendArg
   __shared__ float s_plse[G];
 
   const Dims& d = a.d;
-  const int j = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const GroupBlock gb = group_block(d.B * d.Hkv);
+  const int j = gb.j, g = gb.bg % d.Hkv, b = gb.bg / d.Hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane / LPR, cl = lane % LPR;
   const int64_t bg = (int64_t)b * d.Hkv + g;
@@ -634,7 +639,7 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
   if (selects && (a.unit != kPage || a.sel_idx != nullptr || d.dtype != kBF16 ||
                   a.E > kMaxSelectE || d.max_pages > kMaxSelectU))
     return hipErrorInvalidValue;
-  const dim3 grid(a.S, d.Hkv, d.B);
+  const dim3 grid(a.S * d.Hkv * d.B);  // block id = bg + B*Hkv*j (XCD-aware)
   const bool logits = a.token_logits != nullptr;
   const bool ok = dispatch_tdg(d.dtype, d.D, d.G, [&](auto t, auto dd, auto gg) {
     using T = decltype(t);
@@ -661,12 +666,11 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t st) {
   const int bh = a.d.B * a.d.Hq;
+  if (a.S_known > a.S_max) return hipErrorInvalidValue;
   if (a.d.D == 64)
-    merge_splits_kernel<64><<<bh, 256, 0, st>>>(a.part_o, a.part_lse, a.split_count, a.out,
-                                                a.lse, a.S_max);
+    merge_splits_kernel<64><<<bh, 256, 0, st>>>(a);
   else
-    merge_splits_kernel<128><<<bh, 256, 0, st>>>(a.part_o, a.part_lse, a.split_count, a.out,
-                                                 a.lse, a.S_max);
+    merge_splits_kernel<128><<<bh, 256, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -11,8 +11,10 @@ namespace sdkv {
 // that scoring streams a sequence's statistics without the block table.
 // grid (max_pages, B), block 256: one block per logical page of a sequence,
 // one thread per (KV head, channel) pair, looping over the page's valid rows.
+constexpr int kBoundsThreads = 256;
+
 template <typename T>
-__global__ __launch_bounds__(256) void page_bounds_kernel(
+__global__ __launch_bounds__(kBoundsThreads) void page_bounds_kernel(
     const T* __restrict__ k_pages, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, T* __restrict__ bounds, Dims d) {
   const int u = blockIdx.x, b = blockIdx.y;
@@ -22,7 +24,7 @@ __global__ __launch_bounds__(256) void page_bounds_kernel(
   const int phys = block_table[(int64_t)b * d.max_pages + u];
   if (phys < 0 || phys >= d.num_pages) return;
   const int valid = min(d.P, n - u * d.P);
-  for (int idx = threadIdx.x; idx < d.Hkv * d.D; idx += blockDim.x) {
+  for (int idx = threadIdx.x; idx < d.Hkv * d.D; idx += kBoundsThreads) {
     const int g = idx / d.D, c = idx - g * d.D;
     const T* col = k_pages + ((int64_t)phys * d.Hkv + g) * d.P * d.D + c;
     float lo = to_f(col[0]), hi = lo;
@@ -40,11 +42,11 @@ __global__ __launch_bounds__(256) void page_bounds_kernel(
 hipError_t launch_page_bounds(const BoundsArgs& a, hipStream_t st) {
   const dim3 grid(a.d.max_pages, a.d.B);
   if (a.d.dtype == kF32) {
-    page_bounds_kernel<float><<<grid, 256, 0, st>>>(
+    page_bounds_kernel<float><<<grid, kBoundsThreads, 0, st>>>(
         static_cast<const float*>(a.k_pages), a.block_table, a.seq_lens,
         static_cast<float*>(a.bounds), a.d);
   } else {
-    page_bounds_kernel<bf16_t><<<grid, 256, 0, st>>>(
+    page_bounds_kernel<bf16_t><<<grid, kBoundsThreads, 0, st>>>(
         static_cast<const bf16_t*>(a.k_pages), a.block_table, a.seq_lens,
         static_cast<bf16_t*>(a.bounds), a.d);
   }

@@ -67,6 +67,19 @@ __device__ __forceinline__ void widen8(const Raw8<float>& r, float (&v)[8]) {
   for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(r.w[i / 4][i % 4]);
 }
 
+// XCD-aware placement.  Workgroups are dealt to the eight XCDs round-robin by
+// linear id, so a 1-D grid whose id is bg + BG * j (bg: the (sequence, KV
+// head) index, j: the block's part of it) keeps every part of bg on XCD
+// bg mod 8 when BG is a multiple of 8.  Data one kernel writes for bg and the
+// next kernel reads (scores, partials, histograms) then stays in that XCD's
+// L2 instead of being fetched across XCDs.  Only locality depends on this.
+struct GroupBlock {
+  int bg, j;
+};
+__device__ __forceinline__ GroupBlock group_block(int BG) {
+  return GroupBlock{(int)(blockIdx.x % (unsigned)BG), (int)(blockIdx.x / (unsigned)BG)};
+}
+
 __device__ __forceinline__ int clamp_len(int n, int max_seq) {
   return n < 0 ? 0 : (n > max_seq ? max_seq : n);
 }
@@ -172,6 +185,11 @@ __device__ __forceinline__ float wave_max(float x) {
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += (uint32_t)__shfl_xor((int)x, o);
   return x;
 }
 

@@ -37,7 +37,13 @@ struct ScoreArgs {
   const int32_t* seq_lens;
   float* unit_scores;   // [B][Hkv][U_max]
   float* token_logits;  // [B][Hq][max_seq] (token unit)
+  // Optional (token unit): per scoring block, the min and max order keys of
+  // its valid unit scores, [B*Hkv][ceil(max_seq / score_units_per_block)][2].
+  uint32_t* score_mm;
 };
+
+// Units one token-scoring block covers (the stride of ScoreArgs::score_mm).
+int score_units_per_block(int dtype, int D);
 
 struct SelectArgs {
   Dims d;
@@ -86,7 +92,16 @@ constexpr int kMaxSelectU = 16384;
 
 hipError_t launch_page_bounds(const BoundsArgs& a, hipStream_t st);
 hipError_t launch_score(const ScoreArgs& a, hipStream_t st);
+// One block per (sequence, KV head); U_max <= kMaxSelectU.
 hipError_t launch_select(const SelectArgs& a, hipStream_t st);
+// Many blocks per (sequence, KV head), any U_max; scratch of
+// msel_workspace_bytes(B, Hkv, U_max) bytes (contents need not be set).
+// mm: partial min / max keys of the scores ([B*Hkv][mm_nb][2], each over
+// mm_per consecutive units, e.g. ScoreArgs::score_mm), or NULL to compute
+// them here.
+size_t msel_workspace_bytes(int B, int Hkv, int U_max);
+hipError_t launch_select_multi(const SelectArgs& a, const uint32_t* mm, int mm_nb, int mm_per,
+                               void* ws, hipStream_t st);
 // Log-sum-exp merge of the split partials written by an attention launch.
 struct MergeArgs {
   Dims d;
@@ -94,6 +109,7 @@ struct MergeArgs {
   const float* part_lse;
   const int32_t* split_count;
   int S_max;
+  int S_known;                // > 0: the split count (no read of split_count)
   float* out;                 // [B][Hq][D]
   float* lse;                 // [B][Hq]
 };

@@ -24,7 +24,7 @@
 // attention-scored KV selection reads every key once).  For bf16 the 16-row
 // chunks go through the matrix cores exactly as in the attention kernel
 // (S^T = K Q^T with mfma 16x16x32); for fp32 the vector path is used.
-#include "device.h"
+#include "topk.h"
 
 namespace sdkv {
 
@@ -47,10 +47,11 @@ __global__ __launch_bounds__(kScoreThreads) void score_pages_kernel(
   constexpr int RPW = 64 / LPR;
   constexpr int IT = kScoreIters;
   constexpr int PPB = score_rows_per_block<T, D>();
-  const int g = blockIdx.y, b = blockIdx.z;
+  const GroupBlock gb = group_block(d.B * d.Hkv);
+  const int g = gb.bg % d.Hkv, b = gb.bg / d.Hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane / LPR, cl = lane % LPR;
-  const int u0 = blockIdx.x * PPB;
+  const int u0 = gb.j * PPB;
   float qv[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h)
@@ -89,21 +90,44 @@ __global__ __launch_bounds__(kScoreThreads) void score_pages_kernel(
   }
 }
 
+// Block-wide min and max of the per-lane key ranges, stored as partial x of
+// bg (nx partials per bg): mm[(bg * nx + x) * 2 + {0, 1}].
+__device__ __forceinline__ void block_partial_minmax(uint32_t* mm, uint32_t mn, uint32_t mx,
+                                                     int64_t bg, int x, int nx) {
+  __shared__ uint32_t s_mm[2][kScoreThreads / 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  mn = wave_umin(mn);
+  mx = wave_umax(mx);
+  if (lane == 0) { s_mm[0][wave] = mn; s_mm[1][wave] = mx; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int w = 1; w < kScoreThreads / 64; ++w) {
+      mn = min(mn, s_mm[0][w]);
+      mx = max(mx, s_mm[1][w]);
+    }
+    mm[(bg * nx + x) * 2] = mn;
+    mm[(bg * nx + x) * 2 + 1] = mx;
+  }
+}
+
 // fp32 token scorer (vector FMAs).
 template <int D, int G>
 __global__ __launch_bounds__(kScoreThreads) void score_tokens_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k_pages,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
-    float* __restrict__ scores, float* __restrict__ logits, Dims d) {
+    float* __restrict__ scores, float* __restrict__ logits, uint32_t* __restrict__ mm, Dims d) {
   constexpr int LPR = D / 8;
   constexpr int RPW = 64 / LPR;
   constexpr int IT = kScoreIters;
   constexpr int TPB = score_rows_per_block<float, D>();
-  const int g = blockIdx.y, b = blockIdx.z;
+  const int BG = d.B * d.Hkv;
+  const GroupBlock gb = group_block(BG);
+  const int g = gb.bg % d.Hkv, b = gb.bg / d.Hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane / LPR, cl = lane % LPR;
   const int n = clamp_len(seq_lens[b], d.max_seq);
-  const int t0 = blockIdx.x * TPB;
+  const int t0 = gb.j * TPB;
   if (t0 >= n) return;
 
   float qv[G][8];
@@ -131,6 +155,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_tokens_f32_kernel(
   }
   __builtin_amdgcn_sched_barrier(0);
   float* sc = scores + ((int64_t)b * d.Hkv + g) * d.max_seq;
+  uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     float kv[8];
@@ -150,8 +175,11 @@ __global__ __launch_bounds__(kScoreThreads) void score_tokens_f32_kernel(
       if (!ok[it]) { best = -3.0e38f; mine = -3.0e38f; }
       if (cl < G) logits[((int64_t)b * d.Hq + g * G + cl) * d.max_seq + t] = mine;
       if (cl == 0) sc[t] = best;
+      kmn = min(kmn, order_key(best));
+      kmx = max(kmx, order_key(best));
     }
   }
+  if (mm) block_partial_minmax(mm, kmn, kmx, gb.bg, gb.j, (d.max_seq + TPB - 1) / TPB);
 }
 
 // bf16 token scorer on the matrix cores: each wave scores kScoreIters chunks
@@ -161,16 +189,18 @@ template <int D, int G>
 __global__ __launch_bounds__(kScoreThreads) void score_tokens_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_pages,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
-    float* __restrict__ scores, float* __restrict__ logits, Dims d) {
+    float* __restrict__ scores, float* __restrict__ logits, uint32_t* __restrict__ mm, Dims d) {
   constexpr int KS = D / 32;
   constexpr int IT = kScoreIters;
   constexpr int NW = kScoreThreads / 64;
   constexpr int TPB = NW * IT * 16;
-  const int g = blockIdx.y, b = blockIdx.z;
+  const int BG = d.B * d.Hkv;
+  const GroupBlock gb = group_block(BG);
+  const int g = gb.bg % d.Hkv, b = gb.bg / d.Hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = lane & 15, quad = lane >> 4;
   const int n = clamp_len(seq_lens[b], d.max_seq);
-  const int t0 = blockIdx.x * TPB;
+  const int t0 = gb.j * TPB;
   if (t0 >= n) return;
 
   bf16x8_t qop[KS];
@@ -208,6 +238,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_tokens_mfma_kernel(
   __builtin_amdgcn_sched_barrier(0);
   float* sc = scores + ((int64_t)b * d.Hkv + g) * d.max_seq;
   float* lg = logits + ((int64_t)b * d.Hq + g * G + row) * d.max_seq;
+  uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     if (tc[it] >= n) continue;
@@ -225,9 +256,17 @@ __global__ __launch_bounds__(kScoreThreads) void score_tokens_mfma_kernel(
       if (t < n) {
         if (row < G) lg[t] = x;
         if (row == 0) sc[t] = best;
+        kmn = min(kmn, order_key(best));
+        kmx = max(kmx, order_key(best));
       }
     }
   }
+  if (mm) block_partial_minmax(mm, kmn, kmx, gb.bg, gb.j, (d.max_seq + TPB - 1) / TPB);
+}
+
+int score_units_per_block(int dtype, int D) {
+  if (dtype == kBF16) return (kScoreThreads / 64) * kScoreIters * 16;
+  return D == 64 ? score_rows_per_block<float, 64>() : score_rows_per_block<float, 128>();
 }
 
 hipError_t launch_score(const ScoreArgs& a, hipStream_t st) {
@@ -238,22 +277,22 @@ hipError_t launch_score(const ScoreArgs& a, hipStream_t st) {
     constexpr int G = decltype(gg)::value;
     if (a.unit == kPage) {
       constexpr int R = score_rows_per_block<T, D>();
-      const dim3 grid((d.max_pages + R - 1) / R, d.Hkv, d.B);
+      const dim3 grid((d.max_pages + R - 1) / R * d.Hkv * d.B);
       score_pages_kernel<T, D, G><<<grid, kScoreThreads, 0, st>>>(
           static_cast<const T*>(a.q), static_cast<const T*>(a.bounds), a.seq_lens,
           a.unit_scores, d);
     } else if constexpr (std::is_same<T, float>::value) {
       constexpr int R = score_rows_per_block<T, D>();
-      const dim3 grid((d.max_seq + R - 1) / R, d.Hkv, d.B);
+      const dim3 grid((d.max_seq + R - 1) / R * d.Hkv * d.B);
       score_tokens_f32_kernel<D, G><<<grid, kScoreThreads, 0, st>>>(
           static_cast<const float*>(a.q), static_cast<const float*>(a.k_pages), a.block_table,
-          a.seq_lens, a.unit_scores, a.token_logits, d);
+          a.seq_lens, a.unit_scores, a.token_logits, a.score_mm, d);
     } else {
       constexpr int R = (kScoreThreads / 64) * kScoreIters * 16;
-      const dim3 grid((d.max_seq + R - 1) / R, d.Hkv, d.B);
+      const dim3 grid((d.max_seq + R - 1) / R * d.Hkv * d.B);
       score_tokens_mfma_kernel<D, G><<<grid, kScoreThreads, 0, st>>>(
           static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k_pages), a.block_table,
-          a.seq_lens, a.unit_scores, a.token_logits, d);
+          a.seq_lens, a.unit_scores, a.token_logits, a.score_mm, d);
     }
   });
   if (!ok) return hipErrorInvalidValue;

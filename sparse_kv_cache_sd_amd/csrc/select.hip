@@ -1,9 +1,9 @@
 // Stage 1b: exact top-k of the unit scores of one (sequence, KV head), as a
 // standalone kernel: one block per (sequence, KV head).  The search itself
 // (radix bins over the block's key range, ties to the lower index, ids in
-// ascending order) is in topk.h.  Up to 16384 units the block's threads hold
-// the keys in registers; above that the memory-resident variant re-reads
-// them on every pass.
+// ascending order) is in topk.h.  The block's threads hold the keys in
+// registers (up to 16384 units; more go to select_multi.hip, which spreads
+// one selection over many blocks).
 #include "topk.h"
 
 namespace sdkv {
@@ -37,82 +37,6 @@ __global__ __launch_bounds__(NT) void select_topk_regs_kernel(
                           [&](int pos, int unit_id) { out[pos] = unit_id; });
 }
 
-// Keys re-read from memory on every pass (large U).
-__global__ __launch_bounds__(1024) void select_topk_mem_kernel(
-    const float* __restrict__ scores, const int32_t* __restrict__ seq_lens,
-    int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_count, Dims d, int unit, int U_max,
-    int k_max, int R_ppm) {
-  constexpr int NT = 1024;
-  __shared__ RadixState st;
-  const int g = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int n = clamp_len(seq_lens[b], d.max_seq);
-  const int U = min(unit == kPage ? (n + d.P - 1) / d.P : n, U_max);
-  const int k = min(keep_count_dev(U, R_ppm), k_max);
-  const int64_t bg = (int64_t)b * d.Hkv + g;
-  const float* sc = scores + bg * U_max;
-  int32_t* out = sel_idx + bg * k_max;
-  if (tid == 0) sel_count[bg] = k;
-  if (k == 0) return;
-  if (k == U) {
-    for (int i = tid; i < U; i += NT) out[i] = i;
-    return;
-  }
-  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-  for (int i = tid; i < U; i += NT) {
-    const uint32_t key = order_key(sc[i]);
-    mn = min(mn, key);
-    mx = max(mx, key);
-  }
-  block_minmax(st, mn, mx);
-  if (tid == 0) { st.need = (uint32_t)k; st.whole = 0u; }
-  __syncthreads();
-  uint32_t lo = st.lo, hi = st.hi;
-  bool whole = false;
-  while (!whole && lo != hi) {
-    const uint32_t shift = bin_shift(lo, hi);
-    if (tid < 256) st.hist[tid] = 0u;
-    if (tid == 0) st.shift = shift;
-    __syncthreads();
-    for (int i = tid; i < U; i += NT) {
-      const uint32_t key = order_key(sc[i]);
-      if (key >= lo && key <= hi) atomicAdd(&st.hist[(key - lo) >> shift], 1u);
-    }
-    __syncthreads();
-    if (tid < 64) find_bin(st);
-    __syncthreads();
-    lo = st.lo;
-    hi = st.hi;
-    whole = st.whole != 0u;
-  }
-  const uint32_t need = st.need;
-  const uint32_t T = lo;
-  const int C = (U + NT - 1) / NT;
-  const int i_lo = min(U, tid * C), i_hi = min(U, i_lo + C);
-  uint32_t gt = 0u, eq = 0u;
-  for (int i = i_lo; i < i_hi; ++i) {
-    const uint32_t key = order_key(sc[i]);
-    gt += whole ? key >= T : key > T;
-    eq += !whole && key == T;
-  }
-  uint32_t gt_before, eq_before;
-  block_excl_scan2(st, gt, eq, &gt_before, &eq_before);
-  uint32_t pos = gt_before + min(eq_before, need);
-  uint32_t tie = eq_before;
-  for (int i = i_lo; i < i_hi; ++i) {
-    const uint32_t key = order_key(sc[i]);
-    bool take = whole ? key >= T : key > T;
-    if (!whole && key == T) {
-      take = tie < need;
-      ++tie;
-    }
-    if (take) {
-      if (pos < (uint32_t)k) out[pos] = i;
-      ++pos;
-    }
-  }
-}
-
 hipError_t launch_select(const SelectArgs& a, hipStream_t st) {
   const dim3 grid(a.d.Hkv, a.d.B);
   const int U = a.U_max;
@@ -123,11 +47,8 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t st) {
   if (U <= 2048) SD_SELECT_REGS(512, 4);
   else if (U <= 4096) SD_SELECT_REGS(512, 8);
   else if (U <= 8192) SD_SELECT_REGS(512, 16);
-  else if (U <= 16384) SD_SELECT_REGS(1024, 16);
-  else
-    select_topk_mem_kernel<<<grid, 1024, 0, st>>>(a.unit_scores, a.seq_lens, a.sel_idx,
-                                                  a.sel_count, a.d, a.unit, a.U_max, a.k_max,
-                                                  a.R_ppm);
+  else if (U <= kMaxSelectU) SD_SELECT_REGS(1024, 16);
+  else return hipErrorInvalidValue;  // many units: launch_select_multi
 #undef SD_SELECT_REGS
   return hipGetLastError();
 }

@@ -52,10 +52,13 @@ struct RadixState {
   uint32_t lo, hi, need, whole, shift;
 };
 
-// Block-wide min and max of the keys; result in st.lo / st.hi.
+// Block-wide min and max of the keys (NW waves); result in st.lo / st.hi.
+// (Block sizes are compile-time constants throughout: reading blockDim or
+// gridDim can cost a read of the dispatch packet.)
+template <int NW>
 __device__ __forceinline__ void block_minmax(RadixState& st, uint32_t mn, uint32_t mx) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nw = blockDim.x >> 6;
+  constexpr int nw = NW;
   mn = wave_umin(mn);
   mx = wave_umax(mx);
   if (lane == 0) { st.wa[wave] = mn; st.wb[wave] = mx; }
@@ -99,7 +102,7 @@ __device__ __forceinline__ void find_bin(RadixState& st) {
   }
 }
 
-// Exclusive block scan of two counters at once (blockDim.x <= 1024).
+// Exclusive block scan of two counters at once (at most 16 waves).
 __device__ __forceinline__ void block_excl_scan2(RadixState& st, uint32_t a, uint32_t b,
                                                  uint32_t* ea, uint32_t* eb) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -134,21 +137,28 @@ __device__ __forceinline__ void rank_kept(uint32_t* s_cnt, const uint32_t (&key)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int NT = NW * 64;
   const uint64_t below = lanes_below();
-  uint32_t a_base[KPT], t_base[KPT];
   if constexpr (NW == 1) {
     uint32_t a_run = 0u, t_run = 0u;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const bool v = lane + NT * i < U;
-      const uint64_t ma = __ballot(v && (whole ? key[i] >= T : key[i] > T));
-      const uint64_t mt = __ballot(v && !whole && key[i] == T);
-      a_base[i] = a_run;
-      t_base[i] = t_run;
+      const bool above = v && (whole ? key[i] >= T : key[i] > T);
+      const bool tie = v && !whole && key[i] == T;
+      const uint64_t ma = __ballot(above), mt = __ballot(tie);
+      const uint32_t A = a_run + __popcll(ma & below);
+      const uint32_t Ti = t_run + __popcll(mt & below);
+      if (above || (tie && Ti < need)) {
+        const uint32_t pos = A + min(Ti, need);
+        if (pos < (uint32_t)k) emit((int)pos, lane + NT * i);
+      }
       a_run += __popcll(ma);
       t_run += __popcll(mt);
     }
+    return;
   } else {
-    static_assert(KPT * NW <= 256, "one scan lane holds four (slot, wave) pairs");
+    constexpr int PAIRS = KPT * NW;
+    constexpr int PPL = (PAIRS + 63) / 64;  // (slot, wave) pairs per scanning lane
+    static_assert(PPL <= 8, "at most 512 (slot, wave) pairs");
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const bool v = threadIdx.x + NT * i < U;
@@ -161,21 +171,21 @@ __device__ __forceinline__ void rank_kept(uint32_t* s_cnt, const uint32_t (&key)
     }
     __syncthreads();
     if (wave == 0) {
-      // lane holds pairs 4 lane .. 4 lane + 3 of the (slot, wave) order
-      uint32_t ca[4], ct[4], sa = 0u, st = 0u;
+      // lane holds pairs PPL lane .. PPL lane + PPL - 1 of the (slot, wave) order
+      uint32_t ca[PPL], ct[PPL], sa = 0u, st = 0u;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int e = 4 * lane + q;
-        ca[q] = e < KPT * NW ? s_cnt[2 * e] : 0u;
-        ct[q] = e < KPT * NW ? s_cnt[2 * e + 1] : 0u;
+      for (int q = 0; q < PPL; ++q) {
+        const int e = PPL * lane + q;
+        ca[q] = e < PAIRS ? s_cnt[2 * e] : 0u;
+        ct[q] = e < PAIRS ? s_cnt[2 * e + 1] : 0u;
         sa += ca[q];
         st += ct[q];
       }
       uint32_t ea = wave_scan_dpp(sa) - sa, et = wave_scan_dpp(st) - st;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int e = 4 * lane + q;
-        if (e < KPT * NW) { s_cnt[2 * e] = ea; s_cnt[2 * e + 1] = et; }
+      for (int q = 0; q < PPL; ++q) {
+        const int e = PPL * lane + q;
+        if (e < PAIRS) { s_cnt[2 * e] = ea; s_cnt[2 * e + 1] = et; }
         ea += ca[q];
         et += ct[q];
       }
@@ -183,22 +193,17 @@ __device__ __forceinline__ void rank_kept(uint32_t* s_cnt, const uint32_t (&key)
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-      a_base[i] = s_cnt[2 * (i * NW + wave)];
-      t_base[i] = s_cnt[2 * (i * NW + wave) + 1];
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    const int u = threadIdx.x + NT * i;
-    const bool v = u < U;
-    const bool above = v && (whole ? key[i] >= T : key[i] > T);
-    const bool tie = v && !whole && key[i] == T;
-    const uint64_t ma = __ballot(above), mt = __ballot(tie);
-    const uint32_t A = a_base[i] + __popcll(ma & below);
-    const uint32_t Ti = t_base[i] + __popcll(mt & below);
-    if (above || (tie && Ti < need)) {
-      const uint32_t pos = A + min(Ti, need);
-      if (pos < (uint32_t)k) emit((int)pos, u);
+      const int u = threadIdx.x + NT * i;
+      const bool v = u < U;
+      const bool above = v && (whole ? key[i] >= T : key[i] > T);
+      const bool tie = v && !whole && key[i] == T;
+      const uint64_t ma = __ballot(above), mt = __ballot(tie);
+      const uint32_t A = s_cnt[2 * (i * NW + wave)] + __popcll(ma & below);
+      const uint32_t Ti = s_cnt[2 * (i * NW + wave) + 1] + __popcll(mt & below);
+      if (above || (tie && Ti < need)) {
+        const uint32_t pos = A + min(Ti, need);
+        if (pos < (uint32_t)k) emit((int)pos, u);
+      }
     }
   }
 }
@@ -216,7 +221,7 @@ __device__ __forceinline__ void topk_regs(RadixState& st, uint32_t* s_cnt,
 #pragma unroll
   for (int i = 0; i < KPT; ++i)
     if (tid + NT * i < U) { mn = min(mn, key[i]); mx = max(mx, key[i]); }
-  block_minmax(st, mn, mx);
+  block_minmax<NW>(st, mn, mx);
   if (tid == 0) { st.need = (uint32_t)k; st.whole = 0u; }
   __syncthreads();
   uint32_t lo = st.lo, hi = st.hi;

@@ -110,7 +110,8 @@ def _select_case(scores_np, seq_lens, unit, r_kv, shape):
     k_max = sd.keep_count(r_kv, umax)
     sel = torch.full((s.batch, s.num_kv_heads, k_max), -1, dtype=torch.int32, device="cuda")
     cnt = torch.full((s.batch, s.num_kv_heads), -1, dtype=torch.int32, device="cuda")
-    sd.select_topk(s, unit, torch.from_numpy(seq_lens).cuda(), scores, r_kv, sel, cnt)
+    ws = sd.alloc_workspace(s, unit, r_kv)
+    sd.select_topk(s, unit, torch.from_numpy(seq_lens).cuda(), scores, r_kv, sel, cnt, ws=ws)
     torch.cuda.synchronize()
     sel, cnt = sel.cpu().numpy(), cnt.cpu().numpy()
     for b in range(s.batch):
@@ -126,7 +127,8 @@ def _select_case(scores_np, seq_lens, unit, r_kv, shape):
 @pytest.mark.parametrize("seed", range(4))
 @pytest.mark.parametrize("U,unit,r", [(2048, "page", 0.3), (2048, "page", 0.05), (16384, "page", 0.05),
                                       (1024, "token", 0.25), (131072, "token", 0.2), (37, "page", 0.5),
-                                      (5000, "token", 0.9999)])
+                                      (5000, "token", 0.9999), (16385, "token", 0.5),
+                                      (40000, "page", 0.1)])
 def test_select_bitexact_with_ties(seed, U, unit, r):
     rng = np.random.default_rng(seed)
     P = 16

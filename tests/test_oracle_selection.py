@@ -169,13 +169,16 @@ def test_page_of_one_token_equals_token_unit():
 
 
 def test_tiny_salient_keys_dominate_selection():
-    """In the tiny configuration the planted keys sit about 3 logits above the
-    rest, so nearly all of them are kept; the dropped mass is still large
-    (about half) because 1024 ordinary keys carry a heavy softmax tail."""
+    """In the tiny configuration the planted keys sit about 3|q|/8 logits above
+    the rest, so nearly all of them are kept; the dropped mass stays well above
+    zero because 1024 ordinary keys carry a heavy softmax tail (how much
+    depends on each query's norm: a longer query concentrates more mass on its
+    planted keys)."""
     w = kvsynth.generate(kvsynth.RECIPES["tiny"])
     res = sdref.decode_step(w.q, w.K, w.V, w.seq_lens, dtype="f32", unit="token", page_size=16, r_kv=0.25)
     gr = res[(0, 0)]
     planted = w.salient[(0, 0)]
     assert planted.size == 128
     assert np.isin(planted, gr.kept).mean() > 0.9
-    assert np.all((gr.delta > 0.2) & (gr.delta < 0.8))
+    assert np.all((gr.delta > 0.02) & (gr.delta < 0.8))
+    assert gr.delta.mean() > 0.15
