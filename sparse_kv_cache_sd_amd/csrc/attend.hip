@@ -231,7 +231,7 @@ __global__ __launch_bounds__(kAttendWaves * 64) void attend_mfma_kernel(AttendAr
   __shared__ float s_plse[G];
   __shared__ int s_list[SELECTS ? kMaxSelectE : 1];
   __shared__ RadixState s_rs;
-  __shared__ uint32_t s_rcnt[SELECTS ? 2 * KEYS * NW : 1];
+  __shared__ KeptScratch<SELECTS ? KEYS : 1, NW> s_kept;
   auto s_v = reinterpret_cast<bf16_t(*)[16 * VROW]>(s_raw);
   auto s_o = reinterpret_cast<float(*)[G][D]>(s_raw);
 
@@ -273,7 +273,11 @@ __global__ __launch_bounds__(kAttendWaves * 64) void attend_mfma_kernel(AttendAr
     if (k == U) {
       for (int e = threadIdx.x; e < U; e += NT) emit(e, e);
     } else if (k > 0) {
-      topk_regs<KEYS, NW>(s_rs, s_rcnt, key, U, k, emit);
+      topk_bitmap<KEYS, NW>(s_rs, s_kept, key, U, k);
+      // this split's slice of the ranks, or all of them when split 0 also
+      // writes the selection out
+      emit_kept<KEYS, NW>(s_kept.mask, s_kept.base, full ? 0u : (uint32_t)sp.e0,
+                          full ? (uint32_t)k : (uint32_t)sp.e_hi, emit);
     }
     if (j == 0 && a.sel_count_out && threadIdx.x == 0) a.sel_count_out[bg] = k;
     cnt = k;

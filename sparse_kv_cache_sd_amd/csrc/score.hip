@@ -247,17 +247,29 @@ __global__ __launch_bounds__(kScoreThreads) void score_tokens_mfma_kernel(
     for (int s = 0; s < KS; ++s)
       st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv[it][s]), qop[s],
                                                     st, 0, 0, 0);
-    // lane (row = head, quad) holds tokens tc + 4 quad + r
+    // lane (row = head, quad) holds tokens tc + 4 quad + r: four consecutive
+    // logits of one head, written with one 16-byte store when all are valid
+    const int t4 = tc[it] + 4 * quad;
+    float4_t xs, bs;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int t = tc[it] + 4 * quad + r;
-      const float x = page_ok[it] ? st[r] * d.scale : -3.0e38f;
-      const float best = group_max<16>(row < G ? x : -INFINITY);
-      if (t < n) {
-        if (row < G) lg[t] = x;
-        if (row == 0) sc[t] = best;
-        kmn = min(kmn, order_key(best));
-        kmx = max(kmx, order_key(best));
+      xs[r] = page_ok[it] ? st[r] * d.scale : -3.0e38f;
+      bs[r] = group_max<16>(row < G ? xs[r] : -INFINITY);
+      if (t4 + r < n) {
+        kmn = min(kmn, order_key(bs[r]));
+        kmx = max(kmx, order_key(bs[r]));
+      }
+    }
+    if ((d.max_seq & 3) == 0 && t4 + 3 < n) {  // rows are 16-byte aligned
+      if (row < G) *reinterpret_cast<float4_t*>(lg + t4) = xs;
+      if (row == 0) *reinterpret_cast<float4_t*>(sc + t4) = bs;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (t4 + r < n) {
+          if (row < G) lg[t4 + r] = xs[r];
+          if (row == 0) sc[t4 + r] = bs[r];
+        }
       }
     }
   }

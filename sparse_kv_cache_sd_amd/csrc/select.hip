@@ -14,7 +14,7 @@ __global__ __launch_bounds__(NT) void select_topk_regs_kernel(
     int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_count, Dims d, int unit, int U_max,
     int k_max, int R_ppm) {
   __shared__ RadixState st;
-  __shared__ uint32_t s_cnt[2 * KPT * (NT / 64)];
+  __shared__ KeptScratch<KPT, NT / 64> ks;
   const int g = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x;
   const int64_t bg = (int64_t)b * d.Hkv + g;
@@ -33,7 +33,8 @@ __global__ __launch_bounds__(NT) void select_topk_regs_kernel(
     for (int i = tid; i < U; i += NT) out[i] = i;
     return;
   }
-  topk_regs<KPT, NT / 64>(st, s_cnt, key, U, k,
+  topk_bitmap<KPT, NT / 64>(st, ks, key, U, k);
+  emit_kept<KPT, NT / 64>(ks.mask, ks.base, 0u, (uint32_t)k,
                           [&](int pos, int unit_id) { out[pos] = unit_id; });
 }
 

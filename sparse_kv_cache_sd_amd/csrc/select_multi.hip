@@ -30,9 +30,9 @@ namespace sdkv {
 
 namespace {
 
-constexpr int kMT = 1024;              // threads per block
+constexpr int kMT = 512;               // threads per block
 constexpr int kMNW = kMT / 64;
-constexpr int kMK = 32;                // keys per thread
+constexpr int kMK = 16;                // keys per thread
 constexpr int kMSlice = kMT * kMK;     // units per block
 constexpr int kMBins = 2048;           // 11-bit bins
 constexpr int kMPasses = 3;
@@ -130,29 +130,32 @@ __device__ void narrow(const MArgs& a, MShared& sm, int64_t bg, int p, const MSt
                        int blk, uint32_t* above_before, uint32_t* inside_before) {
   const int tid = threadIdx.x;
   const uint32_t* h = a.hist + ((int64_t)p * a.d.B * a.d.Hkv + bg) * a.NB * kMBins;
-  // thread t holds bins kMBins - 1 - 2t - j (j = 0, 1): descending order; the
-  // pair is one 8-byte load per slice
+  // thread t holds bins kMBins - 1 - BPT t - j (j < BPT): descending order;
+  // its BPT bins are one vector load per slice
   constexpr int BPT = kMBins / kMT;
-  static_assert(BPT == 2, "two bins per thread");
-  uint32_t c[BPT] = {0u, 0u}, cb[BPT] = {0u, 0u};
-  typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+  static_assert(BPT == 2 || BPT == 4 || BPT == 8, "2, 4 or 8 bins per thread");
+  typedef unsigned int vec_t __attribute__((ext_vector_type(BPT)));
+  uint32_t c[BPT] = {}, cb[BPT] = {};
   for (int b0 = 0; b0 < a.NB; b0 += 8) {
-    u32x2_t v[8];
+    vec_t v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int s = min(b0 + i, a.NB - 1);
-      v[i] = *reinterpret_cast<const u32x2_t*>(h + (int64_t)s * kMBins + (kMBins - 2 - 2 * tid));
+      v[i] = *reinterpret_cast<const vec_t*>(h + (int64_t)s * kMBins + (kMBins - BPT - BPT * tid));
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const bool valid = b0 + i < a.NB, before = b0 + i < blk;
-      c[0] += valid ? v[i][1] : 0u;   // bin kMBins - 1 - 2t
-      c[1] += valid ? v[i][0] : 0u;   // bin kMBins - 2 - 2t
-      cb[0] += before ? v[i][1] : 0u;
-      cb[1] += before ? v[i][0] : 0u;
+#pragma unroll
+      for (int j = 0; j < BPT; ++j) {  // bin kMBins - 1 - BPT t - j is element BPT - 1 - j
+        c[j] += valid ? v[i][BPT - 1 - j] : 0u;
+        cb[j] += before ? v[i][BPT - 1 - j] : 0u;
+      }
     }
   }
-  const uint32_t tot = c[0] + c[1];
+  uint32_t tot = 0u;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) tot += c[j];
   uint32_t run, unused;
   block_excl_scan2(sm.rs, tot, 0u, &run, &unused);  // keys in higher bins
   const uint32_t shift = shift_of(prev.lo, prev.hi);
@@ -255,7 +258,7 @@ __global__ __launch_bounds__(kMT) void msel_pass_kernel(MArgs a, int p) {
 // Kept ids of each slice at their place in the ascending list.
 __global__ __launch_bounds__(kMT) void msel_place_kernel(MArgs a) {
   __shared__ MShared sm;
-  __shared__ uint32_t s_cnt[2 * kMK * kMNW];
+  __shared__ KeptScratch<kMK, kMNW> ks;
   const GroupBlock gbk = group_block(a.d.B * a.d.Hkv);
   const int blk = gbk.j, b = gbk.bg / a.d.Hkv;
   const int64_t bg = gbk.bg;
@@ -300,14 +303,15 @@ __global__ __launch_bounds__(kMT) void msel_place_kernel(MArgs a) {
     above_before = ov + ab + (S.whole ? inb : 0u);
     equal_before = S.whole ? 0u : inb;
   }
-  const uint32_t quota = S.need > equal_before ? S.need - equal_before : 0u;
+  // max(need - equal_before, 0), as a signed difference (see kept_words)
+  const uint32_t quota = (uint32_t)max((int)S.need - (int)equal_before, 0);
   const uint32_t base = above_before + min(equal_before, S.need);
   const int n_slice = min(kMSlice, U - s0);
-  rank_kept<kMK, kMNW>(s_cnt, key, n_slice, kMSlice, S.lo, quota, S.whole != 0u,
-                       [&](int pos, int u) {
-                         const uint32_t gp = base + (uint32_t)pos;
-                         if (gp < k) out[gp] = s0 + u;
-                       });
+  kept_words<kMK, kMNW>(ks.mask, ks.tie, ks.base, key, n_slice, S.lo, quota, S.whole != 0u);
+  emit_kept<kMK, kMNW>(ks.mask, ks.base, 0u, (uint32_t)kMSlice, [&](int pos, int u) {
+    const uint32_t gp = base + (uint32_t)pos;
+    if (gp < k) out[gp] = s0 + u;
+  });
 }
 
 }  // namespace

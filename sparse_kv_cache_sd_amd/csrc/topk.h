@@ -18,9 +18,10 @@
 // the LDS counters see little contention.  A pass whose bin is needed whole
 // ends the search: every key >= the bin's lower edge is kept.  Otherwise the
 // bins shrink to single keys, T = lo is the k-th largest key, and the first
-// `need` keys equal to T in index order are kept.  Ballots and a scan in index
-// order give every kept id its rank.  All counting is integer, so the result
-// does not depend on thread timing.
+// `need` keys equal to T in index order are kept.  The kept set is then a
+// bitmap (one ballot per 64 consecutive units), and a scan of the word counts
+// in index order gives every kept id its rank.  All counting is integer, so
+// the result does not depend on thread timing.
 #pragma once
 
 #include "device.h"
@@ -116,105 +117,124 @@ __device__ __forceinline__ void block_excl_scan2(RadixState& st, uint32_t a, uin
   __syncthreads();
 }
 
-// Lanes below this one, as a 64-bit mask.
-__device__ __forceinline__ uint64_t lanes_below() {
-  return (1ull << (threadIdx.x & 63)) - 1ull;
+// The kept set as a bitmap, for keys held interleaved (key[i] of thread t is
+// unit t + NT*i, so the ballot of slot i in wave w is the 64-bit word of units
+// 64 (i*NW + w) .. +63: words in ascending unit order).  Kept = above T (or
+// >= T for a whole bin), plus the first `need` units equal to T in id order.
+// On return (after a barrier) s_mask[e] holds the kept units of word e and
+// s_base[e] the number of kept units in the words before it, so a kept unit's
+// rank in the ascending list is s_base[e] + its position among the word's set
+// bits.  One wave trims the ties and scans the word counts.
+template <int KPT, int NW>
+__device__ __forceinline__ void kept_words(uint64_t* s_mask, uint64_t* s_tie, uint32_t* s_base,
+                                           const uint32_t (&key)[KPT], int U, uint32_t T,
+                                           uint32_t need, bool whole) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int NT = NW * 64, W = KPT * NW;
+  constexpr int PPL = (W + 63) / 64;  // words per scanning lane
+  static_assert(PPL <= 8, "at most 512 words");
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const bool v = (int)threadIdx.x + NT * i < U;
+    const uint64_t above = __ballot(v && (whole ? key[i] >= T : key[i] > T));
+    const uint64_t tie = __ballot(v && !whole && key[i] == T);
+    if (lane == 0) {
+      s_mask[i * NW + wave] = above;
+      s_tie[i * NW + wave] = tie;
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    uint64_t m[PPL], t[PPL];
+    uint32_t tc = 0u;
+#pragma unroll
+    for (int q = 0; q < PPL; ++q) {
+      const int e = PPL * lane + q;
+      m[q] = e < W ? s_mask[e] : 0ull;
+      t[q] = e < W ? s_tie[e] : 0ull;
+      tc += __popcll(t[q]);
+    }
+    uint32_t ties_before = wave_scan_dpp(tc) - tc;
+    uint32_t kc = 0u;
+#pragma unroll
+    for (int q = 0; q < PPL; ++q) {
+      const uint32_t c = __popcll(t[q]);
+      // max(need - ties_before, 0) as a signed difference: written as an
+      // unsigned conditional subtract it became a saturating subtract that
+      // the code generator emitted without its clamp.
+      const int rem = max((int)need - (int)ties_before, 0);
+      const uint32_t keep = min((uint32_t)rem, c);
+      uint64_t rest = t[q];  // drop the `keep` lowest tie bits from rest
+      for (uint32_t r = 0; r < keep; ++r) rest &= rest - 1ull;
+      m[q] |= t[q] ^ rest;
+      ties_before += c;
+      kc += __popcll(m[q]);
+    }
+    uint32_t base = wave_scan_dpp(kc) - kc;
+#pragma unroll
+    for (int q = 0; q < PPL; ++q) {
+      const int e = PPL * lane + q;
+      if (e < W) {
+        s_mask[e] = m[q];
+        s_base[e] = base;
+      }
+      base += __popcll(m[q]);
+    }
+  }
+  __syncthreads();
 }
 
-// Rank of every kept unit among the kept units in ascending unit order, for
-// keys held interleaved (key[i] of thread t is unit t + NT*i):
-//   above(u) = key > T (key >= T for a whole bin), tie(u) = key == T otherwise,
-//   A(u), Ties(u) = numbers of above / tie units with a smaller id,
-//   kept(u) = above(u) or (tie(u) and Ties(u) < need),
-//   rank(u) = A(u) + min(Ties(u), need).
-// Per key slot i and wave w the above / tie counts go to LDS (s_cnt, 2 * KPT *
-// NW words), one wave scans them in (i, w) order, and each wave ranks its
-// lanes with ballots.  NW = 1 needs no barrier.
+// Calls emit(rank, unit) for every kept unit whose rank lies in [r_lo, r_hi),
+// from the bitmap of kept_words.  With few keys per thread each thread ranks
+// its own keys (unit t + NT*i is bit `lane` of word i*NW + wave; a wave skips
+// a word whose ranks lie outside the range); with many, threads take a word
+// each and walk its set bits, skipping words outside the range.
 template <int KPT, int NW, typename Emit>
-__device__ __forceinline__ void rank_kept(uint32_t* s_cnt, const uint32_t (&key)[KPT], int U,
-                                          int k, uint32_t T, uint32_t need, bool whole,
-                                          Emit&& emit) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__device__ __forceinline__ void emit_kept(const uint64_t* s_mask, const uint32_t* s_base,
+                                          uint32_t r_lo, uint32_t r_hi, Emit&& emit) {
   constexpr int NT = NW * 64;
-  const uint64_t below = lanes_below();
-  if constexpr (NW == 1) {
-    uint32_t a_run = 0u, t_run = 0u;
+  if constexpr (KPT < 16) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-      const bool v = lane + NT * i < U;
-      const bool above = v && (whole ? key[i] >= T : key[i] > T);
-      const bool tie = v && !whole && key[i] == T;
-      const uint64_t ma = __ballot(above), mt = __ballot(tie);
-      const uint32_t A = a_run + __popcll(ma & below);
-      const uint32_t Ti = t_run + __popcll(mt & below);
-      if (above || (tie && Ti < need)) {
-        const uint32_t pos = A + min(Ti, need);
-        if (pos < (uint32_t)k) emit((int)pos, lane + NT * i);
-      }
-      a_run += __popcll(ma);
-      t_run += __popcll(mt);
+      const uint64_t m = s_mask[i * NW + wave];
+      const uint32_t base = s_base[i * NW + wave];
+      if (base >= r_hi || base + (uint32_t)__popcll(m) <= r_lo) continue;  // uniform
+      const uint32_t pos = base + (uint32_t)__popcll(m & below);
+      if (((m >> lane) & 1ull) && pos >= r_lo && pos < r_hi)
+        emit((int)pos, (int)threadIdx.x + NT * i);
     }
-    return;
   } else {
-    constexpr int PAIRS = KPT * NW;
-    constexpr int PPL = (PAIRS + 63) / 64;  // (slot, wave) pairs per scanning lane
-    static_assert(PPL <= 8, "at most 512 (slot, wave) pairs");
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const bool v = threadIdx.x + NT * i < U;
-      const uint64_t ma = __ballot(v && (whole ? key[i] >= T : key[i] > T));
-      const uint64_t mt = __ballot(v && !whole && key[i] == T);
-      if (lane == 0) {
-        s_cnt[2 * (i * NW + wave)] = __popcll(ma);
-        s_cnt[2 * (i * NW + wave) + 1] = __popcll(mt);
-      }
-    }
-    __syncthreads();
-    if (wave == 0) {
-      // lane holds pairs PPL lane .. PPL lane + PPL - 1 of the (slot, wave) order
-      uint32_t ca[PPL], ct[PPL], sa = 0u, st = 0u;
-#pragma unroll
-      for (int q = 0; q < PPL; ++q) {
-        const int e = PPL * lane + q;
-        ca[q] = e < PAIRS ? s_cnt[2 * e] : 0u;
-        ct[q] = e < PAIRS ? s_cnt[2 * e + 1] : 0u;
-        sa += ca[q];
-        st += ct[q];
-      }
-      uint32_t ea = wave_scan_dpp(sa) - sa, et = wave_scan_dpp(st) - st;
-#pragma unroll
-      for (int q = 0; q < PPL; ++q) {
-        const int e = PPL * lane + q;
-        if (e < PAIRS) { s_cnt[2 * e] = ea; s_cnt[2 * e + 1] = et; }
-        ea += ca[q];
-        et += ct[q];
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int u = threadIdx.x + NT * i;
-      const bool v = u < U;
-      const bool above = v && (whole ? key[i] >= T : key[i] > T);
-      const bool tie = v && !whole && key[i] == T;
-      const uint64_t ma = __ballot(above), mt = __ballot(tie);
-      const uint32_t A = s_cnt[2 * (i * NW + wave)] + __popcll(ma & below);
-      const uint32_t Ti = s_cnt[2 * (i * NW + wave) + 1] + __popcll(mt & below);
-      if (above || (tie && Ti < need)) {
-        const uint32_t pos = A + min(Ti, need);
-        if (pos < (uint32_t)k) emit((int)pos, u);
+    constexpr int W = KPT * NW;
+    for (int e = threadIdx.x; e < W; e += NT) {
+      uint64_t m = s_mask[e];
+      uint32_t pos = s_base[e];
+      if (pos >= r_hi || pos + (uint32_t)__popcll(m) <= r_lo) continue;
+      while (m != 0ull) {
+        const int bit = __builtin_ctzll(m);
+        if (pos >= r_lo && pos < r_hi) emit((int)pos, 64 * e + bit);
+        ++pos;
+        m &= m - 1ull;
       }
     }
   }
 }
 
-// Top-k by a whole block over keys held in registers, interleaved: key[i] of
-// thread t is unit t + NT*i (keys past U are ignored).  emit(rank, unit) is
-// called once per kept unit, rank = its position among the kept units in
-// ascending unit order.
-template <int KPT, int NW, typename Emit>
-__device__ __forceinline__ void topk_regs(RadixState& st, uint32_t* s_cnt,
-                                          const uint32_t (&key)[KPT], int U, int k, Emit&& emit) {
+template <int KPT, int NW>
+struct KeptScratch {
+  uint64_t mask[KPT * NW], tie[KPT * NW];
+  uint32_t base[KPT * NW];
+};
+
+// The exact top-k search over keys held in registers, interleaved (key[i] of
+// thread t is unit t + NT*i; keys past U are ignored): the final interval in
+// lo / need / whole -- every key above it is kept, and need more from it (all
+// of it when whole; else it is the single k-th largest key T).
+template <int KPT, int NW>
+__device__ __forceinline__ void radix_search(RadixState& st, const uint32_t (&key)[KPT], int U,
+                                             int k, uint32_t* lo_out, uint32_t* need_out,
+                                             bool* whole_out) {
   constexpr int NT = NW * 64;
   const int tid = threadIdx.x;
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
@@ -231,7 +251,6 @@ __device__ __forceinline__ void topk_regs(RadixState& st, uint32_t* s_cnt,
     if (tid < 256) st.hist[tid] = 0u;
     if (tid == 0) st.shift = shift;
     __syncthreads();
-    // every thread adds 0 or 1 for every slot: no divergent branches
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const bool in = tid + NT * i < U && key[i] >= lo && key[i] <= hi;
@@ -244,7 +263,20 @@ __device__ __forceinline__ void topk_regs(RadixState& st, uint32_t* s_cnt,
     hi = st.hi;
     whole = st.whole != 0u;
   }
-  rank_kept<KPT, NW>(s_cnt, key, U, k, lo, st.need, whole, emit);
+  *lo_out = lo;
+  *need_out = st.need;
+  *whole_out = whole;
+}
+
+// Exact top-k search followed by the kept bitmap (in ks, after a barrier);
+// the caller emits the ranks it needs with emit_kept.
+template <int KPT, int NW>
+__device__ __forceinline__ void topk_bitmap(RadixState& st, KeptScratch<KPT, NW>& ks,
+                                            const uint32_t (&key)[KPT], int U, int k) {
+  uint32_t T, need;
+  bool whole;
+  radix_search<KPT, NW>(st, key, U, k, &T, &need, &whole);
+  kept_words<KPT, NW>(ks.mask, ks.tie, ks.base, key, U, T, need, whole);
 }
 
 }  // namespace sdkv
