@@ -90,6 +90,91 @@ __global__ __launch_bounds__(kScoreThreads) void score_pages_kernel(
   }
 }
 
+// bf16 page scorer on the matrix cores.  The bound of one head is a dense
+// contraction over the 2d channels of the stored [kmin | kmax] row:
+//   sum_c q_c * (q_c >= 0 ? kmax_c : kmin_c)
+//     = sum_c min(q_c, 0) kmin_c + sum_c max(q_c, 0) kmax_c,
+// so with Q' = [min(q, 0) | max(q, 0)] (exact in bf16) the scores of 16 pages
+// and the 16 (padded) heads of a group are one 16x16 tile of Q' R^T, R the
+// pages' bound rows: 2d / 32 mfma 16x16x32 steps.  Q' is the A operand (lane
+// (h, quad) holds Q'[h][32 s + 8 quad .. +7]), the bound rows the B operand
+// (lane (u, quad) loads 16 bytes of page u's row), and the result lane
+// (u, quad) holds heads 4 quad .. 4 quad + 3 of page u, so the max over the
+// group needs at most one lane exchange (G = 8).  Each wave scores
+// kPageTiles tiles of 16 pages, all loads issued before the first product.
+// Used for bf16 groups of more than four heads.
+constexpr int kPageTiles = 2;
+
+template <int D, int G>
+__global__ __launch_bounds__(kScoreThreads) void score_pages_mfma_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ bounds,
+    const int32_t* __restrict__ seq_lens, float* __restrict__ scores, Dims d) {
+  constexpr int KS = 2 * D / 32;  // steps over the 2d channels
+  constexpr int NW = kScoreThreads / 64, IT = kPageTiles;
+  constexpr int PPB = NW * IT * 16;
+  static_assert(G <= 8, "at most two quads of heads");
+  const GroupBlock gb = group_block(d.B * d.Hkv);
+  const int g = gb.bg % d.Hkv, b = gb.bg / d.Hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, quad = lane >> 4;
+  const int u0 = gb.j * PPB + wave * IT * 16;
+
+  // statistics are stored in logical page order: no block-table lookup
+  const bf16_t* bnd = bounds + ((int64_t)b * d.Hkv + g) * d.max_pages * 2 * D + 8 * quad;
+  u32x4_t rw[IT][KS];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int uc = min(u0 + 16 * it + col, d.max_pages - 1);
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      rw[it][s] = *reinterpret_cast<const u32x4_t*>(bnd + (int64_t)uc * 2 * D + 32 * s);
+  }
+  u32x4_t qw[KS];
+  {
+    const bf16_t* qrow = q + ((int64_t)b * d.Hq + g * G + min(col, G - 1)) * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      qw[s] = *reinterpret_cast<const u32x4_t*>(qrow + (32 * s + 8 * quad) % D);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // all loads issue before the first use
+  // A operand: the negative parts against kmin (first d channels), the
+  // positive parts against kmax; padded heads are zero.
+  bf16x8_t qop[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const bool neg_half = 32 * s < D;
+    u32x4_t w = qw[s];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // per 16-bit half: keep it when its sign matches the half (sign set
+      // for min(q, 0), clear for max(q, 0)), else zero
+      const uint32_t sgn = w[i] & 0x80008000u;
+      const uint32_t m = (sgn >> 15) * 0xFFFFu;  // 0xFFFF per half with its sign set
+      w[i] &= neg_half ? m : ~m;
+    }
+    if (col >= G) w = u32x4_t{0u, 0u, 0u, 0u};
+    qop[s] = __builtin_bit_cast(bf16x8_t, w);
+  }
+  const int n = clamp_len(seq_lens[b], d.max_seq);
+  const int U = (n + d.P - 1) / d.P;
+  float* out = scores + ((int64_t)b * d.Hkv + g) * d.max_pages;
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    float4_t st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qop[s], __builtin_bit_cast(bf16x8_t, rw[it][s]),
+                                                    st, 0, 0, 0);
+    float best = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (4 * quad + r < G) best = fmaxf(best, st[r] * d.scale);
+    if constexpr (G > 4) best = max_xor16(best);
+    const int u = u0 + 16 * it + col;
+    if (quad == 0 && u < U) out[u] = best;
+  }
+}
+
 // Block-wide min and max of the per-lane key ranges, stored as partial x of
 // bg (nx partials per bg): mm[(bg * nx + x) * 2 + {0, 1}].
 __device__ __forceinline__ void block_partial_minmax(uint32_t* mm, uint32_t mn, uint32_t mx,
@@ -288,11 +373,23 @@ hipError_t launch_score(const ScoreArgs& a, hipStream_t st) {
     constexpr int D = decltype(dd)::value;
     constexpr int G = decltype(gg)::value;
     if (a.unit == kPage) {
-      constexpr int R = score_rows_per_block<T, D>();
-      const dim3 grid((d.max_pages + R - 1) / R * d.Hkv * d.B);
-      score_pages_kernel<T, D, G><<<grid, kScoreThreads, 0, st>>>(
-          static_cast<const T*>(a.q), static_cast<const T*>(a.bounds), a.seq_lens,
-          a.unit_scores, d);
+      // bf16 groups of more than 4 heads go to the matrix cores (their 8
+      // sign-selected products per channel cost the vector path more than
+      // its loads); smaller groups stay on the vector path, which measured
+      // faster there
+      if constexpr (std::is_same<T, float>::value || G <= 4) {
+        constexpr int R = score_rows_per_block<T, D>();
+        const dim3 grid((d.max_pages + R - 1) / R * d.Hkv * d.B);
+        score_pages_kernel<T, D, G><<<grid, kScoreThreads, 0, st>>>(
+            static_cast<const T*>(a.q), static_cast<const T*>(a.bounds), a.seq_lens,
+            a.unit_scores, d);
+      } else {
+        constexpr int R = (kScoreThreads / 64) * kPageTiles * 16;
+        const dim3 grid((d.max_pages + R - 1) / R * d.Hkv * d.B);
+        score_pages_mfma_kernel<D, G><<<grid, kScoreThreads, 0, st>>>(
+            static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.bounds), a.seq_lens,
+            a.unit_scores, d);
+      }
     } else if constexpr (std::is_same<T, float>::value) {
       constexpr int R = score_rows_per_block<T, D>();
       const dim3 grid((d.max_seq + R - 1) / R * d.Hkv * d.B);
