@@ -282,7 +282,8 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this decode-attention path has no multi-GPU "
-              "mode (see DESIGN.md for how it would shard); use --gpus 1.", file=sys.stderr)
+              "mode (its (sequence, KV head) instances are independent, so it would shard "
+              "by sequence or by KV head with no exchange); use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch

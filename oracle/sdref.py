@@ -36,7 +36,7 @@ Sources (page title, then the part of the page):
   full attention is computed over the attended blocks only; GQA query heads
   share one KV head and one block selection. Appendix C: 64-token blocks.
 
-Readings where the pages leave a step open (each is listed in the design doc):
+Readings where the pages leave a step open:
 the page bound form and max-over-group aggregation (step 3), consecutive
 head groups g = h // G, ceil in integer ppm for k (step 4), ties to the lower
 index and ascending output (step 5), scale 1/sqrt(d) on scores too.
@@ -228,6 +228,75 @@ def select_topk(sigma: np.ndarray, k: int):
     return kept, gap
 
 
+# ----------------------------------------------------------------------------
+# structured index sets (instead of step 5)
+# ----------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class Selection:
+    """Which units a decode step keeps.
+
+    kind "topk": step 5 with k = keep_count(r_kv, U).
+    kind "window": the k = keep_count(r_kv, U) most recent units, the KV-window
+        baseline of [Cross/list] Table 3 (a window of 30% of the context).
+    kind "init_local_topk": the union of the first ``init_units`` units, the
+        last ``local_units`` units and the step-5 top-k of all U units
+        ([SparDA] Section 3.1: initial, local sliding-window and top-k blocks;
+        Appendix A: the selected set is B_init U B_local U f_top(scores, k)).
+    """
+    kind: str = "topk"
+    r_kv: float = 0.3
+    init_units: int = 0
+    local_units: int = 0
+
+
+def window_set(U: int, r_kv: float) -> np.ndarray:
+    """The k = keep_count(r_kv, U) most recent units U-k .. U-1, ascending."""
+    k = keep_count(r_kv, U)
+    return np.arange(U - k, U, dtype=np.int64)
+
+
+def init_local_topk_set(sigma: np.ndarray, r_kv: float, init_units: int,
+                        local_units: int) -> np.ndarray:
+    """B_init U B_local U top-k(sigma, keep_count(r_kv, U)), ascending.
+
+    The top-k ranks all U units (scores of initial and local units included),
+    so the three parts may overlap and the set holds between k and
+    min(U, init + local + k) units.
+    """
+    sigma = np.asarray(sigma, np.float64)
+    U = sigma.shape[0]
+    if init_units < 0 or local_units < 0:
+        raise ValueError("init_units and local_units must be >= 0")
+    top, _ = select_topk(sigma, keep_count(r_kv, U))
+    keep = np.zeros(U, dtype=bool)
+    keep[:min(init_units, U)] = True
+    keep[max(U - local_units, 0):] = True
+    keep[top] = True
+    return np.flatnonzero(keep).astype(np.int64)
+
+
+def selected_units(sigma: np.ndarray, sel: Selection) -> np.ndarray:
+    """The kept units of one (sequence, KV head) under ``sel``, ascending."""
+    U = np.asarray(sigma).shape[0]
+    if sel.kind == "topk":
+        return select_topk(sigma, keep_count(sel.r_kv, U))[0]
+    if sel.kind == "window":
+        return window_set(U, sel.r_kv)
+    if sel.kind == "init_local_topk":
+        return init_local_topk_set(sigma, sel.r_kv, sel.init_units, sel.local_units)
+    raise ValueError(f"unknown selection kind {sel.kind!r}")
+
+
+def selection_capacity(sel: Selection, U: int) -> int:
+    """Most units ``sel`` keeps for a sequence of at most U units (the row
+    length of a kept-list buffer)."""
+    k = keep_count(sel.r_kv, U)
+    if sel.kind in ("topk", "window"):
+        return k
+    return min(U, sel.init_units + sel.local_units + k)
+
+
 def unit_tokens(kept: np.ndarray, unit: str, page_size: int, n: int) -> np.ndarray:
     """Token positions covered by the kept units, ascending ([SparDA] Section
     3.1: attention over the attended blocks only).  A page contributes its
@@ -260,12 +329,15 @@ class GroupResult:
 
 
 def group_step(q_group, K, V, *, unit: str, page_size: int, r_kv: float,
-               scale: float, kept_override=None) -> GroupResult:
+               scale: float, kept_override=None, selection: Selection | None = None
+               ) -> GroupResult:
     """Steps 1-7 for one sequence and one KV head.
 
     q_group [G, d], K [n, d], V [n, d]: fp64 values of the valid tokens.
     ``kept_override`` (ascending unit ids) replaces step 5's set, so that an
     output can be recomputed on another selection of the same size.
+    ``selection`` (kind other than "topk") replaces step 5's set by a
+    structured one; k and gap still describe the step-5 top-k.
     """
     K = np.asarray(K, np.float64)
     V = np.asarray(V, np.float64)
@@ -283,6 +355,8 @@ def group_step(q_group, K, V, *, unit: str, page_size: int, r_kv: float,
     U = sigma.shape[0]
     k = keep_count(r_kv, U)
     kept, gap = select_topk(sigma, k)
+    if selection is not None and selection.kind != "topk":
+        kept = selected_units(sigma, selection)
     if kept_override is not None:
         kept = np.asarray(kept_override, dtype=np.int64)
     tokens = unit_tokens(kept, unit, page_size, n)
@@ -298,7 +372,8 @@ def group_step(q_group, K, V, *, unit: str, page_size: int, r_kv: float,
 
 
 def decode_step(q, K, V, seq_lens, *, dtype: str, unit: str, page_size: int,
-                r_kv: float, scale: float | None = None, groups=None):
+                r_kv: float, scale: float | None = None, groups=None,
+                selection: Selection | None = None):
     """Steps 1-7 for a batch.
 
     q: [B, H_q, d]; K, V: [B, H_kv, n_max, d] stored values (float32, or
@@ -320,5 +395,5 @@ def decode_step(q, K, V, seq_lens, *, dtype: str, unit: str, page_size: int,
         Kg = widen(K[b, g, :n], dtype)
         Vg = widen(V[b, g, :n], dtype)
         res[(b, g)] = group_step(qg, Kg, Vg, unit=unit, page_size=page_size,
-                                 r_kv=r_kv, scale=scale)
+                                 r_kv=r_kv, scale=scale, selection=selection)
     return res
