@@ -27,7 +27,8 @@
  *   [SparDA] "SparDA: Sparse Decoupled Attention for Efficient Long-Context
  *     LLM Inference" summary page, Section 3.1: attention is computed over
  *     the attended blocks only; the query heads of a GQA group share one KV
- *     head and one block choice.  Appendix C: 64-token blocks.
+ *     head and one block choice; initial, local and top-k blocks.
+ *     Appendix A: the selected set as a union.  Appendix C: 64-token blocks.
  *
  * Conventions for every entry point
  *   - Pointers named *_host or the shape struct are host memory; every other
@@ -225,6 +226,68 @@ SD_API sd_status sd_decode_step(const sd_shape* shape, const void* q, const void
                          const int32_t* block_table, const int32_t* seq_lens, int32_t unit,
                          double r_kv, float* out, float* lse, int32_t* sel_idx,
                          int32_t* sel_count, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- Structured index sets ----------------------------------------------
+ * Which units a decode step keeps (host struct):
+ *   SD_SEL_TOPK             the exact top-k of sd_select_topk, k_b = keep
+ *                           count of U_b at r_kv;
+ *   SD_SEL_WINDOW           the k_b most recent units U_b - k_b .. U_b - 1:
+ *                           the KV-window baseline of [Cross/list] Table 3
+ *                           (scores are not used);
+ *   SD_SEL_INIT_LOCAL_TOPK  the union of the first init_units units, the last
+ *                           local_units units and the top-k of all U_b units
+ *                           ([SparDA] Section 3.1: initial, local and top-k
+ *                           blocks; Appendix A: B_init U B_local U top-k).
+ * Lists are ascending.  The row length of a kept list is
+ * sd_selection_capacity(sel, U_max): k_max for the first two kinds and
+ * min(U_max, init_units + local_units + k_max) for the union. */
+typedef enum sd_selection_kind {
+  SD_SEL_TOPK = 0,
+  SD_SEL_WINDOW = 1,
+  SD_SEL_INIT_LOCAL_TOPK = 2
+} sd_selection_kind;
+
+typedef struct sd_selection {
+  int32_t kind;         /* sd_selection_kind */
+  int32_t init_units;   /* >= 0; SD_SEL_INIT_LOCAL_TOPK only */
+  int32_t local_units;  /* >= 0; SD_SEL_INIT_LOCAL_TOPK only */
+  double r_kv;          /* keep ratio of the top-k (or of the window) */
+} sd_selection;
+
+/* Row length of a kept list for at most num_units units (host, pure); -1 on
+ * an invalid selection or num_units < 1. */
+SD_API int32_t sd_selection_capacity(const sd_selection* sel, int32_t num_units);
+
+/* Workspace bytes that suffice for sd_select_units and sd_decode_step_sel
+ * with this shape, unit and selection (and for every call that
+ * sd_workspace_bytes covers at sel->r_kv).  Host only. */
+SD_API sd_status sd_workspace_bytes_sel(const sd_shape* shape, int32_t unit,
+                                        const sd_selection* sel, size_t* bytes_host);
+
+/* Stage 1b under a selection: writes the kept units of every (b, g),
+ * ascending, to sel_idx[b][g][0 .. sel_count[b][g] - 1] (rows of
+ * sd_selection_capacity(sel, U_max) entries).  unit_scores as for
+ * sd_select_topk (may be NULL for SD_SEL_WINDOW).  The union is the top-k of
+ * sd_select_topk merged with the two ranges.  ws: sd_workspace_bytes_sel. */
+SD_API sd_status sd_select_units(const sd_shape* shape, int32_t unit, const int32_t* seq_lens,
+                                 const float* unit_scores, const sd_selection* sel,
+                                 int32_t* sel_idx, int32_t* sel_count, void* ws,
+                                 size_t ws_bytes, void* stream);
+
+/* sd_decode_step under a selection.  SD_SEL_TOPK is sd_decode_step at
+ * sel->r_kv.  SD_SEL_WINDOW attends the window directly (no scoring;
+ * page_bounds not read).  SD_SEL_INIT_LOCAL_TOPK scores, selects the union
+ * and attends it; in page unit with bf16 data and at most 16384 pages per
+ * sequence the attention blocks select it themselves, as in
+ * sd_select_attend.  sel_idx / sel_count may be NULL; when given they
+ * receive the kept lists (rows of sd_selection_capacity(sel, U_max)).
+ * ws: sd_workspace_bytes_sel. */
+SD_API sd_status sd_decode_step_sel(const sd_shape* shape, const void* q, const void* k_pages,
+                                    const void* v_pages, const void* page_bounds,
+                                    const int32_t* block_table, const int32_t* seq_lens,
+                                    int32_t unit, const sd_selection* sel, float* out,
+                                    float* lse, int32_t* sel_idx, int32_t* sel_count, void* ws,
+                                    size_t ws_bytes, void* stream);
 
 /* Text of the last non-OK status on this thread ("" if none). */
 SD_API const char* sd_last_error(void);

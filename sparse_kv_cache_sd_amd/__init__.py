@@ -10,20 +10,26 @@ from ._lib import (  # noqa: F401
     EXPORTS,
     LIB_PATH,
     SdError,
+    Selection,
     Shape,
     UNIT_PAGE,
     UNIT_TOKEN,
     alloc_workspace,
+    alloc_workspace_sel,
     attend_partials,
     attend_splitk,
     bounds_shape,
     decode_step,
+    decode_step_sel,
     keep_count,
     lib,
     merge_splits,
     score_pages,
     select_attend,
     select_topk,
+    select_units,
+    selection_capacity,
     update_page_bounds,
     workspace_bytes,
+    workspace_bytes_sel,
 )

@@ -47,8 +47,21 @@ class SdShape(ctypes.Structure):
     ]
 
 
+class SdSelection(ctypes.Structure):
+    _fields_ = [
+        ("kind", ctypes.c_int32),
+        ("init_units", ctypes.c_int32),
+        ("local_units", ctypes.c_int32),
+        ("r_kv", ctypes.c_double),
+    ]
+
+
+SEL_TOPK, SEL_WINDOW, SEL_INIT_LOCAL_TOPK = 0, 1, 2
+_SEL_KINDS = {"topk": SEL_TOPK, "window": SEL_WINDOW, "init_local_topk": SEL_INIT_LOCAL_TOPK}
+
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
+_SELP = ctypes.POINTER(SdSelection)
 _SIGS = {
     "sd_keep_count": (ctypes.c_int32, [ctypes.c_double, _I32]),
     "sd_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(SdShape), _I32, ctypes.c_double,
@@ -68,6 +81,13 @@ _SIGS = {
                                           _P, _I32, _P, _P, ctypes.c_double, _P, _P, _P,
                                           ctypes.c_size_t, _P]),
     "sd_merge_splits": (ctypes.c_int, [ctypes.POINTER(SdShape), _P, _P, _P, ctypes.c_size_t, _P]),
+    "sd_selection_capacity": (ctypes.c_int32, [_SELP, _I32]),
+    "sd_workspace_bytes_sel": (ctypes.c_int, [ctypes.POINTER(SdShape), _I32, _SELP,
+                                              ctypes.POINTER(ctypes.c_size_t)]),
+    "sd_select_units": (ctypes.c_int, [ctypes.POINTER(SdShape), _I32, _P, _P, _SELP, _P, _P, _P,
+                                       ctypes.c_size_t, _P]),
+    "sd_decode_step_sel": (ctypes.c_int, [ctypes.POINTER(SdShape), _P, _P, _P, _P, _P, _P, _I32,
+                                          _SELP, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "sd_last_error": (ctypes.c_char_p, []),
 }
 EXPORTS = tuple(_SIGS)
@@ -368,4 +388,82 @@ def merge_splits(shape: Shape, out, lse, ws, stream=None):
         ctypes.byref(s.c()),
         _dev(out, "out", torch.float32, (s.batch, s.num_q_heads, s.head_dim)),
         _dev(lse, "lse", torch.float32, (s.batch, s.num_q_heads)),
+        wp, wn, _stream(stream)))
+
+
+# ----------------------------------------------------------------------------
+# structured index sets
+# ----------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class Selection:
+    """Which units a decode step keeps: kind "topk", "window" or
+    "init_local_topk" (include/sd.h, sd_selection)."""
+    kind: str = "topk"
+    r_kv: float = 0.3
+    init_units: int = 0
+    local_units: int = 0
+
+    def c(self) -> SdSelection:
+        if self.kind not in _SEL_KINDS:
+            raise ValueError(f"unknown selection kind {self.kind!r}")
+        return SdSelection(_SEL_KINDS[self.kind], int(self.init_units), int(self.local_units),
+                           float(self.r_kv))
+
+
+def selection_capacity(sel: Selection, num_units: int) -> int:
+    c = lib().sd_selection_capacity(ctypes.byref(sel.c()), int(num_units))
+    if c < 0:
+        raise ValueError("invalid selection or num_units < 1")
+    return c
+
+
+def workspace_bytes_sel(shape: Shape, unit, sel: Selection) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().sd_workspace_bytes_sel(ctypes.byref(shape.c()), _unit(unit),
+                                        ctypes.byref(sel.c()), ctypes.byref(out)))
+    return int(out.value)
+
+
+def alloc_workspace_sel(shape: Shape, unit, sel: Selection, device="cuda") -> torch.Tensor:
+    n = max(1, workspace_bytes_sel(shape, unit, sel))
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def select_units(shape: Shape, unit, seq_lens, unit_scores, sel: Selection, sel_idx, sel_count,
+                 ws=None, stream=None):
+    s, u = shape, _unit(unit)
+    umax = s.max_pages_per_seq if u == UNIT_PAGE else s.max_seq_len
+    cap = selection_capacity(sel, umax)
+    wp, wn = _ws(ws, 0)
+    _check(lib().sd_select_units(
+        ctypes.byref(s.c()), u,
+        _dev(seq_lens, "seq_lens", torch.int32, (s.batch,)),
+        _dev(unit_scores, "unit_scores", torch.float32, (s.batch, s.num_kv_heads, umax),
+             optional=sel.kind == "window"),
+        ctypes.byref(sel.c()),
+        _dev(sel_idx, "sel_idx", torch.int32, (s.batch, s.num_kv_heads, cap)),
+        _dev(sel_count, "sel_count", torch.int32, (s.batch, s.num_kv_heads)),
+        wp, wn, _stream(stream)))
+
+
+def decode_step_sel(shape: Shape, q, k_pages, v_pages, page_bounds, block_table, seq_lens, unit,
+                    sel: Selection, out, lse, ws, sel_idx=None, sel_count=None, stream=None):
+    s, u = shape, _unit(unit)
+    umax = s.max_pages_per_seq if u == UNIT_PAGE else s.max_seq_len
+    cap = selection_capacity(sel, umax)
+    wp, wn = _ws(ws, 1)
+    _check(lib().sd_decode_step_sel(
+        ctypes.byref(s.c()),
+        _dev(q, "q", s.torch_dtype, (s.batch, s.num_q_heads, s.head_dim)),
+        _dev(k_pages, "k_pages", s.torch_dtype, _kv_shape(s)),
+        _dev(v_pages, "v_pages", s.torch_dtype, _kv_shape(s)),
+        _dev(page_bounds, "page_bounds", s.torch_dtype, _bounds_shape(s), optional=True),
+        _dev(block_table, "block_table", torch.int32, (s.batch, s.max_pages_per_seq)),
+        _dev(seq_lens, "seq_lens", torch.int32, (s.batch,)),
+        u, ctypes.byref(sel.c()),
+        _dev(out, "out", torch.float32, (s.batch, s.num_q_heads, s.head_dim)),
+        _dev(lse, "lse", torch.float32, (s.batch, s.num_q_heads)),
+        _dev(sel_idx, "sel_idx", torch.int32, (s.batch, s.num_kv_heads, cap), optional=True),
+        _dev(sel_count, "sel_count", torch.int32, (s.batch, s.num_kv_heads), optional=True),
         wp, wn, _stream(stream)))

@@ -111,6 +111,36 @@ int units_max(const sdkv::Dims& d, int unit) {
   return unit == SD_UNIT_PAGE ? d.max_pages : d.max_seq;
 }
 
+// A validated selection (include/sd.h, structured index sets).
+struct Sel {
+  int kind;  // SD_SEL_*
+  double r;
+  int init, local;  // SD_SEL_INIT_LOCAL_TOPK only (else 0)
+};
+
+Sel topk_sel(double r) { return Sel{SD_SEL_TOPK, r, 0, 0}; }
+
+sd_status check_selection(const sd_selection* s, Sel* out) {
+  if (!s) return fail(SD_E_NULL, "sel is NULL");
+  if (s->kind != SD_SEL_TOPK && s->kind != SD_SEL_WINDOW && s->kind != SD_SEL_INIT_LOCAL_TOPK)
+    return fail(SD_E_SHAPE, "unknown selection kind %d", s->kind);
+  sd_status st;
+  if ((st = check_ratio(s->r_kv)) != SD_OK) return st;
+  if (s->init_units < 0 || s->local_units < 0)
+    return fail(SD_E_SHAPE, "init_units and local_units must be >= 0");
+  const bool u = s->kind == SD_SEL_INIT_LOCAL_TOPK;
+  *out = Sel{s->kind, s->r_kv, u ? s->init_units : 0, u ? s->local_units : 0};
+  return SD_OK;
+}
+
+// Row length of a kept list for at most U units.
+int64_t capacity(const Sel& s, int64_t U) {
+  const int64_t k = keep_count_ppm(ratio_ppm(s.r), U);
+  if (s.kind != SD_SEL_INIT_LOCAL_TOPK) return k;
+  const int64_t c = static_cast<int64_t>(s.init) + s.local + k;
+  return c < U ? c : U;
+}
+
 // Split plan of the attention pass for lists of up to k_max units: S splits
 // per (sequence, KV head), each of E units, so that B * H_kv * S is about the
 // block target; E is at least one 16-row chunk.
@@ -136,7 +166,7 @@ Split plan_split(const sdkv::Dims& d, int unit, int64_t k_max) {
 // partials come first so that every entry point agrees on where they live.
 struct Layout {
   size_t split_count, part_o, part_lse, attend_end, scores, logits, sel_idx, sel_count, msel,
-      score_mm, total;
+      score_mm, topk_tmp, topk_cnt, total;
 };
 
 // Scratch of the many-block top-k (units beyond one block's registers).
@@ -152,13 +182,16 @@ int score_mm_parts(const sdkv::Dims& d) {
   return (d.max_seq + per - 1) / per;
 }
 
-Layout layout(const sdkv::Dims& d, int unit, double r_kv) {
+// The union of a selection keeps its top-k list in topk_tmp / topk_cnt.
+Layout layout(const sdkv::Dims& d, int unit, const Sel& sel) {
   Layout L{};
   const int64_t S = max_splits(d);
   const int64_t bh = static_cast<int64_t>(d.B) * d.Hq;
   const int64_t bg = static_cast<int64_t>(d.B) * d.Hkv;
   const int64_t U = units_max(d, unit);
-  const int64_t k_max = keep_count_ppm(ratio_ppm(r_kv), U);
+  const int64_t k_top = keep_count_ppm(ratio_ppm(sel.r), U);
+  const int64_t k_max = capacity(sel, U);
+  const bool uni = sel.kind == SD_SEL_INIT_LOCAL_TOPK;
   size_t off = 0;
   L.split_count = off; off = align_up(off + sizeof(int32_t));
   L.part_o = off;      off = align_up(off + sizeof(float) * bh * S * d.D);
@@ -173,6 +206,34 @@ Layout layout(const sdkv::Dims& d, int unit, double r_kv) {
   L.score_mm = off;
   if (unit == SD_UNIT_TOKEN && multi_select(d, unit))
     off = align_up(off + sizeof(uint32_t) * 2 * bg * score_mm_parts(d));
+  L.topk_tmp = off;
+  if (uni) off = align_up(off + sizeof(int32_t) * bg * k_top);
+  L.topk_cnt = off;
+  if (uni) off = align_up(off + sizeof(int32_t) * bg);
+  L.total = off;
+  return L;
+}
+
+Layout layout(const sdkv::Dims& d, int unit, double r_kv) { return layout(d, unit, topk_sel(r_kv)); }
+
+// Workspace of sd_select_units: the many-block top-k scratch, then (union)
+// the top-k list and counts.
+struct SelectLayout {
+  size_t msel, tmp, cnt, total;
+};
+
+SelectLayout select_layout(const sdkv::Dims& d, int unit, const Sel& sel) {
+  SelectLayout L{};
+  const int64_t bg = static_cast<int64_t>(d.B) * d.Hkv;
+  const int64_t k_top = keep_count_ppm(ratio_ppm(sel.r), units_max(d, unit));
+  const bool uni = sel.kind == SD_SEL_INIT_LOCAL_TOPK;
+  size_t off = 0;
+  L.msel = off;
+  if (sel.kind != SD_SEL_WINDOW) off = align_up(off + select_ws_bytes(d, unit));
+  L.tmp = off;
+  if (uni) off = align_up(off + sizeof(int32_t) * bg * k_top);
+  L.cnt = off;
+  if (uni) off = align_up(off + sizeof(int32_t) * bg);
   L.total = off;
   return L;
 }
@@ -224,15 +285,44 @@ sd_status do_select(const sdkv::Dims& d, int unit, const int32_t* sl, const floa
   return device_status(sdkv::launch_select(a, st), "select kernel launch");
 }
 
+// Window list, or the union of the forced ranges with a top-k list.
+sd_status do_structure(const sdkv::Dims& d, int unit, const int32_t* sl, const Sel& sel,
+                       const int32_t* top, const int32_t* top_cnt, int top_stride,
+                       int32_t* sel_idx, int32_t* sel_count, int cap, hipStream_t st) {
+  sdkv::StructArgs a{};
+  a.d = d;
+  a.unit = unit;
+  a.seq_lens = sl;
+  a.kind = sel.kind == SD_SEL_WINDOW ? sdkv::kWindow : sdkv::kInitLocalTopk;
+  a.R_ppm = ratio_ppm(sel.r);
+  a.init_units = sel.init;
+  a.local_units = sel.local;
+  a.topk_idx = top;
+  a.topk_count = top_cnt;
+  a.topk_stride = top_stride;
+  a.sel_idx = sel_idx;
+  a.sel_count = sel_count;
+  a.cap = cap;
+  return device_status(sdkv::launch_structure(a, st), "structure kernel launch");
+}
+
+// How the attention kernel obtains a list without sel_idx: a window of the
+// last keep_count units, or the forced ranges of an in-kernel union.
+struct ListMode {
+  bool window = false;
+  int window_R = -1;
+  int force_init = 0, force_local = 0;
+};
+
 // Split-K attention partials.  Exactly one list source: sel_idx (list),
-// unit_scores (top-k inside the kernel) or neither (identity).
+// unit_scores (top-k inside the kernel) or neither (identity, or a window).
 sd_status do_partials(const sdkv::Dims& d, const void* q, const void* kp, const void* vp,
                       const int32_t* bt, const int32_t* sl, int unit, const int32_t* sel_idx,
                       const int32_t* sel_count, int k_max, const float* logits, void* ws,
                       hipStream_t st, const float* unit_scores = nullptr, int R_ppm = -1,
                       int32_t* sel_out = nullptr, int32_t* sel_count_out = nullptr,
-                      int* S_out = nullptr) {
-  const bool listed = sel_idx != nullptr || unit_scores != nullptr;
+                      int* S_out = nullptr, ListMode lm = ListMode{}) {
+  const bool listed = sel_idx != nullptr || unit_scores != nullptr || lm.window;
   const int64_t kk = listed ? k_max : units_max(d, unit);
   const Split sp = plan_split(d, unit, kk);
   const Layout L = layout(d, unit, 1.0);
@@ -257,6 +347,12 @@ sd_status do_partials(const sdkv::Dims& d, const void* q, const void* kp, const 
   a.R_ppm = R_ppm;
   a.sel_out = sel_out;
   a.sel_count_out = sel_count_out;
+  a.force_init = lm.force_init;
+  a.force_local = lm.force_local;
+  if (lm.window) {
+    a.window = 1;
+    a.R_ppm = lm.window_R;
+  }
   if (S_out) *S_out = sp.S;
   return device_status(sdkv::launch_attend(a, st), "attention kernel launch");
 }
@@ -286,28 +382,105 @@ bool fused_select(const sdkv::Dims& d, int unit, int k_max) {
   return plan_split(d, unit, k_max).E <= sdkv::kMaxSelectE;
 }
 
-// Page-unit selection + attention: fused when possible, else top-k then a
-// listed attention.
+// The kept lists of a selection (not a window) from unit scores: the top-k,
+// or the top-k (kept in the workspace) merged with the forced ranges.  Rows
+// of idx hold capacity(sel, U_max) entries.
+sd_status do_select_list(const sdkv::Dims& d, int unit, const int32_t* sl, const float* scores,
+                         const Sel& sel, int32_t* idx, int32_t* cnt, void* msel_ws,
+                         int32_t* top_tmp, int32_t* top_cnt, hipStream_t s,
+                         const uint32_t* score_mm = nullptr) {
+  if (sel.kind == SD_SEL_TOPK)
+    return do_select(d, unit, sl, scores, sel.r, idx, cnt, msel_ws, s, score_mm);
+  const int U = units_max(d, unit);
+  const int k_top = static_cast<int>(keep_count_ppm(ratio_ppm(sel.r), U));
+  sd_status st;
+  if ((st = do_select(d, unit, sl, scores, sel.r, top_tmp, top_cnt, msel_ws, s, score_mm)) !=
+      SD_OK)
+    return st;
+  return do_structure(d, unit, sl, sel, top_tmp, top_cnt, k_top, idx, cnt,
+                      static_cast<int>(capacity(sel, U)), s);
+}
+
+// Page-unit selection + attention: fused when possible, else the kept lists
+// then a listed attention.
 sd_status do_select_attend(const sdkv::Dims& d, const void* q, const void* kp, const void* vp,
                            const int32_t* bt, const int32_t* sl, const float* scores,
-                           double r_kv, float* out, float* lse, int32_t* sel_idx,
+                           const Sel& sel, float* out, float* lse, int32_t* sel_idx,
                            int32_t* sel_count, void* ws, hipStream_t s) {
   const int unit = SD_UNIT_PAGE;
-  const Layout L = layout(d, unit, r_kv);
-  const int k_max = static_cast<int>(keep_count_ppm(ratio_ppm(r_kv), units_max(d, unit)));
+  const Layout L = layout(d, unit, sel);
+  const int k_max = static_cast<int>(capacity(sel, units_max(d, unit)));
   sd_status st;
   int S = 0;
   if (fused_select(d, unit, k_max)) {
+    ListMode lm;
+    lm.force_init = sel.init;
+    lm.force_local = sel.local;
     if ((st = do_partials(d, q, kp, vp, bt, sl, unit, nullptr, nullptr, k_max, nullptr, ws, s,
-                          scores, ratio_ppm(r_kv), sel_idx, sel_count, &S)) != SD_OK)
+                          scores, ratio_ppm(sel.r), sel_idx, sel_count, &S, lm)) != SD_OK)
       return st;
     return do_merge(d, out, lse, ws, s, S);
   }
   int32_t* idx = sel_idx ? sel_idx : reinterpret_cast<int32_t*>(at(ws, L.sel_idx));
   int32_t* cnt = sel_count ? sel_count : reinterpret_cast<int32_t*>(at(ws, L.sel_count));
-  if ((st = do_select(d, unit, sl, scores, r_kv, idx, cnt, at(ws, L.msel), s)) != SD_OK) return st;
+  if ((st = do_select_list(d, unit, sl, scores, sel, idx, cnt, at(ws, L.msel),
+                           reinterpret_cast<int32_t*>(at(ws, L.topk_tmp)),
+                           reinterpret_cast<int32_t*>(at(ws, L.topk_cnt)), s)) != SD_OK)
+    return st;
   if ((st = do_partials(d, q, kp, vp, bt, sl, unit, idx, cnt, k_max, nullptr, ws, s, nullptr, -1,
                         nullptr, nullptr, &S)) != SD_OK)
+    return st;
+  return do_merge(d, out, lse, ws, s, S);
+}
+
+// The decode step under a selection (arguments and workspace size checked).
+sd_status decode_impl(const sdkv::Dims& d, const void* q, const void* k_pages,
+                      const void* v_pages, const void* page_bounds, const int32_t* block_table,
+                      const int32_t* seq_lens, int unit, const Sel& sel, float* out, float* lse,
+                      int32_t* sel_idx, int32_t* sel_count, void* ws, hipStream_t s) {
+  const Layout L = layout(d, unit, sel);
+  const int U = units_max(d, unit);
+  const int k_max = static_cast<int>(capacity(sel, U));
+  sd_status st;
+  int S = 0;
+  if (sel.r >= 1.0) {  // every unit: dense
+    if ((st = do_partials(d, q, k_pages, v_pages, block_table, seq_lens, unit, nullptr, nullptr,
+                          0, nullptr, ws, s, nullptr, -1, nullptr, nullptr, &S)) != SD_OK)
+      return st;
+    return do_merge(d, out, lse, ws, s, S);
+  }
+  if (sel.kind == SD_SEL_WINDOW) {  // no scores: the attention reads the window
+    ListMode lm;
+    lm.window = true;
+    lm.window_R = ratio_ppm(sel.r);
+    if (sel_idx &&
+        (st = do_structure(d, unit, seq_lens, sel, nullptr, nullptr, 0, sel_idx, sel_count, k_max,
+                           s)) != SD_OK)
+      return st;
+    if ((st = do_partials(d, q, k_pages, v_pages, block_table, seq_lens, unit, nullptr, nullptr,
+                          k_max, nullptr, ws, s, nullptr, -1, nullptr, nullptr, &S, lm)) != SD_OK)
+      return st;
+    return do_merge(d, out, lse, ws, s, S);
+  }
+  float* scores = reinterpret_cast<float*>(at(ws, L.scores));
+  float* logits = unit == SD_UNIT_TOKEN ? reinterpret_cast<float*>(at(ws, L.logits)) : nullptr;
+  uint32_t* smm = unit == SD_UNIT_TOKEN && multi_select(d, unit)
+                      ? reinterpret_cast<uint32_t*>(at(ws, L.score_mm))
+                      : nullptr;
+  if ((st = do_score(d, q, k_pages, page_bounds, block_table, seq_lens, unit, scores, logits,
+                     s, smm)) != SD_OK)
+    return st;
+  if (unit == SD_UNIT_PAGE)
+    return do_select_attend(d, q, k_pages, v_pages, block_table, seq_lens, scores, sel, out, lse,
+                            sel_idx, sel_count, ws, s);
+  int32_t* idx = sel_idx ? sel_idx : reinterpret_cast<int32_t*>(at(ws, L.sel_idx));
+  int32_t* cnt = sel_count ? sel_count : reinterpret_cast<int32_t*>(at(ws, L.sel_count));
+  if ((st = do_select_list(d, unit, seq_lens, scores, sel, idx, cnt, at(ws, L.msel),
+                           reinterpret_cast<int32_t*>(at(ws, L.topk_tmp)),
+                           reinterpret_cast<int32_t*>(at(ws, L.topk_cnt)), s, smm)) != SD_OK)
+    return st;
+  if ((st = do_partials(d, q, k_pages, v_pages, block_table, seq_lens, unit, idx, cnt, k_max,
+                        logits, ws, s, nullptr, -1, nullptr, nullptr, &S)) != SD_OK)
     return st;
   return do_merge(d, out, lse, ws, s, S);
 }
@@ -494,8 +667,8 @@ sd_status sd_select_attend(const sd_shape* shape, const void* q, const void* k_p
   if ((sel_idx == nullptr) != (sel_count == nullptr))
     return fail(SD_E_NULL, "sel_idx and sel_count are given together or not at all");
   if ((st = check_ws(ws, ws_bytes, layout(d, SD_UNIT_PAGE, r_kv).total)) != SD_OK) return st;
-  if ((st = do_select_attend(d, q, k_pages, v_pages, block_table, seq_lens, unit_scores, r_kv,
-                             out, lse, sel_idx, sel_count, ws,
+  if ((st = do_select_attend(d, q, k_pages, v_pages, block_table, seq_lens, unit_scores,
+                             topk_sel(r_kv), out, lse, sel_idx, sel_count, ws,
                              static_cast<hipStream_t>(stream))) != SD_OK)
     return st;
   return ok();
@@ -519,42 +692,82 @@ sd_status sd_decode_step(const sd_shape* shape, const void* q, const void* k_pag
     return fail(SD_E_NULL, "page unit selection reads page_bounds");
   if ((sel_idx == nullptr) != (sel_count == nullptr))
     return fail(SD_E_NULL, "sel_idx and sel_count are given together or not at all");
-  const Layout L = layout(d, unit, r_kv);
-  if ((st = check_ws(ws, ws_bytes, L.total)) != SD_OK) return st;
+  if ((st = check_ws(ws, ws_bytes, layout(d, unit, r_kv).total)) != SD_OK) return st;
+  if ((st = decode_impl(d, q, k_pages, v_pages, page_bounds, block_table, seq_lens, unit,
+                        topk_sel(r_kv), out, lse, sel_idx, sel_count, ws,
+                        static_cast<hipStream_t>(stream))) != SD_OK)
+    return st;
+  return ok();
+}
+
+int32_t sd_selection_capacity(const sd_selection* sel, int32_t num_units) {
+  Sel v;
+  if (num_units < 1 || check_selection(sel, &v) != SD_OK) return -1;
+  return static_cast<int32_t>(capacity(v, num_units));
+}
+
+sd_status sd_workspace_bytes_sel(const sd_shape* shape, int32_t unit, const sd_selection* sel,
+                                 size_t* bytes_host) {
+  sdkv::Dims d;
+  Sel v;
+  sd_status st;
+  if ((st = check_shape(shape, &d)) != SD_OK) return st;
+  if ((st = check_unit(unit)) != SD_OK) return st;
+  if ((st = check_selection(sel, &v)) != SD_OK) return st;
+  if (!bytes_host) return fail(SD_E_NULL, "bytes_host is NULL");
+  const size_t a = layout(d, unit, v).total, b = select_layout(d, unit, v).total;
+  *bytes_host = a > b ? a : b;
+  return ok();
+}
+
+sd_status sd_select_units(const sd_shape* shape, int32_t unit, const int32_t* seq_lens,
+                          const float* unit_scores, const sd_selection* sel, int32_t* sel_idx,
+                          int32_t* sel_count, void* ws, size_t ws_bytes, void* stream) {
+  sdkv::Dims d;
+  Sel v;
+  sd_status st;
+  if ((st = check_shape(shape, &d)) != SD_OK) return st;
+  if ((st = check_unit(unit)) != SD_OK) return st;
+  if ((st = check_selection(sel, &v)) != SD_OK) return st;
+  if (!seq_lens || !sel_idx || !sel_count || (!unit_scores && v.kind != SD_SEL_WINDOW))
+    return fail(SD_E_NULL, "seq_lens, sel_idx, sel_count and (unless a window) unit_scores "
+                           "are required");
+  const SelectLayout SL = select_layout(d, unit, v);
+  if ((st = check_ws(ws, ws_bytes, SL.total)) != SD_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  int S = 0;
-  if (dense) {
-    if ((st = do_partials(d, q, k_pages, v_pages, block_table, seq_lens, unit, nullptr, nullptr,
-                          0, nullptr, ws, s, nullptr, -1, nullptr, nullptr, &S)) != SD_OK)
-      return st;
-    if ((st = do_merge(d, out, lse, ws, s, S)) != SD_OK) return st;
-    return ok();
-  }
-  const int U = units_max(d, unit);
-  const int k_max = static_cast<int>(keep_count_ppm(ratio_ppm(r_kv), U));
-  float* scores = reinterpret_cast<float*>(at(ws, L.scores));
-  float* logits = unit == SD_UNIT_TOKEN ? reinterpret_cast<float*>(at(ws, L.logits)) : nullptr;
-  uint32_t* smm = unit == SD_UNIT_TOKEN && multi_select(d, unit)
-                      ? reinterpret_cast<uint32_t*>(at(ws, L.score_mm))
-                      : nullptr;
-  if ((st = do_score(d, q, k_pages, page_bounds, block_table, seq_lens, unit, scores, logits,
-                     s, smm)) != SD_OK)
+  const int cap = static_cast<int>(capacity(v, units_max(d, unit)));
+  if (v.kind == SD_SEL_WINDOW)
+    st = do_structure(d, unit, seq_lens, v, nullptr, nullptr, 0, sel_idx, sel_count, cap, s);
+  else
+    st = do_select_list(d, unit, seq_lens, unit_scores, v, sel_idx, sel_count, at(ws, SL.msel),
+                        reinterpret_cast<int32_t*>(at(ws, SL.tmp)),
+                        reinterpret_cast<int32_t*>(at(ws, SL.cnt)), s);
+  if (st != SD_OK) return st;
+  return ok();
+}
+
+sd_status sd_decode_step_sel(const sd_shape* shape, const void* q, const void* k_pages,
+                             const void* v_pages, const void* page_bounds,
+                             const int32_t* block_table, const int32_t* seq_lens, int32_t unit,
+                             const sd_selection* sel, float* out, float* lse, int32_t* sel_idx,
+                             int32_t* sel_count, void* ws, size_t ws_bytes, void* stream) {
+  sdkv::Dims d;
+  Sel v;
+  sd_status st;
+  if ((st = check_shape(shape, &d)) != SD_OK) return st;
+  if ((st = check_unit(unit)) != SD_OK) return st;
+  if ((st = check_selection(sel, &v)) != SD_OK) return st;
+  if (!q || !k_pages || !v_pages || !block_table || !seq_lens || !out || !lse)
+    return fail(SD_E_NULL,
+                "q, k_pages, v_pages, block_table, seq_lens, out and lse are required");
+  if (v.r < 1.0 && v.kind != SD_SEL_WINDOW && unit == SD_UNIT_PAGE && !page_bounds)
+    return fail(SD_E_NULL, "page unit selection reads page_bounds");
+  if ((sel_idx == nullptr) != (sel_count == nullptr))
+    return fail(SD_E_NULL, "sel_idx and sel_count are given together or not at all");
+  if ((st = check_ws(ws, ws_bytes, layout(d, unit, v).total)) != SD_OK) return st;
+  if ((st = decode_impl(d, q, k_pages, v_pages, page_bounds, block_table, seq_lens, unit, v, out,
+                        lse, sel_idx, sel_count, ws, static_cast<hipStream_t>(stream))) != SD_OK)
     return st;
-  if (unit == SD_UNIT_PAGE) {
-    if ((st = do_select_attend(d, q, k_pages, v_pages, block_table, seq_lens, scores, r_kv, out,
-                               lse, sel_idx, sel_count, ws, s)) != SD_OK)
-      return st;
-    return ok();
-  }
-  int32_t* idx = sel_idx ? sel_idx : reinterpret_cast<int32_t*>(at(ws, L.sel_idx));
-  int32_t* cnt = sel_count ? sel_count : reinterpret_cast<int32_t*>(at(ws, L.sel_count));
-  if ((st = do_select(d, unit, seq_lens, scores, r_kv, idx, cnt, at(ws, L.msel), s, smm)) !=
-      SD_OK)
-    return st;
-  if ((st = do_partials(d, q, k_pages, v_pages, block_table, seq_lens, unit, idx, cnt, k_max,
-                        logits, ws, s, nullptr, -1, nullptr, nullptr, &S)) != SD_OK)
-    return st;
-  if ((st = do_merge(d, out, lse, ws, s, S)) != SD_OK) return st;
   return ok();
 }
 

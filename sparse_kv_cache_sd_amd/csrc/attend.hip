@@ -76,6 +76,12 @@ __device__ __forceinline__ Span span_of(const AttendArgs& a, int j, int list_len
   return sp;
 }
 
+// Without a list: the identity (every unit), or with a window the last
+// keep_count(U) units -- list entry e is unit window_start + e.
+__device__ __forceinline__ int window_start(const AttendArgs& a, int U) {
+  return a.window ? U - keep_count_dev(U, a.R_ppm) : 0;
+}
+
 // Pool rows (row-major [num_pages * H_kv * P] index) of row `row` of N
 // chunks c[i] (or -1 where that row is not attended; tok[i] receives its
 // token id).  unit_at(e) returns list entry e for e < sp.e_hi.  Every read is
@@ -245,7 +251,7 @@ __global__ __launch_bounds__(kAttendWaves * 64) void attend_mfma_kernel(AttendAr
   const bf16_t* vp = static_cast<const bf16_t*>(a.v_pages);
   const int32_t* list = a.sel_idx ? a.sel_idx + bg * a.k_max : nullptr;
   const int units_cap = a.unit == kPage ? d.max_pages : d.max_seq;
-  const Span sp = span_of(a, j, (list || SELECTS) ? a.k_max : units_cap);
+  const Span sp = span_of(a, j, (list || SELECTS || a.window) ? a.k_max : units_cap);
   // chunks [w_lo, w_hi) of this block belong to this wave
   const int cpw = (sp.nch + NW - 1) / NW;
   const int w_lo = min(sp.nch, wave * cpw), w_hi = min(sp.nch, w_lo + cpw);
@@ -263,6 +269,7 @@ __global__ __launch_bounds__(kAttendWaves * 64) void attend_mfma_kernel(AttendAr
   const int n = clamp_len(a.seq_lens[b], d.max_seq);
   const int U = a.unit == kPage ? (n + d.P - 1) / d.P : n;
   int cnt;
+  int w0 = 0;  // first unit of a window
   if constexpr (SELECTS) {
     const int k = min(keep_count_dev(U, a.R_ppm), a.k_max);
     int32_t* full = (j == 0 && a.sel_out) ? a.sel_out + bg * a.k_max : nullptr;
@@ -270,27 +277,32 @@ __global__ __launch_bounds__(kAttendWaves * 64) void attend_mfma_kernel(AttendAr
       if (pos >= sp.e0 && pos < sp.e_hi) s_list[pos - sp.e0] = unit_id;
       if (full) full[pos] = unit_id;
     };
+    // kept: the top-k, plus the first force_init and last force_local units
+    const int f_lo = min(a.force_init, U), f_hi = max(U - a.force_local, 0);
+    int kept = k;
     if (k == U) {
       for (int e = threadIdx.x; e < U; e += NT) emit(e, e);
     } else if (k > 0) {
-      topk_bitmap<KEYS, NW>(s_rs, s_kept, key, U, k);
+      topk_bitmap<KEYS, NW>(s_rs, s_kept, key, U, k, f_lo, f_hi);
+      kept = min((int)s_kept.total, a.k_max);
       // this split's slice of the ranks, or all of them when split 0 also
       // writes the selection out
       emit_kept<KEYS, NW>(s_kept.mask, s_kept.base, full ? 0u : (uint32_t)sp.e0,
-                          full ? (uint32_t)k : (uint32_t)sp.e_hi, emit);
+                          full ? (uint32_t)kept : (uint32_t)sp.e_hi, emit);
     }
-    if (j == 0 && a.sel_count_out && threadIdx.x == 0) a.sel_count_out[bg] = k;
-    cnt = k;
+    if (j == 0 && a.sel_count_out && threadIdx.x == 0) a.sel_count_out[bg] = kept;
+    cnt = kept;
     __syncthreads();
   } else {
-    cnt = list ? min(a.sel_count[bg], a.k_max) : U;
+    w0 = window_start(a, U);
+    cnt = list ? min(a.sel_count[bg], a.k_max) : U - w0;
   }
   auto unit_at = [&](int e) -> int {
     if constexpr (SELECTS) return e < cnt ? s_list[e - sp.e0] : -1;
     else {
       // one unconditional load (a valid dummy address in identity mode)
       const int v = *(list ? list + e : a.seq_lens + b);
-      return list ? v : e;
+      return list ? v : w0 + e;
     }
   };
 
@@ -510,13 +522,14 @@ __global__ __launch_bounds__(kAttendWaves * 64) void attend_f32_kernel(AttendArg
   const bool use_logits = a.token_logits != nullptr;
   const int32_t* list = a.sel_idx ? a.sel_idx + bg * a.k_max : nullptr;
   const int units_cap = a.unit == kPage ? d.max_pages : d.max_seq;
-  const Span sp = span_of(a, j, list ? a.k_max : units_cap);
+  const Span sp = span_of(a, j, (list || a.window) ? a.k_max : units_cap);
   const int n = clamp_len(a.seq_lens[b], d.max_seq);
   const int U = a.unit == kPage ? (n + d.P - 1) / d.P : n;
-  const int cnt = list ? min(a.sel_count[bg], a.k_max) : U;
+  const int w0 = list ? 0 : window_start(a, U);
+  const int cnt = list ? min(a.sel_count[bg], a.k_max) : U - w0;
   auto unit_at = [&](int e) -> int {
     const int v = *(list ? list + e : a.seq_lens + b);
-    return list ? v : e;
+    return list ? v : w0 + e;
   };
 
   const float qs = d.scale * kLog2e;
@@ -640,6 +653,8 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
   const Dims& d = a.d;
   if (a.S < 1 || a.S > kMaxSplits) return hipErrorInvalidValue;
   const bool selects = a.unit_scores != nullptr;
+  if (a.window && (selects || a.sel_idx)) return hipErrorInvalidValue;
+  if ((a.force_init | a.force_local) < 0) return hipErrorInvalidValue;
   if (selects && (a.unit != kPage || a.sel_idx != nullptr || d.dtype != kBF16 ||
                   a.E > kMaxSelectE || d.max_pages > kMaxSelectU))
     return hipErrorInvalidValue;

@@ -81,7 +81,35 @@ struct AttendArgs {
   int R_ppm;                  // keep ratio in parts per million (< 0: all)
   int32_t* sel_out;           // optional [B][Hkv][k_max]: kept list (split 0 writes it)
   int32_t* sel_count_out;     // optional [B][Hkv]
+  // In-kernel selection: the first force_init and the last force_local units
+  // are kept besides the top-k (their union, at most k_max units).
+  int force_init, force_local;
+  // Without a list or scores: window != 0 attends only the last
+  // keep_count(U, R_ppm) units (list entry e is unit U - k + e).
+  int window;
 };
+
+// Structured kept lists, one block per (sequence, KV head): kind kWindow
+// writes the last keep_count(U, R_ppm) units; kind kInitLocalTopk writes the
+// union of the first init_units, the last local_units and the ascending
+// top-k list topk_idx (topk_count entries, row stride topk_stride), which
+// must not alias sel_idx.  Rows of sel_idx hold cap entries.
+enum StructKind : int { kWindow = 1, kInitLocalTopk = 2 };
+struct StructArgs {
+  Dims d;
+  int unit;
+  const int32_t* seq_lens;
+  int kind;
+  int R_ppm;
+  int init_units, local_units;
+  const int32_t* topk_idx;
+  const int32_t* topk_count;
+  int topk_stride;
+  int32_t* sel_idx;    // [B][Hkv][cap]
+  int32_t* sel_count;  // [B][Hkv]
+  int cap;
+};
+hipError_t launch_structure(const StructArgs& a, hipStream_t st);
 
 // Most splits one (sequence, KV head) is cut into.
 constexpr int kMaxSplits = 256;

@@ -120,23 +120,29 @@ __device__ __forceinline__ void block_excl_scan2(RadixState& st, uint32_t a, uin
 // The kept set as a bitmap, for keys held interleaved (key[i] of thread t is
 // unit t + NT*i, so the ballot of slot i in wave w is the 64-bit word of units
 // 64 (i*NW + w) .. +63: words in ascending unit order).  Kept = above T (or
-// >= T for a whole bin), plus the first `need` units equal to T in id order.
-// On return (after a barrier) s_mask[e] holds the kept units of word e and
-// s_base[e] the number of kept units in the words before it, so a kept unit's
-// rank in the ascending list is s_base[e] + its position among the word's set
-// bits.  One wave trims the ties and scans the word counts.
+// >= T for a whole bin), plus the first `need` units equal to T in id order,
+// plus every unit u < f_lo or u >= f_hi (forced units, for the union of the
+// top-k with the first and last units).  On return (after a barrier)
+// s_mask[e] holds the kept units of word e and s_base[e] the number of kept
+// units in the words before it, so a kept unit's rank in the ascending list
+// is s_base[e] + its position among the word's set bits; *s_total (if given)
+// is the number of kept units.  One wave trims the ties and scans the word
+// counts.
 template <int KPT, int NW>
 __device__ __forceinline__ void kept_words(uint64_t* s_mask, uint64_t* s_tie, uint32_t* s_base,
                                            const uint32_t (&key)[KPT], int U, uint32_t T,
-                                           uint32_t need, bool whole) {
+                                           uint32_t need, bool whole, int f_lo = 0,
+                                           int f_hi = 0x7FFFFFFF, uint32_t* s_total = nullptr) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int NT = NW * 64, W = KPT * NW;
   constexpr int PPL = (W + 63) / 64;  // words per scanning lane
   static_assert(PPL <= 8, "at most 512 words");
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
-    const bool v = (int)threadIdx.x + NT * i < U;
-    const uint64_t above = __ballot(v && (whole ? key[i] >= T : key[i] > T));
+    const int u = (int)threadIdx.x + NT * i;
+    const bool v = u < U;
+    const uint64_t above =
+        __ballot(v && ((whole ? key[i] >= T : key[i] > T) || u < f_lo || u >= f_hi));
     const uint64_t tie = __ballot(v && !whole && key[i] == T);
     if (lane == 0) {
       s_mask[i * NW + wave] = above;
@@ -180,6 +186,7 @@ __device__ __forceinline__ void kept_words(uint64_t* s_mask, uint64_t* s_tie, ui
       }
       base += __popcll(m[q]);
     }
+    if (s_total && lane == 63) *s_total = base;
   }
   __syncthreads();
 }
@@ -225,6 +232,7 @@ template <int KPT, int NW>
 struct KeptScratch {
   uint64_t mask[KPT * NW], tie[KPT * NW];
   uint32_t base[KPT * NW];
+  uint32_t total;  // kept units
 };
 
 // The exact top-k search over keys held in registers, interleaved (key[i] of
@@ -268,15 +276,17 @@ __device__ __forceinline__ void radix_search(RadixState& st, const uint32_t (&ke
   *whole_out = whole;
 }
 
-// Exact top-k search followed by the kept bitmap (in ks, after a barrier);
-// the caller emits the ranks it needs with emit_kept.
+// Exact top-k search followed by the kept bitmap (in ks, after a barrier),
+// with the units u < f_lo and u >= f_hi added to it; the caller emits the
+// ranks it needs with emit_kept.
 template <int KPT, int NW>
 __device__ __forceinline__ void topk_bitmap(RadixState& st, KeptScratch<KPT, NW>& ks,
-                                            const uint32_t (&key)[KPT], int U, int k) {
+                                            const uint32_t (&key)[KPT], int U, int k,
+                                            int f_lo = 0, int f_hi = 0x7FFFFFFF) {
   uint32_t T, need;
   bool whole;
   radix_search<KPT, NW>(st, key, U, k, &T, &need, &whole);
-  kept_words<KPT, NW>(ks.mask, ks.tie, ks.base, key, U, T, need, whole);
+  kept_words<KPT, NW>(ks.mask, ks.tie, ks.base, key, U, T, need, whole, f_lo, f_hi, &ks.total);
 }
 
 }  // namespace sdkv
