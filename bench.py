@@ -65,13 +65,14 @@ def log(msg):
 # algorithmic byte model (what the method must move per decode-step-layer)
 # ----------------------------------------------------------------------------
 
-def algorithmic_bytes(seq_lens, H_q, H_kv, d, P, elem, unit, r_kv, kept_tokens):
+def algorithmic_bytes(seq_lens, H_q, H_kv, d, P, elem, unit, r_kv, kept_tokens, window=False):
     """Bytes per decode-step-layer.
 
     dense:  every valid K and V row once.
     page:   the page bounds of every page (2 d elements) + K and V of the kept
             pages' valid tokens.
     token:  every valid K row (scoring) + V of the kept tokens.
+    window: K and V of the window's tokens (nothing is scored).
     Plus q (read) and out/lse (written, fp32) in every mode.
     kept_tokens: total valid tokens covered by the kept units over all (b, g).
     """
@@ -79,6 +80,8 @@ def algorithmic_bytes(seq_lens, H_q, H_kv, d, P, elem, unit, r_kv, kept_tokens):
     n_tot = int(np.sum(seq_lens))
     if r_kv >= 1.0:
         return H_kv * n_tot * 2 * d * elem + qo
+    if window:
+        return kept_tokens * 2 * d * elem + qo
     if unit == "page":
         U_tot = int(np.sum([-(-int(n) // P) for n in seq_lens]))
         return H_kv * U_tot * 2 * d * elem + kept_tokens * 2 * d * elem + qo
@@ -219,7 +222,12 @@ def summarize_pmc(fetch_dir, write_dir, workload, out_path, cmd_fetch, cmd_write
 # CPU baseline: the oracle, as it stands, on a bounded sample
 # ----------------------------------------------------------------------------
 
-def cpu_baseline(w, unit, r_kv, budget_s=12.0):
+def sdref_selection(sel):
+    from oracle import sdref
+    return sdref.Selection(sel.kind, sel.r_kv, sel.init_units, sel.local_units)
+
+
+def cpu_baseline(w, unit, r_kv, budget_s=12.0, selection=None):
     from oracle import sdref
     try:
         from threadpoolctl import threadpool_info
@@ -238,7 +246,8 @@ def cpu_baseline(w, unit, r_kv, budget_s=12.0):
         qg = sdref.widen(w.q[b, g * G:(g + 1) * G], r.dtype)
         Kg = sdref.widen(w.K[b, g, :n], r.dtype)
         Vg = sdref.widen(w.V[b, g, :n], r.dtype)
-        sdref.group_step(qg, Kg, Vg, unit=unit, page_size=r.page_size, r_kv=r_kv, scale=scale)
+        sdref.group_step(qg, Kg, Vg, unit=unit, page_size=r.page_size, r_kv=r_kv, scale=scale,
+                         selection=selection)
         done += 1
         el = time.perf_counter() - t0
         if el >= budget_s or done >= 4 * len(groups):
@@ -266,6 +275,13 @@ def main():
     ap.add_argument("--layers", type=int, default=0, help="distinct layer caches (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead")
+    ap.add_argument("--selection", default="topk", choices=["topk", "window", "init_local_topk"],
+                    help="kept set: top-k (default), the KV window, or initial + local + top-k")
+    ap.add_argument("--r-kv", type=float, default=0.0,
+                    help="keep ratio (0 = the workload's own)")
+    ap.add_argument("--init-units", type=int, default=1, help="init_local_topk: first units kept")
+    ap.add_argument("--local-units", type=int, default=0,
+                    help="init_local_topk: last units kept (0 = 2048 tokens' worth)")
     ap.add_argument("--copy-calibrate", action="store_true",
                     help="run a plain 1 GiB copy first (for counter passes)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -297,6 +313,9 @@ def main():
         copy_calibration()
 
     rname, over, unit, r_kv, desc = WORKLOADS[args.workload]
+    if args.r_kv > 0:
+        r_kv = args.r_kv
+        desc += f"; r_KV overridden to {r_kv:g}"
     rec = kvsynth.RECIPES[rname].with_(**over)
     P, d, H_q, H_kv = rec.page_size, rec.head_dim, rec.num_q_heads, rec.num_kv_heads
     elem = 2 if rec.dtype == "bf16" else 4
@@ -340,8 +359,18 @@ def main():
         sd.update_page_bounds(shape, lay["k"], lay["bt"], lay["sl"], lay["bounds"])
     torch.cuda.synchronize()
 
-    k_max = sd.keep_count(r_kv, shape.units_max(unit))
-    ws = sd.alloc_workspace(shape, unit, r_kv)
+    structured = args.selection != "topk"
+    local_units = args.local_units or (2048 // P if unit == "page" else 2048)
+    selection = sd.Selection(args.selection, r_kv, args.init_units if structured else 0,
+                             local_units if args.selection == "init_local_topk" else 0)
+    if structured:
+        config_sel = {"selection": args.selection, "init_units": selection.init_units,
+                      "local_units": selection.local_units}
+        desc += (f"; kept set: {args.selection}" +
+                 (f" ({selection.init_units} initial + {selection.local_units} local units + "
+                  f"top-k)" if args.selection == "init_local_topk" else " (most recent units)"))
+    k_max = sd.selection_capacity(selection, shape.units_max(unit))
+    ws = sd.alloc_workspace_sel(shape, unit, selection)
     ws_dense = sd.alloc_workspace(shape, unit, 1.0)
     out = torch.empty((rec.batch, H_q, d), dtype=torch.float32, device="cuda")
     lse = torch.empty((rec.batch, H_q), dtype=torch.float32, device="cuda")
@@ -351,8 +380,13 @@ def main():
 
     def sparse_step(i):
         lay = layers[i]
-        sd.decode_step(shape, lay["q"], lay["k"], lay["v"], lay["bounds"], lay["bt"], lay["sl"],
-                       unit, r_kv, out, lse, ws, sels[i], cnts[i], stream=stream)
+        if structured:
+            sd.decode_step_sel(shape, lay["q"], lay["k"], lay["v"], lay["bounds"], lay["bt"],
+                               lay["sl"], unit, selection, out, lse, ws, sels[i], cnts[i],
+                               stream=stream)
+        else:
+            sd.decode_step(shape, lay["q"], lay["k"], lay["v"], lay["bounds"], lay["bt"],
+                           lay["sl"], unit, r_kv, out, lse, ws, sels[i], cnts[i], stream=stream)
 
     def dense_step(i):
         lay = layers[i]
@@ -375,7 +409,12 @@ def main():
         runs it: page unit selects inside the attention kernel; token unit
         attends the stored selection with the stored logits."""
         lay = layers[i]
-        if unit == "page":
+        if structured:
+            sd.attend_partials(shape, lay["q"], lay["k"], lay["v"], lay["bt"], lay["sl"], unit, ws,
+                               sel_idx=sels[i], sel_count=cnts[i],
+                               token_logits=logits[i] if args.selection != "window" else None,
+                               stream=stream)
+        elif unit == "page":
             sd.attend_partials(shape, lay["q"], lay["k"], lay["v"], lay["bt"], lay["sl"], unit, ws,
                                unit_scores=scores[i], r_kv=r_kv, stream=stream)
         else:
@@ -433,9 +472,11 @@ def main():
         kept.append(kept_token_count(sels[i].cpu().numpy(), cnts[i].cpu().numpy(),
                                      w0.seq_lens, unit, P))
     kept_mean = float(np.mean(kept))
-    b_sparse = algorithmic_bytes(w0.seq_lens, H_q, H_kv, d, P, elem, unit, r_kv, kept_mean)
+    window = args.selection == "window"
+    b_sparse = algorithmic_bytes(w0.seq_lens, H_q, H_kv, d, P, elem, unit, r_kv, kept_mean,
+                                 window=window)
     b_dense = algorithmic_bytes(w0.seq_lens, H_q, H_kv, d, P, elem, unit, 1.0, 0)
-    b_attend = attend_bytes(kept_mean, d, elem, unit == "token")
+    b_attend = attend_bytes(kept_mean, d, elem, unit == "token" and not window)
     gbps = b_sparse / (us_sparse * 1e-6) / 1e9
     gbps_dense = b_dense / (us_dense * 1e-6) / 1e9
     gbps_att = b_attend / (us_attend * 1e-6) / 1e9
@@ -459,6 +500,7 @@ def main():
             "page_size": P, "context": int(w0.seq_lens.max()), "unit": unit, "r_kv": r_kv,
             "k_per_kv_head": k_max, "layer_caches": L, "timing": "hip-graph" if graph else "eager",
         },
+        "kept_tokens_per_step": round(kept_mean, 1),
         "effective_gbps": round(gbps, 1),
         "pct_hbm_roofline": round(100 * gbps / HBM_PEAK_GBPS, 1),
         "algorithmic_bytes_per_step": int(b_sparse),
@@ -469,19 +511,24 @@ def main():
         "byte_bound_speedup": round(b_dense / b_sparse, 3),
         "eager_us_per_step_layer": round(us_sparse_eager, 3),
         "roofline": {
-            "kernel": ("attend_mfma_kernel: in-kernel top-k + split-K attention partials over "
+            "kernel": ("attend_mfma_kernel: split-K attention partials over the stored kept "
+                       "lists" if structured else
+                       "attend_mfma_kernel: in-kernel top-k + split-K attention partials over "
                        "the kept pages" if unit == "page" else
                        "attend_mfma_kernel: split-K attention partials over the kept tokens "
                        "(stored logits)"),
             "bound": "hbm", "achieved": round(gbps_att, 1), "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": round(gbps_att / HBM_PEAK_GBPS, 4),
-            "traffic": read_traffic(args.workload) if unit == "page" else None,
+            "traffic": read_traffic(args.workload) if unit == "page" and not structured else None,
             "us_per_launch": round(us_attend, 3), "bytes_per_launch": int(b_attend),
         },
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
-        result["cpu_baseline"] = cpu_baseline(w0, unit, r_kv)
+        result["cpu_baseline"] = cpu_baseline(
+            w0, unit, r_kv, selection=None if not structured else sdref_selection(selection))
+    if structured:
+        result["config"].update(config_sel)
     print(json.dumps(result), flush=True)
 
 
