@@ -170,7 +170,9 @@ struct Layout {
 };
 
 // Scratch of the many-block top-k (units beyond one block's registers).
-bool multi_select(const sdkv::Dims& d, int unit) { return units_max(d, unit) > sdkv::kMaxSelectU; }
+bool multi_select(const sdkv::Dims& d, int unit) {
+  return units_max(d, unit) > sdkv::kMaxSelectOne;
+}
 
 size_t select_ws_bytes(const sdkv::Dims& d, int unit) {
   return multi_select(d, unit) ? sdkv::msel_workspace_bytes(d.B, d.Hkv, units_max(d, unit)) : 0;
@@ -267,7 +269,7 @@ sd_status do_score(const sdkv::Dims& d, const void* q, const void* k_pages, cons
   return device_status(sdkv::launch_score(a, st), "score kernel launch");
 }
 
-// msel_ws: select_ws_bytes(d, unit) bytes (unused below kMaxSelectU units);
+// msel_ws: select_ws_bytes(d, unit) bytes (unused up to kMaxSelectOne units);
 // score_mm: the token scorer's partial min / max keys, or NULL.
 sd_status do_select(const sdkv::Dims& d, int unit, const int32_t* sl, const float* scores,
                     double r_kv, int32_t* sel_idx, int32_t* sel_count, void* msel_ws,

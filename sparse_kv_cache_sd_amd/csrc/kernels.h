@@ -117,10 +117,12 @@ constexpr int kMaxSplits = 256;
 // the most units it can select from.
 constexpr int kMaxSelectE = 2048;
 constexpr int kMaxSelectU = 16384;
+// Most units the one-block selection kernel takes (more: select_multi.hip).
+constexpr int kMaxSelectOne = 32768;
 
 hipError_t launch_page_bounds(const BoundsArgs& a, hipStream_t st);
 hipError_t launch_score(const ScoreArgs& a, hipStream_t st);
-// One block per (sequence, KV head); U_max <= kMaxSelectU.
+// One block per (sequence, KV head); U_max <= kMaxSelectOne.
 hipError_t launch_select(const SelectArgs& a, hipStream_t st);
 // Many blocks per (sequence, KV head), any U_max; scratch of
 // msel_workspace_bytes(B, Hkv, U_max) bytes (contents need not be set).

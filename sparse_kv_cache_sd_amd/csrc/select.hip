@@ -2,7 +2,7 @@
 // standalone kernel: one block per (sequence, KV head).  The search itself
 // (radix bins over the block's key range, ties to the lower index, ids in
 // ascending order) is in topk.h.  The block's threads hold the keys in
-// registers (up to 16384 units; more go to select_multi.hip, which spreads
+// registers (up to 32768 units; more go to select_multi.hip, which spreads
 // one selection over many blocks).
 #include "topk.h"
 
@@ -48,7 +48,8 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t st) {
   if (U <= 2048) SD_SELECT_REGS(512, 4);
   else if (U <= 4096) SD_SELECT_REGS(512, 8);
   else if (U <= 8192) SD_SELECT_REGS(512, 16);
-  else if (U <= kMaxSelectU) SD_SELECT_REGS(1024, 16);
+  else if (U <= 16384) SD_SELECT_REGS(1024, 16);
+  else if (U <= kMaxSelectOne) SD_SELECT_REGS(1024, 32);
   else return hipErrorInvalidValue;  // many units: launch_select_multi
 #undef SD_SELECT_REGS
   return hipGetLastError();

@@ -128,6 +128,7 @@ def _select_case(scores_np, seq_lens, unit, r_kv, shape):
 @pytest.mark.parametrize("U,unit,r", [(2048, "page", 0.3), (2048, "page", 0.05), (16384, "page", 0.05),
                                       (1024, "token", 0.25), (131072, "token", 0.2), (37, "page", 0.5),
                                       (5000, "token", 0.9999), (16385, "token", 0.5),
+                                      (32768, "token", 0.2), (32769, "token", 0.3),
                                       (40000, "page", 0.1)])
 def test_select_bitexact_with_ties(seed, U, unit, r):
     rng = np.random.default_rng(seed)
