@@ -243,11 +243,17 @@ class Selection:
         last ``local_units`` units and the step-5 top-k of all U units
         ([SparDA] Section 3.1: initial, local sliding-window and top-k blocks;
         Appendix A: the selected set is B_init U B_local U f_top(scores, k)).
+    kind "mass_budget" (token unit): the shortest prefix of the step-5 order
+        whose dropped dense mass is at most ``max_dropped`` for every head of
+        the group, capped at keep_count(r_kv, U) units ([Cross/cards],
+        pre-hoc sparsity abstract: the dropped mass delta is controlled in
+        advance).
     """
     kind: str = "topk"
     r_kv: float = 0.3
     init_units: int = 0
     local_units: int = 0
+    max_dropped: float = 0.0
 
 
 def window_set(U: int, r_kv: float) -> np.ndarray:
@@ -276,8 +282,40 @@ def init_local_topk_set(sigma: np.ndarray, r_kv: float, init_units: int,
     return np.flatnonzero(keep).astype(np.int64)
 
 
-def selected_units(sigma: np.ndarray, sel: Selection) -> np.ndarray:
-    """The kept units of one (sequence, KV head) under ``sel``, ascending."""
+def mass_budget_count(s_group: np.ndarray, sigma: np.ndarray, max_dropped: float,
+                      k_cap: int) -> int:
+    """Token unit: the smallest k such that keeping the first k units of the
+    step-5 order (decreasing sigma, equal scores to the lower id) leaves a
+    dense softmax mass of at most ``max_dropped`` outside the set for every
+    head h of the group, capped at k_cap.
+
+    s_group [G, n] logits, sigma [n] = max over the group.  The dropped mass
+    after k units is the sum of p_h over the units after position k, summed
+    directly (a suffix sum), as in step 7.
+    """
+    s = np.asarray(s_group, np.float64)
+    sigma = np.asarray(sigma, np.float64)
+    n = sigma.shape[0]
+    if not 1 <= k_cap <= n:
+        raise ValueError("k_cap out of range")
+    if not (math.isfinite(max_dropped) and max_dropped >= 0.0):
+        raise ValueError("max_dropped must be finite and >= 0")
+    order = np.lexsort((np.arange(n), -sigma))
+    m = s.max(axis=1, keepdims=True)
+    w = np.exp(s - m)
+    p = w / w.sum(axis=1, keepdims=True)
+    # dropped[h, k] = sum_{j >= k} p[h, order[j]] for k = 0..n (dropped[:, n] = 0)
+    tail = np.zeros((s.shape[0], n + 1))
+    tail[:, :n] = np.cumsum(p[:, order][:, ::-1], axis=1)[:, ::-1]
+    worst = tail.max(axis=0)                     # over the heads
+    ok = np.flatnonzero(worst[1:] <= max_dropped)  # k = 1..n
+    k = int(ok[0]) + 1 if ok.size else n
+    return min(k, k_cap)
+
+
+def selected_units(sigma: np.ndarray, sel: Selection, s_group=None) -> np.ndarray:
+    """The kept units of one (sequence, KV head) under ``sel``, ascending
+    (``s_group``, the group's logits, is needed by kind "mass_budget")."""
     U = np.asarray(sigma).shape[0]
     if sel.kind == "topk":
         return select_topk(sigma, keep_count(sel.r_kv, U))[0]
@@ -285,6 +323,11 @@ def selected_units(sigma: np.ndarray, sel: Selection) -> np.ndarray:
         return window_set(U, sel.r_kv)
     if sel.kind == "init_local_topk":
         return init_local_topk_set(sigma, sel.r_kv, sel.init_units, sel.local_units)
+    if sel.kind == "mass_budget":
+        if s_group is None:
+            raise ValueError("mass_budget needs the group's logits")
+        k = mass_budget_count(s_group, sigma, sel.max_dropped, keep_count(sel.r_kv, U))
+        return select_topk(sigma, k)[0]
     raise ValueError(f"unknown selection kind {sel.kind!r}")
 
 
@@ -292,7 +335,7 @@ def selection_capacity(sel: Selection, U: int) -> int:
     """Most units ``sel`` keeps for a sequence of at most U units (the row
     length of a kept-list buffer)."""
     k = keep_count(sel.r_kv, U)
-    if sel.kind in ("topk", "window"):
+    if sel.kind in ("topk", "window", "mass_budget"):
         return k
     return min(U, sel.init_units + sel.local_units + k)
 
@@ -356,7 +399,9 @@ def group_step(q_group, K, V, *, unit: str, page_size: int, r_kv: float,
     k = keep_count(r_kv, U)
     kept, gap = select_topk(sigma, k)
     if selection is not None and selection.kind != "topk":
-        kept = selected_units(sigma, selection)
+        if selection.kind == "mass_budget" and unit != "token":
+            raise ValueError("mass_budget is token unit only")
+        kept = selected_units(sigma, selection, s)
     if kept_override is not None:
         kept = np.asarray(kept_override, dtype=np.int64)
     tokens = unit_tokens(kept, unit, page_size, n)

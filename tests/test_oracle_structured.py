@@ -1,5 +1,5 @@
-"""Pins of the oracle's structured index sets (the KV window, and initial +
-local + top-k blocks).
+"""Pins of the oracle's structured index sets (the KV window, initial +
+local + top-k blocks, and the dropped-mass budget).
 
 * window: it is the suffix of the context, so a window of every unit is dense
   attention exactly, and a page-unit window covers exactly the last tokens;
@@ -10,7 +10,12 @@ local + top-k blocks).
   that cover every unit give dense attention; a superset of the top-k drops
   no more mass and obeys the 2 * delta * max|V| bound; the capacity bounds
   the set size, and matches the 64-token-block configuration of the pages
-  (1 initial block, a 2048-token window, 96 top-k blocks).
+  (1 initial block, a 2048-token window, 96 top-k blocks);
+* dropped-mass budget: with one head it is the textbook top-p count (exact
+  sums); in general the shortest step-5 prefix whose step-7 dropped mass is
+  within the target for every head (and one unit fewer is not); 0 and 1 as
+  targets, monotonicity and the cap; whole decode steps report delta within
+  the target.
 """
 
 import math
@@ -140,3 +145,84 @@ def test_unknown_kind_rejected():
         sdref.selected_units(np.zeros(4), Sel("sliding", 0.5))
     with pytest.raises(ValueError):
         sdref.init_local_topk_set(np.zeros(4), 0.5, -1, 0)
+
+
+# ---------------------------------------------------------------- dropped-mass budget
+
+def _nucleus_count(p, max_dropped):
+    """Textbook top-p: sort the probabilities in decreasing order and keep the
+    shortest prefix whose complement sums (exactly, math.fsum) to at most
+    max_dropped."""
+    q = np.sort(np.asarray(p))[::-1]
+    for k in range(1, len(q) + 1):
+        if math.fsum(q[k:]) <= max_dropped:
+            return k
+    return len(q)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_budget_one_head_is_top_p(seed):
+    """With one head, sigma is the head's own logit, so the budget is the
+    nucleus (top-p, p = 1 - max_dropped) count of its softmax."""
+    rng = np.random.default_rng(300 + seed)
+    n = int(rng.integers(5, 400))
+    s = rng.standard_normal((1, n)) * rng.uniform(0.5, 4.0)
+    p = np.exp(s[0] - s[0].max())
+    p /= p.sum()
+    for dstar in rng.uniform(0.0, 0.6, size=6):
+        k = sdref.mass_budget_count(s, s[0], float(dstar), n)
+        # skip thresholds within rounding of a prefix sum
+        q = np.sort(p)[::-1]
+        if np.min(np.abs(np.cumsum(q[::-1])[::-1] - dstar)) < 1e-12:
+            continue
+        assert k == _nucleus_count(p, float(dstar))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_budget_is_smallest_topk_within_delta(seed):
+    """Every head: the kept top-k drops <= max_dropped, and one unit fewer
+    would drop more for some head (step 5's set, step 7's mass)."""
+    rng = np.random.default_rng(400 + seed)
+    G = int(rng.integers(1, 5))
+    n = int(rng.integers(2, 60))
+    s = rng.standard_normal((G, n)) * 2.0
+    if seed % 3 == 0:
+        s = np.round(s)                       # tied group scores
+    sigma = s.max(axis=0)
+    for dstar in (0.0, 0.01, 0.1, 0.3, 0.9, 1.0):
+        k = sdref.mass_budget_count(s, sigma, dstar, n)
+        worst = lambda kk: max(sdref.dropped_mass(s[h], sdref.select_topk(sigma, kk)[0])
+                               for h in range(G))
+        assert worst(k) <= dstar + 1e-12 or k == n
+        if k > 1:
+            assert worst(k - 1) > dstar - 1e-12
+
+
+def test_budget_edges_and_cap():
+    rng = np.random.default_rng(5)
+    s = rng.standard_normal((4, 300))
+    sigma = s.max(axis=0)
+    assert sdref.mass_budget_count(s, sigma, 1.0, 300) == 1
+    assert sdref.mass_budget_count(s, sigma, 0.0, 300) == 300
+    ks = [sdref.mass_budget_count(s, sigma, d, 300) for d in (0.001, 0.01, 0.05, 0.2, 0.5)]
+    assert ks == sorted(ks, reverse=True)
+    assert sdref.mass_budget_count(s, sigma, 0.001, 40) == 40          # the cap
+    with pytest.raises(ValueError):
+        sdref.mass_budget_count(s, sigma, -0.1, 300)
+
+
+def test_budget_decode_step_reports_delta_within_target():
+    w = kvsynth.generate(kvsynth.RECIPES["sweep"].with_(seq_len=2000, num_q_heads=8,
+                                                         num_kv_heads=2))
+    for dstar in (0.02, 0.1):
+        sel = Sel("mass_budget", 0.5, max_dropped=dstar)
+        res = sdref.decode_step(w.q, w.K, w.V, w.seq_lens, dtype="bf16", unit="token",
+                                page_size=16, r_kv=0.5, selection=sel)
+        for gr in res.values():
+            cap = sdref.keep_count(0.5, 2000)
+            assert 1 <= len(gr.kept) <= cap
+            if len(gr.kept) < cap:
+                assert gr.delta.max() <= dstar + 1e-12
+    with pytest.raises(ValueError):
+        sdref.decode_step(w.q, w.K, w.V, w.seq_lens, dtype="bf16", unit="page", page_size=16,
+                          r_kv=0.5, selection=Sel("mass_budget", 0.5, max_dropped=0.1))
