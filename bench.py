@@ -224,7 +224,7 @@ def summarize_pmc(fetch_dir, write_dir, workload, out_path, cmd_fetch, cmd_write
 
 def sdref_selection(sel):
     from oracle import sdref
-    return sdref.Selection(sel.kind, sel.r_kv, sel.init_units, sel.local_units)
+    return sdref.Selection(sel.kind, sel.r_kv, sel.init_units, sel.local_units, sel.max_dropped)
 
 
 def cpu_baseline(w, unit, r_kv, budget_s=12.0, selection=None):
@@ -275,8 +275,12 @@ def main():
     ap.add_argument("--layers", type=int, default=0, help="distinct layer caches (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead")
-    ap.add_argument("--selection", default="topk", choices=["topk", "window", "init_local_topk"],
-                    help="kept set: top-k (default), the KV window, or initial + local + top-k")
+    ap.add_argument("--selection", default="topk",
+                    choices=["topk", "window", "init_local_topk", "mass_budget"],
+                    help="kept set: top-k (default), the KV window, initial + local + top-k, or "
+                         "the dropped-mass budget (token unit)")
+    ap.add_argument("--max-dropped", type=float, default=0.05,
+                    help="mass_budget: most dense softmax mass left outside, per head")
     ap.add_argument("--r-kv", type=float, default=0.0,
                     help="keep ratio (0 = the workload's own)")
     ap.add_argument("--init-units", type=int, default=1, help="init_local_topk: first units kept")
@@ -361,14 +365,20 @@ def main():
 
     structured = args.selection != "topk"
     local_units = args.local_units or (2048 // P if unit == "page" else 2048)
-    selection = sd.Selection(args.selection, r_kv, args.init_units if structured else 0,
-                             local_units if args.selection == "init_local_topk" else 0)
+    selection = sd.Selection(args.selection, r_kv,
+                             args.init_units if args.selection == "init_local_topk" else 0,
+                             local_units if args.selection == "init_local_topk" else 0,
+                             args.max_dropped if args.selection == "mass_budget" else 0.0)
     if structured:
         config_sel = {"selection": args.selection, "init_units": selection.init_units,
-                      "local_units": selection.local_units}
-        desc += (f"; kept set: {args.selection}" +
-                 (f" ({selection.init_units} initial + {selection.local_units} local units + "
-                  f"top-k)" if args.selection == "init_local_topk" else " (most recent units)"))
+                      "local_units": selection.local_units,
+                      "max_dropped": selection.max_dropped}
+        desc += f"; kept set: {args.selection}" + {
+            "init_local_topk": f" ({selection.init_units} initial + {selection.local_units} "
+                               f"local units + top-k)",
+            "window": " (most recent units)",
+            "mass_budget": f" (at most {selection.max_dropped:g} of each head's mass dropped, "
+                           f"capped at r_KV)"}[args.selection]
     k_max = sd.selection_capacity(selection, shape.units_max(unit))
     ws = sd.alloc_workspace_sel(shape, unit, selection)
     ws_dense = sd.alloc_workspace(shape, unit, 1.0)

@@ -237,21 +237,33 @@ SD_API sd_status sd_decode_step(const sd_shape* shape, const void* q, const void
  *   SD_SEL_INIT_LOCAL_TOPK  the union of the first init_units units, the last
  *                           local_units units and the top-k of all U_b units
  *                           ([SparDA] Section 3.1: initial, local and top-k
- *                           blocks; Appendix A: B_init U B_local U top-k).
+ *                           blocks; Appendix A: B_init U B_local U top-k);
+ *   SD_SEL_MASS_BUDGET      token unit only: the shortest prefix of the top-k
+ *                           order (decreasing score, equal scores to the lower
+ *                           id) that leaves at most max_dropped of every
+ *                           head's dense softmax mass outside, capped at k_b
+ *                           ([Cross/cards] pre-hoc sparsity abstract: the
+ *                           dropped mass controlled in advance).  Needs the
+ *                           token logits; at most 32768 tokens per sequence
+ *                           (SD_E_UNSUPPORTED beyond).  The masses are summed
+ *                           as 2^-40 fixed-point integers of the fp32 softmax
+ *                           weights.
  * Lists are ascending.  The row length of a kept list is
- * sd_selection_capacity(sel, U_max): k_max for the first two kinds and
- * min(U_max, init_units + local_units + k_max) for the union. */
+ * sd_selection_capacity(sel, U_max): k_max, or min(U_max, init_units +
+ * local_units + k_max) for the union. */
 typedef enum sd_selection_kind {
   SD_SEL_TOPK = 0,
   SD_SEL_WINDOW = 1,
-  SD_SEL_INIT_LOCAL_TOPK = 2
+  SD_SEL_INIT_LOCAL_TOPK = 2,
+  SD_SEL_MASS_BUDGET = 3
 } sd_selection_kind;
 
 typedef struct sd_selection {
   int32_t kind;         /* sd_selection_kind */
   int32_t init_units;   /* >= 0; SD_SEL_INIT_LOCAL_TOPK only */
   int32_t local_units;  /* >= 0; SD_SEL_INIT_LOCAL_TOPK only */
-  double r_kv;          /* keep ratio of the top-k (or of the window) */
+  double r_kv;          /* keep ratio of the top-k (window; the budget's cap) */
+  double max_dropped;   /* in [0, 1]; SD_SEL_MASS_BUDGET only */
 } sd_selection;
 
 /* Row length of a kept list for at most num_units units (host, pure); -1 on
@@ -268,19 +280,23 @@ SD_API sd_status sd_workspace_bytes_sel(const sd_shape* shape, int32_t unit,
  * ascending, to sel_idx[b][g][0 .. sel_count[b][g] - 1] (rows of
  * sd_selection_capacity(sel, U_max) entries).  unit_scores as for
  * sd_select_topk (may be NULL for SD_SEL_WINDOW).  The union is the top-k of
- * sd_select_topk merged with the two ranges.  ws: sd_workspace_bytes_sel. */
+ * sd_select_topk merged with the two ranges.  token_logits (as written by
+ * sd_score_pages) is read by SD_SEL_MASS_BUDGET only and may be NULL
+ * otherwise.  ws: sd_workspace_bytes_sel. */
 SD_API sd_status sd_select_units(const sd_shape* shape, int32_t unit, const int32_t* seq_lens,
-                                 const float* unit_scores, const sd_selection* sel,
-                                 int32_t* sel_idx, int32_t* sel_count, void* ws,
-                                 size_t ws_bytes, void* stream);
+                                 const float* unit_scores, const float* token_logits,
+                                 const sd_selection* sel, int32_t* sel_idx, int32_t* sel_count,
+                                 void* ws, size_t ws_bytes, void* stream);
 
 /* sd_decode_step under a selection.  SD_SEL_TOPK is sd_decode_step at
  * sel->r_kv.  SD_SEL_WINDOW attends the window directly (no scoring;
  * page_bounds not read).  SD_SEL_INIT_LOCAL_TOPK scores, selects the union
  * and attends it; in page unit with bf16 data and at most 16384 pages per
  * sequence the attention blocks select it themselves, as in
- * sd_select_attend.  sel_idx / sel_count may be NULL; when given they
- * receive the kept lists (rows of sd_selection_capacity(sel, U_max)).
+ * sd_select_attend.  SD_SEL_MASS_BUDGET scores the tokens, selects with the
+ * budget and attends over the stored logits.  sel_idx / sel_count may be
+ * NULL; when given they receive the kept lists (rows of
+ * sd_selection_capacity(sel, U_max)).
  * ws: sd_workspace_bytes_sel. */
 SD_API sd_status sd_decode_step_sel(const sd_shape* shape, const void* q, const void* k_pages,
                                     const void* v_pages, const void* page_bounds,

@@ -53,11 +53,13 @@ class SdSelection(ctypes.Structure):
         ("init_units", ctypes.c_int32),
         ("local_units", ctypes.c_int32),
         ("r_kv", ctypes.c_double),
+        ("max_dropped", ctypes.c_double),
     ]
 
 
-SEL_TOPK, SEL_WINDOW, SEL_INIT_LOCAL_TOPK = 0, 1, 2
-_SEL_KINDS = {"topk": SEL_TOPK, "window": SEL_WINDOW, "init_local_topk": SEL_INIT_LOCAL_TOPK}
+SEL_TOPK, SEL_WINDOW, SEL_INIT_LOCAL_TOPK, SEL_MASS_BUDGET = 0, 1, 2, 3
+_SEL_KINDS = {"topk": SEL_TOPK, "window": SEL_WINDOW, "init_local_topk": SEL_INIT_LOCAL_TOPK,
+              "mass_budget": SEL_MASS_BUDGET}
 
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
@@ -84,8 +86,8 @@ _SIGS = {
     "sd_selection_capacity": (ctypes.c_int32, [_SELP, _I32]),
     "sd_workspace_bytes_sel": (ctypes.c_int, [ctypes.POINTER(SdShape), _I32, _SELP,
                                               ctypes.POINTER(ctypes.c_size_t)]),
-    "sd_select_units": (ctypes.c_int, [ctypes.POINTER(SdShape), _I32, _P, _P, _SELP, _P, _P, _P,
-                                       ctypes.c_size_t, _P]),
+    "sd_select_units": (ctypes.c_int, [ctypes.POINTER(SdShape), _I32, _P, _P, _P, _SELP, _P, _P,
+                                       _P, ctypes.c_size_t, _P]),
     "sd_decode_step_sel": (ctypes.c_int, [ctypes.POINTER(SdShape), _P, _P, _P, _P, _P, _P, _I32,
                                           _SELP, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "sd_last_error": (ctypes.c_char_p, []),
@@ -397,18 +399,19 @@ def merge_splits(shape: Shape, out, lse, ws, stream=None):
 
 @dataclass(frozen=True)
 class Selection:
-    """Which units a decode step keeps: kind "topk", "window" or
-    "init_local_topk" (include/sd.h, sd_selection)."""
+    """Which units a decode step keeps: kind "topk", "window",
+    "init_local_topk" or "mass_budget" (include/sd.h, sd_selection)."""
     kind: str = "topk"
     r_kv: float = 0.3
     init_units: int = 0
     local_units: int = 0
+    max_dropped: float = 0.0
 
     def c(self) -> SdSelection:
         if self.kind not in _SEL_KINDS:
             raise ValueError(f"unknown selection kind {self.kind!r}")
         return SdSelection(_SEL_KINDS[self.kind], int(self.init_units), int(self.local_units),
-                           float(self.r_kv))
+                           float(self.r_kv), float(self.max_dropped))
 
 
 def selection_capacity(sel: Selection, num_units: int) -> int:
@@ -431,7 +434,7 @@ def alloc_workspace_sel(shape: Shape, unit, sel: Selection, device="cuda") -> to
 
 
 def select_units(shape: Shape, unit, seq_lens, unit_scores, sel: Selection, sel_idx, sel_count,
-                 ws=None, stream=None):
+                 ws=None, token_logits=None, stream=None):
     s, u = shape, _unit(unit)
     umax = s.max_pages_per_seq if u == UNIT_PAGE else s.max_seq_len
     cap = selection_capacity(sel, umax)
@@ -441,6 +444,8 @@ def select_units(shape: Shape, unit, seq_lens, unit_scores, sel: Selection, sel_
         _dev(seq_lens, "seq_lens", torch.int32, (s.batch,)),
         _dev(unit_scores, "unit_scores", torch.float32, (s.batch, s.num_kv_heads, umax),
              optional=sel.kind == "window"),
+        _dev(token_logits, "token_logits", torch.float32,
+             (s.batch, s.num_q_heads, s.max_seq_len), optional=sel.kind != "mass_budget"),
         ctypes.byref(sel.c()),
         _dev(sel_idx, "sel_idx", torch.int32, (s.batch, s.num_kv_heads, cap)),
         _dev(sel_count, "sel_count", torch.int32, (s.batch, s.num_kv_heads)),

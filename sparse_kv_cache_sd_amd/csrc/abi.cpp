@@ -116,20 +116,37 @@ struct Sel {
   int kind;  // SD_SEL_*
   double r;
   int init, local;  // SD_SEL_INIT_LOCAL_TOPK only (else 0)
+  double dmax;      // SD_SEL_MASS_BUDGET only
 };
 
-Sel topk_sel(double r) { return Sel{SD_SEL_TOPK, r, 0, 0}; }
+Sel topk_sel(double r) { return Sel{SD_SEL_TOPK, r, 0, 0, 0.0}; }
 
 sd_status check_selection(const sd_selection* s, Sel* out) {
   if (!s) return fail(SD_E_NULL, "sel is NULL");
-  if (s->kind != SD_SEL_TOPK && s->kind != SD_SEL_WINDOW && s->kind != SD_SEL_INIT_LOCAL_TOPK)
+  if (s->kind != SD_SEL_TOPK && s->kind != SD_SEL_WINDOW && s->kind != SD_SEL_INIT_LOCAL_TOPK &&
+      s->kind != SD_SEL_MASS_BUDGET)
     return fail(SD_E_SHAPE, "unknown selection kind %d", s->kind);
+  if (s->kind == SD_SEL_MASS_BUDGET &&
+      !(std::isfinite(s->max_dropped) && s->max_dropped >= 0.0 && s->max_dropped <= 1.0))
+    return fail(SD_E_RATIO, "max_dropped must be in [0, 1]");
   sd_status st;
   if ((st = check_ratio(s->r_kv)) != SD_OK) return st;
   if (s->init_units < 0 || s->local_units < 0)
     return fail(SD_E_SHAPE, "init_units and local_units must be >= 0");
   const bool u = s->kind == SD_SEL_INIT_LOCAL_TOPK;
-  *out = Sel{s->kind, s->r_kv, u ? s->init_units : 0, u ? s->local_units : 0};
+  *out = Sel{s->kind, s->r_kv, u ? s->init_units : 0, u ? s->local_units : 0,
+              s->kind == SD_SEL_MASS_BUDGET ? s->max_dropped : 0.0};
+  return SD_OK;
+}
+
+// The dropped-mass budget's limits: token unit, one block per (b, g).
+sd_status check_budget(const sdkv::Dims& d, int unit, const Sel& s) {
+  if (s.kind != SD_SEL_MASS_BUDGET) return SD_OK;
+  if (unit != SD_UNIT_TOKEN)
+    return fail(SD_E_UNSUPPORTED, "the dropped-mass budget is token unit only");
+  if (d.max_seq > sdkv::kMaxSelectOne)
+    return fail(SD_E_UNSUPPORTED, "the dropped-mass budget takes at most %d tokens per sequence",
+                sdkv::kMaxSelectOne);
   return SD_OK;
 }
 
@@ -388,11 +405,25 @@ bool fused_select(const sdkv::Dims& d, int unit, int k_max) {
 // or the top-k (kept in the workspace) merged with the forced ranges.  Rows
 // of idx hold capacity(sel, U_max) entries.
 sd_status do_select_list(const sdkv::Dims& d, int unit, const int32_t* sl, const float* scores,
-                         const Sel& sel, int32_t* idx, int32_t* cnt, void* msel_ws,
-                         int32_t* top_tmp, int32_t* top_cnt, hipStream_t s,
+                         const float* logits, const Sel& sel, int32_t* idx, int32_t* cnt,
+                         void* msel_ws, int32_t* top_tmp, int32_t* top_cnt, hipStream_t s,
                          const uint32_t* score_mm = nullptr) {
   if (sel.kind == SD_SEL_TOPK)
     return do_select(d, unit, sl, scores, sel.r, idx, cnt, msel_ws, s, score_mm);
+  if (sel.kind == SD_SEL_MASS_BUDGET) {
+    sdkv::BudgetArgs a{};
+    a.d = d;
+    a.seq_lens = sl;
+    a.scores = scores;
+    a.logits = logits;
+    a.U_max = units_max(d, unit);
+    a.R_ppm = ratio_ppm(sel.r);
+    a.k_max = static_cast<int>(keep_count_ppm(a.R_ppm, a.U_max));
+    a.max_dropped = static_cast<float>(sel.dmax);
+    a.sel_idx = idx;
+    a.sel_count = cnt;
+    return device_status(sdkv::launch_select_budget(a, s), "budget selection kernel launch");
+  }
   const int U = units_max(d, unit);
   const int k_top = static_cast<int>(keep_count_ppm(ratio_ppm(sel.r), U));
   sd_status st;
@@ -425,7 +456,7 @@ sd_status do_select_attend(const sdkv::Dims& d, const void* q, const void* kp, c
   }
   int32_t* idx = sel_idx ? sel_idx : reinterpret_cast<int32_t*>(at(ws, L.sel_idx));
   int32_t* cnt = sel_count ? sel_count : reinterpret_cast<int32_t*>(at(ws, L.sel_count));
-  if ((st = do_select_list(d, unit, sl, scores, sel, idx, cnt, at(ws, L.msel),
+  if ((st = do_select_list(d, unit, sl, scores, nullptr, sel, idx, cnt, at(ws, L.msel),
                            reinterpret_cast<int32_t*>(at(ws, L.topk_tmp)),
                            reinterpret_cast<int32_t*>(at(ws, L.topk_cnt)), s)) != SD_OK)
     return st;
@@ -477,7 +508,7 @@ sd_status decode_impl(const sdkv::Dims& d, const void* q, const void* k_pages,
                             sel_idx, sel_count, ws, s);
   int32_t* idx = sel_idx ? sel_idx : reinterpret_cast<int32_t*>(at(ws, L.sel_idx));
   int32_t* cnt = sel_count ? sel_count : reinterpret_cast<int32_t*>(at(ws, L.sel_count));
-  if ((st = do_select_list(d, unit, seq_lens, scores, sel, idx, cnt, at(ws, L.msel),
+  if ((st = do_select_list(d, unit, seq_lens, scores, logits, sel, idx, cnt, at(ws, L.msel),
                            reinterpret_cast<int32_t*>(at(ws, L.topk_tmp)),
                            reinterpret_cast<int32_t*>(at(ws, L.topk_cnt)), s, smm)) != SD_OK)
     return st;
@@ -723,8 +754,9 @@ sd_status sd_workspace_bytes_sel(const sd_shape* shape, int32_t unit, const sd_s
 }
 
 sd_status sd_select_units(const sd_shape* shape, int32_t unit, const int32_t* seq_lens,
-                          const float* unit_scores, const sd_selection* sel, int32_t* sel_idx,
-                          int32_t* sel_count, void* ws, size_t ws_bytes, void* stream) {
+                          const float* unit_scores, const float* token_logits,
+                          const sd_selection* sel, int32_t* sel_idx, int32_t* sel_count, void* ws,
+                          size_t ws_bytes, void* stream) {
   sdkv::Dims d;
   Sel v;
   sd_status st;
@@ -734,6 +766,9 @@ sd_status sd_select_units(const sd_shape* shape, int32_t unit, const int32_t* se
   if (!seq_lens || !sel_idx || !sel_count || (!unit_scores && v.kind != SD_SEL_WINDOW))
     return fail(SD_E_NULL, "seq_lens, sel_idx, sel_count and (unless a window) unit_scores "
                            "are required");
+  if ((st = check_budget(d, unit, v)) != SD_OK) return st;
+  if (v.kind == SD_SEL_MASS_BUDGET && !token_logits)
+    return fail(SD_E_NULL, "the dropped-mass budget reads token_logits");
   const SelectLayout SL = select_layout(d, unit, v);
   if ((st = check_ws(ws, ws_bytes, SL.total)) != SD_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -741,8 +776,8 @@ sd_status sd_select_units(const sd_shape* shape, int32_t unit, const int32_t* se
   if (v.kind == SD_SEL_WINDOW)
     st = do_structure(d, unit, seq_lens, v, nullptr, nullptr, 0, sel_idx, sel_count, cap, s);
   else
-    st = do_select_list(d, unit, seq_lens, unit_scores, v, sel_idx, sel_count, at(ws, SL.msel),
-                        reinterpret_cast<int32_t*>(at(ws, SL.tmp)),
+    st = do_select_list(d, unit, seq_lens, unit_scores, token_logits, v, sel_idx, sel_count,
+                        at(ws, SL.msel), reinterpret_cast<int32_t*>(at(ws, SL.tmp)),
                         reinterpret_cast<int32_t*>(at(ws, SL.cnt)), s);
   if (st != SD_OK) return st;
   return ok();
@@ -762,6 +797,7 @@ sd_status sd_decode_step_sel(const sd_shape* shape, const void* q, const void* k
   if (!q || !k_pages || !v_pages || !block_table || !seq_lens || !out || !lse)
     return fail(SD_E_NULL,
                 "q, k_pages, v_pages, block_table, seq_lens, out and lse are required");
+  if ((st = check_budget(d, unit, v)) != SD_OK) return st;
   if (v.r < 1.0 && v.kind != SD_SEL_WINDOW && unit == SD_UNIT_PAGE && !page_bounds)
     return fail(SD_E_NULL, "page unit selection reads page_bounds");
   if ((sel_idx == nullptr) != (sel_count == nullptr))

@@ -1,0 +1,295 @@
+// Stage 1b with a dropped-mass budget (token unit): per (sequence b, KV head
+// g), keep the shortest prefix of the top-k order (decreasing group score,
+// equal scores to the lower id) whose dense softmax mass left outside is at
+// most max_dropped for every head of the group, capped at keep_count(U).
+// The dropped mass of the discarded entries governs the error and is
+// controlled in advance ("Where Activation Sparsity and KV-Cache Sparsity
+// Cross in LLM Decoding", cards view, pre-hoc sparsity abstract); in token
+// unit every logit exists after scoring, so it can be computed exactly.
+//
+// One block per (b, g), up to kMaxSelectOne units:
+//   1. per head h: m_h = max_t s[h, t] and 1 / Z_h, Z_h = sum_t e^(s - m_h)
+//      (block reductions in a fixed order);
+//   2. a radix search on the order keys of the group scores, like topk.h,
+//      whose 256-bin histograms also accumulate every head's softmax mass
+//      p_h(t) = e^(s - m_h) / Z_h as 2^40 fixed-point integers: integer sums
+//      do not depend on the order of the LDS atomics, so the result does not
+//      depend on timing.  The interval narrows to the first bin (from the
+//      top) whose inclusion leaves at most the target outside for every head;
+//   3. when the interval is one key value, its units (ties) are taken in id
+//      order, one wave scanning 64 ids at a time, until the target holds;
+//   4. the kept list is the exact top-k of topk.h with that count.
+#include "topk.h"
+
+namespace sdkv {
+
+namespace {
+
+constexpr int kBT = 1024;              // threads per block
+constexpr int kBW = kBT / 64;
+constexpr int kBK = kMaxSelectOne / kBT;  // keys per thread
+constexpr int kBBins = 256;
+constexpr int kBMaxG = 8;
+constexpr float kFix = 1099511627776.0f;  // 2^40
+
+typedef unsigned long long u64;
+
+struct BudgetShared {
+  RadixState rs;
+  KeptScratch<kBK, kBW> ks;
+  u64 mass[kBMaxG][kBBins];
+  uint32_t cnt[kBBins];
+  float red[kBW];
+  float m[kBMaxG], invz[kBMaxG];
+  u64 tot[kBMaxG];    // all units' mass per head
+  u64 above[kBMaxG];  // mass of the units above the interval
+  uint32_t c_above;   // units above the interval
+  uint32_t lo, hi;
+  int kstar;          // > 0 once the count is known
+};
+
+__device__ __forceinline__ float block_max(BudgetShared& sm, float x) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  x = wave_max(x);
+  if (lane == 0) sm.red[wave] = x;
+  __syncthreads();
+  float r = sm.red[0];
+#pragma unroll
+  for (int w = 1; w < kBW; ++w) r = fmaxf(r, sm.red[w]);
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ float block_sum(BudgetShared& sm, float x) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  x = wave_sum(x);
+  if (lane == 0) sm.red[wave] = x;
+  __syncthreads();
+  float r = 0.f;
+#pragma unroll
+  for (int w = 0; w < kBW; ++w) r += sm.red[w];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(kBT) void select_budget_kernel(BudgetArgs a) {
+  __shared__ BudgetShared sm;
+  const Dims& d = a.d;
+  const int g = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = d.G;
+  const int64_t bg = (int64_t)b * d.Hkv + g;
+  const float* sc = a.scores + bg * a.U_max;
+  const float* lg = a.logits + ((int64_t)b * d.Hq + (int64_t)g * G) * d.max_seq;
+  uint32_t key[kBK];
+#pragma unroll
+  for (int i = 0; i < kBK; ++i) key[i] = order_key(sc[min(tid + kBT * i, a.U_max - 1)]);
+  const int n = clamp_len(a.seq_lens[b], d.max_seq);
+  const int U = min(n, a.U_max);
+  const int kcap = min(keep_count_dev(U, a.R_ppm), a.k_max);
+  int32_t* out = a.sel_idx + bg * a.k_max;
+  if (kcap == 0) {
+    if (tid == 0) a.sel_count[bg] = 0;
+    return;
+  }
+  // 1. dense softmax normalisers of the group's heads
+  for (int h = 0; h < G; ++h) {
+    const float* row = lg + (int64_t)h * d.max_seq;
+    float mx = -INFINITY;
+#pragma unroll 8
+    for (int i = 0; i < kBK; ++i) {
+      const int t = tid + kBT * i;
+      if (t < U) mx = fmaxf(mx, row[t]);
+    }
+    mx = block_max(sm, mx);
+    float z = 0.f;
+#pragma unroll 8
+    for (int i = 0; i < kBK; ++i) {
+      const int t = tid + kBT * i;
+      if (t < U) z += exp2f((row[t] - mx) * kLog2e);
+    }
+    z = block_sum(sm, z);
+    if (tid == 0) { sm.m[h] = mx; sm.invz[h] = 1.f / z; }
+  }
+  // the target as a fixed-point mass
+  const u64 target = (u64)(fminf(fmaxf(a.max_dropped, 0.f), 1.f) * kFix);
+  auto weight = [&](int h, int t) -> u64 {
+    const float w = exp2f((lg[(int64_t)h * d.max_seq + t] - sm.m[h]) * kLog2e) * sm.invz[h];
+    return (u64)(fminf(w, 1.f) * kFix);
+  };
+  // 2. radix search with mass histograms
+  uint32_t mn = 0xFFFFFFFFu, mxk = 0u;
+#pragma unroll
+  for (int i = 0; i < kBK; ++i)
+    if (tid + kBT * i < U) { mn = min(mn, key[i]); mxk = max(mxk, key[i]); }
+  block_minmax<kBW>(sm.rs, mn, mxk);
+  if (tid == 0) {
+    sm.lo = sm.rs.lo;
+    sm.hi = sm.rs.hi;
+    sm.c_above = 0u;
+    sm.kstar = 0;
+  }
+  if (tid < kBMaxG) sm.above[tid] = 0ull;
+  __syncthreads();
+  bool first = true;
+  while (sm.kstar == 0 && sm.lo != sm.hi) {
+    const uint32_t lo = sm.lo, hi = sm.hi;
+    const uint32_t shift = bin_shift(lo, hi);
+    for (int i = tid; i < kBBins; i += kBT) {
+      sm.cnt[i] = 0u;
+#pragma unroll
+      for (int h = 0; h < kBMaxG; ++h) sm.mass[h][i] = 0ull;
+    }
+    __syncthreads();
+    for (int i = 0; i < kBK; ++i) {
+      const int t = tid + kBT * i;
+      if (t < U && key[i] >= lo && key[i] <= hi) {
+        const uint32_t bin = (key[i] - lo) >> shift;
+        atomicAdd(&sm.cnt[bin], 1u);
+        for (int h = 0; h < G; ++h) atomicAdd(&sm.mass[h][bin], weight(h, t));
+      }
+    }
+    __syncthreads();
+    if (first) {  // every unit is in the first interval: the totals
+      if (tid < G) {
+        u64 s = 0ull;
+        for (int i = 0; i < kBBins; ++i) s += sm.mass[tid][i];
+        sm.tot[tid] = s;
+      }
+      __syncthreads();
+      first = false;
+    }
+    if (wave == 0) {
+      // lane l holds bins 255 - 4l - j (j < 4): descending order.  ok[j]:
+      // keeping everything from bin 255 - 4l - j up meets the target for
+      // every head
+      bool ok[4] = {true, true, true, true};
+      for (int h = 0; h < G; ++h) {
+        u64 mb[4], s = 0ull;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          mb[j] = sm.mass[h][255 - 4 * lane - j];
+          s += mb[j];
+        }
+        u64 run = sm.above[h] + (wave_incl_scan<u64>(s) - s);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          run += mb[j];
+          if (sm.tot[h] > run + target) ok[j] = false;
+        }
+      }
+      int hit = -1;
+#pragma unroll
+      for (int j = 3; j >= 0; --j)
+        if (ok[j]) hit = j;
+      const uint64_t hits = __ballot(hit >= 0);
+      // the first bin meeting the target (the lowest bin as a guard: keeping
+      // the whole interval always meets it)
+      const int fl = hits ? (int)__builtin_ctzll(hits) : 63;
+      const int fj = __shfl(hit >= 0 ? hit : 3, fl, 64);
+      const uint32_t bin = (uint32_t)(255 - 4 * fl - fj);
+      // units and mass in the bins above the chosen one
+      uint32_t c_up = 0u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (lane < fl || (lane == fl && j < fj)) c_up += sm.cnt[255 - 4 * lane - j];
+      c_up = wave_sum(c_up);
+      for (int h = 0; h < G; ++h) {
+        u64 m_up = 0ull;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (lane < fl || (lane == fl && j < fj)) m_up += sm.mass[h][255 - 4 * lane - j];
+        m_up = wave_incl_scan<u64>(m_up);
+        if (lane == 63) sm.above[h] += m_up;
+      }
+      if (lane == 0) {
+        const uint32_t nlo = lo + (bin << shift);
+        const uint64_t top = (uint64_t)nlo + ((1ull << shift) - 1ull);
+        sm.lo = nlo;
+        sm.hi = (uint32_t)(top < (uint64_t)hi ? top : (uint64_t)hi);
+        sm.c_above += c_up;
+        // a bin of one unit: the count is known
+        if (sm.cnt[bin] == 1u) sm.kstar = (int)(sm.c_above + 1u);
+      }
+    }
+    __syncthreads();
+  }
+  if (first) {  // every key was equal: no histogram pass ran, sum the totals
+    if (tid < kBMaxG) sm.tot[tid] = 0ull;
+    __syncthreads();
+    for (int h = 0; h < G; ++h) {
+      u64 s = 0ull;
+      for (int i = 0; i < kBK; ++i)
+        if (tid + kBT * i < U) s += weight(h, tid + kBT * i);
+      atomicAdd(&sm.tot[h], s);
+    }
+    __syncthreads();
+  }
+  // 3. ties: the units whose key is the interval's single value, in id order
+  if (sm.kstar == 0) {
+    const uint32_t T = sm.lo;
+#pragma unroll
+    for (int i = 0; i < kBK; ++i) {
+      const uint64_t tie = __ballot(tid + kBT * i < U && key[i] == T);
+      if (lane == 0) sm.ks.tie[i * kBW + wave] = tie;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      u64 acc[kBMaxG];
+#pragma unroll
+      for (int h = 0; h < kBMaxG; ++h) acc[h] = sm.above[h];
+      uint32_t taken = 0u;
+      int found = 0;
+      for (int e = 0; e < kBK * kBW && !found; ++e) {
+        const uint64_t word = sm.ks.tie[e];
+        if (word == 0ull) continue;
+        const int u = 64 * e + lane;
+        const bool mine = (word >> lane) & 1ull;
+        bool ok = true;
+        u64 tot_word[kBMaxG];
+#pragma unroll
+        for (int h = 0; h < kBMaxG; ++h) {
+          const u64 w = (h < G && mine) ? weight(h, u) : 0ull;
+          const u64 incl = wave_incl_scan<u64>(w);
+          tot_word[h] = __shfl(incl, 63, 64);
+          if (h < G && sm.tot[h] > acc[h] + incl + target) ok = false;
+        }
+        const uint64_t sat = __ballot(mine && ok);
+        if (sat) {
+          const int l = (int)__builtin_ctzll(sat);
+          taken += (uint32_t)__popcll(word & ((2ull << l) - 1ull));
+          found = 1;
+        } else {
+          taken += (uint32_t)__popcll(word);
+#pragma unroll
+          for (int h = 0; h < kBMaxG; ++h) acc[h] += tot_word[h];
+        }
+      }
+      // every tie taken always meets the target (nothing is left outside
+      // below T that the interval search had not already allowed)
+      if (lane == 0) sm.kstar = (int)(sm.c_above + max(taken, 1u));
+    }
+    __syncthreads();
+  }
+  // 4. the exact top-k with that count
+  const int k = max(1, min(sm.kstar, kcap));
+  if (tid == 0) a.sel_count[bg] = k;
+  if (k == U) {
+    for (int i = tid; i < U; i += kBT) out[i] = i;
+    return;
+  }
+  topk_bitmap<kBK, kBW>(sm.rs, sm.ks, key, U, k);
+  emit_kept<kBK, kBW>(sm.ks.mask, sm.ks.base, 0u, (uint32_t)k,
+                      [&](int pos, int unit_id) { out[pos] = unit_id; });
+}
+
+}  // namespace
+
+hipError_t launch_select_budget(const BudgetArgs& a, hipStream_t st) {
+  if (a.U_max < 1 || a.U_max > kMaxSelectOne || a.d.G > kBMaxG || a.k_max < 1)
+    return hipErrorInvalidValue;
+  select_budget_kernel<<<dim3(a.d.Hkv, a.d.B), kBT, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace sdkv

@@ -111,6 +111,23 @@ struct StructArgs {
 };
 hipError_t launch_structure(const StructArgs& a, hipStream_t st);
 
+// Top-k with a dropped-mass budget (token unit), one block per (sequence, KV
+// head), U_max <= kMaxSelectOne, G <= 8: the shortest prefix of the top-k
+// order leaving at most max_dropped of every head's dense softmax mass
+// outside, capped at min(keep_count(U, R_ppm), k_max).  logits: the token
+// scorer's [B][Hq][max_seq].
+struct BudgetArgs {
+  Dims d;
+  const int32_t* seq_lens;
+  const float* scores;   // [B][Hkv][U_max]
+  const float* logits;
+  int U_max, k_max, R_ppm;
+  float max_dropped;
+  int32_t* sel_idx;      // [B][Hkv][k_max]
+  int32_t* sel_count;    // [B][Hkv]
+};
+hipError_t launch_select_budget(const BudgetArgs& a, hipStream_t st);
+
 // Most splits one (sequence, KV head) is cut into.
 constexpr int kMaxSplits = 256;
 // Largest slice of the kept list a selecting attention block may own, and

@@ -33,6 +33,7 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kScoreThreads = 256;
 constexpr int kScoreIters = 4;
+constexpr int kTokenIters = 4;  // 16-token chunks per wave, bf16 token scorer
 
 template <typename T, int D>
 constexpr int score_rows_per_block() {
@@ -267,7 +268,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_tokens_f32_kernel(
   if (mm) block_partial_minmax(mm, kmn, kmx, gb.bg, gb.j, (d.max_seq + TPB - 1) / TPB);
 }
 
-// bf16 token scorer on the matrix cores: each wave scores kScoreIters chunks
+// bf16 token scorer on the matrix cores: each wave scores kTokenIters chunks
 // of 16 consecutive tokens (16 | P, so a chunk lies in one page and its rows
 // are contiguous in the page tile).
 template <int D, int G>
@@ -276,7 +277,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_tokens_mfma_kernel(
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
     float* __restrict__ scores, float* __restrict__ logits, uint32_t* __restrict__ mm, Dims d) {
   constexpr int KS = D / 32;
-  constexpr int IT = kScoreIters;
+  constexpr int IT = kTokenIters;
   constexpr int NW = kScoreThreads / 64;
   constexpr int TPB = NW * IT * 16;
   const int BG = d.B * d.Hkv;
@@ -362,7 +363,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_tokens_mfma_kernel(
 }
 
 int score_units_per_block(int dtype, int D) {
-  if (dtype == kBF16) return (kScoreThreads / 64) * kScoreIters * 16;
+  if (dtype == kBF16) return (kScoreThreads / 64) * kTokenIters * 16;
   return D == 64 ? score_rows_per_block<float, 64>() : score_rows_per_block<float, 128>();
 }
 
@@ -397,7 +398,7 @@ hipError_t launch_score(const ScoreArgs& a, hipStream_t st) {
           static_cast<const float*>(a.q), static_cast<const float*>(a.k_pages), a.block_table,
           a.seq_lens, a.unit_scores, a.token_logits, a.score_mm, d);
     } else {
-      constexpr int R = (kScoreThreads / 64) * kScoreIters * 16;
+      constexpr int R = (kScoreThreads / 64) * kTokenIters * 16;
       const dim3 grid((d.max_seq + R - 1) / R * d.Hkv * d.B);
       score_tokens_mfma_kernel<D, G><<<grid, kScoreThreads, 0, st>>>(
           static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k_pages), a.block_table,

@@ -13,6 +13,13 @@ Cases cover the fused page path (bf16, the attention blocks select the union
 themselves), the listed page path (fp32), token unit with one-block and
 many-block top-k, ragged batches, forced ranges wider than the sequence and
 sequences of a single unit.
+
+Dropped-mass budget (token unit): the kept list must be exactly the top-k of
+the library's own scores at the chosen count; the count must equal the
+oracle's wherever the oracle's dropped mass at that count and one fewer is
+more than 1e-5 from the target (and the score gaps exceed 1e-4), and must
+otherwise be valid with the oracle's fp64 masses: within the target (unless
+capped) and one unit fewer not.
 """
 
 from __future__ import annotations
@@ -169,3 +176,115 @@ def test_selection_rejects():
     for bad in (SEL("init_local_topk", 0.3, -1, 0), SEL("window", 0.0), SEL("sliding", 0.3)):
         with pytest.raises((sd.SdError, ValueError)):
             sd.workspace_bytes_sel(s, "page", bad)
+
+
+# ---------------------------------------------------------------- dropped-mass budget
+
+MARGIN = 1e-5   # fp32 softmax weights summed in 2^-40 fixed point vs the fp64 oracle
+
+
+def _budget_run(dev, sel):
+    s = dev.shape
+    cap = sd.selection_capacity(sel, s.max_seq_len)
+    ws = sd.alloc_workspace_sel(s, "token", sel)
+    out = torch.empty((s.batch, s.num_q_heads, s.head_dim), dtype=torch.float32, device="cuda")
+    lse = torch.empty((s.batch, s.num_q_heads), dtype=torch.float32, device="cuda")
+    idx = torch.full((s.batch, s.num_kv_heads, cap), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((s.batch, s.num_kv_heads), -7, dtype=torch.int32, device="cuda")
+    sd.decode_step_sel(s, dev.q, dev.k, dev.v, None, dev.bt, dev.sl, "token", sel, out, lse, ws,
+                       sel_idx=idx, sel_count=cnt)
+    scores = torch.empty((s.batch, s.num_kv_heads, s.max_seq_len), dtype=torch.float32,
+                         device="cuda")
+    logits = torch.empty((s.batch, s.num_q_heads, s.max_seq_len), dtype=torch.float32,
+                         device="cuda")
+    sd.score_pages(s, dev.q, dev.k, dev.bounds, dev.bt, dev.sl, "token", scores, logits)
+    idx2 = torch.full_like(idx, -7)
+    cnt2 = torch.full_like(cnt, -7)
+    sd.select_units(s, "token", dev.sl, scores, sel, idx2, cnt2, ws=ws, token_logits=logits)
+    torch.cuda.synchronize()
+    return (out.cpu().numpy(), lse.cpu().numpy(), idx.cpu().numpy(), cnt.cpu().numpy(),
+            idx2.cpu().numpy(), cnt2.cpu().numpy(), scores.cpu().numpy().astype(np.float64))
+
+
+def _check_budget(dev, sel):
+    w, s = dev.w, dev.shape
+    scale = 1.0 / math.sqrt(s.head_dim)
+    out, lse, idx, cnt, idx2, cnt2, own = _budget_run(dev, sel)
+    G, tol = s.group, TOL[s.dtype]
+    exact = 0
+    for b in range(s.batch):
+        n = int(w.seq_lens[b])
+        cap = sdref.keep_count(sel.r_kv, n)
+        for g in range(s.num_kv_heads):
+            k = int(cnt[b, g])
+            assert 1 <= k <= cap, f"(b={b}, g={g}) count {k} outside [1, {cap}]"
+            kept = idx[b, g, :k].astype(np.int64)
+            # the list is the exact top-k of the library's own scores at that count
+            np.testing.assert_array_equal(kept, sdref.select_topk(own[b, g, :n], k)[0])
+            assert int(cnt2[b, g]) == k
+            np.testing.assert_array_equal(idx2[b, g, :k], kept)
+            # the count against the oracle's fp64 masses
+            qg = sdref.widen(w.q[b, g * G:(g + 1) * G], s.dtype)
+            Kg = sdref.widen(w.K[b, g, :n], s.dtype)
+            sg = sdref.group_logits(qg, Kg, scale)
+            worst = lambda T: max(sdref.dropped_mass(sg[h], T) for h in range(G))
+            if k < cap:
+                assert worst(kept) <= sel.max_dropped + MARGIN
+            if k > 1:
+                fewer = sdref.select_topk(own[b, g, :n], k - 1)[0]
+                assert worst(fewer) > sel.max_dropped - MARGIN
+            k_or = sdref.mass_budget_count(sg, sg.max(axis=0), sel.max_dropped, cap)
+            sig = sg.max(axis=0)
+            clear = True
+            for kk in (k_or - 1, k_or):
+                if 1 <= kk < n:
+                    top, gap = sdref.select_topk(sig, kk)
+                    clear &= gap > 1e-4 and abs(worst(top) - sel.max_dropped) > MARGIN
+            if clear:
+                assert k == k_or, f"(b={b}, g={g}) count {k} != oracle {k_or}"
+                exact += 1
+            orc = oracle_group(w, b, g, "token", sel.r_kv, scale, kept_override=kept)
+            heads = slice(g * G, (g + 1) * G)
+            e_o = float(np.abs(out[b, heads] - orc.out_sparse).max())
+            e_l = float(np.abs(lse[b, heads] - orc.lse_sparse).max())
+            assert e_o <= tol and e_l <= tol, f"(b={b}, g={g}) out {e_o} lse {e_l} > {tol}"
+    return exact
+
+
+BUDGET_CASES = [
+    ("tiny", R["tiny"], [0.01, 0.1, 0.3]),
+    ("sweep-3k", R["sweep"].with_(seq_len=3000, num_q_heads=8, num_kv_heads=2), [0.02, 0.2]),
+    ("sweep-20k", R["sweep"].with_(seq_len=20000, num_q_heads=8, num_kv_heads=2), [0.05]),
+    ("g8-ragged", R["l70b"].with_(batch=3, seq_len=4000, seq_len_min=1, num_q_heads=16,
+                                  num_kv_heads=2), [0.1]),
+    ("sweep-32k", R["sweep"].with_(seq_len=32768, num_q_heads=8, num_kv_heads=2), [0.1]),
+]
+
+
+@pytest.mark.parametrize("cid,rec,targets", BUDGET_CASES, ids=[c[0] for c in BUDGET_CASES])
+def test_mass_budget_matches_oracle(cid, rec, targets):
+    print(f"[budget] {cid}", flush=True)
+    dev = upload(kvsynth.generate(rec))
+    for t in targets:
+        exact = _check_budget(dev, sd.Selection("mass_budget", 0.5, max_dropped=t))
+        print(f"[budget] {cid} target {t}: {exact} counts equal to the oracle's", flush=True)
+
+
+def test_mass_budget_edges():
+    rec = R["sweep"].with_(seq_len=2000, num_q_heads=8, num_kv_heads=2)
+    dev = upload(kvsynth.generate(rec))
+    s = dev.shape
+    # target 1: one unit; target 0: the cap
+    for t, want in ((1.0, 1), (0.0, sdref.keep_count(0.3, 2000))):
+        out, lse, idx, cnt, *_ = _budget_run(dev, sd.Selection("mass_budget", 0.3, max_dropped=t))
+        assert np.all(cnt == want)
+    # page unit and too many tokens are refused
+    with pytest.raises(sd.SdError):
+        sd.workspace_bytes_sel(s, "page", sd.Selection("mass_budget", 0.3, max_dropped=0.1))
+        ws = sd.alloc_workspace_sel(s, "page", sd.Selection("mass_budget", 0.3, max_dropped=0.1))
+        out = torch.empty((s.batch, s.num_q_heads, s.head_dim), dtype=torch.float32, device="cuda")
+        lse = torch.empty((s.batch, s.num_q_heads), dtype=torch.float32, device="cuda")
+        sd.decode_step_sel(s, dev.q, dev.k, dev.v, dev.bounds, dev.bt, dev.sl, "page",
+                           sd.Selection("mass_budget", 0.3, max_dropped=0.1), out, lse, ws)
+    with pytest.raises(sd.SdError):
+        sd.workspace_bytes_sel(s, "token", sd.Selection("mass_budget", 0.3, max_dropped=1.5))
