@@ -72,6 +72,8 @@ __device__ __forceinline__ float block_sum(BudgetShared& sm, float x) {
   return r;
 }
 
+// VEC: rows of max_seq floats are 16-byte aligned (max_seq % 4 == 0).
+template <bool VEC>
 __global__ __launch_bounds__(kBT) void select_budget_kernel(BudgetArgs a) {
   __shared__ BudgetShared sm;
   const Dims& d = a.d;
@@ -81,9 +83,6 @@ __global__ __launch_bounds__(kBT) void select_budget_kernel(BudgetArgs a) {
   const int64_t bg = (int64_t)b * d.Hkv + g;
   const float* sc = a.scores + bg * a.U_max;
   const float* lg = a.logits + ((int64_t)b * d.Hq + (int64_t)g * G) * d.max_seq;
-  uint32_t key[kBK];
-#pragma unroll
-  for (int i = 0; i < kBK; ++i) key[i] = order_key(sc[min(tid + kBT * i, a.U_max - 1)]);
   const int n = clamp_len(a.seq_lens[b], d.max_seq);
   const int U = min(n, a.U_max);
   const int kcap = min(keep_count_dev(U, a.R_ppm), a.k_max);
@@ -92,36 +91,77 @@ __global__ __launch_bounds__(kBT) void select_budget_kernel(BudgetArgs a) {
     if (tid == 0) a.sel_count[bg] = 0;
     return;
   }
+  // The normaliser and histogram passes take the tokens in groups of four
+  // consecutive ones per thread (thread t, group j: tokens 4 (t + kBT j) ..
+  // +3), read with 16-byte loads when the rows allow it; one CU has to pull
+  // every logit of the group, so bytes in flight per load matter.  Group
+  // starts are clamped to a valid group and masked afterwards, so every load
+  // is issued unconditionally.
+  constexpr int kGroups = kBK / 4;
+  const int last_group = (U - 1) & ~3;
+  auto ld4 = [&](const float* row, int t0) -> float4 {
+    if constexpr (VEC) {
+      return *reinterpret_cast<const float4*>(row + t0);
+    } else {
+      return make_float4(row[min(t0, U - 1)], row[min(t0 + 1, U - 1)], row[min(t0 + 2, U - 1)],
+                         row[min(t0 + 3, U - 1)]);
+    }
+  };
+  auto el = [](const float4& v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; };
   // 1. dense softmax normalisers of the group's heads
-  for (int h = 0; h < G; ++h) {
-    const float* row = lg + (int64_t)h * d.max_seq;
-    float mx = -INFINITY;
-#pragma unroll 8
-    for (int i = 0; i < kBK; ++i) {
-      const int t = tid + kBT * i;
-      if (t < U) mx = fmaxf(mx, row[t]);
+  float acc[kBMaxG];
+  for (int pass = 0; pass < 2; ++pass) {  // 0: max, 1: sum of exponentials
+#pragma unroll
+    for (int h = 0; h < kBMaxG; ++h) acc[h] = pass == 0 ? -INFINITY : 0.f;
+    for (int j = 0; j < kGroups; j += 2) {  // two groups' loads in flight
+#pragma unroll
+      for (int h = 0; h < kBMaxG; ++h) {
+        if (h >= G) break;
+        float4 v[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+          v[q] = ld4(lg + (int64_t)h * d.max_seq, min(4 * (tid + kBT * (j + q)), last_group));
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int t0 = 4 * (tid + kBT * (j + q));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (t0 + i >= U) continue;
+            acc[h] = pass == 0 ? fmaxf(acc[h], el(v[q], i))
+                               : acc[h] + exp2f((el(v[q], i) - sm.m[h]) * kLog2e);
+          }
+        }
+      }
     }
-    mx = block_max(sm, mx);
-    float z = 0.f;
-#pragma unroll 8
-    for (int i = 0; i < kBK; ++i) {
-      const int t = tid + kBT * i;
-      if (t < U) z += exp2f((row[t] - mx) * kLog2e);
+    for (int h = 0; h < G; ++h) {
+      const float r = pass == 0 ? block_max(sm, acc[h]) : block_sum(sm, acc[h]);
+      if (tid == 0) {
+        if (pass == 0) sm.m[h] = r;
+        else sm.invz[h] = 1.f / r;
+      }
     }
-    z = block_sum(sm, z);
-    if (tid == 0) { sm.m[h] = mx; sm.invz[h] = 1.f / z; }
+    __syncthreads();
   }
   // the target as a fixed-point mass
   const u64 target = (u64)(fminf(fmaxf(a.max_dropped, 0.f), 1.f) * kFix);
-  auto weight = [&](int h, int t) -> u64 {
-    const float w = exp2f((lg[(int64_t)h * d.max_seq + t] - sm.m[h]) * kLog2e) * sm.invz[h];
+  auto weight_of = [&](int h, float s) -> u64 {
+    const float w = exp2f((s - sm.m[h]) * kLog2e) * sm.invz[h];
     return (u64)(fminf(w, 1.f) * kFix);
   };
+  auto weight = [&](int h, int t) -> u64 { return weight_of(h, lg[(int64_t)h * d.max_seq + t]); };
   // 2. radix search with mass histograms
   uint32_t mn = 0xFFFFFFFFu, mxk = 0u;
+  for (int j = 0; j < kGroups; ++j) {
+    const int t0 = 4 * (tid + kBT * j);
+    const float4 v = ld4(sc, min(t0, last_group));
 #pragma unroll
-  for (int i = 0; i < kBK; ++i)
-    if (tid + kBT * i < U) { mn = min(mn, key[i]); mxk = max(mxk, key[i]); }
+    for (int i = 0; i < 4; ++i) {
+      if (t0 + i >= U) continue;
+      const uint32_t k = order_key(el(v, i));
+      mn = min(mn, k);
+      mxk = max(mxk, k);
+    }
+  }
   block_minmax<kBW>(sm.rs, mn, mxk);
   if (tid == 0) {
     sm.lo = sm.rs.lo;
@@ -141,12 +181,27 @@ __global__ __launch_bounds__(kBT) void select_budget_kernel(BudgetArgs a) {
       for (int h = 0; h < kBMaxG; ++h) sm.mass[h][i] = 0ull;
     }
     __syncthreads();
-    for (int i = 0; i < kBK; ++i) {
-      const int t = tid + kBT * i;
-      if (t < U && key[i] >= lo && key[i] <= hi) {
-        const uint32_t bin = (key[i] - lo) >> shift;
-        atomicAdd(&sm.cnt[bin], 1u);
-        for (int h = 0; h < G; ++h) atomicAdd(&sm.mass[h][bin], weight(h, t));
+    for (int j = 0; j < kGroups; ++j) {
+      const int t0 = 4 * (tid + kBT * j), tc = min(t0, last_group);
+      const float4 sv = ld4(sc, tc);
+      uint32_t cm = 0u, bin[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t k = order_key(el(sv, i));
+        bin[i] = (k - lo) >> shift;
+        if (t0 + i < U && k >= lo && k <= hi) cm |= 1u << i;
+      }
+      if (cm == 0u) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if ((cm >> i) & 1u) atomicAdd(&sm.cnt[bin[i]], 1u);
+#pragma unroll
+      for (int h = 0; h < kBMaxG; ++h) {
+        if (h >= G) break;
+        const float4 v = ld4(lg + (int64_t)h * d.max_seq, tc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if ((cm >> i) & 1u) atomicAdd(&sm.mass[h][bin[i]], weight_of(h, el(v, i)));
       }
     }
     __syncthreads();
@@ -230,7 +285,8 @@ __global__ __launch_bounds__(kBT) void select_budget_kernel(BudgetArgs a) {
     const uint32_t T = sm.lo;
 #pragma unroll
     for (int i = 0; i < kBK; ++i) {
-      const uint64_t tie = __ballot(tid + kBT * i < U && key[i] == T);
+      const int t = tid + kBT * i;
+      const uint64_t tie = __ballot(t < U && order_key(sc[min(t, U - 1)]) == T);
       if (lane == 0) sm.ks.tie[i * kBW + wave] = tie;
     }
     __syncthreads();
@@ -278,6 +334,9 @@ __global__ __launch_bounds__(kBT) void select_budget_kernel(BudgetArgs a) {
     for (int i = tid; i < U; i += kBT) out[i] = i;
     return;
   }
+  uint32_t key[kBK];
+#pragma unroll
+  for (int i = 0; i < kBK; ++i) key[i] = order_key(sc[min(tid + kBT * i, a.U_max - 1)]);
   topk_bitmap<kBK, kBW>(sm.rs, sm.ks, key, U, k);
   emit_kept<kBK, kBW>(sm.ks.mask, sm.ks.base, 0u, (uint32_t)k,
                       [&](int pos, int unit_id) { out[pos] = unit_id; });
@@ -288,7 +347,10 @@ __global__ __launch_bounds__(kBT) void select_budget_kernel(BudgetArgs a) {
 hipError_t launch_select_budget(const BudgetArgs& a, hipStream_t st) {
   if (a.U_max < 1 || a.U_max > kMaxSelectOne || a.d.G > kBMaxG || a.k_max < 1)
     return hipErrorInvalidValue;
-  select_budget_kernel<<<dim3(a.d.Hkv, a.d.B), kBT, 0, st>>>(a);
+  if ((a.d.max_seq & 3) == 0 && (a.U_max & 3) == 0)
+    select_budget_kernel<true><<<dim3(a.d.Hkv, a.d.B), kBT, 0, st>>>(a);
+  else
+    select_budget_kernel<false><<<dim3(a.d.Hkv, a.d.B), kBT, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -288,3 +288,47 @@ def test_mass_budget_edges():
                            sd.Selection("mass_budget", 0.3, max_dropped=0.1), out, lse, ws)
     with pytest.raises(sd.SdError):
         sd.workspace_bytes_sel(s, "token", sd.Selection("mass_budget", 0.3, max_dropped=1.5))
+
+
+@pytest.mark.parametrize("max_seq,tied", [(1001, False), (1001, True), (4096, True)])
+def test_mass_budget_on_given_logits(max_seq, tied):
+    """sd_select_units on hand-made logits (rows of any length, heavy ties in
+    the group score): the count against the oracle's rule on the same fp32
+    values, and the list the top-k at that count."""
+    rng = np.random.default_rng(max_seq + tied)
+    B, Hq, Hkv, G = 2, 8, 2, 4
+    lens = np.array([max_seq, max_seq // 2 + 3], dtype=np.int32)
+    lg = (rng.standard_normal((B, Hq, max_seq)) * 1.5).astype(np.float32)
+    if tied:
+        lg = np.round(lg * 2.0) / 2.0
+    sig = lg.reshape(B, Hkv, G, max_seq).max(axis=2).astype(np.float32)
+    P = 16
+    s = sd.Shape(B, Hq, Hkv, 64, P, -(-max_seq // P), max_seq, "f32", 64)
+    for t in (0.02, 0.2):
+        sel = sd.Selection("mass_budget", 0.6, max_dropped=t)
+        cap_row = sd.selection_capacity(sel, max_seq)
+        idx = torch.full((B, Hkv, cap_row), -7, dtype=torch.int32, device="cuda")
+        cnt = torch.full((B, Hkv), -7, dtype=torch.int32, device="cuda")
+        ws = sd.alloc_workspace_sel(s, "token", sel)
+        sd.select_units(s, "token", torch.from_numpy(lens).cuda(), torch.from_numpy(sig).cuda(),
+                        sel, idx, cnt, ws=ws, token_logits=torch.from_numpy(lg).cuda())
+        torch.cuda.synchronize()
+        idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+        for b in range(B):
+            n = int(lens[b])
+            cap = sdref.keep_count(0.6, n)
+            for g in range(Hkv):
+                sg = lg[b, g * G:(g + 1) * G, :n].astype(np.float64)
+                sgm = sig[b, g, :n].astype(np.float64)
+                k = int(cnt[b, g])
+                np.testing.assert_array_equal(idx[b, g, :k], sdref.select_topk(sgm, k)[0])
+                worst = lambda kk: max(sdref.dropped_mass(sg[h], sdref.select_topk(sgm, kk)[0])
+                                       for h in range(G))
+                assert 1 <= k <= cap
+                if k < cap:
+                    assert worst(k) <= t + MARGIN
+                if k > 1:
+                    assert worst(k - 1) > t - MARGIN
+                k_or = sdref.mass_budget_count(sg, sgm, t, cap)
+                if all(abs(worst(kk) - t) > MARGIN for kk in (k_or - 1, k_or) if 1 <= kk < n):
+                    assert k == k_or
