@@ -42,13 +42,22 @@ __device__ __forceinline__ int keep_count_dev(int U, int R_ppm) {
   return (int)(kk < 1 ? 1 : (kk > U ? U : kk));
 }
 
-// Bins 256 .. 319 are per-lane sinks: a key outside the interval adds 0 to
-// its lane's sink instead of branching, so no single counter takes every
-// lane's add (a divergent branch per key would serialise on gfx950).
-constexpr int kHistWords = 256 + 64;
+// With many keys per thread the 256 bin counters exist in kHistCopies
+// interleaved copies: lane l adds to copy l % kHistCopies, so lanes of one
+// wave whose keys share a bin mostly hit different words (LDS atomics to one
+// word serialise, and score distributions crowd a few bins).  Rows are 257
+// words apart so that the copies of a bin sit in different banks.  Word 256
+// of each row is that copy's sink: a key outside the interval adds 0 there
+// instead of branching.  The copies are summed into `total` before the bin
+// is chosen; all counts are integers, so the result does not depend on the
+// order of the adds.  With few keys per thread one copy is used (row 0): the
+// extra clearing and summing would cost more than the collisions.
+constexpr int kHistCopies = 16;
+constexpr int kHistRow = 257;
 
 struct RadixState {
-  uint32_t hist[kHistWords];
+  uint32_t hist[kHistCopies * kHistRow];
+  uint32_t total[256];
   uint32_t wa[16], wb[16];
   uint32_t lo, hi, need, whole, shift;
 };
@@ -80,13 +89,14 @@ __device__ __forceinline__ uint32_t bin_shift(uint32_t lo, uint32_t hi) {
 }
 
 // After a histogram pass (wave 0): find the bin holding the need-th largest
-// key of [lo, hi], lanes covering bins from the top down, and narrow to it.
-__device__ __forceinline__ void find_bin(RadixState& st) {
+// key of [lo, hi] from the 256 counts, lanes covering bins from the top
+// down, and narrow to it.
+__device__ __forceinline__ void find_bin(RadixState& st, const uint32_t* counts) {
   const int lane = threadIdx.x & 63;
   const uint32_t need = st.need, lo = st.lo, hi = st.hi, shift = st.shift;
   uint32_t c[4], tot = 0u;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) { c[i] = st.hist[255 - 4 * lane - i]; tot += c[i]; }
+  for (int i = 0; i < 4; ++i) { c[i] = counts[255 - 4 * lane - i]; tot += c[i]; }
   uint32_t run = wave_scan_dpp(tot) - tot;  // keys in higher bins
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -256,16 +266,29 @@ __device__ __forceinline__ void radix_search(RadixState& st, const uint32_t (&ke
   bool whole = false;
   while (!whole && lo != hi) {
     const uint32_t shift = bin_shift(lo, hi);
-    if (tid < 256) st.hist[tid] = 0u;
+    constexpr int C = KPT >= 16 ? kHistCopies : 1;
+    for (int i = tid; i < C * kHistRow; i += NT) st.hist[i] = 0u;
     if (tid == 0) st.shift = shift;
     __syncthreads();
+    uint32_t* row = st.hist + (C > 1 ? (tid % C) * kHistRow : 0);
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const bool in = tid + NT * i < U && key[i] >= lo && key[i] <= hi;
-      atomicAdd(&st.hist[in ? (key[i] - lo) >> shift : 256u + (tid & 63)], in ? 1u : 0u);
+      // one copy: a per-lane sink past the row keeps the zero adds apart
+      atomicAdd(&row[in ? (key[i] - lo) >> shift : (C > 1 ? 256u : 256u + (tid & 63))],
+                in ? 1u : 0u);
     }
     __syncthreads();
-    if (tid < 64) find_bin(st);
+    if constexpr (C > 1) {
+      for (int b = tid; b < 256; b += NT) {
+        uint32_t t = 0u;
+#pragma unroll
+        for (int c = 0; c < C; ++c) t += st.hist[c * kHistRow + b];
+        st.total[b] = t;
+      }
+      __syncthreads();
+    }
+    if (tid < 64) find_bin(st, C > 1 ? st.total : st.hist);
     __syncthreads();
     lo = st.lo;
     hi = st.hi;
