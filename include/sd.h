@@ -262,7 +262,8 @@ typedef struct sd_selection {
   int32_t kind;         /* sd_selection_kind */
   int32_t init_units;   /* >= 0; SD_SEL_INIT_LOCAL_TOPK only */
   int32_t local_units;  /* >= 0; SD_SEL_INIT_LOCAL_TOPK only */
-  double r_kv;          /* keep ratio of the top-k (window; the budget's cap) */
+  double r_kv;          /* keep ratio of the top-k (window; the budget's cap,
+                           where >= 1 means no cap rather than dense) */
   double max_dropped;   /* in [0, 1]; SD_SEL_MASS_BUDGET only */
 } sd_selection;
 

@@ -476,7 +476,7 @@ sd_status decode_impl(const sdkv::Dims& d, const void* q, const void* k_pages,
   const int k_max = static_cast<int>(capacity(sel, U));
   sd_status st;
   int S = 0;
-  if (sel.r >= 1.0) {  // every unit: dense
+  if (sel.r >= 1.0 && sel.kind != SD_SEL_MASS_BUDGET) {  // every unit: dense
     if ((st = do_partials(d, q, k_pages, v_pages, block_table, seq_lens, unit, nullptr, nullptr,
                           0, nullptr, ws, s, nullptr, -1, nullptr, nullptr, &S)) != SD_OK)
       return st;

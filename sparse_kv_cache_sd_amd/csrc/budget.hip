@@ -34,11 +34,21 @@ constexpr float kFix = 1099511627776.0f;  // 2^40
 
 typedef unsigned long long u64;
 
+// The histogram passes add into kMC interleaved copies (copy = lane % kMC,
+// padded apart so that the copies of a counter sit in different banks), then
+// sum them: LDS atomics to one word serialise, and the scores crowd a few
+// bins.
+constexpr int kMC = 4;
+constexpr int kMassStride = kBMaxG * kBBins + 1;  // u64 per copy
+constexpr int kCntStride = kBBins + 1;            // words per copy
+
 struct BudgetShared {
   RadixState rs;
   KeptScratch<kBK, kBW> ks;
-  u64 mass[kBMaxG][kBBins];
+  u64 mass[kBMaxG][kBBins];  // summed over the copies
   uint32_t cnt[kBBins];
+  u64 massc[kMC * kMassStride];
+  uint32_t cntc[kMC * kCntStride];
   float red[kBW];
   float m[kBMaxG], invz[kBMaxG];
   u64 tot[kBMaxG];    // all units' mass per head
@@ -175,12 +185,11 @@ __global__ __launch_bounds__(kBT) void select_budget_kernel(BudgetArgs a) {
   while (sm.kstar == 0 && sm.lo != sm.hi) {
     const uint32_t lo = sm.lo, hi = sm.hi;
     const uint32_t shift = bin_shift(lo, hi);
-    for (int i = tid; i < kBBins; i += kBT) {
-      sm.cnt[i] = 0u;
-#pragma unroll
-      for (int h = 0; h < kBMaxG; ++h) sm.mass[h][i] = 0ull;
-    }
+    for (int i = tid; i < kMC * kMassStride; i += kBT) sm.massc[i] = 0ull;
+    for (int i = tid; i < kMC * kCntStride; i += kBT) sm.cntc[i] = 0u;
     __syncthreads();
+    u64* mrow = sm.massc + (lane % kMC) * kMassStride;
+    uint32_t* crow = sm.cntc + (lane % kMC) * kCntStride;
     for (int j = 0; j < kGroups; ++j) {
       const int t0 = 4 * (tid + kBT * j), tc = min(t0, last_group);
       const float4 sv = ld4(sc, tc);
@@ -194,15 +203,28 @@ __global__ __launch_bounds__(kBT) void select_budget_kernel(BudgetArgs a) {
       if (cm == 0u) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if ((cm >> i) & 1u) atomicAdd(&sm.cnt[bin[i]], 1u);
+        if ((cm >> i) & 1u) atomicAdd(&crow[bin[i]], 1u);
 #pragma unroll
       for (int h = 0; h < kBMaxG; ++h) {
         if (h >= G) break;
         const float4 v = ld4(lg + (int64_t)h * d.max_seq, tc);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if ((cm >> i) & 1u) atomicAdd(&sm.mass[h][bin[i]], weight_of(h, el(v, i)));
+          if ((cm >> i) & 1u) atomicAdd(&mrow[h * kBBins + bin[i]], weight_of(h, el(v, i)));
       }
+    }
+    __syncthreads();
+    for (int i = tid; i < kBBins; i += kBT) {
+      uint32_t c = 0u;
+#pragma unroll
+      for (int q = 0; q < kMC; ++q) c += sm.cntc[q * kCntStride + i];
+      sm.cnt[i] = c;
+    }
+    for (int i = tid; i < kBMaxG * kBBins; i += kBT) {
+      u64 m = 0ull;
+#pragma unroll
+      for (int q = 0; q < kMC; ++q) m += sm.massc[q * kMassStride + i];
+      sm.mass[i / kBBins][i % kBBins] = m;
     }
     __syncthreads();
     if (first) {  // every unit is in the first interval: the totals

@@ -278,6 +278,9 @@ def test_mass_budget_edges():
     for t, want in ((1.0, 1), (0.0, sdref.keep_count(0.3, 2000))):
         out, lse, idx, cnt, *_ = _budget_run(dev, sd.Selection("mass_budget", 0.3, max_dropped=t))
         assert np.all(cnt == want)
+    # without a cap (r_kv >= 1) the budget still decides the count
+    out, lse, idx, cnt, *_ = _budget_run(dev, sd.Selection("mass_budget", 1.0, max_dropped=0.2))
+    assert np.all((cnt >= 1) & (cnt < 2000))
     # page unit and too many tokens are refused
     with pytest.raises(sd.SdError):
         sd.workspace_bytes_sel(s, "page", sd.Selection("mass_budget", 0.3, max_dropped=0.1))
