@@ -181,6 +181,42 @@ def page_scores(q_group: np.ndarray, kmin: np.ndarray, kmax: np.ndarray,
     return per_head.max(axis=0)
 
 
+# Compressed-key block scoring ([SparDA] Section 3.1: a parameter-free
+# selector mean-pools the keys into overlapping compressed representations,
+# sums the per-head relevance over the GQA group and max-pools it to the
+# block score; Appendix C: kernel 32, stride 16, 64-token blocks).
+COMPRESS_KERNEL = 32
+COMPRESS_STRIDE = 16
+
+
+def compressed_keys(K: np.ndarray) -> np.ndarray:
+    """Window j of one KV head: the mean of the valid keys 16 j .. 16 j + 31
+    (fewer at the end of the sequence), for j < ceil(n / 16).  Returns [J, d]."""
+    K = np.asarray(K, np.float64)
+    n = K.shape[0]
+    J = -(-n // COMPRESS_STRIDE)
+    out = np.empty((J, K.shape[1]))
+    for j in range(J):
+        out[j] = K[j * COMPRESS_STRIDE: min(j * COMPRESS_STRIDE + COMPRESS_KERNEL, n)].mean(axis=0)
+    return out
+
+
+def compressed_page_scores(q_group: np.ndarray, ckeys: np.ndarray, page_size: int,
+                           scale: float) -> np.ndarray:
+    """Page score from the compressed keys, for one KV head: the relevance of
+    window j is the sum over the group's heads of scale * <q_h, c_j>, and page
+    u (tokens u P .. u P + P - 1) scores the max over the windows that start
+    inside it, j = u P / 16 .. (u + 1) P / 16 - 1 (j < J).  A 64-token page
+    pools four windows; a 16-token page takes the one window that starts on
+    it (covering it and the next page)."""
+    q_group = np.asarray(q_group, np.float64)
+    rel = scale * (ckeys @ q_group.T).sum(axis=1)          # [J]
+    J = rel.shape[0]
+    per = page_size // COMPRESS_STRIDE
+    U = -(-J // per)
+    return np.array([rel[u * per: min((u + 1) * per, J)].max() for u in range(U)])
+
+
 def token_scores(s_group: np.ndarray) -> np.ndarray:
     """Step 3, token unit, for one KV head: sigma[t] = max over the G heads of s[h, t]."""
     return np.asarray(s_group, np.float64).max(axis=0)
@@ -372,15 +408,17 @@ class GroupResult:
 
 
 def group_step(q_group, K, V, *, unit: str, page_size: int, r_kv: float,
-               scale: float, kept_override=None, selection: Selection | None = None
-               ) -> GroupResult:
+               scale: float, kept_override=None, selection: Selection | None = None,
+               scorer: str = "bounds") -> GroupResult:
     """Steps 1-7 for one sequence and one KV head.
 
     q_group [G, d], K [n, d], V [n, d]: fp64 values of the valid tokens.
     ``kept_override`` (ascending unit ids) replaces step 5's set, so that an
     output can be recomputed on another selection of the same size.
     ``selection`` (kind other than "topk") replaces step 5's set by a
-    structured one; k and gap still describe the step-5 top-k.
+    structured one; k and gap still describe the step-5 top-k.  ``scorer``
+    "compressed" scores pages from the compressed keys instead of the page
+    bounds (page unit).
     """
     K = np.asarray(K, np.float64)
     V = np.asarray(V, np.float64)
@@ -388,7 +426,9 @@ def group_step(q_group, K, V, *, unit: str, page_size: int, r_kv: float,
     s = group_logits(q_group, K, scale)
     G = s.shape[0]
     kmin = kmax = None
-    if unit == "page":
+    if unit == "page" and scorer == "compressed":
+        sigma = compressed_page_scores(q_group, compressed_keys(K), page_size, scale)
+    elif unit == "page":
         kmin, kmax = page_bounds(K, page_size)
         sigma = page_scores(q_group, kmin, kmax, scale)
     elif unit == "token":
@@ -418,7 +458,7 @@ def group_step(q_group, K, V, *, unit: str, page_size: int, r_kv: float,
 
 def decode_step(q, K, V, seq_lens, *, dtype: str, unit: str, page_size: int,
                 r_kv: float, scale: float | None = None, groups=None,
-                selection: Selection | None = None):
+                selection: Selection | None = None, scorer: str = "bounds"):
     """Steps 1-7 for a batch.
 
     q: [B, H_q, d]; K, V: [B, H_kv, n_max, d] stored values (float32, or
@@ -440,5 +480,5 @@ def decode_step(q, K, V, seq_lens, *, dtype: str, unit: str, page_size: int,
         Kg = widen(K[b, g, :n], dtype)
         Vg = widen(V[b, g, :n], dtype)
         res[(b, g)] = group_step(qg, Kg, Vg, unit=unit, page_size=page_size,
-                                 r_kv=r_kv, scale=scale, selection=selection)
+                                 r_kv=r_kv, scale=scale, selection=selection, scorer=scorer)
     return res
