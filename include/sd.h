@@ -258,14 +258,42 @@ typedef enum sd_selection_kind {
   SD_SEL_MASS_BUDGET = 3
 } sd_selection_kind;
 
+typedef enum sd_scorer {
+  SD_SCORER_BOUNDS = 0,     /* page bounds (sd_update_page_bounds) */
+  SD_SCORER_COMPRESSED = 1  /* compressed keys (sd_update_compressed_keys) */
+} sd_scorer;
+
 typedef struct sd_selection {
   int32_t kind;         /* sd_selection_kind */
   int32_t init_units;   /* >= 0; SD_SEL_INIT_LOCAL_TOPK only */
   int32_t local_units;  /* >= 0; SD_SEL_INIT_LOCAL_TOPK only */
+  int32_t scorer;       /* sd_scorer, page unit (token unit scores q.K) */
   double r_kv;          /* keep ratio of the top-k (window; the budget's cap,
                            where >= 1 means no cap rather than dense) */
   double max_dropped;   /* in [0, 1]; SD_SEL_MASS_BUDGET only */
 } sd_selection;
+
+/* ---- Compressed-key page scoring --------------------------------------
+ * A second page scorer ([SparDA] Section 3.1: a parameter-free selector
+ * mean-pools the keys into overlapping compressed representations, sums the
+ * per-head relevance over the GQA group and max-pools it to the block score;
+ * Appendix C: kernel 32, stride 16).  Layout:
+ *   compressed_keys  [B][H_kv][W][d] fp32, W = ceil(max_seq_len / 16): window
+ *                    j is the mean of the valid keys 16 j .. 16 j + 31 (fewer
+ *                    at the end of a sequence; pages whose block-table entry
+ *                    is invalid are left out of the mean).
+ * Setup (not part of the decode step): sd_update_compressed_keys writes the
+ * windows j < ceil(n_b / 16) of every sequence from the K pool.
+ * Scoring: unit_scores[b][g][u] = max over the windows j that start in page
+ * u (j = u P / 16 .. (u + 1) P / 16 - 1, j < ceil(n_b / 16)) of
+ * scale * sum over the G heads h of group g of q[b][h] . c_j, for
+ * u < ceil(n_b / P); page unit, P = 16 or 64. */
+SD_API sd_status sd_update_compressed_keys(const sd_shape* shape, const void* k_pages,
+                                           const int32_t* block_table, const int32_t* seq_lens,
+                                           float* compressed_keys, void* stream);
+SD_API sd_status sd_score_compressed(const sd_shape* shape, const void* q,
+                                     const float* compressed_keys, const int32_t* seq_lens,
+                                     float* unit_scores, void* stream);
 
 /* Row length of a kept list for at most num_units units (host, pure); -1 on
  * an invalid selection or num_units < 1. */
@@ -294,7 +322,10 @@ SD_API sd_status sd_select_units(const sd_shape* shape, int32_t unit, const int3
  * page_bounds not read).  SD_SEL_INIT_LOCAL_TOPK scores, selects the union
  * and attends it; in page unit with bf16 data and at most 16384 pages per
  * sequence the attention blocks select it themselves, as in
- * sd_select_attend.  SD_SEL_MASS_BUDGET scores the tokens, selects with the
+ * sd_select_attend.  With sel->scorer == SD_SCORER_COMPRESSED (page unit)
+ * page_bounds must point to the compressed keys ([B][H_kv][W][d] fp32) and
+ * the pages are scored by sd_score_compressed.  SD_SEL_MASS_BUDGET scores the
+ * tokens, selects with the
  * budget and attends over the stored logits.  sel_idx / sel_count may be
  * NULL; when given they receive the kept lists (rows of
  * sd_selection_capacity(sel, U_max)).

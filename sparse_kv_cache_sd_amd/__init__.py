@@ -19,16 +19,19 @@ from ._lib import (  # noqa: F401
     attend_partials,
     attend_splitk,
     bounds_shape,
+    compressed_keys_shape,
     decode_step,
     decode_step_sel,
     keep_count,
     lib,
     merge_splits,
+    score_compressed,
     score_pages,
     select_attend,
     select_topk,
     select_units,
     selection_capacity,
+    update_compressed_keys,
     update_page_bounds,
     workspace_bytes,
     workspace_bytes_sel,

@@ -52,6 +52,7 @@ class SdSelection(ctypes.Structure):
         ("kind", ctypes.c_int32),
         ("init_units", ctypes.c_int32),
         ("local_units", ctypes.c_int32),
+        ("scorer", ctypes.c_int32),
         ("r_kv", ctypes.c_double),
         ("max_dropped", ctypes.c_double),
     ]
@@ -60,6 +61,7 @@ class SdSelection(ctypes.Structure):
 SEL_TOPK, SEL_WINDOW, SEL_INIT_LOCAL_TOPK, SEL_MASS_BUDGET = 0, 1, 2, 3
 _SEL_KINDS = {"topk": SEL_TOPK, "window": SEL_WINDOW, "init_local_topk": SEL_INIT_LOCAL_TOPK,
               "mass_budget": SEL_MASS_BUDGET}
+_SCORERS = {"bounds": 0, "compressed": 1}
 
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
@@ -90,6 +92,8 @@ _SIGS = {
                                        _P, ctypes.c_size_t, _P]),
     "sd_decode_step_sel": (ctypes.c_int, [ctypes.POINTER(SdShape), _P, _P, _P, _P, _P, _P, _I32,
                                           _SELP, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "sd_update_compressed_keys": (ctypes.c_int, [ctypes.POINTER(SdShape), _P, _P, _P, _P, _P]),
+    "sd_score_compressed": (ctypes.c_int, [ctypes.POINTER(SdShape), _P, _P, _P, _P, _P]),
     "sd_last_error": (ctypes.c_char_p, []),
 }
 EXPORTS = tuple(_SIGS)
@@ -406,12 +410,15 @@ class Selection:
     init_units: int = 0
     local_units: int = 0
     max_dropped: float = 0.0
+    scorer: str = "bounds"   # page unit: "bounds" or "compressed"
 
     def c(self) -> SdSelection:
         if self.kind not in _SEL_KINDS:
             raise ValueError(f"unknown selection kind {self.kind!r}")
+        if self.scorer not in _SCORERS:
+            raise ValueError(f"unknown scorer {self.scorer!r}")
         return SdSelection(_SEL_KINDS[self.kind], int(self.init_units), int(self.local_units),
-                           float(self.r_kv), float(self.max_dropped))
+                           _SCORERS[self.scorer], float(self.r_kv), float(self.max_dropped))
 
 
 def selection_capacity(sel: Selection, num_units: int) -> int:
@@ -452,18 +459,53 @@ def select_units(shape: Shape, unit, seq_lens, unit_scores, sel: Selection, sel_
         wp, wn, _stream(stream)))
 
 
+def compressed_keys_shape(shape: Shape):
+    """Shape of the compressed-key tensor (fp32): [B, H_kv, ceil(max_seq_len / 16), d]."""
+    return (shape.batch, shape.num_kv_heads, -(-shape.max_seq_len // 16), shape.head_dim)
+
+
+def update_compressed_keys(shape: Shape, k_pages, block_table, seq_lens, compressed_keys,
+                           stream=None):
+    s = shape
+    _check(lib().sd_update_compressed_keys(
+        ctypes.byref(s.c()),
+        _dev(k_pages, "k_pages", s.torch_dtype, _kv_shape(s)),
+        _dev(block_table, "block_table", torch.int32, (s.batch, s.max_pages_per_seq)),
+        _dev(seq_lens, "seq_lens", torch.int32, (s.batch,)),
+        _dev(compressed_keys, "compressed_keys", torch.float32, compressed_keys_shape(s)),
+        _stream(stream)))
+
+
+def score_compressed(shape: Shape, q, compressed_keys, seq_lens, unit_scores, stream=None):
+    s = shape
+    _check(lib().sd_score_compressed(
+        ctypes.byref(s.c()),
+        _dev(q, "q", s.torch_dtype, (s.batch, s.num_q_heads, s.head_dim)),
+        _dev(compressed_keys, "compressed_keys", torch.float32, compressed_keys_shape(s)),
+        _dev(seq_lens, "seq_lens", torch.int32, (s.batch,)),
+        _dev(unit_scores, "unit_scores", torch.float32,
+             (s.batch, s.num_kv_heads, s.max_pages_per_seq)),
+        _stream(stream)))
+
+
 def decode_step_sel(shape: Shape, q, k_pages, v_pages, page_bounds, block_table, seq_lens, unit,
                     sel: Selection, out, lse, ws, sel_idx=None, sel_count=None, stream=None):
+    """page_bounds: the page bounds, or with sel.scorer == "compressed" the
+    compressed keys."""
     s, u = shape, _unit(unit)
     umax = s.max_pages_per_seq if u == UNIT_PAGE else s.max_seq_len
     cap = selection_capacity(sel, umax)
     wp, wn = _ws(ws, 1)
+    stats = (_dev(page_bounds, "compressed_keys", torch.float32, compressed_keys_shape(s),
+                  optional=True)
+             if sel.scorer == "compressed" else
+             _dev(page_bounds, "page_bounds", s.torch_dtype, _bounds_shape(s), optional=True))
     _check(lib().sd_decode_step_sel(
         ctypes.byref(s.c()),
         _dev(q, "q", s.torch_dtype, (s.batch, s.num_q_heads, s.head_dim)),
         _dev(k_pages, "k_pages", s.torch_dtype, _kv_shape(s)),
         _dev(v_pages, "v_pages", s.torch_dtype, _kv_shape(s)),
-        _dev(page_bounds, "page_bounds", s.torch_dtype, _bounds_shape(s), optional=True),
+        stats,
         _dev(block_table, "block_table", torch.int32, (s.batch, s.max_pages_per_seq)),
         _dev(seq_lens, "seq_lens", torch.int32, (s.batch,)),
         u, ctypes.byref(sel.c()),

@@ -117,9 +117,10 @@ struct Sel {
   double r;
   int init, local;  // SD_SEL_INIT_LOCAL_TOPK only (else 0)
   double dmax;      // SD_SEL_MASS_BUDGET only
+  int scorer = SD_SCORER_BOUNDS;
 };
 
-Sel topk_sel(double r) { return Sel{SD_SEL_TOPK, r, 0, 0, 0.0}; }
+Sel topk_sel(double r) { return Sel{SD_SEL_TOPK, r, 0, 0, 0.0, SD_SCORER_BOUNDS}; }
 
 sd_status check_selection(const sd_selection* s, Sel* out) {
   if (!s) return fail(SD_E_NULL, "sel is NULL");
@@ -134,8 +135,10 @@ sd_status check_selection(const sd_selection* s, Sel* out) {
   if (s->init_units < 0 || s->local_units < 0)
     return fail(SD_E_SHAPE, "init_units and local_units must be >= 0");
   const bool u = s->kind == SD_SEL_INIT_LOCAL_TOPK;
+  if (s->scorer != SD_SCORER_BOUNDS && s->scorer != SD_SCORER_COMPRESSED)
+    return fail(SD_E_SHAPE, "unknown scorer %d", s->scorer);
   *out = Sel{s->kind, s->r_kv, u ? s->init_units : 0, u ? s->local_units : 0,
-              s->kind == SD_SEL_MASS_BUDGET ? s->max_dropped : 0.0};
+              s->kind == SD_SEL_MASS_BUDGET ? s->max_dropped : 0.0, s->scorer};
   return SD_OK;
 }
 
@@ -284,6 +287,18 @@ sd_status do_score(const sdkv::Dims& d, const void* q, const void* k_pages, cons
                    hipStream_t st, uint32_t* score_mm = nullptr) {
   sdkv::ScoreArgs a{d, unit, q, k_pages, bounds, bt, sl, scores, logits, score_mm};
   return device_status(sdkv::launch_score(a, st), "score kernel launch");
+}
+
+sd_status do_score_compressed(const sdkv::Dims& d, const void* q, const float* ckeys,
+                              const int32_t* sl, float* scores, hipStream_t st) {
+  sdkv::CompressArgs a{};
+  a.d = d;
+  a.q = q;
+  a.ckeys = const_cast<float*>(ckeys);
+  a.seq_lens = sl;
+  a.max_windows = sdkv::compressed_windows(d);
+  a.unit_scores = scores;
+  return device_status(sdkv::launch_score_compressed(a, st), "compressed scoring kernel launch");
 }
 
 // msel_ws: select_ws_bytes(d, unit) bytes (unused up to kMaxSelectOne units);
@@ -500,9 +515,11 @@ sd_status decode_impl(const sdkv::Dims& d, const void* q, const void* k_pages,
   uint32_t* smm = unit == SD_UNIT_TOKEN && multi_select(d, unit)
                       ? reinterpret_cast<uint32_t*>(at(ws, L.score_mm))
                       : nullptr;
-  if ((st = do_score(d, q, k_pages, page_bounds, block_table, seq_lens, unit, scores, logits,
-                     s, smm)) != SD_OK)
-    return st;
+  if (unit == SD_UNIT_PAGE && sel.scorer == SD_SCORER_COMPRESSED)
+    st = do_score_compressed(d, q, static_cast<const float*>(page_bounds), seq_lens, scores, s);
+  else
+    st = do_score(d, q, k_pages, page_bounds, block_table, seq_lens, unit, scores, logits, s, smm);
+  if (st != SD_OK) return st;
   if (unit == SD_UNIT_PAGE)
     return do_select_attend(d, q, k_pages, v_pages, block_table, seq_lens, scores, sel, out, lse,
                             sel_idx, sel_count, ws, s);
@@ -729,6 +746,40 @@ sd_status sd_decode_step(const sd_shape* shape, const void* q, const void* k_pag
   if ((st = decode_impl(d, q, k_pages, v_pages, page_bounds, block_table, seq_lens, unit,
                         topk_sel(r_kv), out, lse, sel_idx, sel_count, ws,
                         static_cast<hipStream_t>(stream))) != SD_OK)
+    return st;
+  return ok();
+}
+
+sd_status sd_update_compressed_keys(const sd_shape* shape, const void* k_pages,
+                                    const int32_t* block_table, const int32_t* seq_lens,
+                                    float* compressed_keys, void* stream) {
+  sdkv::Dims d;
+  sd_status st;
+  if ((st = check_shape(shape, &d)) != SD_OK) return st;
+  if (!k_pages || !block_table || !seq_lens || !compressed_keys)
+    return fail(SD_E_NULL, "k_pages, block_table, seq_lens and compressed_keys are required");
+  sdkv::CompressArgs a{};
+  a.d = d;
+  a.k_pages = k_pages;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.ckeys = compressed_keys;
+  a.max_windows = sdkv::compressed_windows(d);
+  if ((st = device_status(sdkv::launch_compress_keys(a, static_cast<hipStream_t>(stream)),
+                          "compressed keys kernel launch")) != SD_OK)
+    return st;
+  return ok();
+}
+
+sd_status sd_score_compressed(const sd_shape* shape, const void* q, const float* compressed_keys,
+                              const int32_t* seq_lens, float* unit_scores, void* stream) {
+  sdkv::Dims d;
+  sd_status st;
+  if ((st = check_shape(shape, &d)) != SD_OK) return st;
+  if (!q || !compressed_keys || !seq_lens || !unit_scores)
+    return fail(SD_E_NULL, "q, compressed_keys, seq_lens and unit_scores are required");
+  if ((st = do_score_compressed(d, q, compressed_keys, seq_lens, unit_scores,
+                                static_cast<hipStream_t>(stream))) != SD_OK)
     return st;
   return ok();
 }

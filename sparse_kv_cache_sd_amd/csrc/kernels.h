@@ -128,6 +128,25 @@ struct BudgetArgs {
 };
 hipError_t launch_select_budget(const BudgetArgs& a, hipStream_t st);
 
+// Compressed-key page scoring.  ckeys: [B][Hkv][max_windows][D] fp32, window
+// j the mean of the valid keys 16 j .. 16 j + 31 (max_windows =
+// compressed_windows(d)).  launch_compress_keys writes ckeys from the K pool;
+// launch_score_compressed writes unit_scores [B][Hkv][max_pages] (page unit,
+// P = 16 or 64) from q and ckeys.
+struct CompressArgs {
+  Dims d;
+  const void* k_pages;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const void* q;
+  float* ckeys;
+  int max_windows;
+  float* unit_scores;
+};
+int compressed_windows(const Dims& d);
+hipError_t launch_compress_keys(const CompressArgs& a, hipStream_t st);
+hipError_t launch_score_compressed(const CompressArgs& a, hipStream_t st);
+
 // Most splits one (sequence, KV head) is cut into.
 constexpr int kMaxSplits = 256;
 // Largest slice of the kept list a selecting attention block may own, and
