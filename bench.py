@@ -227,7 +227,15 @@ def sdref_selection(sel):
     return sdref.Selection(sel.kind, sel.r_kv, sel.init_units, sel.local_units, sel.max_dropped)
 
 
-def cpu_baseline(w, unit, r_kv, budget_s=12.0, selection=None):
+def algorithmic_stats_bytes(seq_lens, H_kv, d, P, elem, scorer):
+    """Page statistics read by the scorer: 2 d elements per page (bounds) or
+    d fp32 per 16-token window (compressed keys)."""
+    if scorer == "compressed":
+        return H_kv * int(np.sum([-(-int(n) // 16) for n in seq_lens])) * d * 4
+    return H_kv * int(np.sum([-(-int(n) // P) for n in seq_lens])) * 2 * d * elem
+
+
+def cpu_baseline(w, unit, r_kv, budget_s=12.0, selection=None, scorer="bounds"):
     from oracle import sdref
     try:
         from threadpoolctl import threadpool_info
@@ -247,7 +255,7 @@ def cpu_baseline(w, unit, r_kv, budget_s=12.0, selection=None):
         Kg = sdref.widen(w.K[b, g, :n], r.dtype)
         Vg = sdref.widen(w.V[b, g, :n], r.dtype)
         sdref.group_step(qg, Kg, Vg, unit=unit, page_size=r.page_size, r_kv=r_kv, scale=scale,
-                         selection=selection)
+                         selection=selection, scorer=scorer)
         done += 1
         el = time.perf_counter() - t0
         if el >= budget_s or done >= 4 * len(groups):
@@ -279,6 +287,8 @@ def main():
                     choices=["topk", "window", "init_local_topk", "mass_budget"],
                     help="kept set: top-k (default), the KV window, initial + local + top-k, or "
                          "the dropped-mass budget (token unit)")
+    ap.add_argument("--scorer", default="bounds", choices=["bounds", "compressed"],
+                    help="page scorer: page bounds (default) or compressed keys")
     ap.add_argument("--max-dropped", type=float, default=0.05,
                     help="mass_budget: most dense softmax mass left outside, per head")
     ap.add_argument("--r-kv", type=float, default=0.0,
@@ -359,26 +369,35 @@ def main():
     num_pages = layers[0]["num_pages"]
     shape = sd.Shape(rec.batch, H_q, H_kv, d, P, w0.max_pages(), w0.n_alloc, rec.dtype, num_pages)
     for lay in layers:
-        lay["bounds"] = torch.empty(sd.bounds_shape(shape), dtype=dt, device="cuda")
-        sd.update_page_bounds(shape, lay["k"], lay["bt"], lay["sl"], lay["bounds"])
+        if args.scorer == "compressed":
+            lay["bounds"] = torch.empty(sd.compressed_keys_shape(shape), dtype=torch.float32,
+                                        device="cuda")
+            sd.update_compressed_keys(shape, lay["k"], lay["bt"], lay["sl"], lay["bounds"])
+        else:
+            lay["bounds"] = torch.empty(sd.bounds_shape(shape), dtype=dt, device="cuda")
+            sd.update_page_bounds(shape, lay["k"], lay["bt"], lay["sl"], lay["bounds"])
     torch.cuda.synchronize()
 
-    structured = args.selection != "topk"
+    structured = args.selection != "topk" or args.scorer != "bounds"
     local_units = args.local_units or (2048 // P if unit == "page" else 2048)
     selection = sd.Selection(args.selection, r_kv,
                              args.init_units if args.selection == "init_local_topk" else 0,
                              local_units if args.selection == "init_local_topk" else 0,
-                             args.max_dropped if args.selection == "mass_budget" else 0.0)
+                             args.max_dropped if args.selection == "mass_budget" else 0.0,
+                             args.scorer)
     if structured:
         config_sel = {"selection": args.selection, "init_units": selection.init_units,
                       "local_units": selection.local_units,
-                      "max_dropped": selection.max_dropped}
+                      "max_dropped": selection.max_dropped, "scorer": args.scorer}
         desc += f"; kept set: {args.selection}" + {
             "init_local_topk": f" ({selection.init_units} initial + {selection.local_units} "
                                f"local units + top-k)",
             "window": " (most recent units)",
             "mass_budget": f" (at most {selection.max_dropped:g} of each head's mass dropped, "
-                           f"capped at r_KV)"}[args.selection]
+                           f"capped at r_KV)",
+            "topk": ""}[args.selection]
+        if args.scorer == "compressed":
+            desc += "; pages scored from compressed keys (mean-pooled, kernel 32 stride 16)"
     k_max = sd.selection_capacity(selection, shape.units_max(unit))
     ws = sd.alloc_workspace_sel(shape, unit, selection)
     ws_dense = sd.alloc_workspace(shape, unit, 1.0)
@@ -410,8 +429,11 @@ def main():
     logits = [torch.empty((rec.batch, H_q, shape.max_seq_len), dtype=torch.float32, device="cuda")
               if unit == "token" else None for _ in range(L)]
     for i, lay in enumerate(layers):
-        sd.score_pages(shape, lay["q"], lay["k"], lay["bounds"], lay["bt"], lay["sl"], unit,
-                       scores[i], logits[i], stream=stream)
+        if args.scorer == "compressed":
+            sd.score_compressed(shape, lay["q"], lay["bounds"], lay["sl"], scores[i], stream=stream)
+        else:
+            sd.score_pages(shape, lay["q"], lay["k"], lay["bounds"], lay["bt"], lay["sl"], unit,
+                           scores[i], logits[i], stream=stream)
     torch.cuda.synchronize()
 
     def attend_only(i):
@@ -485,6 +507,9 @@ def main():
     window = args.selection == "window"
     b_sparse = algorithmic_bytes(w0.seq_lens, H_q, H_kv, d, P, elem, unit, r_kv, kept_mean,
                                  window=window)
+    if unit == "page" and args.scorer == "compressed" and not window:
+        b_sparse += (algorithmic_stats_bytes(w0.seq_lens, H_kv, d, P, elem, "compressed") -
+                     algorithmic_stats_bytes(w0.seq_lens, H_kv, d, P, elem, "bounds"))
     b_dense = algorithmic_bytes(w0.seq_lens, H_q, H_kv, d, P, elem, unit, 1.0, 0)
     b_attend = attend_bytes(kept_mean, d, elem, unit == "token" and not window)
     gbps = b_sparse / (us_sparse * 1e-6) / 1e9
@@ -536,7 +561,8 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         result["cpu_baseline"] = cpu_baseline(
-            w0, unit, r_kv, selection=None if not structured else sdref_selection(selection))
+            w0, unit, r_kv, selection=None if not structured else sdref_selection(selection),
+            scorer=args.scorer)
     if structured:
         result["config"].update(config_sel)
     print(json.dumps(result), flush=True)
