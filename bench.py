@@ -419,7 +419,7 @@ def main():
 
     def dense_step(i):
         lay = layers[i]
-        sd.decode_step(shape, lay["q"], lay["k"], lay["v"], lay["bounds"], lay["bt"], lay["sl"],
+        sd.decode_step(shape, lay["q"], lay["k"], lay["v"], None, lay["bt"], lay["sl"],
                        unit, 1.0, out, lse, ws_dense, stream=stream)
 
     # scores of every layer, for timing the attention stage on its own
