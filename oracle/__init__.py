@@ -35,4 +35,4 @@ Every function is pinned by ``tests/test_oracle_*.py`` against values the
 pages print, closed forms, invariants or brute force.
 """
 
-from . import sdref, bytemodel  # noqa: F401
+from . import sdref, bytemodel, entmaxref  # noqa: F401
