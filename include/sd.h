@@ -337,6 +337,47 @@ SD_API sd_status sd_decode_step_sel(const sd_shape* shape, const void* q, const 
                                     float* lse, int32_t* sel_idx, int32_t* sel_count, void* ws,
                                     size_t ws_bytes, void* stream);
 
+/* ---- alpha-entmax attention over the kept set ---------------------------
+ * [Cross/cards] EntmaxKV abstract: alpha-entmax attention gives exact zeros,
+ * so sparse decoding becomes support recovery -- when the kept candidates
+ * hold the entmax support the sparse output equals the dense one; otherwise
+ * the error is governed by the dropped mass delta.  The scores, the kept
+ * lists and the split-K structure are those of sd_decode_step_sel; only the
+ * weights differ.  For query head h of sequence b over its kept tokens T:
+ *   z_t = scale * q[b][h] . K_t,   x_t = (alpha - 1) z_t,
+ *   p_t = max(x_t - tau, 0) ** (1 / (alpha - 1)),  sum_{t in T} p_t = 1,
+ *   out[b][h] = sum_{t in T} p_t V_t,   tau[b][h] = tau.
+ * alpha = 2 is sparsemax; 1.5 is the usual entmax; alpha -> 1 tends to
+ * softmax.  The steps: scoring and selection as sd_decode_step_sel (the
+ * same scorer, keep count, top-k, window, union or budget); the logits of
+ * the kept tokens (token unit: those of the token scorer; page unit, a
+ * window or every unit: a logits-only pass of the attention kernel over the
+ * kept list, which reads K but not V); tau per head by Newton steps from
+ * the left end of its bracket [max x - 1, max x] (fp32; guarded by
+ * bisection); split-K attention with these weights over the stored logits
+ * (reads V), merged as sum_j a_j / sum_j l_j, which also removes the
+ * residual of tau's rounding.
+ *   page_stats  as page_bounds of sd_decode_step_sel (the page bounds, or
+ *               the compressed keys with sel->scorer == SD_SCORER_COMPRESSED);
+ *               not read in token unit, for a window or with r_kv >= 1.
+ *   alpha       in (1, 2]; SD_E_RATIO otherwise.
+ *   out         [B][H_q][d] fp32.
+ *   tau         [B][H_q] fp32 or NULL: the threshold of every head (+inf for
+ *               a sequence with no attended token, whose out is 0).
+ *   sel_idx / sel_count  as for sd_decode_step_sel (not written when every
+ *               unit is kept).
+ *   ws          sd_workspace_bytes_entmax bytes (contents need not be set).
+ * The dropped-mass budget (SD_SEL_MASS_BUDGET) still measures softmax mass. */
+SD_API sd_status sd_workspace_bytes_entmax(const sd_shape* shape, int32_t unit,
+                                           const sd_selection* sel, size_t* bytes_host);
+SD_API sd_status sd_decode_step_entmax(const sd_shape* shape, const void* q, const void* k_pages,
+                                       const void* v_pages, const void* page_stats,
+                                       const int32_t* block_table, const int32_t* seq_lens,
+                                       int32_t unit, const sd_selection* sel, double alpha,
+                                       float* out, float* tau, int32_t* sel_idx,
+                                       int32_t* sel_count, void* ws, size_t ws_bytes,
+                                       void* stream);
+
 /* Text of the last non-OK status on this thread ("" if none). */
 SD_API const char* sd_last_error(void);
 

@@ -15,12 +15,14 @@ from ._lib import (  # noqa: F401
     UNIT_PAGE,
     UNIT_TOKEN,
     alloc_workspace,
+    alloc_workspace_entmax,
     alloc_workspace_sel,
     attend_partials,
     attend_splitk,
     bounds_shape,
     compressed_keys_shape,
     decode_step,
+    decode_step_entmax,
     decode_step_sel,
     keep_count,
     lib,
@@ -34,5 +36,6 @@ from ._lib import (  # noqa: F401
     update_compressed_keys,
     update_page_bounds,
     workspace_bytes,
+    workspace_bytes_entmax,
     workspace_bytes_sel,
 )

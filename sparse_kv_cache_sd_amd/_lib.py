@@ -94,6 +94,11 @@ _SIGS = {
                                           _SELP, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "sd_update_compressed_keys": (ctypes.c_int, [ctypes.POINTER(SdShape), _P, _P, _P, _P, _P]),
     "sd_score_compressed": (ctypes.c_int, [ctypes.POINTER(SdShape), _P, _P, _P, _P, _P]),
+    "sd_workspace_bytes_entmax": (ctypes.c_int, [ctypes.POINTER(SdShape), _I32, _SELP,
+                                                 ctypes.POINTER(ctypes.c_size_t)]),
+    "sd_decode_step_entmax": (ctypes.c_int, [ctypes.POINTER(SdShape), _P, _P, _P, _P, _P, _P,
+                                             _I32, _SELP, ctypes.c_double, _P, _P, _P, _P, _P,
+                                             ctypes.c_size_t, _P]),
     "sd_last_error": (ctypes.c_char_p, []),
 }
 EXPORTS = tuple(_SIGS)
@@ -511,6 +516,51 @@ def decode_step_sel(shape: Shape, q, k_pages, v_pages, page_bounds, block_table,
         u, ctypes.byref(sel.c()),
         _dev(out, "out", torch.float32, (s.batch, s.num_q_heads, s.head_dim)),
         _dev(lse, "lse", torch.float32, (s.batch, s.num_q_heads)),
+        _dev(sel_idx, "sel_idx", torch.int32, (s.batch, s.num_kv_heads, cap), optional=True),
+        _dev(sel_count, "sel_count", torch.int32, (s.batch, s.num_kv_heads), optional=True),
+        wp, wn, _stream(stream)))
+
+
+# ----------------------------------------------------------------------------
+# alpha-entmax attention over the kept set
+# ----------------------------------------------------------------------------
+
+def workspace_bytes_entmax(shape: Shape, unit, sel: Selection) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().sd_workspace_bytes_entmax(ctypes.byref(shape.c()), _unit(unit),
+                                           ctypes.byref(sel.c()), ctypes.byref(out)))
+    return int(out.value)
+
+
+def alloc_workspace_entmax(shape: Shape, unit, sel: Selection, device="cuda") -> torch.Tensor:
+    n = max(1, workspace_bytes_entmax(shape, unit, sel))
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def decode_step_entmax(shape: Shape, q, k_pages, v_pages, page_stats, block_table, seq_lens, unit,
+                       sel: Selection, alpha: float, out, ws, tau=None, sel_idx=None,
+                       sel_count=None, stream=None):
+    """page_stats: the page bounds, or with sel.scorer == "compressed" the
+    compressed keys (may be None where they are not read)."""
+    s, u = shape, _unit(unit)
+    umax = s.max_pages_per_seq if u == UNIT_PAGE else s.max_seq_len
+    cap = selection_capacity(sel, umax)
+    wp, wn = _ws(ws, 1)
+    stats = (_dev(page_stats, "compressed_keys", torch.float32, compressed_keys_shape(s),
+                  optional=True)
+             if sel.scorer == "compressed" else
+             _dev(page_stats, "page_bounds", s.torch_dtype, _bounds_shape(s), optional=True))
+    _check(lib().sd_decode_step_entmax(
+        ctypes.byref(s.c()),
+        _dev(q, "q", s.torch_dtype, (s.batch, s.num_q_heads, s.head_dim)),
+        _dev(k_pages, "k_pages", s.torch_dtype, _kv_shape(s)),
+        _dev(v_pages, "v_pages", s.torch_dtype, _kv_shape(s)),
+        stats,
+        _dev(block_table, "block_table", torch.int32, (s.batch, s.max_pages_per_seq)),
+        _dev(seq_lens, "seq_lens", torch.int32, (s.batch,)),
+        u, ctypes.byref(sel.c()), float(alpha),
+        _dev(out, "out", torch.float32, (s.batch, s.num_q_heads, s.head_dim)),
+        _dev(tau, "tau", torch.float32, (s.batch, s.num_q_heads), optional=True),
         _dev(sel_idx, "sel_idx", torch.int32, (s.batch, s.num_kv_heads, cap), optional=True),
         _dev(sel_count, "sel_count", torch.int32, (s.batch, s.num_kv_heads), optional=True),
         wp, wn, _stream(stream)))

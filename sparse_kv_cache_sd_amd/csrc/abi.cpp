@@ -348,6 +348,15 @@ struct ListMode {
   int force_init = 0, force_local = 0;
 };
 
+// What the attention pass does with the logits: softmax (default),
+// alpha-entmax against the thresholds tau (with stored logits), or write the
+// logits of the attended tokens to logits_out and nothing else.
+struct Weights {
+  const float* tau = nullptr;
+  float alpha_m1 = 0.f, beta = 0.f;
+  float* logits_out = nullptr;
+};
+
 // Split-K attention partials.  Exactly one list source: sel_idx (list),
 // unit_scores (top-k inside the kernel) or neither (identity, or a window).
 sd_status do_partials(const sdkv::Dims& d, const void* q, const void* kp, const void* vp,
@@ -355,7 +364,7 @@ sd_status do_partials(const sdkv::Dims& d, const void* q, const void* kp, const 
                       const int32_t* sel_count, int k_max, const float* logits, void* ws,
                       hipStream_t st, const float* unit_scores = nullptr, int R_ppm = -1,
                       int32_t* sel_out = nullptr, int32_t* sel_count_out = nullptr,
-                      int* S_out = nullptr, ListMode lm = ListMode{}) {
+                      int* S_out = nullptr, ListMode lm = ListMode{}, Weights wt = Weights{}) {
   const bool listed = sel_idx != nullptr || unit_scores != nullptr || lm.window;
   const int64_t kk = listed ? k_max : units_max(d, unit);
   const Split sp = plan_split(d, unit, kk);
@@ -387,6 +396,10 @@ sd_status do_partials(const sdkv::Dims& d, const void* q, const void* kp, const 
     a.window = 1;
     a.R_ppm = lm.window_R;
   }
+  a.tau = wt.tau;
+  a.alpha_m1 = wt.alpha_m1;
+  a.beta = wt.beta;
+  a.logits_out = wt.logits_out;
   if (S_out) *S_out = sp.S;
   return device_status(sdkv::launch_attend(a, st), "attention kernel launch");
 }
@@ -533,6 +546,112 @@ sd_status decode_impl(const sdkv::Dims& d, const void* q, const void* k_pages,
                         logits, ws, s, nullptr, -1, nullptr, nullptr, &S)) != SD_OK)
     return st;
   return do_merge(d, out, lse, ws, s, S);
+}
+
+// ---- alpha-entmax decode step ----
+
+// Workspace of the entmax step: the decode-step layout, then (page unit) the
+// logits of the attended tokens -- token unit keeps them where the token
+// scorer writes them -- the thresholds, and the lse the merge writes (not
+// reported: the entmax weights already sum to one).
+struct EntLayout {
+  Layout L;
+  size_t logits, tau, lse, total;
+};
+
+EntLayout ent_layout(const sdkv::Dims& d, int unit, const Sel& sel) {
+  EntLayout E{};
+  E.L = layout(d, unit, sel);
+  const int64_t bh = static_cast<int64_t>(d.B) * d.Hq;
+  size_t off = E.L.total;
+  E.logits = E.L.logits;
+  if (unit == SD_UNIT_PAGE) {
+    E.logits = off;
+    off = align_up(off + sizeof(float) * bh * d.max_seq);
+  }
+  E.tau = off;  off = align_up(off + sizeof(float) * bh);
+  E.lse = off;  off = align_up(off + sizeof(float) * bh);
+  E.total = off;
+  return E;
+}
+
+// Selection as in decode_impl, then: the logits of the attended tokens (the
+// token scorer's, or a logits-only pass of the attention kernel over the
+// kept list), the threshold of every head over them, and the attention
+// pass with entmax weights over the stored logits, merged by the LSE merge
+// (each split reports the log of its weight sum; the merge divides the
+// summed weighted values by the summed weights).
+sd_status entmax_impl(const sdkv::Dims& d, const void* q, const void* k_pages,
+                      const void* v_pages, const void* page_stats, const int32_t* block_table,
+                      const int32_t* seq_lens, int unit, const Sel& sel, double alpha, float* out,
+                      float* tau_out, int32_t* sel_idx, int32_t* sel_count, void* ws,
+                      hipStream_t s) {
+  const EntLayout E = ent_layout(d, unit, sel);
+  const Layout& L = E.L;
+  const int U = units_max(d, unit);
+  const int k_max = static_cast<int>(capacity(sel, U));
+  const bool dense = sel.r >= 1.0 && sel.kind != SD_SEL_MASS_BUDGET;
+  float* logits = reinterpret_cast<float*>(at(ws, E.logits));
+  float* tau = tau_out ? tau_out : reinterpret_cast<float*>(at(ws, E.tau));
+  int32_t* idx = nullptr;
+  int32_t* cnt = nullptr;
+  sd_status st;
+  bool have_logits = false;
+  if (!dense) {
+    idx = sel_idx ? sel_idx : reinterpret_cast<int32_t*>(at(ws, L.sel_idx));
+    cnt = sel_count ? sel_count : reinterpret_cast<int32_t*>(at(ws, L.sel_count));
+    if (sel.kind == SD_SEL_WINDOW) {
+      st = do_structure(d, unit, seq_lens, sel, nullptr, nullptr, 0, idx, cnt, k_max, s);
+    } else {
+      float* scores = reinterpret_cast<float*>(at(ws, L.scores));
+      uint32_t* smm = unit == SD_UNIT_TOKEN && multi_select(d, unit)
+                          ? reinterpret_cast<uint32_t*>(at(ws, L.score_mm))
+                          : nullptr;
+      if (unit == SD_UNIT_PAGE && sel.scorer == SD_SCORER_COMPRESSED)
+        st = do_score_compressed(d, q, static_cast<const float*>(page_stats), seq_lens, scores,
+                                 s);
+      else
+        st = do_score(d, q, k_pages, page_stats, block_table, seq_lens, unit, scores,
+                      unit == SD_UNIT_TOKEN ? logits : nullptr, s, smm);
+      if (st != SD_OK) return st;
+      have_logits = unit == SD_UNIT_TOKEN;
+      st = do_select_list(d, unit, seq_lens, scores, have_logits ? logits : nullptr, sel, idx,
+                          cnt, at(ws, L.msel), reinterpret_cast<int32_t*>(at(ws, L.topk_tmp)),
+                          reinterpret_cast<int32_t*>(at(ws, L.topk_cnt)), s, smm);
+    }
+    if (st != SD_OK) return st;
+  }
+  const float am1 = static_cast<float>(alpha - 1.0);
+  const float beta = static_cast<float>(1.0 / (alpha - 1.0));
+  if (!have_logits) {
+    Weights w;
+    w.logits_out = logits;
+    if ((st = do_partials(d, q, k_pages, v_pages, block_table, seq_lens, unit, idx, cnt, k_max,
+                          nullptr, ws, s, nullptr, -1, nullptr, nullptr, nullptr, ListMode{},
+                          w)) != SD_OK)
+      return st;
+  }
+  sdkv::TauArgs ta{d, unit, seq_lens, block_table, idx, cnt, idx ? k_max : 0, logits, am1, beta,
+                   tau};
+  if ((st = device_status(sdkv::launch_entmax_tau(ta, s), "entmax threshold kernel launch")) !=
+      SD_OK)
+    return st;
+  Weights w;
+  w.tau = tau;
+  w.alpha_m1 = am1;
+  w.beta = beta;
+  int S = 0;
+  if ((st = do_partials(d, q, k_pages, v_pages, block_table, seq_lens, unit, idx, cnt, k_max,
+                        logits, ws, s, nullptr, -1, nullptr, nullptr, &S, ListMode{}, w)) !=
+      SD_OK)
+    return st;
+  return do_merge(d, out, reinterpret_cast<float*>(at(ws, E.lse)), ws, s, S);
+}
+
+sd_status check_alpha(double alpha) {
+  if (!(std::isfinite(alpha) && alpha > 1.0 && alpha <= 2.0))
+    return fail(SD_E_RATIO, "alpha must lie in (1, 2]");
+  return SD_OK;
 }
 
 // Shared checks of the attention entry points.
@@ -856,6 +975,47 @@ sd_status sd_decode_step_sel(const sd_shape* shape, const void* q, const void* k
   if ((st = check_ws(ws, ws_bytes, layout(d, unit, v).total)) != SD_OK) return st;
   if ((st = decode_impl(d, q, k_pages, v_pages, page_bounds, block_table, seq_lens, unit, v, out,
                         lse, sel_idx, sel_count, ws, static_cast<hipStream_t>(stream))) != SD_OK)
+    return st;
+  return ok();
+}
+
+sd_status sd_workspace_bytes_entmax(const sd_shape* shape, int32_t unit,
+                                    const sd_selection* sel, size_t* bytes_host) {
+  sdkv::Dims d;
+  Sel v;
+  sd_status st;
+  if ((st = check_shape(shape, &d)) != SD_OK) return st;
+  if ((st = check_unit(unit)) != SD_OK) return st;
+  if ((st = check_selection(sel, &v)) != SD_OK) return st;
+  if (!bytes_host) return fail(SD_E_NULL, "bytes_host is NULL");
+  *bytes_host = ent_layout(d, unit, v).total;
+  return ok();
+}
+
+sd_status sd_decode_step_entmax(const sd_shape* shape, const void* q, const void* k_pages,
+                                const void* v_pages, const void* page_stats,
+                                const int32_t* block_table, const int32_t* seq_lens,
+                                int32_t unit, const sd_selection* sel, double alpha, float* out,
+                                float* tau, int32_t* sel_idx, int32_t* sel_count, void* ws,
+                                size_t ws_bytes, void* stream) {
+  sdkv::Dims d;
+  Sel v;
+  sd_status st;
+  if ((st = check_shape(shape, &d)) != SD_OK) return st;
+  if ((st = check_unit(unit)) != SD_OK) return st;
+  if ((st = check_selection(sel, &v)) != SD_OK) return st;
+  if ((st = check_alpha(alpha)) != SD_OK) return st;
+  if (!q || !k_pages || !v_pages || !block_table || !seq_lens || !out)
+    return fail(SD_E_NULL, "q, k_pages, v_pages, block_table, seq_lens and out are required");
+  if ((st = check_budget(d, unit, v)) != SD_OK) return st;
+  if (v.r < 1.0 && v.kind != SD_SEL_WINDOW && unit == SD_UNIT_PAGE && !page_stats)
+    return fail(SD_E_NULL, "page unit selection reads page_stats");
+  if ((sel_idx == nullptr) != (sel_count == nullptr))
+    return fail(SD_E_NULL, "sel_idx and sel_count are given together or not at all");
+  if ((st = check_ws(ws, ws_bytes, ent_layout(d, unit, v).total)) != SD_OK) return st;
+  if ((st = entmax_impl(d, q, k_pages, v_pages, page_stats, block_table, seq_lens, unit, v, alpha,
+                        out, tau, sel_idx, sel_count, ws, static_cast<hipStream_t>(stream))) !=
+      SD_OK)
     return st;
   return ok();
 }

@@ -51,6 +51,13 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 constexpr int kAttendWaves = 8;     // waves per block
 constexpr int kResolveWindow = 8;   // chunks a wave resolves per round
 
+// What a block does with the attended tokens' logits.
+enum WeightMode : int {
+  kWSoftmax = 0,  // online softmax (running max, exp2)
+  kWEntmax = 1,   // alpha-entmax weights against a precomputed threshold
+  kWLogits = 2    // no attention: write the logits out (V is not read)
+};
+
 // How a block obtains its kept list.
 enum SelMode : int {
   kListed = 0,     // from memory (sel_idx) or the identity
@@ -218,7 +225,7 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(MergeArgs a) {
 // bf16: matrix-core kernel
 // ----------------------------------------------------------------------------
 
-template <int D, int G, bool LOGITS, int SEL>
+template <int D, int G, bool LOGITS, int SEL, int WM>
 __global__ __launch_bounds__(kAttendWaves * 64) void attend_mfma_kernel(AttendArgs a) {
   constexpr int NW = kAttendWaves, NT = NW * 64, RW = kResolveWindow;
   constexpr int KS = D / 32;        // 16x16x32 steps over the channels
@@ -226,12 +233,15 @@ __global__ __launch_bounds__(kAttendWaves * 64) void attend_mfma_kernel(AttendAr
   constexpr int VROW = D + 8;       // staged V row, bf16 elements (16-byte aligned rows)
   constexpr bool SELECTS = SEL != kListed;
   constexpr int KEYS = SELECTS ? SEL : 1;
+  constexpr bool TOK = LOGITS || WM == kWLogits;  // rows' token ids are kept
+  static_assert(WM != kWEntmax || LOGITS, "entmax weights read stored logits");
+  static_assert(WM != kWLogits || (!LOGITS && !SELECTS), "logits are computed from a list");
   // The V staging area is reused after the chunk loop for the per-wave outputs.
   constexpr int kStage = NW * 16 * VROW * 2;
   constexpr int kAfter = NW * G * D * 4;
   __shared__ __align__(16) unsigned char s_raw[kStage > kAfter ? kStage : kAfter];
   __shared__ int s_rows[NW][RW][16];
-  __shared__ int s_tok[LOGITS ? NW : 1][RW][16];
+  __shared__ int s_tok[TOK ? NW : 1][RW][16];
   __shared__ float s_m[NW][16], s_l[NW][16];
   __shared__ __align__(16) float s_po[G * D];
   __shared__ float s_plse[G];
@@ -329,46 +339,74 @@ __global__ __launch_bounds__(kAttendWaves * 64) void attend_mfma_kernel(AttendAr
   float4_t acc[CT];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) acc[ct] = float4_t{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.f;
+  // Entmax weights are absolute (no running max): m stays 0 and l sums them.
+  float m = WM == kWEntmax ? 0.f : -INFINITY, l = 0.f;
+  const float tau_row =
+      WM == kWEntmax ? a.tau[(int64_t)b * d.Hq + g * G + min(row, G - 1)] : 0.f;
+  float* logit_out_row =
+      WM == kWLogits ? a.logits_out + ((int64_t)b * d.Hq + g * G + min(row, G - 1)) * d.max_seq
+                     : nullptr;
   bf16_t* sv = &s_v[wave][0];
 
-  // One 16-row chunk: scores, online softmax, value accumulation.  lg holds
-  // the chunk's stored logits in token unit (rows 4 quad + r of head `row`).
+  // One 16-row chunk: scores, weights, value accumulation.  lg holds the
+  // chunk's stored logits (rows 4 quad + r of head `row`) when LOGITS; tk
+  // holds those rows' token ids when logits are written out.
   auto process = [&](const u32x4_t (&kv)[KS], const u32x4_t (&vv)[KS], const float (&lg)[4],
-                     uint32_t vmask) {
+                     const int (&tk)[4], uint32_t vmask) {
+    if constexpr (WM != kWLogits) {
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
-      *reinterpret_cast<u32x4_t*>(sv + row * VROW + 32 * s + 8 * quad) = vv[s];
-    float x[4];
+      for (int s = 0; s < KS; ++s)
+        *reinterpret_cast<u32x4_t*>(sv + row * VROW + 32 * s + 8 * quad) = vv[s];
+    }
+    float4_t st = {0.f, 0.f, 0.f, 0.f};
     if constexpr (!LOGITS) {
-      float4_t st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s)
         st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv[s]), qop[s],
                                                       st, 0, 0, 0);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) x[r] = st[r] * qs;
-    } else {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) x[r] = row < G ? lg[r] * kLog2e : 0.f;
     }
+    if constexpr (WM == kWLogits) {
+      if (row < G) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (!((vmask >> (4 * quad + r)) & 1u)) x[r] = -INFINITY;
-    float cm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    cm = max_xor32(cm);
-    cm = max_xor16(cm);
-    const float mn = fmaxf(m, cm);
-    const float alpha = exp2f(m - mn);
+        for (int r = 0; r < 4; ++r)
+          if ((vmask >> (4 * quad + r)) & 1u) logit_out_row[tk[r]] = st[r] * d.scale;
+      }
+      return;
+    }
     float p[4];
+    if constexpr (WM == kWEntmax) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) p[r] = exp2f(x[r] - mn);
-    l = fmaf(l, alpha, (p[0] + p[1]) + (p[2] + p[3]));
-    if (alpha != 1.f) {
+      for (int r = 0; r < 4; ++r)
+        p[r] = row < G && ((vmask >> (4 * quad + r)) & 1u)
+                   ? entmax_weight(fmaf(a.alpha_m1, lg[r], -tau_row), a.beta)
+                   : 0.f;
+      l += (p[0] + p[1]) + (p[2] + p[3]);
+    } else {
+      float x[4];
+      if constexpr (!LOGITS) {
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) acc[ct] *= alpha;
+        for (int r = 0; r < 4; ++r) x[r] = st[r] * qs;
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[r] = row < G ? lg[r] * kLog2e : 0.f;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (!((vmask >> (4 * quad + r)) & 1u)) x[r] = -INFINITY;
+      float cm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      cm = max_xor32(cm);
+      cm = max_xor16(cm);
+      const float mn = fmaxf(m, cm);
+      const float alpha = exp2f(m - mn);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[r] = exp2f(x[r] - mn);
+      l = fmaf(l, alpha, (p[0] + p[1]) + (p[2] + p[3]));
+      if (alpha != 1.f) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) acc[ct] *= alpha;
+      }
+      m = mn;
     }
-    m = mn;
     short4_t phi, plo;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -407,7 +445,7 @@ __global__ __launch_bounds__(kAttendWaves * 64) void attend_mfma_kernel(AttendAr
 #pragma unroll
       for (int it = 0; it < NR; ++it) {
         s_rows[wave][it * 4 + quad][row] = pr[it];
-        if constexpr (LOGITS) s_tok[wave][it * 4 + quad][row] = tk[it];
+        if constexpr (TOK) s_tok[wave][it * 4 + quad][row] = tk[it];
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -419,9 +457,10 @@ __global__ __launch_bounds__(kAttendWaves * 64) void attend_mfma_kernel(AttendAr
     // flight; a branch around a load would make it drain all of them.
     u32x4_t kA[2][KS], vA[2][KS], kB[2][KS], vB[2][KS];
     float lA[2][4], lB[2][4];
+    int tA[2][4], tB[2][4];
     uint32_t mA[2], mB[2];
     auto load2 = [&](u32x4_t (&kk)[2][KS], u32x4_t (&vv)[2][KS], float (&ll)[2][4],
-                     uint32_t (&mm)[2], int c0) {
+                     int (&tt)[2][4], uint32_t (&mm)[2], int c0) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int c = c0 + i;
@@ -434,34 +473,38 @@ __global__ __launch_bounds__(kAttendWaves * 64) void attend_mfma_kernel(AttendAr
         for (int s = 0; s < KS; ++s) {
           if constexpr (!LOGITS) kk[i][s] = *reinterpret_cast<const u32x4_t*>(kr + 32 * s + 8 * quad);
           else kk[i][s] = u32x4_t{0u, 0u, 0u, 0u};
-          vv[i][s] = *reinterpret_cast<const u32x4_t*>(vr + 32 * s + 8 * quad);
+          if constexpr (WM != kWLogits) vv[i][s] = *reinterpret_cast<const u32x4_t*>(vr + 32 * s + 8 * quad);
+          else vv[i][s] = u32x4_t{0u, 0u, 0u, 0u};
         }
-        if constexpr (LOGITS) {
+        if constexpr (TOK) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            int t = s_tok[LOGITS ? wave : 0][min(c, RW - 1)][4 * quad + r];
+            int t = s_tok[TOK ? wave : 0][min(c, RW - 1)][4 * quad + r];
             t = t < 0 ? 0 : (t >= d.max_seq ? d.max_seq - 1 : t);
-            ll[i][r] = logit_row[t];
+            tt[i][r] = t;
+            if constexpr (LOGITS) ll[i][r] = logit_row[t];
+            else ll[i][r] = 0.f;
           }
         }
       }
     };
     auto run2 = [&](u32x4_t (&kk)[2][KS], u32x4_t (&vv)[2][KS], float (&ll)[2][4],
-                    uint32_t (&mm)[2]) {
+                    int (&tt)[2][4], uint32_t (&mm)[2]) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        if (mm[i] != 0u) process(kk[i], vv[i], ll[i], mm[i]);
+        if (mm[i] != 0u) process(kk[i], vv[i], ll[i], tt[i], mm[i]);
     };
-    load2(kA, vA, lA, mA, 0);
+    load2(kA, vA, lA, tA, mA, 0);
     for (int c = 0;; c += 4) {
-      load2(kB, vB, lB, mB, c + 2);
-      run2(kA, vA, lA, mA);
+      load2(kB, vB, lB, tB, mB, c + 2);
+      run2(kA, vA, lA, tA, mA);
       if (c + 2 >= nc) break;
-      load2(kA, vA, lA, mA, c + 4);
-      run2(kB, vB, lB, mB);
+      load2(kA, vA, lA, tA, mA, c + 4);
+      run2(kB, vB, lB, tB, mB);
       if (c + 4 >= nc) break;
     }
   }
+  if constexpr (WM == kWLogits) return;
 
   // lane (row, quad) holds head `row`: sum over the four quads of l; the
   // running max is already shared by them.
@@ -520,6 +563,8 @@ __global__ __launch_bounds__(kAttendWaves * 64) void attend_f32_kernel(AttendArg
   const float* kp = static_cast<const float*>(a.k_pages);
   const float* vp = static_cast<const float*>(a.v_pages);
   const bool use_logits = a.token_logits != nullptr;
+  const bool ent = a.tau != nullptr;          // entmax weights (with use_logits)
+  const bool wl = a.logits_out != nullptr;    // write logits, no attention
   const int32_t* list = a.sel_idx ? a.sel_idx + bg * a.k_max : nullptr;
   const int units_cap = a.unit == kPage ? d.max_pages : d.max_seq;
   const Span sp = span_of(a, j, (list || a.window) ? a.k_max : units_cap);
@@ -532,7 +577,8 @@ __global__ __launch_bounds__(kAttendWaves * 64) void attend_f32_kernel(AttendArg
     return list ? v : w0 + e;
   };
 
-  const float qs = d.scale * kLog2e;
+  // scores in the exp2 domain, or natural logits when they are written out
+  const float qs = wl ? d.scale : d.scale * kLog2e;
   float qv[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -540,10 +586,13 @@ __global__ __launch_bounds__(kAttendWaves * 64) void attend_f32_kernel(AttendArg
 #pragma unroll
     for (int c = 0; c < 8; ++c) qv[h][c] *= qs;
   }
+  float tauv[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) tauv[h] = ent ? a.tau[(int64_t)b * d.Hq + g * G + h] : 0.f;
   float m[G], l[G], acc[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    m[h] = -INFINITY;
+    m[h] = ent ? 0.f : -INFINITY;
     l[h] = 0.f;
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[h][c] = 0.f;
@@ -560,8 +609,10 @@ __global__ __launch_bounds__(kAttendWaves * 64) void attend_f32_kernel(AttendArg
     float s[G];
     if (use_logits) {
 #pragma unroll
-      for (int h = 0; h < G; ++h)
-        s[h] = ok ? a.token_logits[((int64_t)b * d.Hq + g * G + h) * d.max_seq + t] * kLog2e : 0.f;
+      for (int h = 0; h < G; ++h) {
+        const float z = ok ? a.token_logits[((int64_t)b * d.Hq + g * G + h) * d.max_seq + t] : 0.f;
+        s[h] = ent ? z : z * kLog2e;
+      }
     } else {
       float kv[8];
       if (ok) {
@@ -578,7 +629,27 @@ __global__ __launch_bounds__(kAttendWaves * 64) void attend_f32_kernel(AttendArg
         s[h] = group_sum<LPR>(dot);
       }
     }
-    if (ok) {
+    if (wl) {
+      if (ok) {
+        float mine = 0.f;
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+          if (h == cl) mine = s[h];
+        if (cl < G) a.logits_out[((int64_t)b * d.Hq + g * G + cl) * d.max_seq + t] = mine;
+      }
+      continue;
+    }
+    if (ok && ent) {
+      float vv[8];
+      load8(vp + off, vv);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float p = entmax_weight(fmaf(a.alpha_m1, s[h], -tauv[h]), a.beta);
+        l[h] += p;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[h][c] = fmaf(p, vv[c], acc[h][c]);
+      }
+    } else if (ok) {
       float vv[8];
       load8(vp + off, vv);
 #pragma unroll
@@ -593,6 +664,7 @@ __global__ __launch_bounds__(kAttendWaves * 64) void attend_f32_kernel(AttendArg
       }
     }
   }
+  if (wl) return;
   // per wave: lane-rows to LDS, merged below together with the other waves
   if (cl == 0) {
 #pragma unroll
@@ -660,6 +732,10 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
     return hipErrorInvalidValue;
   const dim3 grid(a.S * d.Hkv * d.B);  // block id = bg + B*Hkv*j (XCD-aware)
   const bool logits = a.token_logits != nullptr;
+  const bool ent = a.tau != nullptr, wl = a.logits_out != nullptr;
+  if (ent && (!logits || wl || selects)) return hipErrorInvalidValue;
+  if (wl && (logits || selects)) return hipErrorInvalidValue;
+  if (ent && !(a.alpha_m1 > 0.f && a.alpha_m1 <= 1.f && a.beta >= 1.f)) return hipErrorInvalidValue;
   const bool ok = dispatch_tdg(d.dtype, d.D, d.G, [&](auto t, auto dd, auto gg) {
     using T = decltype(t);
     constexpr int D = decltype(dd)::value;
@@ -669,14 +745,18 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
       attend_f32_kernel<D, G><<<grid, NT, 0, st>>>(a);
     } else if (selects) {
       switch (select_mode(d.max_pages)) {
-        case kBlock4: attend_mfma_kernel<D, G, false, kBlock4><<<grid, NT, 0, st>>>(a); break;
-        case kBlock8: attend_mfma_kernel<D, G, false, kBlock8><<<grid, NT, 0, st>>>(a); break;
-        default: attend_mfma_kernel<D, G, false, kBlock32><<<grid, NT, 0, st>>>(a); break;
+        case kBlock4: attend_mfma_kernel<D, G, false, kBlock4, kWSoftmax><<<grid, NT, 0, st>>>(a); break;
+        case kBlock8: attend_mfma_kernel<D, G, false, kBlock8, kWSoftmax><<<grid, NT, 0, st>>>(a); break;
+        default: attend_mfma_kernel<D, G, false, kBlock32, kWSoftmax><<<grid, NT, 0, st>>>(a); break;
       }
+    } else if (wl) {
+      attend_mfma_kernel<D, G, false, kListed, kWLogits><<<grid, NT, 0, st>>>(a);
+    } else if (logits && ent) {
+      attend_mfma_kernel<D, G, true, kListed, kWEntmax><<<grid, NT, 0, st>>>(a);
     } else if (logits) {
-      attend_mfma_kernel<D, G, true, kListed><<<grid, NT, 0, st>>>(a);
+      attend_mfma_kernel<D, G, true, kListed, kWSoftmax><<<grid, NT, 0, st>>>(a);
     } else {
-      attend_mfma_kernel<D, G, false, kListed><<<grid, NT, 0, st>>>(a);
+      attend_mfma_kernel<D, G, false, kListed, kWSoftmax><<<grid, NT, 0, st>>>(a);
     }
   });
   if (!ok) return hipErrorInvalidValue;

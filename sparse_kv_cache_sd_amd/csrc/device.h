@@ -205,6 +205,17 @@ __device__ __forceinline__ V wave_incl_scan(V v) {
   return v;
 }
 
+// alpha-entmax weight max(t, 0) ** beta of t = (alpha - 1) logit - tau, with
+// beta = 1 / (alpha - 1): t^2 at alpha = 1.5, t at alpha = 2 (sparsemax).
+// Every kernel forms t as fmaf(alpha - 1, logit, -tau), so the threshold
+// kernel and the attention kernel weigh a token identically.
+__device__ __forceinline__ float entmax_weight(float t, float beta) {
+  if (!(t > 0.f)) return 0.f;
+  if (beta == 2.f) return t * t;
+  if (beta == 1.f) return t;
+  return exp2f(beta * log2f(t));
+}
+
 // Calls fn(T{}, std::integral_constant<int, D>{}, std::integral_constant<int, G>{})
 // for the supported (dtype, head_dim, group) combinations; returns false otherwise.
 template <typename Fn>

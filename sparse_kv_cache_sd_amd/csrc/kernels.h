@@ -87,7 +87,35 @@ struct AttendArgs {
   // Without a list or scores: window != 0 attends only the last
   // keep_count(U, R_ppm) units (list entry e is unit U - k + e).
   int window;
+  // alpha-entmax weights instead of softmax (needs token_logits): token t of
+  // head h weighs max(alpha_m1 * logit - tau[b][h], 0) ** beta with
+  // alpha_m1 = alpha - 1 and beta = 1 / (alpha - 1); a split then reports
+  // log(sum of its weights) as its lse.
+  const float* tau;           // [B][Hq], NULL: softmax
+  float alpha_m1, beta;
+  // logits_out != NULL: no attention; the logits scale * q.K of every
+  // attended token are written to logits_out [B][Hq][max_seq] (V not read).
+  float* logits_out;
 };
+
+// alpha-entmax threshold of every (sequence, query head) over the logits of
+// the tokens of its kept list (or of every unit without a list), one block
+// per head: tau with sum_t max(alpha_m1 * logit_t - tau, 0) ** beta = 1.
+// Tokens on pages with an invalid block-table entry are left out, as the
+// attention kernel leaves them out.
+struct TauArgs {
+  Dims d;
+  int unit;
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+  const int32_t* sel_idx;    // NULL: every unit
+  const int32_t* sel_count;
+  int k_max;
+  const float* logits;       // [B][Hq][max_seq]
+  float alpha_m1, beta;
+  float* tau;                // [B][Hq]
+};
+hipError_t launch_entmax_tau(const TauArgs& a, hipStream_t st);
 
 // Structured kept lists, one block per (sequence, KV head): kind kWindow
 // writes the last keep_count(U, R_ppm) units; kind kInitLocalTopk writes the

@@ -100,3 +100,32 @@ def test_workspace_size_and_alignment_checked():
     assert st == 5 and b"aligned" in lib.sd_last_error()
     st = lib.sd_merge_splits(sh, fake, fake, ctypes.c_void_p(0x10000), 16, None)
     assert st == 5 and b"smaller" in lib.sd_last_error()
+
+
+def test_entmax_validation_before_any_launch():
+    lib = sd.lib()
+    sh = ctypes.byref(_shape().c())
+    sel = ctypes.byref(sd.Selection("topk", 0.3).c())
+    for bad in (1.0, 0.5, 2.01, float("nan"), float("inf")):
+        st = lib.sd_decode_step_entmax(sh, None, None, None, None, None, None, 1, sel, bad, None,
+                                       None, None, None, None, 0, None)
+        assert st == 4 and b"alpha" in lib.sd_last_error()
+    st = lib.sd_decode_step_entmax(sh, None, None, None, None, None, None, 1, sel, 1.5, None,
+                                   None, None, None, None, 0, None)
+    assert st == 1 and b"required" in lib.sd_last_error()
+    fake = ctypes.c_void_p(0x10000)       # never dereferenced: validation fails first
+    st = lib.sd_decode_step_entmax(sh, fake, fake, fake, fake, fake, fake, 1, sel, 1.5, fake,
+                                   None, None, None, ctypes.c_void_p(0x10000), 16, None)
+    assert st == 5 and b"smaller" in lib.sd_last_error()
+
+
+def test_entmax_workspace_holds_logits_and_thresholds():
+    s = _shape()
+    for unit in ("page", "token"):
+        sel = sd.Selection("topk", 0.3)
+        ent = sd.workspace_bytes_entmax(s, unit, sel)
+        soft = sd.workspace_bytes_sel(s, unit, sel)
+        extra = 2 * 4 * s.batch * s.num_q_heads       # thresholds and lse
+        if unit == "page":
+            extra += 4 * s.batch * s.num_q_heads * s.max_seq_len   # logits of kept tokens
+        assert ent >= soft + extra
