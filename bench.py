@@ -184,9 +184,11 @@ def summarize_pmc(fetch_dir, write_dir, workload, out_path, cmd_fetch, cmd_write
         return sum(v) / len(v), len(v)
 
     fr, wr = rows(fetch_dir), rows(write_dir)
-    # the in-kernel-selection attention instance (SEL != 0, no stored logits)
-    att = lambda n, gsz: ("attend_mfma_kernel" in n and "false, 0>" not in n
-                          and "true" not in n)
+    # the in-kernel-selection attention instance: attend_mfma_kernel<D, G,
+    # LOGITS = false, SEL in {4, 8, 32}, softmax weights>
+    import re
+    sel_inst = re.compile(r"attend_mfma_kernel<\d+, \d+, false, (4|8|32), 0>")
+    att = lambda n, gsz: sel_inst.search(n) is not None
     af, an = mean(fr, att)
     aw, _ = mean(wr, att)
     # the plain copy: the blit dispatches with the grid of the 1 GiB copy, whose
@@ -235,8 +237,8 @@ def algorithmic_stats_bytes(seq_lens, H_kv, d, P, elem, scorer):
     return H_kv * int(np.sum([-(-int(n) // P) for n in seq_lens])) * 2 * d * elem
 
 
-def cpu_baseline(w, unit, r_kv, budget_s=12.0, selection=None, scorer="bounds"):
-    from oracle import sdref
+def cpu_baseline(w, unit, r_kv, budget_s=12.0, selection=None, scorer="bounds", alpha=None):
+    from oracle import entmaxref, sdref
     try:
         from threadpoolctl import threadpool_info
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
@@ -254,8 +256,12 @@ def cpu_baseline(w, unit, r_kv, budget_s=12.0, selection=None, scorer="bounds"):
         qg = sdref.widen(w.q[b, g * G:(g + 1) * G], r.dtype)
         Kg = sdref.widen(w.K[b, g, :n], r.dtype)
         Vg = sdref.widen(w.V[b, g, :n], r.dtype)
-        sdref.group_step(qg, Kg, Vg, unit=unit, page_size=r.page_size, r_kv=r_kv, scale=scale,
-                         selection=selection, scorer=scorer)
+        if alpha is None:
+            sdref.group_step(qg, Kg, Vg, unit=unit, page_size=r.page_size, r_kv=r_kv,
+                             scale=scale, selection=selection, scorer=scorer)
+        else:
+            entmaxref.group_step(qg, Kg, Vg, unit=unit, page_size=r.page_size, r_kv=r_kv,
+                                 scale=scale, alpha=alpha, selection=selection, scorer=scorer)
         done += 1
         el = time.perf_counter() - t0
         if el >= budget_s or done >= 4 * len(groups):
@@ -264,9 +270,11 @@ def cpu_baseline(w, unit, r_kv, budget_s=12.0, selection=None, scorer="bounds"):
     us_per_step = per_group * len(groups) * 1e6
     return {"value": round(us_per_step, 1), "unit": "us/step-layer", "cores": int(cores),
             "kind": "oracle",
-            "sample": f"{done} of the step's {len(groups)} (sequence, KV head) selection "
-                      f"instances of layer 0 run through oracle.sdref.group_step (fp64 numpy: "
-                      f"page bounds, scores, top-k, dense + sparse attention, delta) in "
+            "sample": f"{done} runs over the step's {len(groups)} (sequence, KV head) selection "
+                      f"instances of layer 0 through "
+                      f"{'oracle.sdref' if alpha is None else 'oracle.entmaxref'}.group_step "
+                      f"(fp64 numpy: page statistics, scores, top-k, dense + sparse "
+                      f"{'softmax' if alpha is None else f'{alpha:g}-entmax'} attention, delta) in "
                       f"{el:.1f} s; value = mean time per instance x {len(groups)}"}
 
 
@@ -296,6 +304,9 @@ def main():
     ap.add_argument("--init-units", type=int, default=1, help="init_local_topk: first units kept")
     ap.add_argument("--local-units", type=int, default=0,
                     help="init_local_topk: last units kept (0 = 2048 tokens' worth)")
+    ap.add_argument("--attention", default="softmax", choices=["softmax", "entmax"],
+                    help="attention over the kept set: softmax (default) or alpha-entmax")
+    ap.add_argument("--alpha", type=float, default=1.5, help="entmax alpha in (1, 2]")
     ap.add_argument("--copy-calibrate", action="store_true",
                     help="run a plain 1 GiB copy first (for counter passes)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -398,9 +409,17 @@ def main():
             "topk": ""}[args.selection]
         if args.scorer == "compressed":
             desc += "; pages scored from compressed keys (mean-pooled, kernel 32 stride 16)"
+    entmax = args.attention == "entmax"
+    if entmax:
+        desc += f"; {args.alpha:g}-entmax attention over the kept set (dense: every unit)"
     k_max = sd.selection_capacity(selection, shape.units_max(unit))
     ws = sd.alloc_workspace_sel(shape, unit, selection)
     ws_dense = sd.alloc_workspace(shape, unit, 1.0)
+    dense_sel = sd.Selection("topk", 1.0)
+    if entmax:
+        ws = sd.alloc_workspace_entmax(shape, unit, selection)
+        ws_dense = sd.alloc_workspace_entmax(shape, unit, dense_sel)
+        tau = torch.empty((rec.batch, H_q), dtype=torch.float32, device="cuda")
     out = torch.empty((rec.batch, H_q, d), dtype=torch.float32, device="cuda")
     lse = torch.empty((rec.batch, H_q), dtype=torch.float32, device="cuda")
     sels = [torch.empty((rec.batch, H_kv, k_max), dtype=torch.int32, device="cuda") for _ in range(L)]
@@ -409,7 +428,11 @@ def main():
 
     def sparse_step(i):
         lay = layers[i]
-        if structured:
+        if entmax:
+            sd.decode_step_entmax(shape, lay["q"], lay["k"], lay["v"], lay["bounds"], lay["bt"],
+                                  lay["sl"], unit, selection, args.alpha, out, ws, tau=tau,
+                                  sel_idx=sels[i], sel_count=cnts[i], stream=stream)
+        elif structured:
             sd.decode_step_sel(shape, lay["q"], lay["k"], lay["v"], lay["bounds"], lay["bt"],
                                lay["sl"], unit, selection, out, lse, ws, sels[i], cnts[i],
                                stream=stream)
@@ -419,8 +442,13 @@ def main():
 
     def dense_step(i):
         lay = layers[i]
-        sd.decode_step(shape, lay["q"], lay["k"], lay["v"], None, lay["bt"], lay["sl"],
-                       unit, 1.0, out, lse, ws_dense, stream=stream)
+        if entmax:
+            sd.decode_step_entmax(shape, lay["q"], lay["k"], lay["v"], None, lay["bt"], lay["sl"],
+                                  unit, dense_sel, args.alpha, out, ws_dense, tau=tau,
+                                  stream=stream)
+        else:
+            sd.decode_step(shape, lay["q"], lay["k"], lay["v"], None, lay["bt"], lay["sl"],
+                           unit, 1.0, out, lse, ws_dense, stream=stream)
 
     # scores of every layer, for timing the attention stage on its own
     umax = shape.units_max(unit)
@@ -493,8 +521,9 @@ def main():
     log(f"sparse step: {us_sparse:.2f} us/step-layer over {n_steps} steps ({'graph' if graph else 'eager'})")
     us_dense, _ = timed(dense_step, args.steps, args.warmup, graph)
     log(f"dense step:  {us_dense:.2f} us/step-layer")
-    us_attend, n_att = timed(attend_only, args.steps, args.warmup, graph)
-    log(f"attend alone (HIP events on its stream): {us_attend:.2f} us/launch")
+    if not entmax:
+        us_attend, n_att = timed(attend_only, args.steps, args.warmup, graph)
+        log(f"attend alone (HIP events on its stream): {us_attend:.2f} us/launch")
     us_sparse_eager, _ = timed(sparse_step, min(args.steps, 400), 10, False)
     log(f"sparse step eager: {us_sparse_eager:.2f} us/step-layer")
 
@@ -514,6 +543,12 @@ def main():
     b_attend = attend_bytes(kept_mean, d, elem, unit == "token" and not window)
     gbps = b_sparse / (us_sparse * 1e-6) / 1e9
     gbps_dense = b_dense / (us_dense * 1e-6) / 1e9
+    if entmax:
+        # The entmax step is several launches (scores, selection, logits of
+        # the kept tokens, thresholds, attention, merge) behind one entry
+        # point, so the roofline here is that of the whole step on its
+        # algorithmic bytes; per-kernel durations come from a kernel trace.
+        us_attend, b_attend = us_sparse, b_sparse
     gbps_att = b_attend / (us_attend * 1e-6) / 1e9
 
     result = {
@@ -546,7 +581,8 @@ def main():
         "byte_bound_speedup": round(b_dense / b_sparse, 3),
         "eager_us_per_step_layer": round(us_sparse_eager, 3),
         "roofline": {
-            "kernel": ("attend_mfma_kernel: split-K attention partials over the stored kept "
+            "kernel": ("whole alpha-entmax decode step (sd_decode_step_entmax)" if entmax else
+                       "attend_mfma_kernel: split-K attention partials over the stored kept "
                        "lists" if structured else
                        "attend_mfma_kernel: in-kernel top-k + split-K attention partials over "
                        "the kept pages" if unit == "page" else
@@ -554,7 +590,8 @@ def main():
                        "(stored logits)"),
             "bound": "hbm", "achieved": round(gbps_att, 1), "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": round(gbps_att / HBM_PEAK_GBPS, 4),
-            "traffic": read_traffic(args.workload) if unit == "page" and not structured else None,
+            "traffic": (read_traffic(args.workload)
+                        if unit == "page" and not structured and not entmax else None),
             "us_per_launch": round(us_attend, 3), "bytes_per_launch": int(b_attend),
         },
     }
@@ -562,9 +599,11 @@ def main():
         log("timing the CPU oracle on a bounded sample ...")
         result["cpu_baseline"] = cpu_baseline(
             w0, unit, r_kv, selection=None if not structured else sdref_selection(selection),
-            scorer=args.scorer)
+            scorer=args.scorer, alpha=args.alpha if entmax else None)
     if structured:
         result["config"].update(config_sel)
+    if entmax:
+        result["config"].update({"attention": "entmax", "alpha": args.alpha})
     print(json.dumps(result), flush=True)
 
 

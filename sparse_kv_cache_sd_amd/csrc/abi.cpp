@@ -597,10 +597,36 @@ sd_status entmax_impl(const sdkv::Dims& d, const void* q, const void* k_pages,
   int32_t* cnt = nullptr;
   sd_status st;
   bool have_logits = false;
+  const float am1 = static_cast<float>(alpha - 1.0);
+  const float beta = static_cast<float>(1.0 / (alpha - 1.0));
+  // Page unit, top-k or union, where the attention kernel can select: the
+  // logits-only pass selects the pages itself and writes the kept lists.
+  const bool fused = !dense && unit == SD_UNIT_PAGE &&
+                     (sel.kind == SD_SEL_TOPK || sel.kind == SD_SEL_INIT_LOCAL_TOPK) &&
+                     fused_select(d, unit, k_max);
   if (!dense) {
     idx = sel_idx ? sel_idx : reinterpret_cast<int32_t*>(at(ws, L.sel_idx));
     cnt = sel_count ? sel_count : reinterpret_cast<int32_t*>(at(ws, L.sel_count));
-    if (sel.kind == SD_SEL_WINDOW) {
+    if (fused) {
+      float* scores = reinterpret_cast<float*>(at(ws, L.scores));
+      if (sel.scorer == SD_SCORER_COMPRESSED)
+        st = do_score_compressed(d, q, static_cast<const float*>(page_stats), seq_lens, scores,
+                                 s);
+      else
+        st = do_score(d, q, k_pages, page_stats, block_table, seq_lens, unit, scores, nullptr, s);
+      if (st != SD_OK) return st;
+      ListMode lm;
+      lm.force_init = sel.init;
+      lm.force_local = sel.local;
+      Weights w;
+      w.logits_out = logits;
+      if ((st = do_partials(d, q, k_pages, v_pages, block_table, seq_lens, unit, nullptr, nullptr,
+                            k_max, nullptr, ws, s, scores, ratio_ppm(sel.r), idx, cnt, nullptr,
+                            lm, w)) != SD_OK)
+        return st;
+      have_logits = true;
+      st = SD_OK;
+    } else if (sel.kind == SD_SEL_WINDOW) {
       st = do_structure(d, unit, seq_lens, sel, nullptr, nullptr, 0, idx, cnt, k_max, s);
     } else {
       float* scores = reinterpret_cast<float*>(at(ws, L.scores));
@@ -621,8 +647,6 @@ sd_status entmax_impl(const sdkv::Dims& d, const void* q, const void* k_pages,
     }
     if (st != SD_OK) return st;
   }
-  const float am1 = static_cast<float>(alpha - 1.0);
-  const float beta = static_cast<float>(1.0 / (alpha - 1.0));
   if (!have_logits) {
     Weights w;
     w.logits_out = logits;

@@ -235,7 +235,7 @@ __global__ __launch_bounds__(kAttendWaves * 64) void attend_mfma_kernel(AttendAr
   constexpr int KEYS = SELECTS ? SEL : 1;
   constexpr bool TOK = LOGITS || WM == kWLogits;  // rows' token ids are kept
   static_assert(WM != kWEntmax || LOGITS, "entmax weights read stored logits");
-  static_assert(WM != kWLogits || (!LOGITS && !SELECTS), "logits are computed from a list");
+  static_assert(WM != kWLogits || !LOGITS, "logits are computed from K");
   // The V staging area is reused after the chunk loop for the per-wave outputs.
   constexpr int kStage = NW * 16 * VROW * 2;
   constexpr int kAfter = NW * G * D * 4;
@@ -734,7 +734,7 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
   const bool logits = a.token_logits != nullptr;
   const bool ent = a.tau != nullptr, wl = a.logits_out != nullptr;
   if (ent && (!logits || wl || selects)) return hipErrorInvalidValue;
-  if (wl && (logits || selects)) return hipErrorInvalidValue;
+  if (wl && logits) return hipErrorInvalidValue;
   if (ent && !(a.alpha_m1 > 0.f && a.alpha_m1 <= 1.f && a.beta >= 1.f)) return hipErrorInvalidValue;
   const bool ok = dispatch_tdg(d.dtype, d.D, d.G, [&](auto t, auto dd, auto gg) {
     using T = decltype(t);
@@ -744,10 +744,17 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
     if constexpr (std::is_same<T, float>::value) {
       attend_f32_kernel<D, G><<<grid, NT, 0, st>>>(a);
     } else if (selects) {
+      // the in-kernel top-k feeds softmax attention, or (logits only) the
+      // kept tokens' logits that entmax attention later reads
+      auto go = [&](auto sel) {
+        constexpr int SEL = decltype(sel)::value;
+        if (wl) attend_mfma_kernel<D, G, false, SEL, kWLogits><<<grid, NT, 0, st>>>(a);
+        else attend_mfma_kernel<D, G, false, SEL, kWSoftmax><<<grid, NT, 0, st>>>(a);
+      };
       switch (select_mode(d.max_pages)) {
-        case kBlock4: attend_mfma_kernel<D, G, false, kBlock4, kWSoftmax><<<grid, NT, 0, st>>>(a); break;
-        case kBlock8: attend_mfma_kernel<D, G, false, kBlock8, kWSoftmax><<<grid, NT, 0, st>>>(a); break;
-        default: attend_mfma_kernel<D, G, false, kBlock32, kWSoftmax><<<grid, NT, 0, st>>>(a); break;
+        case kBlock4: go(std::integral_constant<int, kBlock4>{}); break;
+        case kBlock8: go(std::integral_constant<int, kBlock8>{}); break;
+        default: go(std::integral_constant<int, kBlock32>{}); break;
       }
     } else if (wl) {
       attend_mfma_kernel<D, G, false, kListed, kWLogits><<<grid, NT, 0, st>>>(a);

@@ -6,31 +6,56 @@
 // weights over a kept set T are p_t = max((alpha - 1) z_t - tau, 0) ** beta,
 // beta = 1 / (alpha - 1), with tau chosen so that they sum to one over T.
 //
-// f(tau) = sum_t max((alpha - 1) z_t - tau, 0) ** beta - 1 is convex and
-// decreasing for 1 < alpha <= 2, with f((alpha - 1) max z - 1) >= 0 and
-// f((alpha - 1) max z) = -1.  Newton steps from the left end stay left of
-// the root (the tangent of a convex decreasing function lies below it), so
-// the iteration climbs monotonically; a bracket [lo, hi] with a bisection
-// step guards against rounding.  It stops when a step no longer moves tau
-// (typically 4-10 steps at alpha = 1.5; sparsemax ends exactly).
+// Root finding.  With t_i = (alpha - 1) z_i - tau and S0 = sum max(t_i, 0)^beta,
+// the root of S0 = 1 is the root of g(tau) = S0^(1/beta) - 1, the beta-norm of
+// the positive parts minus one.  g is convex and decreasing in tau (a norm,
+// monotone in each entry, of entries that are convex and decreasing in tau),
+// g((alpha - 1) max z - 1) >= 0, and g is linear when the positive t_i are
+// equal.  Newton steps on g from that left end therefore climb monotonically
+// to the root (the tangent of a convex decreasing function lies below it):
+//   tau += (S0 - S0^(2 - alpha)) / S1,   S1 = sum max(t_i, 0)^(beta - 1),
+// a handful of steps for any alpha in (1, 2] (sparsemax ends exactly).  The
+// iteration stops once S0 <= 1 (the root, up to rounding) or a step no longer
+// moves tau.  Every later tau is >= the first, so tokens with t_i <= 0 there
+// weigh 0 from then on and only the others ("candidates") take part.
 //
 // One 1024-thread block per (sequence, query head); block id
 // bg + B * H_kv * (h mod G) puts the G heads of a KV head on the XCD that
-// runs the attention blocks of that KV head.  The first 32768 kept tokens'
-// logits stay in registers (32 per thread) across the iteration; beyond that
-// they are re-read each step.  Sums run in a fixed order, so tau does not
-// depend on timing.
+// runs the attention blocks of that KV head.  The block gathers the kept
+// logits (the first 16384 into registers, 16 per thread), finds their max,
+// and compacts the candidates into LDS in slot order (wave ballots and
+// prefix offsets, so the order -- and with it every fp32 sum -- does not
+// depend on timing).  One wave then runs the Newton steps over the compacted
+// candidates with wave-level sums only.  With more than kTauCap candidates
+// the whole block iterates instead, over its registers and the rest of the
+// logits, re-read each step.
 #include "device.h"
 
 namespace sdkv {
 
 constexpr int kTauThreads = 1024;
-constexpr int kTauKeys = 32;
+constexpr int kTauKeys = 16;     // logits per thread held in registers
+constexpr int kTauCap = 12288;   // candidates compacted into LDS (48 KB)
+
+// Sum and max over the 64 lanes without the LDS crossbar: DPP within rows of
+// 16, then the gfx950 permlane swaps across rows.  Every lane gets the result.
+__device__ __forceinline__ float wave_sum_dpp(float x) {
+  x = group_sum<16>(x);
+  x = sum_xor16(x);
+  return sum_xor32(x);
+}
+__device__ __forceinline__ float wave_max_dpp(float x) {
+  x = group_max<16>(x);
+  x = max_xor16(x);
+  return max_xor32(x);
+}
 
 __global__ __launch_bounds__(kTauThreads) void entmax_tau_kernel(TauArgs a) {
   constexpr int NT = kTauThreads, NW = NT / 64, KPT = kTauKeys;
+  __shared__ float s_c[kTauCap];
   __shared__ float s_red[2][2][NW];
   __shared__ float s_max[NW];
+  __shared__ int s_cnt[NW];
   const Dims& d = a.d;
   const GroupBlock gb = group_block(d.B * d.Hkv);
   const int g = gb.bg % d.Hkv, b = gb.bg / d.Hkv, h = g * d.G + gb.j;
@@ -43,31 +68,45 @@ __global__ __launch_bounds__(kTauThreads) void entmax_tau_kernel(TauArgs a) {
   const int slots = pg ? cnt * d.P : cnt;
   const float* row = a.logits + ((int64_t)b * d.Hq + h) * d.max_seq;
   const int32_t* bt = a.block_table + (int64_t)b * d.max_pages;
+  const int lp = __builtin_ctz(d.P);  // P is a power of two (16 or 64)
 
-  // Logit of kept slot i (token i of the list, or row i % P of its page i / P),
-  // -inf where the attention kernel attends nothing.  Loads are issued with
-  // clamped indices and the result is selected afterwards.
-  auto slot_logit = [&](int i) -> float {
-    const int e = pg ? i / d.P : i;
-    const int u = list ? list[min(e, a.k_max - 1)] : e;
-    const int t = pg ? u * d.P + (i - e * d.P) : u;
+  // Slot i of the kept set is token i of the list, or row i % P of its page
+  // i / P.  unit_of(i) is the slot's list entry (one load, clamped in range,
+  // issued for any i >= 0); logit_of(i, u) is its logit, -inf where the
+  // attention kernel attends nothing or past the kept set.  Every load is
+  // issued with clamped indices and the result selected afterwards, so a
+  // lane's loads overlap instead of draining one slot at a time.
+  auto unit_of = [&](int i) -> int {
+    const int e = pg ? i >> lp : i;
+    return list ? list[min(e, a.k_max - 1)] : e;
+  };
+  auto logit_of = [&](int i, int u) -> float {
+    const int t = pg ? (u << lp) + (i & (d.P - 1)) : u;
     const int tc = t < 0 ? 0 : (t >= n ? max(n - 1, 0) : t);
-    const int ph = bt[min(tc / d.P, d.max_pages - 1)];
+    const int ph = bt[min(tc >> lp, d.max_pages - 1)];
     const float z = row[tc];
-    const bool ok = u >= 0 && u < U && t < n && ph >= 0 && ph < d.num_pages;
+    // bitwise, not short-circuit: a && chain lets the compiler sink the
+    // block-table and logit loads under a branch, one slot at a time
+    const bool ok = (i < slots) & (u >= 0) & (u < U) & (t < n) & (ph >= 0) &
+                    ((int64_t)ph < d.num_pages);
     return ok ? z : -INFINITY;
   };
+  auto slot_logit = [&](int i) -> float { return logit_of(i, unit_of(i)); };
 
   float lg[KPT];
   float mx = -INFINITY;
+  {
+    int uu[KPT];
 #pragma unroll
-  for (int r = 0; r < KPT; ++r) {
-    const int i = r * NT + tid;
-    lg[r] = i < slots ? slot_logit(i) : -INFINITY;
-    mx = fmaxf(mx, lg[r]);
+    for (int r = 0; r < KPT; ++r) uu[r] = unit_of(r * NT + tid);
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) {
+      lg[r] = logit_of(r * NT + tid, uu[r]);
+      mx = fmaxf(mx, lg[r]);
+    }
   }
   for (int i = KPT * NT + tid; i < slots; i += NT) mx = fmaxf(mx, slot_logit(i));
-  mx = wave_max(mx);
+  mx = wave_max_dpp(mx);
   if (lane == 0) s_max[wave] = mx;
   __syncthreads();
   mx = -INFINITY;
@@ -80,35 +119,89 @@ __global__ __launch_bounds__(kTauThreads) void entmax_tau_kernel(TauArgs a) {
   }
 
   const float am1 = a.alpha_m1, beta = a.beta;
-  // s0 = sum of weights, s1 = sum of weight / t (= -f'(tau) / beta)
+  const float lo = am1 * mx - 1.f;  // g(lo) >= 0: the largest term alone is ~1
+  auto is_cand = [&](float z) { return fmaf(am1, z, -lo) > 0.f; };
+  const int tail_rounds = slots > KPT * NT ? (slots - KPT * NT + NT - 1) / NT : 0;
+
+  // Candidates per wave, in slot order: registers r = 0..KPT-1, then the
+  // tail rounds, lanes in order within each.
+  const uint64_t below = (1ull << lane) - 1ull;
+  int wc = 0;
+#pragma unroll
+  for (int r = 0; r < KPT; ++r) wc += __popcll(__ballot(is_cand(lg[r])));
+  for (int k = 0; k < tail_rounds; ++k) {
+    const int i = KPT * NT + k * NT + tid;
+    wc += __popcll(__ballot(i < slots && is_cand(slot_logit(i))));
+  }
+  if (lane == 0) s_cnt[wave] = wc;
+  __syncthreads();
+  int base = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    base += w < wave ? s_cnt[w] : 0;
+    total += s_cnt[w];
+  }
+
   auto accum = [&](float z, float tau, float& s0, float& s1) {
     const float t = fmaf(am1, z, -tau);
     const float w = entmax_weight(t, beta);
     s0 += w;
     s1 += t > 0.f ? (beta == 2.f ? t : (beta == 1.f ? 1.f : w / t)) : 0.f;
   };
-  const float top = am1 * mx;
-  float lo = top - 1.f, hi = top, tau = lo;
-  for (int it = 0; it < 64; ++it) {
-    float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-    for (int r = 0; r < KPT; ++r) accum(lg[r], tau, s0, s1);
-    for (int i = KPT * NT + tid; i < slots; i += NT) accum(slot_logit(i), tau, s0, s1);
-    s0 = wave_sum(s0);
-    s1 = wave_sum(s1);
-    const int par = it & 1;
-    if (lane == 0) { s_red[par][0][wave] = s0; s_red[par][1][wave] = s1; }
-    __syncthreads();
-    s0 = 0.f; s1 = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) { s0 += s_red[par][0][w]; s1 += s_red[par][1][w]; }
-    const float f = s0 - 1.f;
-    if (f >= 0.f) lo = tau; else hi = tau;
-    float nt = tau + f / (beta * s1);
-    if (f == 0.f || nt == tau) break;
-    if (!(nt > lo && nt < hi)) nt = 0.5f * (lo + hi);
-    if (nt == tau) break;
+  // Newton step from the sums; returns false when the iteration ends.
+  const float e_sub = 1.f - am1;  // S0^(1 - 1/beta) = S0^(2 - alpha)
+  auto step = [&](float s0, float s1, float& tau) -> bool {
+    if (!(s0 > 1.f)) return false;  // at the root, up to rounding
+    const float sub = beta == 1.f ? 1.f : (beta == 2.f ? sqrtf(s0) : exp2f(e_sub * log2f(s0)));
+    const float nt = tau + (s0 - sub) / s1;
+    if (!(nt > tau)) return false;  // the step no longer moves tau
     tau = nt;
+    return true;
+  };
+
+  float tau = lo;
+  if (total <= kTauCap) {
+    int pos = base;
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) {
+      const bool c = is_cand(lg[r]);
+      const uint64_t m = __ballot(c);
+      if (c) s_c[pos + __popcll(m & below)] = lg[r];
+      pos += __popcll(m);
+    }
+    for (int k = 0; k < tail_rounds; ++k) {
+      const int i = KPT * NT + k * NT + tid;
+      const float z = slot_logit(i);
+      const bool c = i < slots && is_cand(z);
+      const uint64_t m = __ballot(c);
+      if (c) s_c[pos + __popcll(m & below)] = z;
+      pos += __popcll(m);
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    for (int it = 0; it < 64; ++it) {
+      float s0 = 0.f, s1 = 0.f;
+      for (int j = lane; j < total; j += 64) accum(s_c[j], tau, s0, s1);
+      s0 = wave_sum_dpp(s0);
+      s1 = wave_sum_dpp(s1);
+      if (!step(s0, s1, tau)) break;
+    }
+  } else {
+    for (int it = 0; it < 64; ++it) {
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int r = 0; r < KPT; ++r) accum(lg[r], tau, s0, s1);
+      for (int i = KPT * NT + tid; i < slots; i += NT) accum(slot_logit(i), tau, s0, s1);
+      s0 = wave_sum_dpp(s0);
+      s1 = wave_sum_dpp(s1);
+      const int par = it & 1;
+      if (lane == 0) { s_red[par][0][wave] = s0; s_red[par][1][wave] = s1; }
+      __syncthreads();
+      s0 = 0.f; s1 = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) { s0 += s_red[par][0][w]; s1 += s_red[par][1][w]; }
+      if (!step(s0, s1, tau)) break;
+    }
   }
   if (tid == 0) *out = tau;
 }
@@ -117,6 +210,7 @@ hipError_t launch_entmax_tau(const TauArgs& a, hipStream_t st) {
   const Dims& d = a.d;
   if (!(a.alpha_m1 > 0.f && a.alpha_m1 <= 1.f) || !(a.beta >= 1.f)) return hipErrorInvalidValue;
   if (a.sel_idx && (a.k_max < 1 || !a.sel_count)) return hipErrorInvalidValue;
+  if (d.P != 16 && d.P != 64) return hipErrorInvalidValue;
   entmax_tau_kernel<<<dim3(d.B * d.Hq), kTauThreads, 0, st>>>(a);
   return hipGetLastError();
 }

@@ -229,3 +229,22 @@ def test_entmax_rejects_bad_alpha():
     for bad in (1.0, 0.9, 2.5, float("nan")):
         with pytest.raises(sd.SdError, match="SD_E_RATIO"):
             _run(dev, "page", sel, bad)
+
+
+@pytest.mark.parametrize("alpha", [1.5, 1.25])
+def test_entmax_flat_logits_many_candidates(alpha):
+    """q = 0: every logit is 0, every kept token is a candidate and the weights
+    are uniform.  With 36000 kept tokens the threshold kernel holds 16384 in
+    registers and has more candidates per thread than its LDS slots, so it
+    re-reads the rest each step."""
+    rec = R["tiny"].with_(seq_len=40000, seed=22)
+    w = kvsynth.generate(rec)
+    w.q[...] = 0
+    dev = upload(w)
+    sel = sd.Selection("topk", 0.9)
+    res = _run(dev, "token", sel, alpha)
+    _compare(w, dev, "token", sel, alpha, res)
+    k = int(res[3][0, 0])
+    # tau solves k * (-tau)^beta = 1
+    want = -(1.0 / k) ** (alpha - 1.0)
+    assert np.abs(res[1][0] - want).max() <= 1e-6
