@@ -36,6 +36,7 @@ namespace sdkv {
 constexpr int kTauThreads = 1024;
 constexpr int kTauKeys = 16;     // logits per thread held in registers
 constexpr int kTauCap = 12288;   // candidates compacted into LDS (48 KB)
+constexpr int kTauBatch = 8;     // tail rounds whose loads are issued together
 
 // Sum and max over the 64 lanes without the LDS crossbar: DPP within rows of
 // 16, then the gfx950 permlane swaps across rows.  Every lane gets the result.
@@ -91,7 +92,24 @@ __global__ __launch_bounds__(kTauThreads) void entmax_tau_kernel(TauArgs a) {
                     ((int64_t)ph < d.num_pages);
     return ok ? z : -INFINITY;
   };
-  auto slot_logit = [&](int i) -> float { return logit_of(i, unit_of(i)); };
+  // Slots past the registers, in rounds of NT (round k covers slots
+  // KPT * NT + k * NT + tid): fn(z) sees every lane's logit of every round in
+  // a fixed order (rounds past the end give -inf, and fn is called on every
+  // lane, so it may use wave ballots).  Rounds are loaded kTauBatch at a
+  // time, list entries first and logits second, so their loads overlap.
+  const int tail_rounds = slots > KPT * NT ? (slots - KPT * NT + NT - 1) / NT : 0;
+  auto for_tail = [&](auto&& fn) {
+    for (int k0 = 0; k0 < tail_rounds; k0 += kTauBatch) {
+      int uu[kTauBatch];
+      float zz[kTauBatch];
+#pragma unroll
+      for (int t = 0; t < kTauBatch; ++t) uu[t] = unit_of(KPT * NT + (k0 + t) * NT + tid);
+#pragma unroll
+      for (int t = 0; t < kTauBatch; ++t) zz[t] = logit_of(KPT * NT + (k0 + t) * NT + tid, uu[t]);
+#pragma unroll
+      for (int t = 0; t < kTauBatch; ++t) fn(zz[t]);
+    }
+  };
 
   float lg[KPT];
   float mx = -INFINITY;
@@ -105,7 +123,7 @@ __global__ __launch_bounds__(kTauThreads) void entmax_tau_kernel(TauArgs a) {
       mx = fmaxf(mx, lg[r]);
     }
   }
-  for (int i = KPT * NT + tid; i < slots; i += NT) mx = fmaxf(mx, slot_logit(i));
+  for_tail([&](float z) { mx = fmaxf(mx, z); });
   mx = wave_max_dpp(mx);
   if (lane == 0) s_max[wave] = mx;
   __syncthreads();
@@ -120,8 +138,7 @@ __global__ __launch_bounds__(kTauThreads) void entmax_tau_kernel(TauArgs a) {
 
   const float am1 = a.alpha_m1, beta = a.beta;
   const float lo = am1 * mx - 1.f;  // g(lo) >= 0: the largest term alone is ~1
-  auto is_cand = [&](float z) { return fmaf(am1, z, -lo) > 0.f; };
-  const int tail_rounds = slots > KPT * NT ? (slots - KPT * NT + NT - 1) / NT : 0;
+  auto is_cand = [&](float z) { return fmaf(am1, z, -lo) > 0.f; };  // false for -inf
 
   // Candidates per wave, in slot order: registers r = 0..KPT-1, then the
   // tail rounds, lanes in order within each.
@@ -129,10 +146,7 @@ __global__ __launch_bounds__(kTauThreads) void entmax_tau_kernel(TauArgs a) {
   int wc = 0;
 #pragma unroll
   for (int r = 0; r < KPT; ++r) wc += __popcll(__ballot(is_cand(lg[r])));
-  for (int k = 0; k < tail_rounds; ++k) {
-    const int i = KPT * NT + k * NT + tid;
-    wc += __popcll(__ballot(i < slots && is_cand(slot_logit(i))));
-  }
+  for_tail([&](float z) { wc += __popcll(__ballot(is_cand(z))); });
   if (lane == 0) s_cnt[wave] = wc;
   __syncthreads();
   int base = 0, total = 0;
@@ -169,14 +183,12 @@ __global__ __launch_bounds__(kTauThreads) void entmax_tau_kernel(TauArgs a) {
       if (c) s_c[pos + __popcll(m & below)] = lg[r];
       pos += __popcll(m);
     }
-    for (int k = 0; k < tail_rounds; ++k) {
-      const int i = KPT * NT + k * NT + tid;
-      const float z = slot_logit(i);
-      const bool c = i < slots && is_cand(z);
+    for_tail([&](float z) {
+      const bool c = is_cand(z);
       const uint64_t m = __ballot(c);
       if (c) s_c[pos + __popcll(m & below)] = z;
       pos += __popcll(m);
-    }
+    });
     __syncthreads();
     if (wave != 0) return;
     for (int it = 0; it < 64; ++it) {
@@ -191,7 +203,7 @@ __global__ __launch_bounds__(kTauThreads) void entmax_tau_kernel(TauArgs a) {
       float s0 = 0.f, s1 = 0.f;
 #pragma unroll
       for (int r = 0; r < KPT; ++r) accum(lg[r], tau, s0, s1);
-      for (int i = KPT * NT + tid; i < slots; i += NT) accum(slot_logit(i), tau, s0, s1);
+      for_tail([&](float z) { accum(z, tau, s0, s1); });
       s0 = wave_sum_dpp(s0);
       s1 = wave_sum_dpp(s1);
       const int par = it & 1;
