@@ -110,3 +110,70 @@ def test_full_size(cid, name, context, unit, r_kv, groups):
     e_o, e_l = compare_step(dev, unit, r_kv, groups=groups)
     print(f"[fullsize] {cid}: {len(groups)} instances vs oracle, max-abs out {e_o:.2e} "
           f"lse {e_l:.2e}", flush=True)
+
+
+# ---------------------------------------------------------------- alpha-entmax
+
+def _entmax_step(dev, unit: str, r_kv: float, alpha: float):
+    s = dev.shape
+    sel = sd.Selection("topk", r_kv)
+    cap = sd.selection_capacity(sel, s.units_max(unit))
+    ws = sd.alloc_workspace_entmax(s, unit, sel)
+    out = torch.full((s.batch, s.num_q_heads, s.head_dim), float("nan"), device="cuda")
+    tau = torch.full((s.batch, s.num_q_heads), float("nan"), device="cuda")
+    idx = torch.full((s.batch, s.num_kv_heads, cap), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((s.batch, s.num_kv_heads), -7, dtype=torch.int32, device="cuda")
+    sd.decode_step_entmax(s, dev.q, dev.k, dev.v, dev.bounds, dev.bt, dev.sl, unit, sel, alpha,
+                          out, ws, tau=tau, sel_idx=idx, sel_count=cnt)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), tau.cpu().numpy(), idx.cpu().numpy(), cnt.cpu().numpy()
+
+
+ENTMAX_CASES = [
+    ("l8b-32k-page-0.3", "l8b", None, "page", 0.3, "all"),
+    ("sweep-128k-token-0.3", "sweep", 128 * K, "token", 0.3, [(0, 2), (0, 5)]),
+    ("l70b-128k-page-0.05", "l70b", 128 * K, "page", 0.05, "all"),
+    ("batch-page-0.2", "batch", None, "page", 0.2, "extremes"),
+    ("l70b-1m-page-0.05", "l70b", 1024 * K, "page", 0.05, [(0, 3)]),
+]
+
+
+@pytest.mark.parametrize("cid,name,context,unit,r_kv,groups", ENTMAX_CASES,
+                         ids=[c[0] for c in ENTMAX_CASES])
+def test_full_size_entmax(cid, name, context, unit, r_kv, groups):
+    """1.5-entmax over the kept set at full size: the kept lists are the
+    softmax path's (the top-k of the library's own scores for every
+    instance), and sampled instances match the fp64 entmax oracle (gap rule
+    for the set; out max-abs 2e-2, tau 1e-3)."""
+    from oracle import entmaxref
+    from gpu_util import GAP, check_selection
+    print(f"[fullsize] entmax {cid}", flush=True)
+    alpha = 1.5
+    dev = _dev(name, context)
+    s, w = dev.shape, dev.w
+    out, tau, idx, cnt = _entmax_step(dev, unit, r_kv, alpha)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(tau))
+    _own_topk_property(dev, unit, r_kv, idx, cnt)
+    if groups == "all":
+        groups = [(b, g) for b in range(s.batch) for g in range(s.num_kv_heads)]
+    elif groups == "extremes":
+        lens = w.seq_lens
+        groups = [(int(np.argmin(lens)), 0), (int(np.argmax(lens)), 7)]
+    G, scale = s.group, 1.0 / math.sqrt(s.head_dim)
+    e_o = e_t = 0.0
+    for b, g in groups:
+        n = int(w.seq_lens[b])
+        args = (sdref.widen(w.q[b, g * G:(g + 1) * G], s.dtype), sdref.widen(w.K[b, g, :n], s.dtype),
+                sdref.widen(w.V[b, g, :n], s.dtype))
+        kw = dict(unit=unit, page_size=s.page_size, r_kv=r_kv, scale=scale, alpha=alpha)
+        orc = entmaxref.group_step(*args, **kw)
+        kept = idx[b, g, :int(cnt[b, g])].astype(np.int64)
+        if not check_selection(kept, orc):
+            orc = entmaxref.group_step(*args, kept_override=kept, **kw)
+        heads = slice(g * G, (g + 1) * G)
+        eo = float(np.abs(out[b, heads] - orc.out_sparse).max())
+        et = float(np.abs(tau[b, heads] - orc.tau_sparse).max())
+        assert eo <= 2e-2 and et <= 1e-3, f"(b={b}, g={g}) out {eo} tau {et}"
+        e_o, e_t = max(e_o, eo), max(e_t, et)
+    print(f"[fullsize] entmax {cid}: {len(groups)} instances vs oracle, max-abs out {e_o:.2e} "
+          f"tau {e_t:.2e}", flush=True)
