@@ -556,8 +556,17 @@ sd_status decode_impl(const sdkv::Dims& d, const void* q, const void* k_pages,
 // reported: the entmax weights already sum to one).
 struct EntLayout {
   Layout L;
-  size_t logits, tau, lse, total;
+  size_t logits, tau, lse, cand, cmax, ccnt, total;
+  int nch;  // threshold chunks per head (0: one block per head)
 };
+
+// Most kept token slots of one head: the kept list's units (token unit) or
+// their pages' rows (page unit); every unit when nothing is dropped.
+int64_t entmax_slots(const sdkv::Dims& d, int unit, const Sel& sel) {
+  const bool dense = sel.r >= 1.0 && sel.kind != SD_SEL_MASS_BUDGET;
+  const int64_t units = dense ? units_max(d, unit) : capacity(sel, units_max(d, unit));
+  return unit == SD_UNIT_PAGE ? units * d.P : units;
+}
 
 EntLayout ent_layout(const sdkv::Dims& d, int unit, const Sel& sel) {
   EntLayout E{};
@@ -571,6 +580,12 @@ EntLayout ent_layout(const sdkv::Dims& d, int unit, const Sel& sel) {
   }
   E.tau = off;  off = align_up(off + sizeof(float) * bh);
   E.lse = off;  off = align_up(off + sizeof(float) * bh);
+  const int64_t slots = entmax_slots(d, unit, sel);
+  E.nch = slots > sdkv::kTauChunk ? static_cast<int>(ceil_div(slots, sdkv::kTauChunk)) : 0;
+  const int64_t hc = bh * E.nch;
+  E.cand = off; off = align_up(off + sizeof(float) * hc * sdkv::kTauChunkCap);
+  E.cmax = off; off = align_up(off + sizeof(float) * hc);
+  E.ccnt = off; off = align_up(off + sizeof(int32_t) * hc);
   E.total = off;
   return E;
 }
@@ -656,7 +671,9 @@ sd_status entmax_impl(const sdkv::Dims& d, const void* q, const void* k_pages,
       return st;
   }
   sdkv::TauArgs ta{d, unit, seq_lens, block_table, idx, cnt, idx ? k_max : 0, logits, am1, beta,
-                   tau};
+                   tau, E.nch, reinterpret_cast<float*>(at(ws, E.cand)),
+                   reinterpret_cast<float*>(at(ws, E.cmax)),
+                   reinterpret_cast<int32_t*>(at(ws, E.ccnt))};
   if ((st = device_status(sdkv::launch_entmax_tau(ta, s), "entmax threshold kernel launch")) !=
       SD_OK)
     return st;

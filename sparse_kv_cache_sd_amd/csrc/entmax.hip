@@ -17,26 +17,32 @@
 // a handful of steps for any alpha in (1, 2] (sparsemax ends exactly).  The
 // iteration stops once S0 <= 1 (the root, up to rounding) or a step no longer
 // moves tau.  Every later tau is >= the first, so tokens with t_i <= 0 there
-// weigh 0 from then on and only the others ("candidates") take part.
+// weigh exactly 0 at every step: only the others ("candidates") take part,
+// and summing a superset of them changes nothing.
 //
-// One 1024-thread block per (sequence, query head); block id
-// bg + B * H_kv * (h mod G) puts the G heads of a KV head on the XCD that
-// runs the attention blocks of that KV head.  The block gathers the kept
-// logits (the first 16384 into registers, 16 per thread), finds their max,
-// and compacts the candidates into LDS in slot order (wave ballots and
-// prefix offsets, so the order -- and with it every fp32 sum -- does not
-// depend on timing).  One wave then runs the Newton steps over the compacted
-// candidates with wave-level sums only.  With more than kTauCap candidates
-// the whole block iterates instead, over its registers and the rest of the
-// logits, re-read each step.
+// Up to kTauChunk (16384) kept slots per head, one 1024-thread block per
+// (sequence, query head) holds the logits in registers (16 per thread),
+// finds their max, compacts the candidates into LDS in slot order (wave
+// ballots and prefix offsets) and lets one wave run the Newton steps with
+// wave-level sums only.  With more slots, chunks of kTauChunk slots go to
+// blocks of their own, which leave their max and the slots within
+// 1 / (alpha - 1) of it (a superset of the candidates, since a chunk's max
+// never exceeds the head's) in the workspace; a merge block per head keeps
+// those within reach of the head's max, in chunk order, and iterates as
+// above, in a fixed order.  If the candidates do not fit (very flat logits),
+// the whole block iterates over every kept logit, re-read each step.  Block ids keep bg =
+// (sequence, KV head) fastest, so all blocks of a KV head share the XCD of
+// its attention blocks.  Sums run in a fixed order, so tau does not depend
+// on timing.
 #include "device.h"
 
 namespace sdkv {
 
 constexpr int kTauThreads = 1024;
-constexpr int kTauKeys = 16;     // logits per thread held in registers
+constexpr int kTauKeys = kTauChunk / kTauThreads;  // logits per thread in registers
 constexpr int kTauCap = 12288;   // candidates compacted into LDS (48 KB)
-constexpr int kTauBatch = 8;     // tail rounds whose loads are issued together
+constexpr int kTauBatch = 8;     // rounds whose loads are issued together
+static_assert(kTauKeys * kTauThreads == kTauChunk, "a chunk fills the registers");
 
 // Sum and max over the 64 lanes without the LDS crossbar: DPP within rows of
 // 16, then the gfx950 permlane swaps across rows.  Every lane gets the result.
@@ -51,6 +57,149 @@ __device__ __forceinline__ float wave_max_dpp(float x) {
   return max_xor32(x);
 }
 
+// The kept slots of one (sequence, query head).  Slot i is token i of the
+// list, or row i % P of its page i / P.  unit_of(i) is the slot's list entry
+// (one load, clamped in range, issued for any i >= 0); logit_of(i, u) is its
+// logit, -inf where the attention kernel attends nothing or past the kept
+// set.  Every load is issued with clamped indices and the result selected
+// afterwards, so a lane's loads overlap instead of draining one slot at a
+// time.
+struct Slots {
+  const int32_t* list;
+  const int32_t* bt;
+  const float* row;
+  int k_max, n, U, slots, lp, P, max_pages;
+  int64_t num_pages;
+  bool pg;
+
+  __device__ Slots(const TauArgs& a, int b, int bg, int h) {
+    const Dims& d = a.d;
+    n = clamp_len(a.seq_lens[b], d.max_seq);
+    pg = a.unit == kPage;
+    P = d.P;
+    lp = __builtin_ctz(d.P);  // P is a power of two (16 or 64)
+    U = pg ? (n + d.P - 1) / d.P : n;
+    list = a.sel_idx ? a.sel_idx + (int64_t)bg * a.k_max : nullptr;
+    k_max = a.k_max;
+    const int cnt = list ? max(0, min(a.sel_count[bg], a.k_max)) : U;
+    slots = pg ? cnt * d.P : cnt;
+    row = a.logits + ((int64_t)b * d.Hq + h) * d.max_seq;
+    bt = a.block_table + (int64_t)b * d.max_pages;
+    max_pages = d.max_pages;
+    num_pages = d.num_pages;
+  }
+  __device__ __forceinline__ int unit_of(int i) const {
+    const int e = pg ? i >> lp : i;
+    return list ? list[min(e, k_max - 1)] : e;
+  }
+  __device__ __forceinline__ float logit_of(int i, int u) const {
+    const int t = pg ? (u << lp) + (i & (P - 1)) : u;
+    const int tc = t < 0 ? 0 : (t >= n ? max(n - 1, 0) : t);
+    const int ph = bt[min(tc >> lp, max_pages - 1)];
+    const float z = row[tc];
+    // bitwise, not short-circuit: a && chain lets the compiler sink the
+    // block-table and logit loads under a branch, one slot at a time
+    const bool ok = (i < slots) & (u >= 0) & (u < U) & (t < n) & (ph >= 0) &
+                    ((int64_t)ph < num_pages);
+    return ok ? z : -INFINITY;
+  }
+  // fn(z) for every slot in [from, to), in rounds of kTauThreads (round k
+  // covers slots from + k * NT + tid; slots past `to` give -inf), on every
+  // lane, kTauBatch rounds' loads issued together.
+  template <typename Fn>
+  __device__ __forceinline__ void for_range(int from, int to, Fn&& fn) const {
+    constexpr int NT = kTauThreads;
+    const int tid = threadIdx.x;
+    const int rounds = to > from ? (to - from + NT - 1) / NT : 0;
+    for (int k0 = 0; k0 < rounds; k0 += kTauBatch) {
+      int uu[kTauBatch];
+      float zz[kTauBatch];
+#pragma unroll
+      for (int t = 0; t < kTauBatch; ++t) uu[t] = unit_of(from + (k0 + t) * NT + tid);
+#pragma unroll
+      for (int t = 0; t < kTauBatch; ++t) {
+        const int i = from + (k0 + t) * NT + tid;
+        const float z = logit_of(i, uu[t]);
+        zz[t] = i < to ? z : -INFINITY;
+      }
+#pragma unroll
+      for (int t = 0; t < kTauBatch; ++t) fn(zz[t]);
+    }
+  }
+};
+
+// The alpha-entmax arithmetic of one head.
+struct Newton {
+  float am1, beta, e_sub;
+  __device__ Newton(const TauArgs& a) : am1(a.alpha_m1), beta(a.beta), e_sub(1.f - a.alpha_m1) {}
+  // s0 = sum of weights, s1 = sum of weight / t (= -f'(tau) / beta)
+  __device__ __forceinline__ void accum(float z, float tau, float& s0, float& s1) const {
+    const float t = fmaf(am1, z, -tau);
+    const float w = entmax_weight(t, beta);
+    s0 += w;
+    s1 += t > 0.f ? (beta == 2.f ? t : (beta == 1.f ? 1.f : w / t)) : 0.f;
+  }
+  // Newton step on g from the sums; false when the iteration ends.
+  __device__ __forceinline__ bool step(float s0, float s1, float& tau) const {
+    if (!(s0 > 1.f)) return false;  // at the root, up to rounding
+    const float sub = beta == 1.f ? 1.f : (beta == 2.f ? sqrtf(s0) : exp2f(e_sub * log2f(s0)));
+    const float nt = tau + (s0 - sub) / s1;
+    if (!(nt > tau)) return false;  // the step no longer moves tau
+    tau = nt;
+    return true;
+  }
+  __device__ __forceinline__ bool cand(float z, float lo) const { return fmaf(am1, z, -lo) > 0.f; }
+};
+
+// Block-wide max of a per-thread value (every thread gets it).
+template <int NW>
+__device__ __forceinline__ float block_max(float v, float* s_max) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  v = wave_max_dpp(v);
+  if (lane == 0) s_max[wave] = v;
+  __syncthreads();
+  v = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) v = fmaxf(v, s_max[w]);
+  return v;
+}
+
+// Newton steps by one wave over n values at s_c; returns tau.
+__device__ __forceinline__ float newton_wave(const Newton& nw, const float* s_c, int n, float tau) {
+  const int lane = threadIdx.x & 63;
+  for (int it = 0; it < 64; ++it) {
+    float s0 = 0.f, s1 = 0.f;
+    for (int j = lane; j < n; j += 64) nw.accum(s_c[j], tau, s0, s1);
+    s0 = wave_sum_dpp(s0);
+    s1 = wave_sum_dpp(s1);
+    if (!nw.step(s0, s1, tau)) break;
+  }
+  return tau;
+}
+
+// Newton steps by the whole block over every kept logit, re-read each step
+// (the fallback for candidates that do not fit in LDS).
+template <int NW>
+__device__ __forceinline__ float newton_block(const Newton& nw, const Slots& sl, float tau,
+                                              float (*s_red)[2][NW]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int it = 0; it < 64; ++it) {
+    float s0 = 0.f, s1 = 0.f;
+    sl.for_range(0, sl.slots, [&](float z) { nw.accum(z, tau, s0, s1); });
+    s0 = wave_sum_dpp(s0);
+    s1 = wave_sum_dpp(s1);
+    const int par = it & 1;
+    if (lane == 0) { s_red[par][0][wave] = s0; s_red[par][1][wave] = s1; }
+    __syncthreads();
+    s0 = 0.f; s1 = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) { s0 += s_red[par][0][w]; s1 += s_red[par][1][w]; }
+    if (!nw.step(s0, s1, tau)) break;
+  }
+  return tau;
+}
+
+// One block per head, at most kTauChunk kept slots.
 __global__ __launch_bounds__(kTauThreads) void entmax_tau_kernel(TauArgs a) {
   constexpr int NT = kTauThreads, NW = NT / 64, KPT = kTauKeys;
   __shared__ float s_c[kTauCap];
@@ -61,92 +210,43 @@ __global__ __launch_bounds__(kTauThreads) void entmax_tau_kernel(TauArgs a) {
   const GroupBlock gb = group_block(d.B * d.Hkv);
   const int g = gb.bg % d.Hkv, b = gb.bg / d.Hkv, h = g * d.G + gb.j;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = clamp_len(a.seq_lens[b], d.max_seq);
-  const bool pg = a.unit == kPage;
-  const int U = pg ? (n + d.P - 1) / d.P : n;
-  const int32_t* list = a.sel_idx ? a.sel_idx + (int64_t)gb.bg * a.k_max : nullptr;
-  const int cnt = list ? max(0, min(a.sel_count[gb.bg], a.k_max)) : U;
-  const int slots = pg ? cnt * d.P : cnt;
-  const float* row = a.logits + ((int64_t)b * d.Hq + h) * d.max_seq;
-  const int32_t* bt = a.block_table + (int64_t)b * d.max_pages;
-  const int lp = __builtin_ctz(d.P);  // P is a power of two (16 or 64)
-
-  // Slot i of the kept set is token i of the list, or row i % P of its page
-  // i / P.  unit_of(i) is the slot's list entry (one load, clamped in range,
-  // issued for any i >= 0); logit_of(i, u) is its logit, -inf where the
-  // attention kernel attends nothing or past the kept set.  Every load is
-  // issued with clamped indices and the result selected afterwards, so a
-  // lane's loads overlap instead of draining one slot at a time.
-  auto unit_of = [&](int i) -> int {
-    const int e = pg ? i >> lp : i;
-    return list ? list[min(e, a.k_max - 1)] : e;
-  };
-  auto logit_of = [&](int i, int u) -> float {
-    const int t = pg ? (u << lp) + (i & (d.P - 1)) : u;
-    const int tc = t < 0 ? 0 : (t >= n ? max(n - 1, 0) : t);
-    const int ph = bt[min(tc >> lp, d.max_pages - 1)];
-    const float z = row[tc];
-    // bitwise, not short-circuit: a && chain lets the compiler sink the
-    // block-table and logit loads under a branch, one slot at a time
-    const bool ok = (i < slots) & (u >= 0) & (u < U) & (t < n) & (ph >= 0) &
-                    ((int64_t)ph < d.num_pages);
-    return ok ? z : -INFINITY;
-  };
-  // Slots past the registers, in rounds of NT (round k covers slots
-  // KPT * NT + k * NT + tid): fn(z) sees every lane's logit of every round in
-  // a fixed order (rounds past the end give -inf, and fn is called on every
-  // lane, so it may use wave ballots).  Rounds are loaded kTauBatch at a
-  // time, list entries first and logits second, so their loads overlap.
-  const int tail_rounds = slots > KPT * NT ? (slots - KPT * NT + NT - 1) / NT : 0;
-  auto for_tail = [&](auto&& fn) {
-    for (int k0 = 0; k0 < tail_rounds; k0 += kTauBatch) {
-      int uu[kTauBatch];
-      float zz[kTauBatch];
-#pragma unroll
-      for (int t = 0; t < kTauBatch; ++t) uu[t] = unit_of(KPT * NT + (k0 + t) * NT + tid);
-#pragma unroll
-      for (int t = 0; t < kTauBatch; ++t) zz[t] = logit_of(KPT * NT + (k0 + t) * NT + tid, uu[t]);
-#pragma unroll
-      for (int t = 0; t < kTauBatch; ++t) fn(zz[t]);
-    }
-  };
+  const Slots sl(a, b, gb.bg, h);
+  const Newton nw(a);
 
   float lg[KPT];
   float mx = -INFINITY;
   {
     int uu[KPT];
 #pragma unroll
-    for (int r = 0; r < KPT; ++r) uu[r] = unit_of(r * NT + tid);
+    for (int r = 0; r < KPT; ++r) uu[r] = sl.unit_of(r * NT + tid);
 #pragma unroll
     for (int r = 0; r < KPT; ++r) {
-      lg[r] = logit_of(r * NT + tid, uu[r]);
+      lg[r] = sl.logit_of(r * NT + tid, uu[r]);
       mx = fmaxf(mx, lg[r]);
     }
   }
-  for_tail([&](float z) { mx = fmaxf(mx, z); });
-  mx = wave_max_dpp(mx);
-  if (lane == 0) s_max[wave] = mx;
-  __syncthreads();
-  mx = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) mx = fmaxf(mx, s_max[w]);
+  // (the host sends more slots than the registers hold to the chunk
+  // kernels; should it not, the slots past them still count)
+  const bool fits = sl.slots <= KPT * NT;
+  if (!fits) sl.for_range(KPT * NT, sl.slots, [&](float z) { mx = fmaxf(mx, z); });
+  mx = block_max<NW>(mx, s_max);
   float* out = a.tau + (int64_t)b * d.Hq + h;
   if (mx == -INFINITY) {  // nothing attended: every weight is 0
     if (tid == 0) *out = INFINITY;
     return;
   }
+  const float lo = nw.am1 * mx - 1.f;  // g(lo) >= 0: the largest term alone is ~1
+  if (!fits) {
+    const float tau = newton_block<NW>(nw, sl, lo, s_red);
+    if (tid == 0) *out = tau;
+    return;
+  }
 
-  const float am1 = a.alpha_m1, beta = a.beta;
-  const float lo = am1 * mx - 1.f;  // g(lo) >= 0: the largest term alone is ~1
-  auto is_cand = [&](float z) { return fmaf(am1, z, -lo) > 0.f; };  // false for -inf
-
-  // Candidates per wave, in slot order: registers r = 0..KPT-1, then the
-  // tail rounds, lanes in order within each.
+  // Candidates per wave, in slot order (register r, then lane).
   const uint64_t below = (1ull << lane) - 1ull;
   int wc = 0;
 #pragma unroll
-  for (int r = 0; r < KPT; ++r) wc += __popcll(__ballot(is_cand(lg[r])));
-  for_tail([&](float z) { wc += __popcll(__ballot(is_cand(z))); });
+  for (int r = 0; r < KPT; ++r) wc += __popcll(__ballot(nw.cand(lg[r], lo)));
   if (lane == 0) s_cnt[wave] = wc;
   __syncthreads();
   int base = 0, total = 0;
@@ -155,65 +255,147 @@ __global__ __launch_bounds__(kTauThreads) void entmax_tau_kernel(TauArgs a) {
     base += w < wave ? s_cnt[w] : 0;
     total += s_cnt[w];
   }
-
-  auto accum = [&](float z, float tau, float& s0, float& s1) {
-    const float t = fmaf(am1, z, -tau);
-    const float w = entmax_weight(t, beta);
-    s0 += w;
-    s1 += t > 0.f ? (beta == 2.f ? t : (beta == 1.f ? 1.f : w / t)) : 0.f;
-  };
-  // Newton step from the sums; returns false when the iteration ends.
-  const float e_sub = 1.f - am1;  // S0^(1 - 1/beta) = S0^(2 - alpha)
-  auto step = [&](float s0, float s1, float& tau) -> bool {
-    if (!(s0 > 1.f)) return false;  // at the root, up to rounding
-    const float sub = beta == 1.f ? 1.f : (beta == 2.f ? sqrtf(s0) : exp2f(e_sub * log2f(s0)));
-    const float nt = tau + (s0 - sub) / s1;
-    if (!(nt > tau)) return false;  // the step no longer moves tau
-    tau = nt;
-    return true;
-  };
-
   float tau = lo;
   if (total <= kTauCap) {
     int pos = base;
 #pragma unroll
     for (int r = 0; r < KPT; ++r) {
-      const bool c = is_cand(lg[r]);
+      const bool c = nw.cand(lg[r], lo);
       const uint64_t m = __ballot(c);
       if (c) s_c[pos + __popcll(m & below)] = lg[r];
       pos += __popcll(m);
     }
-    for_tail([&](float z) {
-      const bool c = is_cand(z);
-      const uint64_t m = __ballot(c);
-      if (c) s_c[pos + __popcll(m & below)] = z;
-      pos += __popcll(m);
-    });
     __syncthreads();
     if (wave != 0) return;
-    for (int it = 0; it < 64; ++it) {
-      float s0 = 0.f, s1 = 0.f;
-      for (int j = lane; j < total; j += 64) accum(s_c[j], tau, s0, s1);
-      s0 = wave_sum_dpp(s0);
-      s1 = wave_sum_dpp(s1);
-      if (!step(s0, s1, tau)) break;
-    }
+    tau = newton_wave(nw, s_c, total, tau);
   } else {
-    for (int it = 0; it < 64; ++it) {
-      float s0 = 0.f, s1 = 0.f;
+    tau = newton_block<NW>(nw, sl, tau, s_red);
+  }
+  if (tid == 0) *out = tau;
+}
+
+// One block per (head, chunk of kTauChunk slots): the chunk's max and its
+// slots within 1 / (alpha - 1) of it, in slot order, to the workspace
+// (count kTauChunkCap + 1: more than fit, none written).
+__global__ __launch_bounds__(kTauThreads) void entmax_chunk_kernel(TauArgs a) {
+  constexpr int NT = kTauThreads, NW = NT / 64, KPT = kTauKeys;
+  __shared__ float s_max[NW];
+  __shared__ int s_cnt[NW];
+  const Dims& d = a.d;
+  const int BG = d.B * d.Hkv;
+  const GroupBlock gb = group_block(BG);  // gb.j = head in group + G * chunk
+  const int j = gb.j % d.G, c = gb.j / d.G;
+  const int g = gb.bg % d.Hkv, b = gb.bg / d.Hkv, h = g * d.G + j;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const Slots sl(a, b, gb.bg, h);
+  const Newton nw(a);
+  const int64_t hc = ((int64_t)b * d.Hq + h) * a.nch + c;
+  const int from = c * kTauChunk;
+
+  float lg[KPT];
+  float mx = -INFINITY;
+  {
+    int uu[KPT];
 #pragma unroll
-      for (int r = 0; r < KPT; ++r) accum(lg[r], tau, s0, s1);
-      for_tail([&](float z) { accum(z, tau, s0, s1); });
-      s0 = wave_sum_dpp(s0);
-      s1 = wave_sum_dpp(s1);
-      const int par = it & 1;
-      if (lane == 0) { s_red[par][0][wave] = s0; s_red[par][1][wave] = s1; }
-      __syncthreads();
-      s0 = 0.f; s1 = 0.f;
+    for (int r = 0; r < KPT; ++r) uu[r] = sl.unit_of(from + r * NT + tid);
 #pragma unroll
-      for (int w = 0; w < NW; ++w) { s0 += s_red[par][0][w]; s1 += s_red[par][1][w]; }
-      if (!step(s0, s1, tau)) break;
+    for (int r = 0; r < KPT; ++r) {
+      lg[r] = sl.logit_of(from + r * NT + tid, uu[r]);
+      mx = fmaxf(mx, lg[r]);
     }
+  }
+  mx = block_max<NW>(mx, s_max);
+  const float lo = nw.am1 * mx - 1.f;
+  const uint64_t below = (1ull << lane) - 1ull;
+  int wc = 0;
+#pragma unroll
+  for (int r = 0; r < KPT; ++r) wc += __popcll(__ballot(nw.cand(lg[r], lo)));
+  if (lane == 0) s_cnt[wave] = wc;
+  __syncthreads();
+  int base = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    base += w < wave ? s_cnt[w] : 0;
+    total += s_cnt[w];
+  }
+  if (tid == 0) {
+    a.cmax[hc] = mx;
+    a.ccnt[hc] = total <= kTauChunkCap ? total : kTauChunkCap + 1;
+  }
+  if (total > kTauChunkCap) return;
+  float* dst = a.cand + hc * kTauChunkCap;
+  int pos = base;
+#pragma unroll
+  for (int r = 0; r < KPT; ++r) {
+    const bool cnd = nw.cand(lg[r], lo);  // false for -inf (empty chunk)
+    const uint64_t m = __ballot(cnd);
+    if (cnd) dst[pos + __popcll(m & below)] = lg[r];
+    pos += __popcll(m);
+  }
+}
+
+// One block per head after entmax_chunk_kernel: the head's max over the
+// chunks, its candidates gathered from the chunks' lists in chunk order,
+// then the Newton steps (one wave), or the block-wide fallback.
+__global__ __launch_bounds__(kTauThreads) void entmax_merge_kernel(TauArgs a) {
+  constexpr int NT = kTauThreads, NW = NT / 64;
+  __shared__ float s_c[kTauCap];
+  __shared__ float s_red[2][2][NW];
+  __shared__ int s_cnt[NW];
+  const Dims& d = a.d;
+  const GroupBlock gb = group_block(d.B * d.Hkv);
+  const int g = gb.bg % d.Hkv, b = gb.bg / d.Hkv, h = g * d.G + gb.j;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const Slots sl(a, b, gb.bg, h);
+  const Newton nw(a);
+  const int64_t h0 = ((int64_t)b * d.Hq + h) * a.nch;
+  const int nch = min(a.nch, (sl.slots + kTauChunk - 1) / kTauChunk);
+
+  float mx = -INFINITY;
+  bool over = false;
+  for (int c = 0; c < nch; ++c) {
+    mx = fmaxf(mx, a.cmax[h0 + c]);
+    over |= a.ccnt[h0 + c] > kTauChunkCap;
+  }
+  float* out = a.tau + (int64_t)b * d.Hq + h;
+  if (mx == -INFINITY) {  // nothing attended: every weight is 0
+    if (tid == 0) *out = INFINITY;
+    return;
+  }
+  const float lo = nw.am1 * mx - 1.f;
+  float tau = lo;
+  // Gather the candidates: chunk by chunk, kTauThreads entries at a time,
+  // kept in order by block-wide ballot prefix offsets.
+  const uint64_t below = (1ull << lane) - 1ull;
+  int total = 0;
+  for (int c = 0; c < nch && !over; ++c) {
+    const int cc = a.ccnt[h0 + c];
+    const float* src = a.cand + (h0 + c) * kTauChunkCap;
+    for (int e0 = 0; e0 < cc; e0 += NT) {
+      const int e = e0 + tid;
+      const float z = e < cc ? src[e] : -INFINITY;
+      const bool cnd = nw.cand(z, lo);
+      const uint64_t m = __ballot(cnd);
+      if (lane == 0) s_cnt[wave] = __popcll(m);
+      __syncthreads();
+      int base = total, add = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        base += w < wave ? s_cnt[w] : 0;
+        add += s_cnt[w];
+      }
+      const int pos = base + __popcll(m & below);
+      if (cnd && pos < kTauCap) s_c[pos] = z;
+      total += add;
+      __syncthreads();  // s_cnt is rewritten next round
+    }
+    over = total > kTauCap;
+  }
+  if (!over) {
+    if (wave != 0) return;
+    tau = newton_wave(nw, s_c, total, tau);
+  } else {
+    tau = newton_block<NW>(nw, sl, tau, s_red);
   }
   if (tid == 0) *out = tau;
 }
@@ -223,7 +405,13 @@ hipError_t launch_entmax_tau(const TauArgs& a, hipStream_t st) {
   if (!(a.alpha_m1 > 0.f && a.alpha_m1 <= 1.f) || !(a.beta >= 1.f)) return hipErrorInvalidValue;
   if (a.sel_idx && (a.k_max < 1 || !a.sel_count)) return hipErrorInvalidValue;
   if (d.P != 16 && d.P != 64) return hipErrorInvalidValue;
-  entmax_tau_kernel<<<dim3(d.B * d.Hq), kTauThreads, 0, st>>>(a);
+  if (a.nch < 0 || (a.nch > 0 && (!a.cand || !a.cmax || !a.ccnt))) return hipErrorInvalidValue;
+  if (a.nch == 0) {
+    entmax_tau_kernel<<<dim3(d.B * d.Hq), kTauThreads, 0, st>>>(a);
+  } else {
+    entmax_chunk_kernel<<<dim3(d.B * d.Hq * a.nch), kTauThreads, 0, st>>>(a);
+    entmax_merge_kernel<<<dim3(d.B * d.Hq), kTauThreads, 0, st>>>(a);
+  }
   return hipGetLastError();
 }
 

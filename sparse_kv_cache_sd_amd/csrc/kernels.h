@@ -114,7 +114,17 @@ struct TauArgs {
   const float* logits;       // [B][Hq][max_seq]
   float alpha_m1, beta;
   float* tau;                // [B][Hq]
+  // More than kTauChunk kept slots per head: nch chunks of kTauChunk slots,
+  // one block each, leave their max and their candidates in cand / cmax /
+  // ccnt ([B*Hq][nch][kTauChunkCap], [B*Hq][nch], [B*Hq][nch]); a second
+  // kernel merges them.  nch = 0: one block per head does everything.
+  int nch;
+  float* cand;
+  float* cmax;
+  int32_t* ccnt;
 };
+constexpr int kTauChunk = 16384;     // kept slots per threshold block
+constexpr int kTauChunkCap = 2048;   // candidates a chunk hands on
 hipError_t launch_entmax_tau(const TauArgs& a, hipStream_t st);
 
 // Structured kept lists, one block per (sequence, KV head): kind kWindow
