@@ -58,6 +58,17 @@ __global__ __launch_bounds__(kScoreThreads) void score_pages_kernel(
   for (int h = 0; h < G; ++h)
     load8(q + ((int64_t)b * d.Hq + g * G + h) * D + cl * 8, qv[h]);
 
+  // Rows past a sequence's pages are not read.  With one sequence the loads
+  // go out before its length is known (the length's round trip then
+  // overlaps them, and nothing is skipped but the last block's tail); in a
+  // batch of ragged sequences the length is read first, so blocks past the
+  // end stop and rows past it re-read the last one.
+  int rows = d.max_pages;
+  if (d.B > 1) {
+    const int nb = clamp_len(seq_lens[b], d.max_seq);
+    rows = (nb + d.P - 1) / d.P;
+    if (u0 >= rows) return;
+  }
   // statistics are stored in logical page order: no block-table lookup
   const T* bnd = bounds + ((int64_t)b * d.Hkv + g) * d.max_pages * 2 * D + cl * 8;
   Raw8<T> lo_w[IT], hi_w[IT];
@@ -65,7 +76,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_pages_kernel(
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     uu[it] = u0 + (wave * IT + it) * RPW + sub;
-    const int uc = min(uu[it], d.max_pages - 1);
+    const int uc = min(uu[it], rows - 1);
     lo_w[it] = load_raw8(bnd + (int64_t)uc * 2 * D);
     hi_w[it] = load_raw8(bnd + (int64_t)uc * 2 * D + D);
   }
@@ -120,12 +131,16 @@ __global__ __launch_bounds__(kScoreThreads) void score_pages_mfma_kernel(
   const int col = lane & 15, quad = lane >> 4;
   const int u0 = gb.j * PPB + wave * IT * 16;
 
+  // rows past a sequence's pages: as in score_pages_kernel (re-read the
+  // last row in a batch, whose lengths are read first)
+  int rows = d.max_pages;
+  if (d.B > 1) rows = max((clamp_len(seq_lens[b], d.max_seq) + d.P - 1) / d.P, 1);
   // statistics are stored in logical page order: no block-table lookup
   const bf16_t* bnd = bounds + ((int64_t)b * d.Hkv + g) * d.max_pages * 2 * D + 8 * quad;
   u32x4_t rw[IT][KS];
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
-    const int uc = min(u0 + 16 * it + col, d.max_pages - 1);
+    const int uc = min(u0 + 16 * it + col, rows - 1);
 #pragma unroll
     for (int s = 0; s < KS; ++s)
       rw[it][s] = *reinterpret_cast<const u32x4_t*>(bnd + (int64_t)uc * 2 * D + 32 * s);
