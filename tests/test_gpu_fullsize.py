@@ -177,3 +177,91 @@ def test_full_size_entmax(cid, name, context, unit, r_kv, groups):
         e_o, e_t = max(e_o, eo), max(e_t, et)
     print(f"[fullsize] entmax {cid}: {len(groups)} instances vs oracle, max-abs out {e_o:.2e} "
           f"tau {e_t:.2e}", flush=True)
+
+
+# ------------------------------------------- structured sets, budget, compressed scorer
+
+def _structured_cases():
+    SEL = sd.Selection
+    return [
+        # the bench's union at 32K: 1 initial + 2048 tokens of local pages + top-k r 0.3
+        ("l8b-32k-union", "l8b", None, "page", SEL("init_local_topk", 0.3, 1, 128), "all"),
+        ("l8b-32k-window", "l8b", None, "page", SEL("window", 0.3), "all"),
+        # SparDA App. C's setup at 1M: 1 initial block, a 2048-token window, 96 blocks
+        ("l70b-1m-appc", "l70b", 1024 * K, "page",
+         SEL("init_local_topk", 96 / 16384, 1, 32), [(0, 1), (0, 6)]),
+    ]
+
+
+@pytest.mark.parametrize("cid,name,context,unit,sel,groups", _structured_cases(),
+                         ids=[c[0] for c in _structured_cases()])
+def test_full_size_structured(cid, name, context, unit, sel, groups):
+    """Kept lists bit-exact against the oracle's rule on the library's own
+    scores (and on the oracle's fp64 scores where the gap rule applies), for
+    every instance or the sampled ones; outputs against the oracle."""
+    from test_gpu_structured import _check
+    print(f"[fullsize] {cid}", flush=True)
+    dev = _dev(name, context)
+    worst = _check(dev, unit, sel, groups=None if groups == "all" else groups)
+    print(f"[fullsize] {cid}: max-abs {worst:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("target,cap", [(0.05, 0.5), (0.6, 0.9)], ids=["bench", "binding"])
+def test_full_size_mass_budget(target, cap):
+    """The dropped-mass budget at 32K token, every instance: the bench's
+    setting (at most 5% of each head's softmax mass dropped, capped at r 0.5,
+    where these inputs reach the cap) and one where the target binds below
+    the cap."""
+    from test_gpu_structured import _check_budget
+    print(f"[fullsize] sweep-32k budget {target} cap {cap}", flush=True)
+    dev = _dev("sweep", 32 * K)
+    exact = _check_budget(dev, sd.Selection("mass_budget", cap, max_dropped=target))
+    print(f"[fullsize] sweep-32k budget {target} cap {cap}: {exact} counts equal to the "
+          f"oracle's", flush=True)
+
+
+@pytest.mark.parametrize("cid,name,context,r_kv,groups", [
+    ("l8b-32k-compressed", "l8b", None, 0.3, "all"),
+    ("l70b-128k-compressed", "l70b", 128 * K, 0.05, [(0, 0), (0, 4), (0, 7)]),
+], ids=["l8b-32k-compressed", "l70b-128k-compressed"])
+def test_full_size_compressed_scorer(cid, name, context, r_kv, groups):
+    """The compressed-key scorer's step at full size: kept pages under the gap
+    rule against the oracle's compressed scorer (fp64 windows), outputs
+    against the oracle on the kept set."""
+    from gpu_util import TOL, check_selection
+    print(f"[fullsize] {cid}", flush=True)
+    dev = _dev(name, context)
+    s, w = dev.shape, dev.w
+    ck = torch.empty(sd.compressed_keys_shape(s), dtype=torch.float32, device="cuda")
+    sd.update_compressed_keys(s, dev.k, dev.bt, dev.sl, ck)
+    sel = sd.Selection("topk", r_kv, scorer="compressed")
+    cap = sd.selection_capacity(sel, s.max_pages_per_seq)
+    ws = sd.alloc_workspace_sel(s, "page", sel)
+    out = torch.empty((s.batch, s.num_q_heads, s.head_dim), device="cuda")
+    lse = torch.empty((s.batch, s.num_q_heads), device="cuda")
+    idx = torch.full((s.batch, s.num_kv_heads, cap), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((s.batch, s.num_kv_heads), -7, dtype=torch.int32, device="cuda")
+    sd.decode_step_sel(s, dev.q, dev.k, dev.v, ck, dev.bt, dev.sl, "page", sel, out, lse, ws,
+                       sel_idx=idx, sel_count=cnt)
+    torch.cuda.synchronize()
+    out, lse, idx, cnt = out.cpu().numpy(), lse.cpu().numpy(), idx.cpu().numpy(), cnt.cpu().numpy()
+    _finite(out, lse)
+    if groups == "all":
+        groups = [(b, g) for b in range(s.batch) for g in range(s.num_kv_heads)]
+    G, scale, tol = s.group, 1.0 / math.sqrt(s.head_dim), TOL[s.dtype]
+    worst = 0.0
+    for b, g in groups:
+        n = int(w.seq_lens[b])
+        args = (sdref.widen(w.q[b, g * G:(g + 1) * G], s.dtype), sdref.widen(w.K[b, g, :n], s.dtype),
+                sdref.widen(w.V[b, g, :n], s.dtype))
+        kw = dict(unit="page", page_size=s.page_size, r_kv=r_kv, scale=scale, scorer="compressed")
+        orc = sdref.group_step(*args, **kw)
+        kept = idx[b, g, :int(cnt[b, g])].astype(np.int64)
+        if not check_selection(kept, orc):
+            orc = sdref.group_step(*args, kept_override=kept, **kw)
+        heads = slice(g * G, (g + 1) * G)
+        e_o = float(np.abs(out[b, heads] - orc.out_sparse).max())
+        e_l = float(np.abs(lse[b, heads] - orc.lse_sparse).max())
+        assert e_o <= tol and e_l <= tol, f"(b={b}, g={g}) out {e_o} lse {e_l}"
+        worst = max(worst, e_o, e_l)
+    print(f"[fullsize] {cid}: {len(groups)} instances, max-abs {worst:.2e}", flush=True)
