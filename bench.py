@@ -595,6 +595,17 @@ def main():
             "us_per_launch": round(us_attend, 3), "bytes_per_launch": int(b_attend),
         },
     }
+    if unit == "token" and not entmax and shape.max_seq_len <= 262144:
+        # dropped dense softmax mass of layer 0's kept lists (token unit: every
+        # logit is stored, so the library computes it on the GPU)
+        delta = torch.empty((rec.batch, H_q), dtype=torch.float32, device="cuda")
+        sd.dropped_mass(shape, layers[0]["sl"], layers[0]["bt"], logits[0], sels[0], cnts[0],
+                        delta, stream=stream)
+        torch.cuda.synchronize()
+        dl = delta.cpu().numpy()
+        result["dropped_mass"] = {"mean": round(float(dl.mean()), 5),
+                                  "max": round(float(dl.max()), 5),
+                                  "of": "layer 0, every query head (sd_dropped_mass)"}
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         result["cpu_baseline"] = cpu_baseline(

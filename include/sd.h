@@ -378,6 +378,30 @@ SD_API sd_status sd_decode_step_entmax(const sd_shape* shape, const void* q, con
                                        int32_t* sel_count, void* ws, size_t ws_bytes,
                                        void* stream);
 
+/* ---- Dropped mass on the device (token unit) -------------------------
+ * [Cross/cards] pre-hoc sparsity abstract: the dropped mass delta -- the
+ * dense attention probability of the entries a selection leaves out --
+ * governs the error of sparse attention ([Cross/cards] EntmaxKV abstract:
+ * ||o - o_S|| <= 2 delta max ||v||).  In token unit every logit is stored,
+ * so delta costs one more pass over them:
+ *   delta[b][h] = sum over the attended tokens t of sequence b NOT in
+ *                 sel_idx[b][h / G][0 .. sel_count - 1] of exp(s_t - m)
+ *                 / sum over all its attended tokens of exp(s_t - m),
+ * s = token_logits[b][h] (as sd_score_pages writes them), m their max; a
+ * token is attended when t < seq_lens[b] and its page's block-table entry
+ * is valid.  The dropped tokens are summed directly (not as one minus the
+ * kept mass), in fp32 and a fixed order; list entries outside [0, n_b) are
+ * ignored; a sequence with no attended token gets delta = 0.
+ *   sel_idx / sel_count: token ids as sd_select_topk or sd_select_units
+ *   write them ([B][H_kv][k_max], [B][H_kv]); any ascending or unordered
+ *   set of distinct ids works.
+ *   delta: [B][H_q] fp32.
+ * max_seq_len <= 262144 (SD_E_UNSUPPORTED beyond). */
+SD_API sd_status sd_dropped_mass(const sd_shape* shape, const int32_t* seq_lens,
+                                 const int32_t* block_table, const float* token_logits,
+                                 const int32_t* sel_idx, const int32_t* sel_count, int32_t k_max,
+                                 float* delta, void* stream);
+
 /* Text of the last non-OK status on this thread ("" if none). */
 SD_API const char* sd_last_error(void);
 

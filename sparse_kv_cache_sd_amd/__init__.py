@@ -24,6 +24,7 @@ from ._lib import (  # noqa: F401
     decode_step,
     decode_step_entmax,
     decode_step_sel,
+    dropped_mass,
     keep_count,
     lib,
     merge_splits,

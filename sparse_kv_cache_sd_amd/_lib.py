@@ -99,6 +99,8 @@ _SIGS = {
     "sd_decode_step_entmax": (ctypes.c_int, [ctypes.POINTER(SdShape), _P, _P, _P, _P, _P, _P,
                                              _I32, _SELP, ctypes.c_double, _P, _P, _P, _P, _P,
                                              ctypes.c_size_t, _P]),
+    "sd_dropped_mass": (ctypes.c_int, [ctypes.POINTER(SdShape), _P, _P, _P, _P, _P, _I32, _P,
+                                       _P]),
     "sd_last_error": (ctypes.c_char_p, []),
 }
 EXPORTS = tuple(_SIGS)
@@ -564,3 +566,27 @@ def decode_step_entmax(shape: Shape, q, k_pages, v_pages, page_stats, block_tabl
         _dev(sel_idx, "sel_idx", torch.int32, (s.batch, s.num_kv_heads, cap), optional=True),
         _dev(sel_count, "sel_count", torch.int32, (s.batch, s.num_kv_heads), optional=True),
         wp, wn, _stream(stream)))
+
+
+# ----------------------------------------------------------------------------
+# dropped mass on the device (token unit)
+# ----------------------------------------------------------------------------
+
+def dropped_mass(shape: Shape, seq_lens, block_table, token_logits, sel_idx, sel_count, delta,
+                 stream=None):
+    """delta [B, H_q] fp32 from the stored token logits and a kept token list
+    (sel_idx [B, H_kv, k_max], sel_count [B, H_kv])."""
+    s = shape
+    if sel_idx.dim() != 3:
+        raise ValueError("sel_idx must be [B, H_kv, k_max]")
+    k_max = int(sel_idx.shape[2])
+    _check(lib().sd_dropped_mass(
+        ctypes.byref(s.c()),
+        _dev(seq_lens, "seq_lens", torch.int32, (s.batch,)),
+        _dev(block_table, "block_table", torch.int32, (s.batch, s.max_pages_per_seq)),
+        _dev(token_logits, "token_logits", torch.float32, (s.batch, s.num_q_heads, s.max_seq_len)),
+        _dev(sel_idx, "sel_idx", torch.int32, (s.batch, s.num_kv_heads, k_max)),
+        _dev(sel_count, "sel_count", torch.int32, (s.batch, s.num_kv_heads)),
+        k_max,
+        _dev(delta, "delta", torch.float32, (s.batch, s.num_q_heads)),
+        _stream(stream)))

@@ -1061,6 +1061,28 @@ sd_status sd_decode_step_entmax(const sd_shape* shape, const void* q, const void
   return ok();
 }
 
+sd_status sd_dropped_mass(const sd_shape* shape, const int32_t* seq_lens,
+                          const int32_t* block_table, const float* token_logits,
+                          const int32_t* sel_idx, const int32_t* sel_count, int32_t k_max,
+                          float* delta, void* stream) {
+  sdkv::Dims d;
+  sd_status st;
+  if ((st = check_shape(shape, &d)) != SD_OK) return st;
+  if (!seq_lens || !block_table || !token_logits || !sel_idx || !sel_count || !delta)
+    return fail(SD_E_NULL, "seq_lens, block_table, token_logits, sel_idx, sel_count and delta "
+                           "are required");
+  if (k_max < 1 || k_max > d.max_seq)
+    return fail(SD_E_SHAPE, "k_max %d outside [1, %d]", k_max, d.max_seq);
+  if (d.max_seq > sdkv::kMaxDropSeq)
+    return fail(SD_E_UNSUPPORTED, "the dropped mass takes at most %d tokens per sequence",
+                sdkv::kMaxDropSeq);
+  sdkv::DropArgs a{d, seq_lens, block_table, token_logits, sel_idx, sel_count, k_max, delta};
+  if ((st = device_status(sdkv::launch_dropped_mass(a, static_cast<hipStream_t>(stream)),
+                          "dropped mass kernel launch")) != SD_OK)
+    return st;
+  return ok();
+}
+
 const char* sd_last_error(void) { return g_err; }
 
 }  // extern "C"

@@ -127,6 +127,25 @@ constexpr int kTauChunk = 16384;     // kept slots per threshold block
 constexpr int kTauChunkCap = 2048;   // candidates a chunk hands on
 hipError_t launch_entmax_tau(const TauArgs& a, hipStream_t st);
 
+// Dropped mass of the dense softmax (token unit), one block per (sequence,
+// query head): delta[b][h] = sum over the attended tokens NOT in the kept
+// list of (b, h / G) of exp(s_t - m) / sum over all attended tokens of
+// exp(s_t - m), m the max logit.  A token is attended when t < n_b and its
+// page's block-table entry is valid.  max_seq <= kMaxDropSeq (the kept set
+// is a bitmap in LDS).
+struct DropArgs {
+  Dims d;
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+  const float* logits;       // [B][Hq][max_seq]
+  const int32_t* sel_idx;    // [B][Hkv][k_max] token ids
+  const int32_t* sel_count;  // [B][Hkv]
+  int k_max;
+  float* delta;              // [B][Hq]
+};
+constexpr int kMaxDropSeq = 262144;
+hipError_t launch_dropped_mass(const DropArgs& a, hipStream_t st);
+
 // Structured kept lists, one block per (sequence, KV head): kind kWindow
 // writes the last keep_count(U, R_ppm) units; kind kInitLocalTopk writes the
 // union of the first init_units, the last local_units and the ascending

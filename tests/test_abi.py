@@ -129,3 +129,16 @@ def test_entmax_workspace_holds_logits_and_thresholds():
         if unit == "page":
             extra += 4 * s.batch * s.num_q_heads * s.max_seq_len   # logits of kept tokens
         assert ent >= soft + extra
+
+
+def test_dropped_mass_validation_before_any_launch():
+    lib = sd.lib()
+    sh = ctypes.byref(_shape().c())
+    fake = ctypes.c_void_p(0x10000)       # never dereferenced: validation fails first
+    st = lib.sd_dropped_mass(sh, None, fake, fake, fake, fake, 4, fake, None)
+    assert st == 1 and b"required" in lib.sd_last_error()
+    st = lib.sd_dropped_mass(sh, fake, fake, fake, fake, fake, 0, fake, None)
+    assert st == 2
+    big = ctypes.byref(_shape(max_pages_per_seq=32768, max_seq_len=300000, num_pages=32768).c())
+    st = lib.sd_dropped_mass(big, fake, fake, fake, fake, fake, 4, fake, None)
+    assert st == 6
