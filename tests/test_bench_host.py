@@ -1,0 +1,133 @@
+"""Host logic of bench.py (no GPU): the algorithmic byte model the roofline
+divides by, the kept-token count from selections, the traffic summariser
+and its staleness check.
+
+The byte model is pinned to the per-configuration figures derived from the
+method's byte accounting (all K and V once for dense; page statistics plus
+the kept pages' K and V in page unit; all K plus the kept tokens' V in token
+unit), computed here from the shapes by hand.
+"""
+
+import csv
+import os
+
+import numpy as np
+import pytest
+
+import bench
+
+K = 1024
+
+
+def _mb(x):
+    return x / 1e6
+
+
+def test_dense_bytes_cfg2():
+    # 8 KV heads x 32768 tokens x (K + V) x 128 x 2 B, plus q / out / lse
+    b = bench.algorithmic_bytes(np.array([32 * K]), 32, 8, 128, 16, 2, "page", 1.0, 0)
+    qo = 32 * (128 * 2 + 128 * 4 + 4)
+    assert b == 8 * 32 * K * 2 * 128 * 2 + qo
+    assert abs(_mb(b) - 134.2) < 0.1
+
+
+def test_page_bytes_cfg2():
+    # k = 615 of 2048 pages per KV head, all full: 615 * 16 tokens kept per head
+    kept = 615 * 16 * 8
+    b = bench.algorithmic_bytes(np.array([32 * K]), 32, 8, 128, 16, 2, "page", 0.3, kept)
+    meta = 8 * 2048 * 2 * 128 * 2
+    kv = kept * 2 * 128 * 2
+    assert abs(_mb(meta) - 8.39) < 0.01 and abs(_mb(kv) - 40.30) < 0.01
+    assert b == meta + kv + 32 * (128 * 2 + 128 * 4 + 4)
+    assert b == 48717952  # the figure the bench line reports at this workload
+
+
+@pytest.mark.parametrize("n,k,want_mb", [(128 * K, 103, 35.4), (1024 * K, 820, 282.1)])
+def test_page_bytes_cfg5(n, k, want_mb):
+    U = n // 64
+    kept = k * 64 * 8
+    b = bench.algorithmic_bytes(np.array([n]), 64, 8, 128, 64, 2, "page", 0.05, kept)
+    assert abs(_mb(b) - want_mb) < 0.1
+    assert abs(_mb(8 * U * 2 * 128 * 2) - (8.39 if n == 128 * K else 67.1)) < 0.1
+
+
+@pytest.mark.parametrize("r,k,want_mb", [(0.3, 39322, 349.0), (0.2, 26215, 322.1)])
+def test_token_bytes_cfg3(r, k, want_mb):
+    n = 128 * K
+    b = bench.algorithmic_bytes(np.array([n]), 32, 8, 128, 16, 2, "token", r, k * 8)
+    # every K row once, V of the kept tokens only
+    assert b == 8 * n * 128 * 2 + 8 * k * 128 * 2 + 32 * (128 * 2 + 128 * 4 + 4)
+    assert abs(_mb(b) - want_mb) < 0.1
+
+
+def test_window_bytes_read_only_the_window():
+    b = bench.algorithmic_bytes(np.array([32 * K]), 32, 8, 128, 16, 2, "page", 0.3, 1000,
+                                window=True)
+    assert b == 1000 * 2 * 128 * 2 + 32 * (128 * 2 + 128 * 4 + 4)
+
+
+def test_attend_bytes():
+    assert bench.attend_bytes(100, 128, 2, token_unit=False) == 100 * 2 * 128 * 2
+    assert bench.attend_bytes(100, 128, 2, token_unit=True) == 100 * 128 * 2
+
+
+def test_kept_token_count_partial_last_page():
+    # one sequence of 40 tokens, pages of 16: pages 0, 1, 2 hold 16, 16, 8 tokens
+    sel = np.array([[[0, 2], [1, 2]]], dtype=np.int32)
+    cnt = np.array([[2, 1]], dtype=np.int32)
+    assert bench.kept_token_count(sel, cnt, np.array([40]), "page", 16) == (16 + 8) + 16
+    assert bench.kept_token_count(sel, cnt, np.array([40]), "token", 16) == 3
+
+
+def _write_pmc(path, rows):
+    os.makedirs(path, exist_ok=True)
+    with open(os.path.join(path, "pmc_counter_collection.csv"), "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Kernel_Name", "Grid_Size", "Counter_Value"])
+        w.writeheader()
+        for r in rows:
+            w.writerow(r)
+
+
+def test_summarize_pmc_picks_the_selecting_instance(tmp_path, monkeypatch):
+    att = "void sdkv::attend_mfma_kernel<128, 4, false, 4, 0>(sdkv::AttendArgs)"
+    dense = "void sdkv::attend_mfma_kernel<128, 4, false, 0, 0>(sdkv::AttendArgs)"
+    ent = "void sdkv::attend_mfma_kernel<128, 4, false, 4, 2>(sdkv::AttendArgs)"
+    copy = "__amd_rocclr_copyBuffer"
+    gib = bench.COPY_BYTES / 1024
+    fetch = [dict(Kernel_Name=att, Grid_Size=131072, Counter_Value=1000.0),
+             dict(Kernel_Name=att, Grid_Size=131072, Counter_Value=1200.0),
+             dict(Kernel_Name=dense, Grid_Size=131072, Counter_Value=9999.0),
+             dict(Kernel_Name=ent, Grid_Size=131072, Counter_Value=7777.0),
+             dict(Kernel_Name=copy, Grid_Size=4096, Counter_Value=gib / 2),
+             dict(Kernel_Name=copy, Grid_Size=64, Counter_Value=1.0)]
+    write = [dict(Kernel_Name=att, Grid_Size=131072, Counter_Value=50.0),
+             dict(Kernel_Name=copy, Grid_Size=4096, Counter_Value=gib),
+             dict(Kernel_Name=copy, Grid_Size=64, Counter_Value=1.0)]
+    _write_pmc(str(tmp_path / "f"), fetch)
+    _write_pmc(str(tmp_path / "w"), write)
+    out = str(tmp_path / "summary.txt")
+    bench.summarize_pmc(str(tmp_path / "f"), str(tmp_path / "w"), "l8b", out, "cmd-f", "cmd-w")
+    kv = dict(l.split(" = ", 1) for l in open(out).read().splitlines() if " = " in l
+              and not l.startswith("#"))
+    assert float(kv["attend_fetch_kib_per_dispatch"]) == 1100.0   # mean of the selecting instance
+    assert float(kv["attend_write_kib_per_dispatch"]) == 50.0
+    assert abs(float(kv["fetch_scale"]) - 2.0) < 1e-3            # the copy's fetch reads half
+    assert abs(float(kv["write_scale"]) - 1.0) < 1e-3
+    # the summary is read back only while the kernel sources are unchanged
+    monkeypatch.setattr(bench, "traffic_file", lambda wl: out)
+    # FETCH and WRITE KiB per dispatch, each scaled by the copy's factor (the
+    # scales are stored to four decimals)
+    assert abs(bench.read_traffic("l8b") - (1100 * 1024 * 2.0 + 50 * 1024)) < 1024
+    stale = str(tmp_path / "stale.txt")
+    with open(stale, "w") as fh:
+        fh.write(open(out).read().replace(bench.kernel_sources_sha(), "0" * 16))
+    monkeypatch.setattr(bench, "traffic_file", lambda wl: stale)
+    assert bench.read_traffic("l8b") is None
+
+
+def test_gpus_other_than_one_are_refused():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
