@@ -352,11 +352,14 @@ SD_API sd_status sd_decode_step_sel(const sd_shape* shape, const void* q, const 
  * same scorer, keep count, top-k, window, union or budget); the logits of
  * the kept tokens (token unit: those of the token scorer; page unit, a
  * window or every unit: a logits-only pass of the attention kernel over the
- * kept list, which reads K but not V); tau per head by Newton steps from
- * the left end of its bracket [max x - 1, max x] (fp32; guarded by
- * bisection); split-K attention with these weights over the stored logits
+ * kept list, which reads K but not V; in page unit with the top-k or the
+ * union this pass also selects the pages); tau per head by Newton steps,
+ * in fp32, on (sum max(x - tau, 0)^(1/(alpha-1)))^(alpha-1) - 1 from
+ * tau = max x - 1, which climb monotonically to the root (one block per
+ * head, or past 16384 kept tokens a block per 16384 of them and a merge
+ * block); split-K attention with these weights over the stored logits
  * (reads V), merged as sum_j a_j / sum_j l_j, which also removes the
- * residual of tau's rounding.
+ * residual of tau's rounding.  Launches use the caller's workspace only.
  *   page_stats  as page_bounds of sd_decode_step_sel (the page bounds, or
  *               the compressed keys with sel->scorer == SD_SCORER_COMPRESSED);
  *               not read in token unit, for a window or with r_kv >= 1.
