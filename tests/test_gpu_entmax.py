@@ -248,3 +248,45 @@ def test_entmax_flat_logits_many_candidates(alpha):
     # tau solves k * (-tau)^beta = 1
     want = -(1.0 / k) ** (alpha - 1.0)
     assert np.abs(res[1][0] - want).max() <= 1e-6
+
+
+@pytest.mark.parametrize("cid,rec", [
+    ("l70b-20k", R["l70b"].with_(seq_len=20000)),
+    ("l8b-6k", R["l8b"].with_(seq_len=6000, num_q_heads=16, num_kv_heads=4)),
+], ids=["l70b-20k", "l8b-6k"])
+def test_entmax_with_compressed_scorer(cid, rec):
+    """Entmax over the pages the compressed-key scorer keeps (the fused page
+    path selects them from those scores)."""
+    w = kvsynth.generate(rec)
+    dev = upload(w)
+    s = dev.shape
+    ck = torch.empty(sd.compressed_keys_shape(s), dtype=torch.float32, device="cuda")
+    sd.update_compressed_keys(s, dev.k, dev.bt, dev.sl, ck)
+    r = 0.05 if s.page_size == 64 else 0.3
+    sel = sd.Selection("topk", r, scorer="compressed")
+    out, tau, idx, cnt = _run(dev, "page", sel, 1.5, stats=ck)
+    G, scale = s.group, 1.0 / math.sqrt(s.head_dim)
+    for g in range(s.num_kv_heads):
+        n = int(w.seq_lens[0])
+        args = (sdref.widen(w.q[0, g * G:(g + 1) * G], s.dtype), sdref.widen(w.K[0, g, :n], s.dtype),
+                sdref.widen(w.V[0, g, :n], s.dtype))
+        # the kept pages against the oracle's compressed scorer (gap rule)
+        soft = sdref.group_step(*args, unit="page", page_size=s.page_size, r_kv=r, scale=scale,
+                                scorer="compressed")
+        kept = idx[0, g, :int(cnt[0, g])].astype(np.int64)
+        check_selection(kept, soft)
+        orc = entmaxref.group_step(*args, unit="page", page_size=s.page_size, r_kv=r,
+                                   scale=scale, alpha=1.5, kept_override=kept)
+        heads = slice(g * G, (g + 1) * G)
+        assert np.abs(out[0, heads] - orc.out_sparse).max() <= TOL[s.dtype]
+        assert np.abs(tau[0, heads] - orc.tau_sparse).max() <= TAU_TOL[s.dtype]
+
+
+def test_entmax_token_ragged_batch():
+    rec = R["batch"].with_(batch=4, seq_len=5000, seq_len_min=1, num_q_heads=16, num_kv_heads=4,
+                           unit="token")
+    w = kvsynth.generate(rec)
+    dev = upload(w)
+    for r in (0.2, 1.0):
+        sel = sd.Selection("topk", r)
+        _compare(w, dev, "token", sel, 1.5, _run(dev, "token", sel, 1.5))
