@@ -264,7 +264,7 @@ def cpu_baseline(w, unit, r_kv, budget_s=12.0, selection=None, scorer="bounds", 
                                  scale=scale, alpha=alpha, selection=selection, scorer=scorer)
         done += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or done >= 4 * len(groups):
+        if el >= budget_s or done >= 64 * len(groups):
             break
     per_group = el / done
     us_per_step = per_group * len(groups) * 1e6
