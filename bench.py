@@ -2,6 +2,8 @@
 """Decode-attention benchmark on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload l8b]
+                    [--selection topk|window|init_local_topk|mass_budget]
+                    [--scorer bounds|compressed] [--attention softmax|entmax]
 
 A step is one decode step of one attention layer: page-bound (or exact)
 scoring, top-k selection under r_KV and split-K attention over the kept
@@ -14,7 +16,8 @@ Prints ONE JSON line: the metric (microseconds per decode-step-layer, lower
 is better), effective HBM GB/s on the algorithmic bytes, the roofline of the
 dominant kernel (the split-K attention kernel, timed alone with HIP events on
 its stream), the same-kernel dense step for comparison, and the fp64 CPU
-oracle timed on a bounded sample on the host cores.
+oracle timed on a bounded sample on the host cores.  Token-unit lines also
+report the dropped softmax mass of layer 0's selection (computed on the GPU).
 """
 
 from __future__ import annotations
