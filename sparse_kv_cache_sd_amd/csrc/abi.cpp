@@ -142,14 +142,12 @@ sd_status check_selection(const sd_selection* s, Sel* out) {
   return SD_OK;
 }
 
-// The dropped-mass budget's limits: token unit, one block per (b, g).
+// The dropped-mass budget's limits: token unit.
 sd_status check_budget(const sdkv::Dims& d, int unit, const Sel& s) {
+  (void)d;
   if (s.kind != SD_SEL_MASS_BUDGET) return SD_OK;
   if (unit != SD_UNIT_TOKEN)
     return fail(SD_E_UNSUPPORTED, "the dropped-mass budget is token unit only");
-  if (d.max_seq > sdkv::kMaxSelectOne)
-    return fail(SD_E_UNSUPPORTED, "the dropped-mass budget takes at most %d tokens per sequence",
-                sdkv::kMaxSelectOne);
   return SD_OK;
 }
 
@@ -198,6 +196,19 @@ size_t select_ws_bytes(const sdkv::Dims& d, int unit) {
   return multi_select(d, unit) ? sdkv::msel_workspace_bytes(d.B, d.Hkv, units_max(d, unit)) : 0;
 }
 
+// The budget runs in one block per (b, g) up to kBudgetOneMax tokens, past
+// that over many blocks (with the many-block top-k's scratch inside its own).
+constexpr int kBudgetOneMax = sdkv::kMaxSelectOne;
+
+bool budget_multi(const sdkv::Dims& d, int unit, const Sel& s) {
+  return s.kind == SD_SEL_MASS_BUDGET && units_max(d, unit) > kBudgetOneMax;
+}
+
+size_t select_ws_bytes(const sdkv::Dims& d, int unit, const Sel& s) {
+  if (budget_multi(d, unit, s)) return sdkv::budget_multi_workspace_bytes(d, units_max(d, unit));
+  return select_ws_bytes(d, unit);
+}
+
 // Partial min / max keys written by the token scorer for the many-block top-k.
 int score_mm_parts(const sdkv::Dims& d) {
   const int per = sdkv::score_units_per_block(d.dtype, d.D);
@@ -224,7 +235,7 @@ Layout layout(const sdkv::Dims& d, int unit, const Sel& sel) {
   if (unit == SD_UNIT_TOKEN) off = align_up(off + sizeof(float) * bh * d.max_seq);
   L.sel_idx = off;     off = align_up(off + sizeof(int32_t) * bg * k_max);
   L.sel_count = off;   off = align_up(off + sizeof(int32_t) * bg);
-  L.msel = off;        off = align_up(off + select_ws_bytes(d, unit));
+  L.msel = off;        off = align_up(off + select_ws_bytes(d, unit, sel));
   L.score_mm = off;
   if (unit == SD_UNIT_TOKEN && multi_select(d, unit))
     off = align_up(off + sizeof(uint32_t) * 2 * bg * score_mm_parts(d));
@@ -251,7 +262,7 @@ SelectLayout select_layout(const sdkv::Dims& d, int unit, const Sel& sel) {
   const bool uni = sel.kind == SD_SEL_INIT_LOCAL_TOPK;
   size_t off = 0;
   L.msel = off;
-  if (sel.kind != SD_SEL_WINDOW) off = align_up(off + select_ws_bytes(d, unit));
+  if (sel.kind != SD_SEL_WINDOW) off = align_up(off + select_ws_bytes(d, unit, sel));
   L.tmp = off;
   if (uni) off = align_up(off + sizeof(int32_t) * bg * k_top);
   L.cnt = off;
@@ -431,7 +442,8 @@ bool fused_select(const sdkv::Dims& d, int unit, int k_max) {
 
 // The kept lists of a selection (not a window) from unit scores: the top-k,
 // or the top-k (kept in the workspace) merged with the forced ranges.  Rows
-// of idx hold capacity(sel, U_max) entries.
+// of idx hold capacity(sel, U_max) entries; msel_ws holds
+// select_ws_bytes(d, unit, sel) bytes.
 sd_status do_select_list(const sdkv::Dims& d, int unit, const int32_t* sl, const float* scores,
                          const float* logits, const Sel& sel, int32_t* idx, int32_t* cnt,
                          void* msel_ws, int32_t* top_tmp, int32_t* top_cnt, hipStream_t s,
@@ -450,6 +462,9 @@ sd_status do_select_list(const sdkv::Dims& d, int unit, const int32_t* sl, const
     a.max_dropped = static_cast<float>(sel.dmax);
     a.sel_idx = idx;
     a.sel_count = cnt;
+    if (budget_multi(d, unit, sel))
+      return device_status(sdkv::launch_select_budget_multi(a, msel_ws, s),
+                           "budget selection kernels launch");
     return device_status(sdkv::launch_select_budget(a, s), "budget selection kernel launch");
   }
   const int U = units_max(d, unit);

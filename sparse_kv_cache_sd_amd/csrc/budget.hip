@@ -235,6 +235,16 @@ __global__ __launch_bounds__(kBT) void select_budget_kernel(BudgetArgs a) {
       }
       __syncthreads();
       first = false;
+      // keeping no unit already meets the target: one unit is kept (the
+      // descent below needs a head above the target with the units above
+      // the interval alone, or it would pick an empty top bin)
+      bool met = true;
+      for (int h = 0; h < G; ++h) met = met && sm.tot[h] <= target;
+      if (met) {
+        if (tid == 0) sm.kstar = 1;
+        __syncthreads();
+        break;
+      }
     }
     if (wave == 0) {
       // lane l holds bins 255 - 4l - j (j < 4): descending order.  ok[j]:

@@ -184,6 +184,11 @@ struct BudgetArgs {
   int32_t* sel_count;    // [B][Hkv]
 };
 hipError_t launch_select_budget(const BudgetArgs& a, hipStream_t st);
+// The same count and list spread over many blocks per (b, g): any U_max
+// (<= max_seq), G <= 8; scratch of budget_multi_workspace_bytes(d, U_max)
+// bytes (contents need not be set).
+size_t budget_multi_workspace_bytes(const Dims& d, int U_max);
+hipError_t launch_select_budget_multi(const BudgetArgs& a, void* ws, hipStream_t st);
 
 // Compressed-key page scoring.  ckeys: [B][Hkv][max_windows][D] fp32, window
 // j the mean of the valid keys 16 j .. 16 j + 31 (max_windows =
@@ -221,10 +226,11 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t st);
 // msel_workspace_bytes(B, Hkv, U_max) bytes (contents need not be set).
 // mm: partial min / max keys of the scores ([B*Hkv][mm_nb][2], each over
 // mm_per consecutive units, e.g. ScoreArgs::score_mm), or NULL to compute
-// them here.
+// them here.  k_of: the count to keep per (b, g) ([B*Hkv], at most k_max),
+// or NULL for min(keep_count(U, R_ppm), k_max).
 size_t msel_workspace_bytes(int B, int Hkv, int U_max);
 hipError_t launch_select_multi(const SelectArgs& a, const uint32_t* mm, int mm_nb, int mm_per,
-                               void* ws, hipStream_t st);
+                               void* ws, hipStream_t st, const int32_t* k_of = nullptr);
 // Log-sum-exp merge of the split partials written by an attention launch.
 struct MergeArgs {
   Dims d;

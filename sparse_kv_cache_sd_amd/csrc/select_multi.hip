@@ -55,6 +55,7 @@ struct MArgs {
   uint32_t* hist;            // [kMPasses][B*Hkv][NB][kMBins]
   int32_t* sel_idx;          // [B][Hkv][k_max]
   int32_t* sel_count;        // [B][Hkv]
+  const int32_t* k_of;       // [B*Hkv] counts to keep, or NULL: min(keep_count(U), k_max)
 };
 
 struct MShared {
@@ -109,7 +110,7 @@ __device__ void initial_state(const MArgs& a, MShared& sm, int64_t bg, int U) {
   }
   block_minmax<kMNW>(sm.rs, mn, mx);
   if (threadIdx.x == 0) {
-    const int k = min(keep_count_dev(U, a.R_ppm), a.k_max);
+    const int k = a.k_of ? min(max(a.k_of[bg], 0), U) : min(keep_count_dev(U, a.R_ppm), a.k_max);
     MState S{};
     S.lo = sm.rs.lo;
     S.hi = sm.rs.hi;
@@ -324,7 +325,7 @@ size_t msel_workspace_bytes(int B, int Hkv, int U_max) {
 }
 
 hipError_t launch_select_multi(const SelectArgs& sa, const uint32_t* mm, int mm_nb, int mm_per,
-                               void* ws, hipStream_t stream) {
+                               void* ws, hipStream_t stream, const int32_t* k_of) {
   MArgs a{};
   a.d = sa.d;
   a.unit = sa.unit;
@@ -345,6 +346,7 @@ hipError_t launch_select_multi(const SelectArgs& sa, const uint32_t* mm, int mm_
   a.hist = reinterpret_cast<uint32_t*>(p);
   a.sel_idx = sa.sel_idx;
   a.sel_count = sa.sel_count;
+  a.k_of = k_of;
   const dim3 grid(a.NB * sa.d.Hkv * sa.d.B);  // block id = bg + B*Hkv*slice
   if (mm) {
     a.mm = mm;

@@ -220,6 +220,17 @@ def test_full_size_mass_budget(target, cap):
           f"oracle's", flush=True)
 
 
+def test_full_size_mass_budget_128k():
+    """The dropped-mass budget at 128K token (many blocks per (b, g)), the
+    target binding below the cap; sampled instances against the oracle."""
+    from test_gpu_structured import _check_budget
+    print("[fullsize] sweep-128k budget 0.3 cap 0.9", flush=True)
+    dev = _dev("sweep", 128 * K)
+    exact = _check_budget(dev, sd.Selection("mass_budget", 0.9, max_dropped=0.3),
+                          groups=[(0, 0), (0, 3), (0, 7)])
+    print(f"[fullsize] sweep-128k budget: {exact} counts equal to the oracle's", flush=True)
+
+
 @pytest.mark.parametrize("cid,name,context,r_kv,groups", [
     ("l8b-32k-compressed", "l8b", None, 0.3, "all"),
     ("l70b-128k-compressed", "l70b", 128 * K, 0.05, [(0, 0), (0, 4), (0, 7)]),

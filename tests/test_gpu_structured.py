@@ -206,7 +206,10 @@ def _budget_run(dev, sel):
             idx2.cpu().numpy(), cnt2.cpu().numpy(), scores.cpu().numpy().astype(np.float64))
 
 
-def _check_budget(dev, sel):
+def _check_budget(dev, sel, groups=None):
+    """Every (b, g), or the listed ones: the count against the oracle's rule,
+    the list against the top-k of the library's own scores at that count, the
+    output against the oracle on the kept set."""
     w, s = dev.w, dev.shape
     scale = 1.0 / math.sqrt(s.head_dim)
     out, lse, idx, cnt, idx2, cnt2, own = _budget_run(dev, sel)
@@ -216,6 +219,8 @@ def _check_budget(dev, sel):
         n = int(w.seq_lens[b])
         cap = sdref.keep_count(sel.r_kv, n)
         for g in range(s.num_kv_heads):
+            if groups is not None and (b, g) not in groups:
+                continue
             k = int(cnt[b, g])
             assert 1 <= k <= cap, f"(b={b}, g={g}) count {k} outside [1, {cap}]"
             kept = idx[b, g, :k].astype(np.int64)
@@ -258,6 +263,11 @@ BUDGET_CASES = [
     ("g8-ragged", R["l70b"].with_(batch=3, seq_len=4000, seq_len_min=1, num_q_heads=16,
                                   num_kv_heads=2), [0.1]),
     ("sweep-32k", R["sweep"].with_(seq_len=32768, num_q_heads=8, num_kv_heads=2), [0.1]),
+    # past 32768 tokens the budget runs over many blocks per (b, g): 20
+    # slices with a ragged last one, and a ragged G = 8 batch
+    ("sweep-40k", R["sweep"].with_(seq_len=40000, num_q_heads=8, num_kv_heads=2), [0.05, 0.3]),
+    ("g8-ragged-70k", R["l70b"].with_(batch=3, seq_len=70000, seq_len_min=1, num_q_heads=16,
+                                      num_kv_heads=2), [0.1]),
 ]
 
 
@@ -293,7 +303,22 @@ def test_mass_budget_edges():
         sd.workspace_bytes_sel(s, "token", sd.Selection("mass_budget", 0.3, max_dropped=1.5))
 
 
-@pytest.mark.parametrize("max_seq,tied", [(1001, False), (1001, True), (4096, True)])
+def test_mass_budget_edges_many_blocks():
+    """Targets 1 and 0 past 32768 tokens (the many-block kernels), with an
+    empty and a one-token sequence in the batch."""
+    rec = R["sweep"].with_(batch=3, seq_len=40000, num_q_heads=8, num_kv_heads=2)
+    w = kvsynth.generate(rec, seq_lens=[40000, 0, 1])
+    dev = upload(w)
+    for t in (1.0, 0.0):
+        out, lse, idx, cnt, *_ = _budget_run(dev, sd.Selection("mass_budget", 0.3, max_dropped=t))
+        for b, n in enumerate(w.seq_lens):
+            want = 0 if n == 0 else (1 if t == 1.0 else sdref.keep_count(0.3, int(n)))
+            assert np.all(cnt[b] == want), (t, b, cnt[b], want)
+        assert np.all(idx[2, :, 0] == 0)
+
+
+@pytest.mark.parametrize("max_seq,tied", [(1001, False), (1001, True), (4096, True),
+                                           (40000, False), (40000, True)])
 def test_mass_budget_on_given_logits(max_seq, tied):
     """sd_select_units on hand-made logits (rows of any length, heavy ties in
     the group score): the count against the oracle's rule on the same fp32
