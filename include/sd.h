@@ -244,10 +244,12 @@ SD_API sd_status sd_decode_step(const sd_shape* shape, const void* q, const void
  *                           head's dense softmax mass outside, capped at k_b
  *                           ([Cross/cards] pre-hoc sparsity abstract: the
  *                           dropped mass controlled in advance).  Needs the
- *                           token logits; at most 32768 tokens per sequence
- *                           (SD_E_UNSUPPORTED beyond).  The masses are summed
- *                           as 2^-40 fixed-point integers of the fp32 softmax
- *                           weights.
+ *                           token logits; any number of tokens (one block per
+ *                           (b, g) up to 16384, many past that, with the same
+ *                           count).  The masses are summed as 2^-40
+ *                           fixed-point integers of the fp32 softmax weights;
+ *                           when no unit needs keeping to meet the target,
+ *                           one unit is kept.
  * Lists are ascending.  The row length of a kept list is
  * sd_selection_capacity(sel, U_max): k_max, or min(U_max, init_units +
  * local_units + k_max) for the union. */

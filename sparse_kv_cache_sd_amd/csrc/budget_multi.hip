@@ -20,12 +20,13 @@
 //              2^40 fixed-point integers, built in LDS, then added into the
 //              (b, g)'s histogram of the pass with global atomics (integer
 //              sums do not depend on the order of the atomics, so the result
-//              does not depend on timing);
-//   bm_narrow  one block per (b, g), after each pass: the first bin from the
-//              top whose inclusion brings every head within the target
-//              becomes the interval, as in the one-block kernel;
-//   bm_ties    one block per (b, g): when the interval is one key value, its
-//              tokens in id order until the target holds; writes the count;
+//              does not depend on timing).  Before pass p > 0 each block
+//              narrows the interval from pass p - 1's sums: the first bin
+//              from the top whose inclusion brings every head within the
+//              target, as in the one-block kernel;
+//   bm_ties    one block per (b, g): narrows after the last pass; when the
+//              interval is one key value, takes its tokens in id order until
+//              the target holds; writes the count;
 // then the many-block top-k (select_multi.hip) keeps that many units.
 #include "topk.h"
 
@@ -66,7 +67,7 @@ struct QArgs {
   int slice, NB;        // tokens per slice (a multiple of kQChunk); slices per (b, g)
   float2* part;         // [BG][NB][kQMaxG] (largest logit, sum of exponentials)
   uint32_t* mm;         // [BG][NB][2] min / max order key
-  QState* st;           // [BG]
+  QState* st;           // [kQPasses][BG]: the state pass p runs with
   u64* hist;            // [kQPasses][BG][1 + G][kQBins]: counts, then each head's
                         // mass, summed over the slices; cleared by bm_init
   int32_t* kk;          // [BG] the count
@@ -227,13 +228,14 @@ __global__ __launch_bounds__(kDT) void bm_init_kernel(QArgs q) {
       s.m[h] = m;
       s.invz[h] = 1.f / z;
     }
-    q.st[bg] = s;
+    q.st[bg] = s;  // pass 0's state
   }
 }
 
 // After histogram pass p of a (b, g) (rows: its summed histogram in LDS,
 // counts then each head's mass; S: the state the pass ran with, in LDS): the
-// next state, written to *gs.  Every thread of the block calls it.
+// next state, also written to *gs unless gs is NULL.  Every thread of the
+// block calls it; S is final after a barrier.
 __device__ void narrow_after(const BudgetArgs& a, QState& S, const u64* rows, int p,
                              QState* gs) {
   const int G = a.d.G;
@@ -254,7 +256,7 @@ __device__ void narrow_after(const BudgetArgs& a, QState& S, const u64* rows, in
       if (tid == 0) {
         S.kstar = 1;
         S.done = 1u;
-        *gs = S;
+        if (gs) *gs = S;
       }
       return;
     }
@@ -262,7 +264,7 @@ __device__ void narrow_after(const BudgetArgs& a, QState& S, const u64* rows, in
   if (S.lo == S.hi) {  // one key value: the tie scan decides
     if (tid == 0) {
       S.done = 1u;
-      *gs = S;
+      if (gs) *gs = S;
     }
     return;
   }
@@ -323,10 +325,13 @@ __device__ void narrow_after(const BudgetArgs& a, QState& S, const u64* rows, in
     }
   }
   __syncthreads();
-  if (tid == 0) *gs = S;
+  if (tid == 0 && gs) *gs = S;
 }
 
-// Histogram pass p over one slice, added into the (b, g)'s sums.
+// Histogram pass p over one slice, added into the (b, g)'s sums.  For p > 0
+// every block first narrows the interval from pass p - 1's sums itself (the
+// same integer steps on the same inputs in every block, so they agree);
+// slice 0 records the state in st[p].  This saves a launch per pass.
 __global__ __launch_bounds__(kQT) void bm_hist_kernel(QArgs q, int p) {
   __shared__ u64 h[(1 + kQMaxG) * kQBins];
   __shared__ QState S;
@@ -338,11 +343,23 @@ __global__ __launch_bounds__(kQT) void bm_hist_kernel(QArgs q, int p) {
   const int s0 = gb.j * q.slice;
   if (s0 >= U) return;
   const int tid = threadIdx.x;
-  if (tid == 0) S = q.st[gb.bg];
   const int HS = (1 + G) * kQBins;
-  for (int i = tid; i < HS; i += kQT) h[i] = 0ull;
+  if (tid == 0) S = q.st[(int64_t)(p > 0 ? p - 1 : 0) * BG + gb.bg];
+  if (p > 0) {
+    const u64* prev = q.hist + ((int64_t)(p - 1) * BG + gb.bg) * HS;
+    for (int i = tid; i < HS; i += kQT) h[i] = prev[i];
+  }
   __syncthreads();
-  if (S.done) return;  // the same state for every block of the (b, g)
+  if (p > 0) {
+    QState* rec = gb.j == 0 ? q.st + (int64_t)p * BG + gb.bg : nullptr;
+    if (!S.done) {
+      narrow_after(a, S, h, p - 1, rec);
+      __syncthreads();
+    } else if (rec && tid == 0) {
+      *rec = S;
+    }
+  }
+  if (S.done) return;  // the same state in every block of the (b, g)
   const uint32_t lo = S.lo, hi = S.hi, shift = bin_shift(lo, hi);
   float m[kQMaxG], invz[kQMaxG];
 #pragma unroll
@@ -350,6 +367,9 @@ __global__ __launch_bounds__(kQT) void bm_hist_kernel(QArgs q, int p) {
     m[i] = S.m[i];
     invz[i] = S.invz[i];
   }
+  __syncthreads();  // h is cleared below
+  for (int i = tid; i < HS; i += kQT) h[i] = 0ull;
+  __syncthreads();
   const int s1 = min(s0 + q.slice, U);
   const float* sc = a.scores + (int64_t)gb.bg * a.U_max;
   const float* lg = a.logits + ((int64_t)b * a.d.Hq + (int64_t)g * G) * a.d.max_seq;
@@ -379,30 +399,16 @@ __global__ __launch_bounds__(kQT) void bm_hist_kernel(QArgs q, int p) {
   }
 }
 
-// After histogram pass p, one block per (b, g): the next interval.
-__global__ __launch_bounds__(kDT) void bm_narrow_kernel(QArgs q, int p) {
-  __shared__ u64 rows[(1 + kQMaxG) * kQBins];
-  __shared__ QState S;
-  const BudgetArgs& a = q.a;
-  const int BG = a.d.B * a.d.Hkv, bg = blockIdx.x;
-  const int tid = threadIdx.x;
-  if (tid == 0) S = q.st[bg];
-  __syncthreads();
-  if (S.done) return;
-  const int HS = (1 + a.d.G) * kQBins;
-  const u64* hb = q.hist + ((int64_t)p * BG + bg) * HS;
-  for (int i = tid; i < HS; i += kDT) rows[i] = hb[i];
-  __syncthreads();
-  narrow_after(a, S, rows, p, q.st + bg);
-}
-
 __global__ __launch_bounds__(kTT) void bm_ties_kernel(QArgs q) {
   __shared__ QState S;
+  __shared__ u64 rows[(1 + kQMaxG) * kQBins];
   __shared__ uint64_t tie[kTK * kTW];
   __shared__ int found_s;
   const BudgetArgs& a = q.a;
+  const int BG = a.d.B * a.d.Hkv;
   const int bg = blockIdx.x, b = bg / a.d.Hkv, g = bg % a.d.Hkv, G = a.d.G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // an empty sequence stops at pass 0 (no slice block records later states)
   if (tid == 0) {
     S = q.st[bg];
     found_s = 0;
@@ -411,6 +417,17 @@ __global__ __launch_bounds__(kTT) void bm_ties_kernel(QArgs q) {
   if (S.kcap == 0) {
     if (tid == 0) q.kk[bg] = 0;
     return;
+  }
+  // the state after the last pass
+  const int HS = (1 + G) * kQBins;
+  __syncthreads();
+  if (tid == 0) S = q.st[(int64_t)(kQPasses - 1) * BG + bg];
+  const u64* last = q.hist + ((int64_t)(kQPasses - 1) * BG + bg) * HS;
+  for (int i = tid; i < HS; i += kTT) rows[i] = last[i];
+  __syncthreads();
+  if (!S.done) {
+    narrow_after(a, S, rows, kQPasses - 1, nullptr);
+    __syncthreads();
   }
   if (S.kstar > 0) {
     if (tid == 0) q.kk[bg] = max(1, min(S.kstar, S.kcap));
@@ -486,7 +503,7 @@ QLayout q_layout(const Dims& d, int U_max) {
   size_t off = 0;
   L.part = off; off = up(off + sizeof(float2) * bg * L.NB * kQMaxG);
   L.mm = off;   off = up(off + sizeof(uint32_t) * 2 * bg * L.NB);
-  L.st = off;   off = up(off + sizeof(QState) * bg);
+  L.st = off;   off = up(off + sizeof(QState) * kQPasses * bg);
   L.hist = off; off = up(off + sizeof(u64) * kQPasses * bg * (1 + d.G) * kQBins);
   L.kk = off;   off = up(off + sizeof(int32_t) * bg);
   L.msel = off; off = up(off + msel_workspace_bytes(d.B, d.Hkv, U_max));
@@ -519,10 +536,7 @@ hipError_t launch_select_budget_multi(const BudgetArgs& a, void* ws, hipStream_t
   const dim3 grid(BG * L.NB);  // block id = bg + B*Hkv*slice
   bm_norm_kernel<<<grid, kQT, 0, st>>>(q);
   bm_init_kernel<<<BG, kDT, 0, st>>>(q);
-  for (int p = 0; p < kQPasses; ++p) {
-    bm_hist_kernel<<<grid, kQT, 0, st>>>(q, p);
-    bm_narrow_kernel<<<BG, kDT, 0, st>>>(q, p);
-  }
+  for (int p = 0; p < kQPasses; ++p) bm_hist_kernel<<<grid, kQT, 0, st>>>(q, p);
   bm_ties_kernel<<<BG, kTT, 0, st>>>(q);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
