@@ -113,12 +113,15 @@ __device__ __forceinline__ uint32_t wave_umax32(uint32_t x) {
   return x;
 }
 
+// G as a template parameter: every head's loads of a chunk are issued
+// before any of them is reduced.
+template <int G>
 __global__ __launch_bounds__(kQT) void bm_norm_kernel(QArgs q) {
   __shared__ float2 red[kQW][kQMaxG];
   __shared__ uint32_t rmn[kQW], rmx[kQW];
   const BudgetArgs& a = q.a;
   const GroupBlock gb = group_block(a.d.B * a.d.Hkv);
-  const int b = gb.bg / a.d.Hkv, g = gb.bg % a.d.Hkv, G = a.d.G;
+  const int b = gb.bg / a.d.Hkv, g = gb.bg % a.d.Hkv;
   const int U = tokens_of(a, b);
   const int s0 = gb.j * q.slice;
   if (s0 >= U) return;  // the init kernel reads only slices holding tokens
@@ -127,39 +130,39 @@ __global__ __launch_bounds__(kQT) void bm_norm_kernel(QArgs q) {
   const float* sc = a.scores + (int64_t)gb.bg * a.U_max;
   const float* lg = a.logits + ((int64_t)b * a.d.Hq + (int64_t)g * G) * a.d.max_seq;
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-  float m[kQMaxG], z[kQMaxG];
+  float m[G], z[G];
 #pragma unroll
-  for (int h = 0; h < kQMaxG; ++h) { m[h] = -INFINITY; z[h] = 0.f; }
+  for (int h = 0; h < G; ++h) { m[h] = -INFINITY; z[h] = 0.f; }
   for (int c0 = s0; c0 < s1; c0 += kQChunk) {
     uint32_t key[kQK];
+    float x[G][kQK];
 #pragma unroll
-    for (int i = 0; i < kQK; ++i) key[i] = order_key(sc[min(c0 + tid + kQT * i, a.U_max - 1)]);
+    for (int i = 0; i < kQK; ++i) {
+      const int t = min(c0 + tid + kQT * i, a.U_max - 1);
+      key[i] = order_key(sc[t]);
+#pragma unroll
+      for (int h = 0; h < G; ++h) x[h][i] = lg[(int64_t)h * a.d.max_seq + t];
+    }
 #pragma unroll
     for (int i = 0; i < kQK; ++i)
       if (c0 + tid + kQT * i < s1) { mn = min(mn, key[i]); mx = max(mx, key[i]); }
 #pragma unroll
-    for (int h = 0; h < kQMaxG; ++h) {
-      if (h >= G) break;
-      float x[kQK];
-#pragma unroll
-      for (int i = 0; i < kQK; ++i)
-        x[i] = lg[(int64_t)h * a.d.max_seq + min(c0 + tid + kQT * i, a.U_max - 1)];
+    for (int h = 0; h < G; ++h) {
       float cm = -INFINITY;
 #pragma unroll
       for (int i = 0; i < kQK; ++i)
-        if (c0 + tid + kQT * i < s1) cm = fmaxf(cm, x[i]);
+        if (c0 + tid + kQT * i < s1) cm = fmaxf(cm, x[h][i]);
       float cz = 0.f;
 #pragma unroll
       for (int i = 0; i < kQK; ++i)
-        if (c0 + tid + kQT * i < s1) cz += exp2f((x[i] - cm) * kLog2e);
+        if (c0 + tid + kQT * i < s1) cz += exp2f((x[h][i] - cm) * kLog2e);
       lse_combine(m[h], z[h], cm, cz);
     }
   }
   mn = wave_umin32(mn);
   mx = wave_umax32(mx);
 #pragma unroll
-  for (int h = 0; h < kQMaxG; ++h) {
-    if (h >= G) break;
+  for (int h = 0; h < G; ++h) {
     wave_lse(m[h], z[h]);
     if (lane == 0) red[wave][h] = make_float2(m[h], z[h]);
   }
@@ -197,20 +200,23 @@ __global__ __launch_bounds__(kDT) void bm_init_kernel(QArgs q) {
     u64* hz = q.hist + ((int64_t)pp * BG + bg) * HS;
     for (int i = tid; i < HS; i += kDT) hz[i] = 0ull;
   }
-  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-  for (int j = tid; j < nbv; j += kDT) {
-    mn = min(mn, q.mm[((int64_t)bg * q.NB + j) * 2]);
-    mx = max(mx, q.mm[((int64_t)bg * q.NB + j) * 2 + 1]);
-  }
+  // thread t holds slice t (NB <= kQMaxSlices <= kDT): every load is issued
+  // before any is combined
+  static_assert(kQMaxSlices <= kDT, "one slice per thread");
+  const bool have = tid < nbv;
+  const int64_t slot = (int64_t)bg * q.NB + (have ? tid : 0);
+  uint32_t mn = q.mm[slot * 2], mx = q.mm[slot * 2 + 1];
+  float2 pz[kQMaxG];
+#pragma unroll
+  for (int h = 0; h < kQMaxG; ++h) pz[h] = q.part[slot * kQMaxG + h];
+  if (!have) { mn = 0xFFFFFFFFu; mx = 0u; }
   mn = wave_umin32(mn);
   mx = wave_umax32(mx);
   if (lane == 0) { rmn[wave] = mn; rmx[wave] = mx; }
-  for (int h = 0; h < G; ++h) {
-    float m = -INFINITY, z = 0.f;
-    for (int j = tid; j < nbv; j += kDT) {
-      const float2 pz = q.part[((int64_t)bg * q.NB + j) * kQMaxG + h];
-      lse_combine(m, z, pz.x, pz.y);
-    }
+#pragma unroll
+  for (int h = 0; h < kQMaxG; ++h) {
+    if (h >= G) break;
+    float m = have ? pz[h].x : -INFINITY, z = have ? pz[h].y : 0.f;
     wave_lse(m, z);
     if (lane == 0) red[wave][h] = make_float2(m, z);
   }
@@ -534,7 +540,13 @@ hipError_t launch_select_budget_multi(const BudgetArgs& a, void* ws, hipStream_t
   q.kk = reinterpret_cast<int32_t*>(base + L.kk);
   const int BG = a.d.B * a.d.Hkv;
   const dim3 grid(BG * L.NB);  // block id = bg + B*Hkv*slice
-  bm_norm_kernel<<<grid, kQT, 0, st>>>(q);
+  switch (a.d.G) {
+    case 1: bm_norm_kernel<1><<<grid, kQT, 0, st>>>(q); break;
+    case 2: bm_norm_kernel<2><<<grid, kQT, 0, st>>>(q); break;
+    case 4: bm_norm_kernel<4><<<grid, kQT, 0, st>>>(q); break;
+    case 8: bm_norm_kernel<8><<<grid, kQT, 0, st>>>(q); break;
+    default: return hipErrorInvalidValue;
+  }
   bm_init_kernel<<<BG, kDT, 0, st>>>(q);
   for (int p = 0; p < kQPasses; ++p) bm_hist_kernel<<<grid, kQT, 0, st>>>(q, p);
   bm_ties_kernel<<<BG, kTT, 0, st>>>(q);
