@@ -134,11 +134,14 @@ def test_dropped_mass_edges():
                 assert abs(float(delta[b, g * G + i]) - ref) <= 1e-6 + 2e-4 * ref
 
 
-def test_dropped_mass_of_the_budget():
+@pytest.mark.parametrize("n", [6000, 50000])
+def test_dropped_mass_of_the_budget(n):
     """The budget keeps the shortest prefix leaving at most the target of every
     head's mass outside: delta on its lists is within the target (up to the
-    fp32 decision margin) wherever the cap does not bind."""
-    rec = R["sweep"].with_(seq_len=6000, num_q_heads=16, num_kv_heads=4)
+    fp32 decision margin) wherever the cap does not bind, and one unit fewer
+    leaves more than the target for some head.  50000 tokens: the budget
+    over many blocks per (b, g)."""
+    rec = R["sweep"].with_(seq_len=n, num_q_heads=16, num_kv_heads=4)
     dev = upload(kvsynth.generate(rec))
     s = dev.shape
     scores, logits = _scores(dev)
@@ -155,6 +158,17 @@ def test_dropped_mass_of_the_budget():
             if c[0, g] < cap:
                 assert delta[0, g * s.group:(g + 1) * s.group].max() <= target + 1e-5
         _compare(dev, delta, idx.cpu().numpy(), c)
+        # one unit fewer (the top-k of the same scores at count - 1) leaves
+        # more than the target for some head of the group
+        own = scores.cpu().numpy().astype(np.float64)
+        fewer = np.zeros(idx.shape, dtype=np.int32)
+        fcnt = np.maximum(c - 1, 1).astype(np.int32)
+        for g in range(s.num_kv_heads):
+            fewer[0, g, :fcnt[0, g]] = sdref.select_topk(own[0, g, :n], int(fcnt[0, g]))[0]
+        d_f = _delta(dev, logits, torch.from_numpy(fewer).cuda(), torch.from_numpy(fcnt).cuda())
+        for g in range(s.num_kv_heads):
+            if c[0, g] >= 2:
+                assert d_f[0, g * s.group:(g + 1) * s.group].max() > target - 1e-5
 
 
 def test_dropped_mass_rejects():

@@ -151,8 +151,10 @@ def test_entmax_structured(kind, unit):
     _compare(w, dev, unit, sel, 1.5, _run(dev, unit, sel, 1.5))
 
 
-def test_entmax_mass_budget():
-    rec = R["l8b"].with_(seq_len=3000, num_q_heads=8, num_kv_heads=2)
+@pytest.mark.parametrize("n", [3000, 20000])
+def test_entmax_mass_budget(n):
+    # 20000 tokens: the budget over many blocks per (b, g)
+    rec = R["l8b"].with_(seq_len=n, num_q_heads=8, num_kv_heads=2)
     w = kvsynth.generate(rec)
     dev = upload(w)
     sel = sd.Selection("mass_budget", 0.5, max_dropped=0.2)
@@ -163,7 +165,9 @@ def test_entmax_mass_budget():
     # the budget's count is checked by the softmax tests; here the entmax
     # outputs over the GPU's own kept list
     for g in range(s.num_kv_heads):
+        assert 1 <= int(cnt[0, g]) <= sdref.keep_count(0.5, n)
         kept = idx[0, g, :int(cnt[0, g])].astype(np.int64)
+        assert np.all(np.diff(kept) > 0) and kept[0] >= 0 and kept[-1] < n
         orc = _oracle(w, 0, g, "token", 0.5, scale, 1.5, kept_override=kept)
         heads = slice(g * G, (g + 1) * G)
         assert np.abs(out[0, heads] - orc.out_sparse).max() <= TOL["bf16"]
