@@ -42,7 +42,7 @@ constexpr int kQMaxSlices = 64;          // slices per (b, g)
 constexpr int kQBins = 256;
 constexpr int kQMaxG = 8;
 constexpr int kQPasses = 4;              // 8-bit bins cover any 32-bit interval
-constexpr int kDT = 256;                 // decide threads: one bin each
+constexpr int kDT = 256;                 // threads of the per-(b, g) init block
 constexpr int kTT = 1024;                // tie scan threads
 constexpr int kTW = kTT / 64;
 constexpr int kTK = 8;                   // ids per thread per tie chunk
