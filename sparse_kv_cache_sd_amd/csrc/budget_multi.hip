@@ -12,18 +12,18 @@
 // the partials exchanged below stay in its L2.
 //   bm_norm    per slice: each head's largest logit and the sum of the
 //              exponentials below it; the min / max order key of the group
-//              scores;
-//   bm_init    one block per (b, g): the softmax normalisers (the slices
-//              combined in slice order) and the key interval;
+//              scores; clears pass 0's histogram;
 //   bm_hist    per slice: 256-bin histograms of the keys inside the interval,
 //              the count and each head's mass p_h(t) = e^(s - m_h) / Z_h as
 //              2^40 fixed-point integers, built in LDS, then added into the
 //              (b, g)'s histogram of the pass with global atomics (integer
 //              sums do not depend on the order of the atomics, so the result
-//              does not depend on timing).  Before pass p > 0 each block
-//              narrows the interval from pass p - 1's sums: the first bin
-//              from the top whose inclusion brings every head within the
-//              target, as in the one-block kernel;
+//              does not depend on timing).  Before pass 0 each block
+//              combines the slice partials (the softmax normalisers and the
+//              key interval); before pass p > 0 it narrows the interval from
+//              pass p - 1's sums: the first bin from the top whose inclusion
+//              brings every head within the target, as in the one-block
+//              kernel.  Pass p clears pass p + 1's histogram;
 //   bm_ties    one block per (b, g): narrows after the last pass; when the
 //              interval is one key value, takes its tokens in id order until
 //              the target holds; writes the count;
@@ -42,7 +42,6 @@ constexpr int kQMaxSlices = 64;          // slices per (b, g)
 constexpr int kQBins = 256;
 constexpr int kQMaxG = 8;
 constexpr int kQPasses = 4;              // 8-bit bins cover any 32-bit interval
-constexpr int kDT = 256;                 // threads of the per-(b, g) init block
 constexpr int kTT = 1024;                // tie scan threads
 constexpr int kTW = kTT / 64;
 constexpr int kTK = 8;                   // ids per thread per tie chunk
@@ -69,7 +68,7 @@ struct QArgs {
   uint32_t* mm;         // [BG][NB][2] min / max order key
   QState* st;           // [kQPasses][BG]: the state pass p runs with
   u64* hist;            // [kQPasses][BG][1 + G][kQBins]: counts, then each head's
-                        // mass, summed over the slices; cleared by bm_init
+                        // mass, summed over the slices
   int32_t* kk;          // [BG] the count
 };
 
@@ -113,6 +112,16 @@ __device__ __forceinline__ uint32_t wave_umax32(uint32_t x) {
   return x;
 }
 
+// Clears this block's share of the (b, g)'s histogram of pass p: the NB
+// blocks of the (b, g) share it (block j takes rows j kQT + tid, stepping by
+// NB kQT), so every entry is cleared whether or not the block has tokens.
+__device__ __forceinline__ void clear_pass_share(const QArgs& q, int bg, int j, int p) {
+  const int BG = q.a.d.B * q.a.d.Hkv;
+  const int HS = (1 + q.a.d.G) * kQBins;
+  u64* hz = q.hist + ((int64_t)p * BG + bg) * HS;
+  for (int i = j * kQT + (int)threadIdx.x; i < HS; i += q.NB * kQT) hz[i] = 0ull;
+}
+
 // G as a template parameter: every head's loads of a chunk are issued
 // before any of them is reduced.
 template <int G>
@@ -124,7 +133,8 @@ __global__ __launch_bounds__(kQT) void bm_norm_kernel(QArgs q) {
   const int b = gb.bg / a.d.Hkv, g = gb.bg % a.d.Hkv;
   const int U = tokens_of(a, b);
   const int s0 = gb.j * q.slice;
-  if (s0 >= U) return;  // the init kernel reads only slices holding tokens
+  clear_pass_share(q, gb.bg, gb.j, 0);
+  if (s0 >= U) return;  // pass 0 reads only slices holding tokens
   const int s1 = min(s0 + q.slice, U);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* sc = a.scores + (int64_t)gb.bg * a.U_max;
@@ -183,26 +193,20 @@ __global__ __launch_bounds__(kQT) void bm_norm_kernel(QArgs q) {
   }
 }
 
-// Pass 0 of a (b, g): the softmax normalisers (slice partials combined in
-// slice order, then lanes and waves in a fixed order), the key interval
-// [min, max], the cap; clears the pass histograms.
-__global__ __launch_bounds__(kDT) void bm_init_kernel(QArgs q) {
-  __shared__ float2 red[kDT / 64][kQMaxG];
-  __shared__ uint32_t rmn[kDT / 64], rmx[kDT / 64];
+// Pass 0's state of a (b, g) into S (every thread of a kQT-thread block
+// calls it; S is final after it returns): the softmax normalisers (slice
+// partials combined across lanes and waves in a fixed order), the key
+// interval [min, max], the cap.
+__device__ void initial_state(const QArgs& q, int bg, int U, QState& S) {
+  __shared__ float2 red[kQW][kQMaxG];
+  __shared__ uint32_t rmn[kQW], rmx[kQW];
   const BudgetArgs& a = q.a;
-  const int BG = a.d.B * a.d.Hkv;
-  const int bg = blockIdx.x, b = bg / a.d.Hkv, G = a.d.G;
+  const int G = a.d.G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int U = tokens_of(a, b);
   const int nbv = (U + q.slice - 1) / q.slice;
-  const int HS = (1 + G) * kQBins;
-  for (int pp = 0; pp < kQPasses; ++pp) {
-    u64* hz = q.hist + ((int64_t)pp * BG + bg) * HS;
-    for (int i = tid; i < HS; i += kDT) hz[i] = 0ull;
-  }
-  // thread t holds slice t (NB <= kQMaxSlices <= kDT): every load is issued
+  // thread t holds slice t (NB <= kQMaxSlices <= kQT): every load is issued
   // before any is combined
-  static_assert(kQMaxSlices <= kDT, "one slice per thread");
+  static_assert(kQMaxSlices <= kQT, "one slice per thread");
   const bool have = tid < nbv;
   const int64_t slot = (int64_t)bg * q.NB + (have ? tid : 0);
   uint32_t mn = q.mm[slot * 2], mx = q.mm[slot * 2 + 1];
@@ -225,17 +229,18 @@ __global__ __launch_bounds__(kDT) void bm_init_kernel(QArgs q) {
     QState s{};
     s.lo = rmn[0];
     s.hi = rmx[0];
-    for (int w = 1; w < kDT / 64; ++w) { s.lo = min(s.lo, rmn[w]); s.hi = max(s.hi, rmx[w]); }
+    for (int w = 1; w < kQW; ++w) { s.lo = min(s.lo, rmn[w]); s.hi = max(s.hi, rmx[w]); }
     s.kcap = U > 0 ? min(keep_count_dev(U, a.R_ppm), a.k_max) : 0;
     s.done = s.kcap == 0 ? 1u : 0u;
     for (int h = 0; h < G; ++h) {
       float m = red[0][h].x, z = red[0][h].y;
-      for (int w = 1; w < kDT / 64; ++w) lse_combine(m, z, red[w][h].x, red[w][h].y);
+      for (int w = 1; w < kQW; ++w) lse_combine(m, z, red[w][h].x, red[w][h].y);
       s.m[h] = m;
       s.invz[h] = 1.f / z;
     }
-    q.st[bg] = s;  // pass 0's state
+    S = s;
   }
+  __syncthreads();
 }
 
 // After histogram pass p of a (b, g) (rows: its summed histogram in LDS,
@@ -334,10 +339,11 @@ __device__ void narrow_after(const BudgetArgs& a, QState& S, const u64* rows, in
   if (tid == 0 && gs) *gs = S;
 }
 
-// Histogram pass p over one slice, added into the (b, g)'s sums.  For p > 0
-// every block first narrows the interval from pass p - 1's sums itself (the
-// same integer steps on the same inputs in every block, so they agree);
-// slice 0 records the state in st[p].  This saves a launch per pass.
+// Histogram pass p over one slice, added into the (b, g)'s sums.  Every
+// block first derives the pass's state itself -- for p = 0 from the slice
+// partials, for p > 0 by narrowing from pass p - 1's sums -- with the same
+// steps on the same inputs in every block, so they agree; slice 0 records it
+// in st[p].  This saves a launch per pass.
 __global__ __launch_bounds__(kQT) void bm_hist_kernel(QArgs q, int p) {
   __shared__ u64 h[(1 + kQMaxG) * kQBins];
   __shared__ QState S;
@@ -347,15 +353,20 @@ __global__ __launch_bounds__(kQT) void bm_hist_kernel(QArgs q, int p) {
   const int b = gb.bg / a.d.Hkv, g = gb.bg % a.d.Hkv, G = a.d.G;
   const int U = tokens_of(a, b);
   const int s0 = gb.j * q.slice;
+  if (p + 1 < kQPasses) clear_pass_share(q, gb.bg, gb.j, p + 1);
   if (s0 >= U) return;
   const int tid = threadIdx.x;
   const int HS = (1 + G) * kQBins;
-  if (tid == 0) S = q.st[(int64_t)(p > 0 ? p - 1 : 0) * BG + gb.bg];
-  if (p > 0) {
+  if (p == 0) {
+    // every block combines the slice partials itself; slice 0 records them
+    initial_state(q, gb.bg, U, S);
+    if (gb.j == 0 && tid == 0) q.st[gb.bg] = S;
+  } else {
+    if (tid == 0) S = q.st[(int64_t)(p - 1) * BG + gb.bg];
     const u64* prev = q.hist + ((int64_t)(p - 1) * BG + gb.bg) * HS;
     for (int i = tid; i < HS; i += kQT) h[i] = prev[i];
+    __syncthreads();
   }
-  __syncthreads();
   if (p > 0) {
     QState* rec = gb.j == 0 ? q.st + (int64_t)p * BG + gb.bg : nullptr;
     if (!S.done) {
@@ -414,20 +425,18 @@ __global__ __launch_bounds__(kTT) void bm_ties_kernel(QArgs q) {
   const int BG = a.d.B * a.d.Hkv;
   const int bg = blockIdx.x, b = bg / a.d.Hkv, g = bg % a.d.Hkv, G = a.d.G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // an empty sequence stops at pass 0 (no slice block records later states)
-  if (tid == 0) {
-    S = q.st[bg];
-    found_s = 0;
-  }
-  __syncthreads();
-  if (S.kcap == 0) {
+  // an empty sequence has no slice block, so no recorded state: nothing kept
+  const int U = tokens_of(a, b);
+  if (U == 0) {
     if (tid == 0) q.kk[bg] = 0;
     return;
   }
   // the state after the last pass
   const int HS = (1 + G) * kQBins;
-  __syncthreads();
-  if (tid == 0) S = q.st[(int64_t)(kQPasses - 1) * BG + bg];
+  if (tid == 0) {
+    S = q.st[(int64_t)(kQPasses - 1) * BG + bg];
+    found_s = 0;
+  }
   const u64* last = q.hist + ((int64_t)(kQPasses - 1) * BG + bg) * HS;
   for (int i = tid; i < HS; i += kTT) rows[i] = last[i];
   __syncthreads();
@@ -440,7 +449,6 @@ __global__ __launch_bounds__(kTT) void bm_ties_kernel(QArgs q) {
     return;
   }
   // the units whose key is the interval's single value T, in id order
-  const int U = tokens_of(a, b);
   const uint32_t T = S.lo;
   const u64 target = target_of(a);
   const float* sc = a.scores + (int64_t)bg * a.U_max;
@@ -547,7 +555,6 @@ hipError_t launch_select_budget_multi(const BudgetArgs& a, void* ws, hipStream_t
     case 8: bm_norm_kernel<8><<<grid, kQT, 0, st>>>(q); break;
     default: return hipErrorInvalidValue;
   }
-  bm_init_kernel<<<BG, kDT, 0, st>>>(q);
   for (int p = 0; p < kQPasses; ++p) bm_hist_kernel<<<grid, kQT, 0, st>>>(q, p);
   bm_ties_kernel<<<BG, kTT, 0, st>>>(q);
   hipError_t e = hipGetLastError();
