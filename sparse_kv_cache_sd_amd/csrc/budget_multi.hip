@@ -1,8 +1,10 @@
 // Stage 1b with a dropped-mass budget, spread over many blocks per (sequence
-// b, KV head g): the same count as the one-block kernel (budget.hip) -- the
+// b, KV head g): the same rule as the one-block kernel (budget.hip) -- the
 // shortest prefix of the top-k order (decreasing group score, equal scores to
 // the lower id) that leaves at most max_dropped of every head's dense softmax
-// mass outside, capped at keep_count(U) -- for any number of tokens.  The
+// mass outside, capped at keep_count(U) -- for any number of tokens (the
+// softmax normalisers are summed in slice order, so their fp32 rounding can
+// differ from the one-block kernel's).  The
 // dropped mass of the discarded entries governs the error and is fixed in
 // advance ("Where Activation Sparsity and KV-Cache Sparsity Cross in LLM
 // Decoding", cards view, pre-hoc sparsity abstract).

@@ -184,7 +184,7 @@ struct BudgetArgs {
   int32_t* sel_count;    // [B][Hkv]
 };
 hipError_t launch_select_budget(const BudgetArgs& a, hipStream_t st);
-// The same count and list spread over many blocks per (b, g): any U_max
+// The same rule spread over many blocks per (b, g): any U_max
 // (<= max_seq), G <= 8; scratch of budget_multi_workspace_bytes(d, U_max)
 // bytes (contents need not be set).
 size_t budget_multi_workspace_bytes(const Dims& d, int U_max);
