@@ -4,14 +4,15 @@
 // the lower id) that leaves at most max_dropped of every head's dense softmax
 // mass outside, capped at keep_count(U) -- for any number of tokens (the
 // softmax normalisers are summed in slice order, so their fp32 rounding can
-// differ from the one-block kernel's).  The
-// dropped mass of the discarded entries governs the error and is fixed in
-// advance ("Where Activation Sparsity and KV-Cache Sparsity Cross in LLM
-// Decoding", cards view, pre-hoc sparsity abstract).
+// differ from the one-block kernel's).  The dropped mass of the discarded
+// entries governs the error and is fixed in advance ("Where Activation
+// Sparsity and KV-Cache Sparsity Cross in LLM Decoding", cards view, pre-hoc
+// sparsity abstract).
 //
 // A (b, g) is cut into NB <= kQMaxSlices slices of whole 2048-token chunks.
-// Every block of one (b, g) sits on one XCD (block id bg + B*Hkv*slice), so
-// the partials exchanged below stay in its L2.
+// Block ids are bg + B*Hkv*slice: when B*Hkv is a multiple of the eight XCDs,
+// every block of one (b, g) sits on one XCD and the partials exchanged below
+// stay in its L2 (any other count is correct, only less local).
 //   bm_norm    per slice: each head's largest logit and the sum of the
 //              exponentials below it; the min / max order key of the group
 //              scores; clears pass 0's histogram;
