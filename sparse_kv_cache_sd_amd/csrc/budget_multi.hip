@@ -9,7 +9,8 @@
 // Sparsity and KV-Cache Sparsity Cross in LLM Decoding", cards view, pre-hoc
 // sparsity abstract).
 //
-// A (b, g) is cut into NB <= kQMaxSlices slices of whole 2048-token chunks.
+// A (b, g) is cut into NB <= kQMaxSlices slices of whole 1024-token chunks
+// (more, smaller slices measured slower at 128K, fewer larger ones at 32K).
 // Block ids are bg + B*Hkv*slice: when B*Hkv is a multiple of the eight XCDs,
 // every block of one (b, g) sits on one XCD and the partials exchanged below
 // stay in its L2 (any other count is correct, only less local).
@@ -39,8 +40,8 @@ namespace {
 
 constexpr int kQT = 256;                 // threads of a slice block
 constexpr int kQW = kQT / 64;
-constexpr int kQK = 8;                   // tokens per thread per chunk
-constexpr int kQChunk = kQT * kQK;       // 2048 tokens
+constexpr int kQK = 4;                   // tokens per thread per chunk
+constexpr int kQChunk = kQT * kQK;       // 1024 tokens
 constexpr int kQMaxSlices = 64;          // slices per (b, g)
 constexpr int kQBins = 256;
 constexpr int kQMaxG = 8;
