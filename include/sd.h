@@ -245,7 +245,7 @@ SD_API sd_status sd_decode_step(const sd_shape* shape, const void* q, const void
  *                           ([Cross/cards] pre-hoc sparsity abstract: the
  *                           dropped mass controlled in advance).  Needs the
  *                           token logits; any number of tokens (one block per
- *                           (b, g) up to 16384, many past that: the same rule,
+ *                           (b, g) up to 8192, many past that: the same rule,
  *                           with the fp32 softmax normalisers summed in another
  *                           order).  The masses are summed as 2^-40
  *                           fixed-point integers of the fp32 softmax weights;

@@ -199,8 +199,8 @@ size_t select_ws_bytes(const sdkv::Dims& d, int unit) {
 // The budget runs in one block per (b, g) up to kBudgetOneMax tokens, past
 // that over many blocks (with the many-block top-k's scratch inside its own):
 // the one-block kernel's time grows with the tokens, the many-block one's is
-// mostly its launches, and the two meet near 16K tokens.
-constexpr int kBudgetOneMax = 16384;
+// mostly its launches, and the two meet near 8K tokens.
+constexpr int kBudgetOneMax = 8192;
 
 bool budget_multi(const sdkv::Dims& d, int unit, const Sel& s) {
   return s.kind == SD_SEL_MASS_BUDGET && units_max(d, unit) > kBudgetOneMax;

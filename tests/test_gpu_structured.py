@@ -264,9 +264,9 @@ BUDGET_CASES = [
                                   num_kv_heads=2), [0.1]),
     ("sweep-32k", R["sweep"].with_(seq_len=32768, num_q_heads=8, num_kv_heads=2), [0.1]),
     # the switch between one and many blocks per (b, g)
-    ("sweep-16384", R["sweep"].with_(seq_len=16384, num_q_heads=8, num_kv_heads=2), [0.1]),
-    ("sweep-16385", R["sweep"].with_(seq_len=16385, num_q_heads=8, num_kv_heads=2), [0.1]),
-    # past 16384 tokens the budget runs over many blocks per (b, g): 20
+    ("sweep-8192", R["sweep"].with_(seq_len=8192, num_q_heads=8, num_kv_heads=2), [0.1]),
+    ("sweep-8193", R["sweep"].with_(seq_len=8193, num_q_heads=8, num_kv_heads=2), [0.1]),
+    # past 8192 tokens the budget runs over many blocks per (b, g): 40
     # slices with a ragged last one, and a ragged G = 8 batch
     ("sweep-40k", R["sweep"].with_(seq_len=40000, num_q_heads=8, num_kv_heads=2), [0.05, 0.3]),
     ("g8-ragged-70k", R["l70b"].with_(batch=3, seq_len=70000, seq_len_min=1, num_q_heads=16,
