@@ -336,12 +336,17 @@ __global__ __launch_bounds__(kTauThreads) void entmax_chunk_kernel(TauArgs a) {
 
 // One block per head after entmax_chunk_kernel: the head's max over the
 // chunks, its candidates gathered from the chunks' lists in chunk order,
-// then the Newton steps (one wave), or the block-wide fallback.
+// then the Newton steps (one wave), or the block-wide fallback.  Thread c
+// reads chunk c's max and count (one round trip for all chunks; nch <=
+// kTauThreads); the lists are then read as one concatenated list, in rounds
+// of kTauThreads entries.
 __global__ __launch_bounds__(kTauThreads) void entmax_merge_kernel(TauArgs a) {
   constexpr int NT = kTauThreads, NW = NT / 64;
   __shared__ float s_c[kTauCap];
   __shared__ float s_red[2][2][NW];
+  __shared__ float s_max[NW];
   __shared__ int s_cnt[NW];
+  __shared__ int s_off[NT + 1];  // chunk c's entries start at s_off[c]
   const Dims& d = a.d;
   const GroupBlock gb = group_block(d.B * d.Hkv);
   const int g = gb.bg % d.Hkv, b = gb.bg / d.Hkv, h = g * d.G + gb.j;
@@ -351,12 +356,11 @@ __global__ __launch_bounds__(kTauThreads) void entmax_merge_kernel(TauArgs a) {
   const int64_t h0 = ((int64_t)b * d.Hq + h) * a.nch;
   const int nch = min(a.nch, (sl.slots + kTauChunk - 1) / kTauChunk);
 
-  float mx = -INFINITY;
-  bool over = false;
-  for (int c = 0; c < nch; ++c) {
-    mx = fmaxf(mx, a.cmax[h0 + c]);
-    over |= a.ccnt[h0 + c] > kTauChunkCap;
-  }
+  const bool mine = tid < nch;
+  const float cm = mine ? a.cmax[h0 + tid] : -INFINITY;
+  const int cc = mine ? a.ccnt[h0 + tid] : 0;
+  const bool over = __syncthreads_or(cc > kTauChunkCap);
+  const float mx = block_max<NW>(cm, s_max);
   float* out = a.tau + (int64_t)b * d.Hq + h;
   if (mx == -INFINITY) {  // nothing attended: every weight is 0
     if (tid == 0) *out = INFINITY;
@@ -364,16 +368,37 @@ __global__ __launch_bounds__(kTauThreads) void entmax_merge_kernel(TauArgs a) {
   }
   const float lo = nw.am1 * mx - 1.f;
   float tau = lo;
-  // Gather the candidates: chunk by chunk, kTauThreads entries at a time,
-  // kept in order by block-wide ballot prefix offsets.
-  const uint64_t below = (1ull << lane) - 1ull;
-  int total = 0;
-  for (int c = 0; c < nch && !over; ++c) {
-    const int cc = a.ccnt[h0 + c];
-    const float* src = a.cand + (h0 + c) * kTauChunkCap;
-    for (int e0 = 0; e0 < cc; e0 += NT) {
+  bool full = over;
+  if (!over) {
+    // exclusive prefix of the chunk counts, in chunk order
+    const int incl = wave_incl_scan<int>(cc);
+    if (lane == 63) s_cnt[wave] = incl;
+    __syncthreads();
+    int wbase = 0, raw = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      wbase += w < wave ? s_cnt[w] : 0;
+      raw += s_cnt[w];
+    }
+    if (mine) s_off[tid] = wbase + incl - cc;
+    if (tid == 0) s_off[nch] = raw;
+    __syncthreads();  // s_cnt is rewritten below
+    // the candidates of the head's max, kept in order by block-wide ballot
+    // prefix offsets
+    const uint64_t below = (1ull << lane) - 1ull;
+    int total = 0;
+    for (int e0 = 0; e0 < raw; e0 += NT) {
       const int e = e0 + tid;
-      const float z = e < cc ? src[e] : -INFINITY;
+      float z = -INFINITY;
+      if (e < raw) {
+        int lo_c = 0, hi_c = nch - 1;  // the chunk holding entry e
+        while (lo_c < hi_c) {
+          const int mid = (lo_c + hi_c + 1) >> 1;
+          if (s_off[mid] <= e) lo_c = mid;
+          else hi_c = mid - 1;
+        }
+        z = a.cand[(h0 + lo_c) * kTauChunkCap + (e - s_off[lo_c])];
+      }
       const bool cnd = nw.cand(z, lo);
       const uint64_t m = __ballot(cnd);
       if (lane == 0) s_cnt[wave] = __popcll(m);
@@ -389,14 +414,15 @@ __global__ __launch_bounds__(kTauThreads) void entmax_merge_kernel(TauArgs a) {
       total += add;
       __syncthreads();  // s_cnt is rewritten next round
     }
-    over = total > kTauCap;
+    full = total > kTauCap;
+    if (!full) {
+      if (wave != 0) return;
+      tau = newton_wave(nw, s_c, total, tau);
+      if (tid == 0) *out = tau;
+      return;
+    }
   }
-  if (!over) {
-    if (wave != 0) return;
-    tau = newton_wave(nw, s_c, total, tau);
-  } else {
-    tau = newton_block<NW>(nw, sl, tau, s_red);
-  }
+  tau = newton_block<NW>(nw, sl, tau, s_red);
   if (tid == 0) *out = tau;
 }
 
@@ -406,6 +432,7 @@ hipError_t launch_entmax_tau(const TauArgs& a, hipStream_t st) {
   if (a.sel_idx && (a.k_max < 1 || !a.sel_count)) return hipErrorInvalidValue;
   if (d.P != 16 && d.P != 64) return hipErrorInvalidValue;
   if (a.nch < 0 || (a.nch > 0 && (!a.cand || !a.cmax || !a.ccnt))) return hipErrorInvalidValue;
+  if (a.nch > kTauThreads) return hipErrorInvalidValue;  // one chunk per merge thread
   if (a.nch == 0) {
     entmax_tau_kernel<<<dim3(d.B * d.Hq), kTauThreads, 0, st>>>(a);
   } else {
