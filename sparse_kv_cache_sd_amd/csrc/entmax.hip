@@ -164,12 +164,36 @@ __device__ __forceinline__ float block_max(float v, float* s_max) {
   return v;
 }
 
-// Newton steps by one wave over n values at s_c; returns tau.
-__device__ __forceinline__ float newton_wave(const Newton& nw, const float* s_c, int n, float tau) {
+// Newton steps by one wave over n values at s_c; returns tau.  Lane l owns
+// the values s_c[l + 64 k] and sums them in k order.  tau only grows, so a
+// value whose weight is zero at one step is zero at every later one: each
+// step keeps, in order and in place, only the lane's values still positive,
+// and later steps read fewer.  Dropped values add exactly 0 to both sums, so
+// the sums (and tau) are those of the full list.  The LDS reads of eight
+// values are issued together.  s_c is overwritten.
+__device__ __forceinline__ float newton_wave(const Newton& nw, float* s_c, int n, float tau) {
+  constexpr int R = 8;
   const int lane = threadIdx.x & 63;
+  int m = lane < n ? (n - 1 - lane) / 64 + 1 : 0;  // this lane's values
   for (int it = 0; it < 64; ++it) {
     float s0 = 0.f, s1 = 0.f;
-    for (int j = lane; j < n; j += 64) nw.accum(s_c[j], tau, s0, s1);
+    int keep = 0, k = 0;
+    for (; k + R <= m; k += R) {
+      float z[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) z[r] = s_c[lane + 64 * (k + r)];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        nw.accum(z[r], tau, s0, s1);
+        if (fmaf(nw.am1, z[r], -tau) > 0.f) s_c[lane + 64 * keep++] = z[r];
+      }
+    }
+    for (; k < m; ++k) {
+      const float z = s_c[lane + 64 * k];
+      nw.accum(z, tau, s0, s1);
+      if (fmaf(nw.am1, z, -tau) > 0.f) s_c[lane + 64 * keep++] = z;
+    }
+    m = keep;
     s0 = wave_sum_dpp(s0);
     s1 = wave_sum_dpp(s1);
     if (!nw.step(s0, s1, tau)) break;
