@@ -378,7 +378,10 @@ __global__ __launch_bounds__(kTauThreads) void entmax_merge_kernel(TauArgs a) {
   const Slots sl(a, b, gb.bg, h);
   const Newton nw(a);
   const int64_t h0 = ((int64_t)b * d.Hq + h) * a.nch;
-  const int nch = min(a.nch, (sl.slots + kTauChunk - 1) / kTauChunk);
+  // every allocated chunk: entmax_chunk_kernel writes max -inf and count 0
+  // for the chunks past the kept slots, so the reads need not wait for the
+  // list's count
+  const int nch = a.nch;
 
   const bool mine = tid < nch;
   const float cm = mine ? a.cmax[h0 + tid] : -INFINITY;
