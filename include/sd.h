@@ -360,7 +360,8 @@ SD_API sd_status sd_decode_step_sel(const sd_shape* shape, const void* q, const 
  * in fp32, on (sum max(x - tau, 0)^(1/(alpha-1)))^(alpha-1) - 1 from
  * tau = max x - 1, which climb monotonically to the root (one block per
  * head, or past 16384 kept tokens a block per 16384 of them and a merge
- * block); split-K attention with these weights over the stored logits
+ * block; at most 1024 such blocks, 16777216 kept tokens per head:
+ * SD_E_UNSUPPORTED beyond); split-K attention with these weights over the stored logits
  * (reads V), merged as sum_j a_j / sum_j l_j, which also removes the
  * residual of tau's rounding.  Launches use the caller's workspace only.
  *   page_stats  as page_bounds of sd_decode_step_sel (the page bounds, or

@@ -712,6 +712,15 @@ sd_status check_alpha(double alpha) {
   return SD_OK;
 }
 
+// The thresholds take at most kTauMaxChunks chunks of kTauChunk kept slots
+// per head.
+sd_status check_entmax_size(const EntLayout& E) {
+  if (E.nch > sdkv::kTauMaxChunks)
+    return fail(SD_E_UNSUPPORTED, "alpha-entmax takes at most %lld kept slots per head",
+                static_cast<long long>(sdkv::kTauMaxChunks) * sdkv::kTauChunk);
+  return SD_OK;
+}
+
 // Shared checks of the attention entry points.
 sd_status check_attend_args(const sdkv::Dims& d, int32_t unit, const void* q, const void* k_pages,
                             const void* v_pages, const int32_t* block_table,
@@ -1046,7 +1055,9 @@ sd_status sd_workspace_bytes_entmax(const sd_shape* shape, int32_t unit,
   if ((st = check_unit(unit)) != SD_OK) return st;
   if ((st = check_selection(sel, &v)) != SD_OK) return st;
   if (!bytes_host) return fail(SD_E_NULL, "bytes_host is NULL");
-  *bytes_host = ent_layout(d, unit, v).total;
+  const EntLayout E = ent_layout(d, unit, v);
+  if ((st = check_entmax_size(E)) != SD_OK) return st;
+  *bytes_host = E.total;
   return ok();
 }
 
@@ -1070,7 +1081,9 @@ sd_status sd_decode_step_entmax(const sd_shape* shape, const void* q, const void
     return fail(SD_E_NULL, "page unit selection reads page_stats");
   if ((sel_idx == nullptr) != (sel_count == nullptr))
     return fail(SD_E_NULL, "sel_idx and sel_count are given together or not at all");
-  if ((st = check_ws(ws, ws_bytes, ent_layout(d, unit, v).total)) != SD_OK) return st;
+  const EntLayout E = ent_layout(d, unit, v);
+  if ((st = check_entmax_size(E)) != SD_OK) return st;
+  if ((st = check_ws(ws, ws_bytes, E.total)) != SD_OK) return st;
   if ((st = entmax_impl(d, q, k_pages, v_pages, page_stats, block_table, seq_lens, unit, v, alpha,
                         out, tau, sel_idx, sel_count, ws, static_cast<hipStream_t>(stream))) !=
       SD_OK)

@@ -41,6 +41,7 @@ namespace sdkv {
 constexpr int kTauThreads = 1024;
 constexpr int kTauKeys = kTauChunk / kTauThreads;  // logits per thread in registers
 constexpr int kTauCap = 12288;   // candidates compacted into LDS (48 KB)
+static_assert(kTauMaxChunks <= kTauThreads, "the merge reads a chunk per thread");
 constexpr int kTauBatch = 8;     // rounds whose loads are issued together
 static_assert(kTauKeys * kTauThreads == kTauChunk, "a chunk fills the registers");
 
@@ -362,7 +363,7 @@ __global__ __launch_bounds__(kTauThreads) void entmax_chunk_kernel(TauArgs a) {
 // chunks, its candidates gathered from the chunks' lists in chunk order,
 // then the Newton steps (one wave), or the block-wide fallback.  Thread c
 // reads chunk c's max and count (one round trip for all chunks; nch <=
-// kTauThreads); the lists are then read as one concatenated list, in rounds
+// kTauMaxChunks); the lists are then read as one concatenated list, in rounds
 // of kTauThreads entries.
 __global__ __launch_bounds__(kTauThreads) void entmax_merge_kernel(TauArgs a) {
   constexpr int NT = kTauThreads, NW = NT / 64;
@@ -370,7 +371,7 @@ __global__ __launch_bounds__(kTauThreads) void entmax_merge_kernel(TauArgs a) {
   __shared__ float s_red[2][2][NW];
   __shared__ float s_max[NW];
   __shared__ int s_cnt[NW];
-  __shared__ int s_off[NT + 1];  // chunk c's entries start at s_off[c]
+  __shared__ int s_off[kTauMaxChunks + 1];  // chunk c's entries start at s_off[c]
   const Dims& d = a.d;
   const GroupBlock gb = group_block(d.B * d.Hkv);
   const int g = gb.bg % d.Hkv, b = gb.bg / d.Hkv, h = g * d.G + gb.j;
@@ -459,7 +460,7 @@ hipError_t launch_entmax_tau(const TauArgs& a, hipStream_t st) {
   if (a.sel_idx && (a.k_max < 1 || !a.sel_count)) return hipErrorInvalidValue;
   if (d.P != 16 && d.P != 64) return hipErrorInvalidValue;
   if (a.nch < 0 || (a.nch > 0 && (!a.cand || !a.cmax || !a.ccnt))) return hipErrorInvalidValue;
-  if (a.nch > kTauThreads) return hipErrorInvalidValue;  // one chunk per merge thread
+  if (a.nch > kTauMaxChunks) return hipErrorInvalidValue;  // one chunk per merge thread
   if (a.nch == 0) {
     entmax_tau_kernel<<<dim3(d.B * d.Hq), kTauThreads, 0, st>>>(a);
   } else {

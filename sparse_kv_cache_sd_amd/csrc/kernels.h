@@ -125,6 +125,7 @@ struct TauArgs {
 };
 constexpr int kTauChunk = 16384;     // kept slots per threshold block
 constexpr int kTauChunkCap = 2048;   // candidates a chunk hands on
+constexpr int kTauMaxChunks = 1024;  // chunks per head (one per merge thread)
 hipError_t launch_entmax_tau(const TauArgs& a, hipStream_t st);
 
 // Dropped mass of the dense softmax (token unit), one block per (sequence,

@@ -134,6 +134,19 @@ def test_budget_workspace_past_one_block(n):
         assert bud >= top + hist
 
 
+def test_entmax_kept_slots_limit():
+    # the thresholds take at most 1024 chunks of 16384 kept slots per head
+    def shp(n):
+        return sd.Shape(batch=1, num_q_heads=8, num_kv_heads=8, head_dim=64, page_size=64,
+                        max_pages_per_seq=n // 64 + 1, max_seq_len=n, dtype="bf16",
+                        num_pages=n // 64 + 1)
+    dense = sd.Selection("topk", 1.0)
+    assert sd.workspace_bytes_entmax(shp(1024 * 16384), "token", dense) > 0
+    with pytest.raises(sd.SdError) as e:
+        sd.workspace_bytes_entmax(shp(1024 * 16384 + 1), "token", dense)
+    assert "UNSUPPORTED" in str(e.value)
+
+
 def test_entmax_workspace_holds_logits_and_thresholds():
     s = _shape()
     for unit in ("page", "token"):
