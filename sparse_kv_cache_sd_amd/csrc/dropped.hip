@@ -15,7 +15,10 @@
 // of the head's KV head becomes a bitmap in LDS (bits set with LDS atomic
 // OR, which gives the same bitmap in any order); the logits are read twice
 // (max, then the two sums), eight rounds of loads issued together; every
-// sum runs in a fixed order, so delta does not depend on timing.
+// sum runs in a fixed order, so delta does not depend on timing.  One block
+// per head keeps few bytes in flight per CU, so where the rows are 16-byte
+// aligned (max_seq % 4 == 0) a thread reads four consecutive tokens per
+// load: they share a page (P is 16 or 64) and a bitmap word.
 #include "device.h"
 
 namespace sdkv {
@@ -34,6 +37,7 @@ __device__ __forceinline__ float drop_wave_max(float x) {
   return max_xor32(x);
 }
 
+template <int V>  // tokens per load: 4 (aligned rows) or 1
 __global__ __launch_bounds__(kDropThreads) void dropped_mass_kernel(DropArgs a) {
   constexpr int NT = kDropThreads, NW = NT / 64;
   __shared__ uint32_t s_kept[kMaxDropSeq / 32];
@@ -57,23 +61,30 @@ __global__ __launch_bounds__(kDropThreads) void dropped_mass_kernel(DropArgs a) 
   __syncthreads();
   const float* row = a.logits + ((int64_t)b * d.Hq + h) * d.max_seq;
   const int32_t* bt = a.block_table + (int64_t)b * d.max_pages;
-  // logit of token t, -inf where not attended; loads issued unconditionally
-  // with clamped indices (a branch around them would drain each round)
-  auto logit = [&](int t) -> float {
-    const int tc = min(t, max(n - 1, 0));
+  // logits of tokens t .. t + V - 1 (t a multiple of V), -inf where not
+  // attended; loads issued unconditionally with clamped indices (a branch
+  // around them would drain each round)
+  typedef float vec_t __attribute__((ext_vector_type(V)));
+  auto logits_at = [&](int t) -> vec_t {
+    const int tc = min(t, max(((n - 1) / V) * V, 0));
     const int ph = bt[min(tc / d.P, d.max_pages - 1)];
-    const float z = row[tc];
-    const bool ok = (t < n) & (ph >= 0) & ((int64_t)ph < d.num_pages);
-    return ok ? z : -INFINITY;
+    const vec_t z = *reinterpret_cast<const vec_t*>(row + tc);
+    const bool pg = (ph >= 0) & ((int64_t)ph < d.num_pages);
+    vec_t out;
+#pragma unroll
+    for (int i = 0; i < V; ++i) out[i] = (pg & (t + i < n)) ? z[i] : -INFINITY;
+    return out;
   };
-  const int rounds = (n + NT - 1) / NT;
+  const int rounds = (n + NT * V - 1) / (NT * V);
   auto for_tokens = [&](auto&& fn) {
     for (int k0 = 0; k0 < rounds; k0 += kDropBatch) {
-      float zz[kDropBatch];
+      vec_t zz[kDropBatch];
 #pragma unroll
-      for (int r = 0; r < kDropBatch; ++r) zz[r] = logit((k0 + r) * NT + tid);
+      for (int r = 0; r < kDropBatch; ++r) zz[r] = logits_at(((k0 + r) * NT + tid) * V);
 #pragma unroll
-      for (int r = 0; r < kDropBatch; ++r) fn((k0 + r) * NT + tid, zz[r]);
+      for (int r = 0; r < kDropBatch; ++r)
+#pragma unroll
+        for (int i = 0; i < V; ++i) fn(((k0 + r) * NT + tid) * V + i, zz[r][i]);
     }
   };
   float m = -INFINITY;
@@ -110,7 +121,10 @@ __global__ __launch_bounds__(kDropThreads) void dropped_mass_kernel(DropArgs a) 
 hipError_t launch_dropped_mass(const DropArgs& a, hipStream_t st) {
   const Dims& d = a.d;
   if (d.max_seq > kMaxDropSeq || a.k_max < 1) return hipErrorInvalidValue;
-  dropped_mass_kernel<<<dim3(d.B * d.Hq), kDropThreads, 0, st>>>(a);
+  if ((d.max_seq & 3) == 0)
+    dropped_mass_kernel<4><<<dim3(d.B * d.Hq), kDropThreads, 0, st>>>(a);
+  else
+    dropped_mass_kernel<1><<<dim3(d.B * d.Hq), kDropThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -71,6 +71,8 @@ def _compare(dev, delta, idx, cnt):
 CASES = [
     ("tiny", R["tiny"], 0.25),
     ("sweep-5k", R["sweep"].with_(seq_len=5000, num_q_heads=16, num_kv_heads=4), 0.2),
+    # rows of a length not a multiple of 4: the one-token-per-load path
+    ("sweep-5001", R["sweep"].with_(seq_len=5001, num_q_heads=16, num_kv_heads=4), 0.2),
     ("g8-ragged", R["l70b"].with_(batch=3, seq_len=4000, seq_len_min=1, num_q_heads=16,
                                   num_kv_heads=2), 0.1),
     ("sweep-128k", kvsynth.sweep_recipe(128 * kvsynth.KTOK, 0.3), 0.3),
