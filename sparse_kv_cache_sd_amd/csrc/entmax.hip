@@ -170,29 +170,27 @@ __device__ __forceinline__ float block_max(float v, float* s_max) {
 // value whose weight is zero at one step is zero at every later one: each
 // step keeps, in order and in place, only the lane's values still positive,
 // and later steps read fewer.  Dropped values add exactly 0 to both sums, so
-// the sums (and tau) are those of the full list.  The LDS reads of eight
-// values are issued together.  s_c is overwritten.
+// the sums (and tau) are those of the full list.  The LDS reads go in
+// batches of eight, issued together.  s_c is overwritten.
 __device__ __forceinline__ float newton_wave(const Newton& nw, float* s_c, int n, float tau) {
   constexpr int R = 8;
   const int lane = threadIdx.x & 63;
   int m = lane < n ? (n - 1 - lane) / 64 + 1 : 0;  // this lane's values
   for (int it = 0; it < 64; ++it) {
     float s0 = 0.f, s1 = 0.f;
-    int keep = 0, k = 0;
-    for (; k + R <= m; k += R) {
+    int keep = 0;
+    for (int k = 0; k < m; k += R) {
+      // all R reads first (indices clamped to the lane's last value), then
+      // the values in order; writes land at or below the values read
       float z[R];
 #pragma unroll
-      for (int r = 0; r < R; ++r) z[r] = s_c[lane + 64 * (k + r)];
+      for (int r = 0; r < R; ++r) z[r] = s_c[lane + 64 * min(k + r, m - 1)];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
+        if (k + r >= m) break;
         nw.accum(z[r], tau, s0, s1);
         if (fmaf(nw.am1, z[r], -tau) > 0.f) s_c[lane + 64 * keep++] = z[r];
       }
-    }
-    for (; k < m; ++k) {
-      const float z = s_c[lane + 64 * k];
-      nw.accum(z, tau, s0, s1);
-      if (fmaf(nw.am1, z, -tau) > 0.f) s_c[lane + 64 * keep++] = z;
     }
     m = keep;
     s0 = wave_sum_dpp(s0);
