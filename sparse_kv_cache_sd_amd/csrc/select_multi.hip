@@ -293,12 +293,13 @@ __global__ __launch_bounds__(kMT) void msel_place_kernel(MArgs a) {
     above_before = 0u;
     equal_before = (uint32_t)s0;
   } else {
+    // keys above hi_L in the slices before this one (loaded before the
+    // narrowing so that the two reads overlap)
+    uint32_t ov = 0u;
+    for (int j = tid; j < blk; j += kMT) ov += a.over[(L * BG + bg) * a.NB + j];
     uint32_t ab, inb;
     narrow(a, sm, bg, L, prev, blk, &ab, &inb);
     S = sm.S;
-    // keys above hi_L in the slices before this one
-    uint32_t ov = 0u;
-    for (int j = tid; j < blk; j += kMT) ov += a.over[(L * BG + bg) * a.NB + j];
     uint32_t unused = 0u;
     block_sum2(sm, ov, unused);
     above_before = ov + ab + (S.whole ? inb : 0u);
