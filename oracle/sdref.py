@@ -119,6 +119,41 @@ def attention(s: np.ndarray, V: np.ndarray, tokens: np.ndarray | None = None):
     return (w @ V) / Z, m + math.log(Z)
 
 
+def split_partial(s: np.ndarray, V: np.ndarray, tokens: np.ndarray):
+    """One split of split-K attention ([Cross/list] Abstract: dense and sparse
+    decoding through one split-K kernel): the attention of one query head
+    over the split's own ``tokens`` alone, as (o_j [d], lse_j).  An empty
+    split is (0, -inf), which weighs nothing in the merge."""
+    tokens = np.asarray(tokens, dtype=np.int64)
+    if tokens.size == 0:
+        return np.zeros(np.asarray(V).shape[1]), -math.inf
+    return attention(s, V, tokens)
+
+
+def merge_splits(parts):
+    """Log-sum-exp merge of split partials [(o_j, lse_j), ...] in fp64:
+    M = max_j lse_j, w_j = exp(lse_j - M), o = sum_j w_j o_j / sum_j w_j,
+    lse = M + log sum_j w_j.  Splits with lse_j = -inf contribute nothing;
+    if every split is empty the result is (0, -inf), an empty sequence."""
+    lses = np.array([p[1] for p in parts], dtype=np.float64)
+    os_ = np.array([p[0] for p in parts], dtype=np.float64)
+    if lses.size == 0 or not np.any(np.isfinite(lses)):
+        return np.zeros(os_.shape[1] if os_.ndim == 2 else 0), -math.inf
+    M = lses.max()
+    w = np.exp(lses - M)
+    Z = w.sum()
+    return (w @ os_) / Z, M + math.log(Z)
+
+
+def split_attention(s: np.ndarray, V: np.ndarray, splits):
+    """Split-K attention of one head: ``splits`` is a list of token-index
+    arrays (any partition of the attended tokens, empty parts allowed); each
+    is attended alone (``split_partial``) and the partials are merged
+    (``merge_splits``).  The partition is free: the result equals one-shot
+    attention over the union up to rounding."""
+    return merge_splits([split_partial(s, V, t) for t in splits])
+
+
 def dropped_mass(s: np.ndarray, tokens: np.ndarray) -> float:
     """Step 7: delta = sum of the dense softmax weights of the positions NOT in
     ``tokens`` ([Cross/cards], pre-hoc sparsity abstract), summed directly over

@@ -94,6 +94,69 @@ def test_attention_subset_matches_attention_on_sliced_arrays():
     assert l1 == l2
 
 
+# ---------------------------------------------------------------- split-K merge
+
+def test_merge_worked_example():
+    """Two one-token splits, s = (0, ln 3), V = (4, 0): the dense weights are
+    1/4 and 3/4, so o = 1 and lse = ln 4 (by hand).  A merge that averaged the
+    split outputs without their exp(lse) weights would give 2."""
+    V = np.array([[4.0], [0.0]])
+    s = np.array([0.0, math.log(3.0)])
+    o, lse = sdref.split_attention(s, V, [np.array([0]), np.array([1])])
+    np.testing.assert_allclose(o, [1.0], rtol=0, atol=1e-15)
+    assert abs(lse - math.log(4.0)) < 1e-15
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_merge_partition_invariance_with_empty_splits(seed):
+    """Any partition of the attended tokens into splits, empty ones included
+    and in any order, merges to the one-shot attention over their union
+    (to fp64 rounding: 1e-13)."""
+    rng = np.random.default_rng(100 + seed)
+    n, d = int(rng.integers(1, 400)), 16
+    s = rng.standard_normal(n) * 4.0
+    V = rng.standard_normal((n, d))
+    tokens = np.sort(rng.choice(n, size=int(rng.integers(1, n + 1)), replace=False))
+    o1, l1 = sdref.attention(s, V, tokens)
+    for _ in range(5):
+        S = int(rng.integers(1, 40))
+        owner = rng.integers(0, S, size=tokens.size)          # random split of each token
+        splits = [tokens[owner == j] for j in range(S)]       # many are empty when S > |T|
+        splits += [np.array([], dtype=np.int64)] * int(rng.integers(0, 3))
+        rng.shuffle(splits)
+        o2, l2 = sdref.split_attention(s, V, splits)
+        np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-13)
+        assert abs(l2 - l1) < 1e-13
+
+
+def test_merge_contiguous_splits_of_the_dense_row():
+    """Contiguous equal splits, as a split-K kernel cuts a kept list, with a
+    trailing empty split: the dense result."""
+    rng = np.random.default_rng(7)
+    n = 1000
+    s = rng.standard_normal(n) * 3.0
+    V = rng.standard_normal((n, 8))
+    E = 96
+    splits = [np.arange(j * E, min((j + 1) * E, n)) for j in range(-(-n // E) + 1)]
+    assert splits[-1].size == 0
+    o, lse = sdref.split_attention(s, V, splits)
+    o1, l1 = sdref.attention(s, V)
+    np.testing.assert_allclose(o, o1, rtol=0, atol=1e-13)
+    assert abs(lse - l1) < 1e-13
+
+
+def test_merge_empty_and_single_split():
+    V = np.arange(6.0).reshape(3, 2)
+    s = np.array([0.5, -1.0, 2.0])
+    o, lse = sdref.merge_splits([sdref.split_partial(s, V, [])] * 3)
+    np.testing.assert_array_equal(o, [0.0, 0.0])
+    assert lse == -math.inf
+    only = sdref.split_partial(s, V, [0, 2])
+    o, lse = sdref.merge_splits([sdref.split_partial(s, V, []), only, sdref.split_partial(s, V, [])])
+    np.testing.assert_array_equal(o, only[0])
+    assert lse == only[1]
+
+
 # ---------------------------------------------------------------- dropped mass
 
 def test_dropped_mass_worked_example():
