@@ -116,18 +116,43 @@ typedef struct sd_shape {
 SD_API int32_t sd_keep_count(double r_kv, int32_t num_units);
 
 /* Workspace bytes that suffice for every call below made with this shape,
- * unit and r_KV (sd_decode_step included).  Host only; needs no GPU. */
+ * unit and r_KV (sd_decode_step included), on the current device: the split
+ * plan follows its compute-unit count (on a host with no GPU, 256, an
+ * MI355X's).  Host only; enqueues nothing. */
 SD_API sd_status sd_workspace_bytes(const sd_shape* shape, int32_t unit, double r_kv, size_t* bytes_host);
 
-/* Setup step, not part of the decode step: for every sequence b and logical
- * page u < ceil(n_b / P), the channel-wise min and max of the keys of page
- * block_table[b][u] over the page's VALID tokens only, written to
- * page_bounds[b][g][u].  These are the light per-page statistics of
- * [Cross/cards] (EntmaxKV abstract).  Kept in logical order so that scoring
- * needs no block-table lookup. */
+/* Setup step, not part of the decode step: the channel-wise min and max of
+ * the keys of logical page u of sequence b (physical page
+ * block_table[b][u]) over the page's VALID tokens only, written to
+ * page_bounds[b][g][u] for every KV head g.  These are the light per-page
+ * statistics of [Cross/cards] (EntmaxKV abstract), known before any page is
+ * loaded.  Kept in logical order so that scoring needs no block-table lookup.
+ *   pages == NULL: every page u < ceil(n_b / P) of every sequence.
+ *   pages != NULL: only the n_pages listed (sequence, logical page) pairs
+ *     (device int32 [n_pages][2]); pairs outside the batch or past a
+ *     sequence's last page are skipped; n_pages = 0 enqueues nothing;
+ *     SD_E_SHAPE if n_pages < 0.  A decode loop passes the pages its new
+ *     tokens landed in.
+ * A page whose block-table entry is outside [0, num_pages) is left as is. */
 SD_API sd_status sd_update_page_bounds(const sd_shape* shape, const void* k_pages,
                                 const int32_t* block_table, const int32_t* seq_lens,
-                                void* page_bounds, void* stream);
+                                const int32_t* pages, int32_t n_pages, void* page_bounds,
+                                void* stream);
+
+/* The per-token form of sd_update_page_bounds, O(d) per appended token and
+ * KV head: sequence b gained the tokens n_b - a_b .. n_b - 1 since its
+ * bounds were last current (seq_lens already counts them; a_b =
+ * appended[b], device int32 [B], clamped to [0, min(n_b, max_appended)]).
+ * Each such token is folded into its page's bounds (min with the stored
+ * minima, max with the stored maxima); a page that an appended token opens
+ * (its row 0 is appended) starts from that token.  The result equals a full
+ * sd_update_page_bounds bit for bit, provided the bounds of the rows before
+ * the first appended one were current.  max_appended (host) bounds every
+ * a_b: SD_E_SHAPE outside [1, max_seq_len]. */
+SD_API sd_status sd_append_page_bounds(const sd_shape* shape, const void* k_pages,
+                                       const int32_t* block_table, const int32_t* seq_lens,
+                                       const int32_t* appended, int32_t max_appended,
+                                       void* page_bounds, void* stream);
 
 /* Stage 1a, scoring ([Cross/cards] EntmaxKV abstract; [Cross/list] Abstract).
  *   unit == SD_UNIT_PAGE: reads q and page_bounds;

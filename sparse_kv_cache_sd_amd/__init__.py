@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     UNIT_PAGE,
     UNIT_TOKEN,
     alloc_workspace,
+    append_page_bounds,
     alloc_workspace_entmax,
     alloc_workspace_sel,
     attend_partials,

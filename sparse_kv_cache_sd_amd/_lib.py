@@ -70,7 +70,10 @@ _SIGS = {
     "sd_keep_count": (ctypes.c_int32, [ctypes.c_double, _I32]),
     "sd_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(SdShape), _I32, ctypes.c_double,
                                           ctypes.POINTER(ctypes.c_size_t)]),
-    "sd_update_page_bounds": (ctypes.c_int, [ctypes.POINTER(SdShape), _P, _P, _P, _P, _P]),
+    "sd_update_page_bounds": (ctypes.c_int, [ctypes.POINTER(SdShape), _P, _P, _P, _P, _I32, _P,
+                                             _P]),
+    "sd_append_page_bounds": (ctypes.c_int, [ctypes.POINTER(SdShape), _P, _P, _P, _P, _I32, _P,
+                                             _P]),
     "sd_score_pages": (ctypes.c_int, [ctypes.POINTER(SdShape), _P, _P, _P, _P, _P, _I32, _P,
                                       _P, _P]),
     "sd_select_topk": (ctypes.c_int, [ctypes.POINTER(SdShape), _I32, _P, _P, ctypes.c_double,
@@ -239,15 +242,41 @@ def bounds_shape(shape: Shape):
     return _bounds_shape(shape)
 
 
-def update_page_bounds(shape: Shape, k_pages, block_table, seq_lens, page_bounds, stream=None):
+def update_page_bounds(shape: Shape, k_pages, block_table, seq_lens, page_bounds, pages=None,
+                       stream=None):
+    """Page bounds of every page, or of the listed (sequence, logical page)
+    pairs only (``pages``: int32 [n, 2] on the device)."""
     s = shape
+    n = 0
+    if pages is not None:
+        if pages.dim() != 2 or pages.shape[1] != 2:
+            raise ValueError("pages must have shape (n, 2)")
+        n = int(pages.shape[0])
+        if n == 0:
+            return  # nothing to update (an empty tensor has no device address to pass)
     _check(lib().sd_update_page_bounds(
         ctypes.byref(s.c()),
         _dev(k_pages, "k_pages", s.torch_dtype, _kv_shape(s)),
         _dev(block_table, "block_table", torch.int32, (s.batch, s.max_pages_per_seq)),
         _dev(seq_lens, "seq_lens", torch.int32, (s.batch,)),
+        _dev(pages, "pages", torch.int32, optional=True), n,
         _dev(page_bounds, "page_bounds", s.torch_dtype,
              _bounds_shape(s)),
+        _stream(stream)))
+
+
+def append_page_bounds(shape: Shape, k_pages, block_table, seq_lens, appended, max_appended,
+                       page_bounds, stream=None):
+    """Fold the tokens each sequence gained (``appended``: int32 [B] on the
+    device, each at most ``max_appended``) into their pages' bounds."""
+    s = shape
+    _check(lib().sd_append_page_bounds(
+        ctypes.byref(s.c()),
+        _dev(k_pages, "k_pages", s.torch_dtype, _kv_shape(s)),
+        _dev(block_table, "block_table", torch.int32, (s.batch, s.max_pages_per_seq)),
+        _dev(seq_lens, "seq_lens", torch.int32, (s.batch,)),
+        _dev(appended, "appended", torch.int32, (s.batch,)), int(max_appended),
+        _dev(page_bounds, "page_bounds", s.torch_dtype, _bounds_shape(s)),
         _stream(stream)))
 
 

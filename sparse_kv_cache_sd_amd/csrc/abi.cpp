@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -32,15 +33,38 @@ sd_status ok() {
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// Attention blocks the split plan aims for: one 8-wave block per CU of an
-// MI355X (256 CUs).  SD_ATTEND_BLOCKS overrides it (read once).
+// Attention blocks the split plan aims for: one 8-wave block per compute unit
+// of the current device (asked once per device; 256 on an MI355X), or
+// SD_ATTEND_BLOCKS when set (read once).  Without a device (sizing a
+// workspace on a host with no GPU) the MI355X's 256 is assumed; a call on a
+// device with more compute units then finds that workspace too small and
+// says so (SD_E_WORKSPACE), as the plan is recomputed at every call.
+constexpr int kMaxDevices = 64;
+constexpr int64_t kDefaultBlocks = 256;
+
 int64_t target_blocks() {
-  static const int64_t v = [] {
+  static const int64_t env = [] {
     const char* e = std::getenv("SD_ATTEND_BLOCKS");
     const long x = e ? std::strtol(e, nullptr, 10) : 0;
-    return static_cast<int64_t>(x > 0 ? x : 256);
+    return static_cast<int64_t>(x > 0 ? x : 0);
   }();
-  return v;
+  if (env > 0) return env;
+  static std::atomic<int> cus[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return kDefaultBlocks;
+  }
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n < 1) {
+      (void)hipGetLastError();
+      return kDefaultBlocks;
+    }
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -765,15 +789,42 @@ sd_status sd_workspace_bytes(const sd_shape* shape, int32_t unit, double r_kv,
 
 sd_status sd_update_page_bounds(const sd_shape* shape, const void* k_pages,
                                 const int32_t* block_table, const int32_t* seq_lens,
-                                void* page_bounds, void* stream) {
+                                const int32_t* pages, int32_t n_pages, void* page_bounds,
+                                void* stream) {
   sdkv::Dims d;
   sd_status st;
   if ((st = check_shape(shape, &d)) != SD_OK) return st;
   if (!k_pages || !block_table || !seq_lens || !page_bounds)
     return fail(SD_E_NULL, "k_pages, block_table, seq_lens and page_bounds are required");
+  if (pages && n_pages < 0) return fail(SD_E_SHAPE, "n_pages (%d) must be >= 0", n_pages);
+  if (pages && n_pages == 0) return ok();  // an empty list: nothing to enqueue
   sdkv::BoundsArgs a{d, k_pages, block_table, seq_lens, page_bounds};
+  a.pages = pages;
+  a.n_pages = pages ? n_pages : 0;
   if ((st = device_status(sdkv::launch_page_bounds(a, static_cast<hipStream_t>(stream)),
                           "page bounds kernel launch")) != SD_OK)
+    return st;
+  return ok();
+}
+
+sd_status sd_append_page_bounds(const sd_shape* shape, const void* k_pages,
+                                const int32_t* block_table, const int32_t* seq_lens,
+                                const int32_t* appended, int32_t max_appended,
+                                void* page_bounds, void* stream) {
+  sdkv::Dims d;
+  sd_status st;
+  if ((st = check_shape(shape, &d)) != SD_OK) return st;
+  if (!k_pages || !block_table || !seq_lens || !appended || !page_bounds)
+    return fail(SD_E_NULL,
+                "k_pages, block_table, seq_lens, appended and page_bounds are required");
+  if (max_appended < 1 || max_appended > d.max_seq)
+    return fail(SD_E_SHAPE, "max_appended (%d) outside [1, max_seq_len = %d]", max_appended,
+                d.max_seq);
+  sdkv::BoundsArgs a{d, k_pages, block_table, seq_lens, page_bounds};
+  a.appended = appended;
+  a.max_appended = max_appended;
+  if ((st = device_status(sdkv::launch_page_bounds(a, static_cast<hipStream_t>(stream)),
+                          "page bounds append kernel launch")) != SD_OK)
     return st;
   return ok();
 }

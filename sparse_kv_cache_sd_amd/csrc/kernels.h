@@ -25,6 +25,14 @@ struct BoundsArgs {
   const int32_t* block_table;
   const int32_t* seq_lens;
   void* bounds;
+  // At most one of the two: pages ([n_pages][2] (sequence, logical page)
+  // pairs to recompute) or appended ([B] tokens that joined each sequence
+  // since the bounds were last current, folded in; at most max_appended
+  // each).  Neither: every page.
+  const int32_t* pages = nullptr;
+  int n_pages = 0;
+  const int32_t* appended = nullptr;
+  int max_appended = 0;
 };
 
 struct ScoreArgs {

@@ -111,9 +111,12 @@ def check_selection(gpu_kept: np.ndarray, orc: sdref.GroupResult) -> bool:
     return False
 
 
-def compare_step(dev: Dev, unit: str, r_kv: float, groups=None, report=None):
+def compare_step(dev: Dev, unit: str, r_kv: float, groups=None, report=None, counts=None):
     """Run the whole decode step on the GPU and compare every (b, g) in
-    ``groups`` (default all) with the oracle.  Returns the max errors."""
+    ``groups`` (default all) with the oracle.  Returns the max errors.
+    ``counts`` (a dict), if given, receives how many instances were compared
+    as exact sets ("exact", oracle gap > 1e-4) and how many under the gap
+    rule's fallback ("fallback")."""
     w, s = dev.w, dev.shape
     scale = 1.0 / math.sqrt(s.head_dim) if s.softmax_scale <= 0 else s.softmax_scale
     out, lse, sel, cnt = run_decode(dev, unit, r_kv)
@@ -129,7 +132,11 @@ def compare_step(dev: Dev, unit: str, r_kv: float, groups=None, report=None):
         else:
             assert int(cnt[b, g]) == orc.k
             kept = sel[b, g, :orc.k].astype(np.int64)
-            if check_selection(kept, orc):
+            exact = check_selection(kept, orc)
+            if counts is not None:
+                key = "exact" if exact else "fallback"
+                counts[key] = counts.get(key, 0) + 1
+            if exact:
                 ref_o, ref_l = orc.out_sparse, orc.lse_sparse
             else:
                 o2 = oracle_group(w, b, g, unit, r_kv, scale, kept_override=kept)

@@ -170,3 +170,17 @@ def test_dropped_mass_validation_before_any_launch():
     big = ctypes.byref(_shape(max_pages_per_seq=32768, max_seq_len=300000, num_pages=32768).c())
     st = lib.sd_dropped_mass(big, fake, fake, fake, fake, fake, 4, fake, None)
     assert st == 6
+
+
+def test_page_bounds_list_arguments():
+    """An empty page list is accepted and enqueues nothing; a negative count
+    is refused; the append form needs max_appended in [1, max_seq_len]."""
+    s = _shape()
+    p = ctypes.c_void_p(16)     # never dereferenced: nothing is enqueued
+    f = sd.lib().sd_update_page_bounds
+    assert f(ctypes.byref(s.c()), p, p, p, p, 0, p, None) == 0
+    assert f(ctypes.byref(s.c()), p, p, p, p, -1, p, None) == 2
+    g = sd.lib().sd_append_page_bounds
+    assert g(ctypes.byref(s.c()), p, p, p, p, 0, p, None) == 2
+    assert g(ctypes.byref(s.c()), p, p, p, p, 32769, p, None) == 2
+    assert g(ctypes.byref(s.c()), p, p, p, None, 1, p, None) == 1

@@ -77,24 +77,30 @@ def _finite(out, lse):
     assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
 
 
-# (id, recipe name, context, unit, r_kv, sampled (b, g) instances or "all")
+# (id, recipe name, context, unit, r_kv, sampled (b, g) instances or "all",
+#  instances whose oracle score gap at k exceeds 1e-4, so that their kept set
+#  is compared exactly; the rest take the gap rule's fallback.  Counted from
+#  the oracle on these seeded inputs: a drop means the comparison got weaker)
 CASES = [
-    ("l8b-32k-page-0.3", "l8b", None, "page", 0.3, "all"),
-    ("l8b-32k-dense", "l8b", None, "page", 1.0, [(0, 0), (0, 5)]),
-    ("sweep-128k-token-0.3", "sweep", 128 * K, "token", 0.3, [(0, 0), (0, 3), (0, 7)]),
-    ("sweep-128k-token-0.2", "sweep", 128 * K, "token", 0.2, [(0, 1), (0, 6)]),
-    ("sweep-128k-dense", "sweep", 128 * K, "token", 1.0, [(0, 2)]),
-    ("sweep-64k-token-0.2", "sweep", 64 * K, "token", 0.2, [(0, 4)]),
-    ("sweep-8k-token-0.3", "sweep", 8 * K, "token", 0.3, "all"),
-    ("sweep-2k-token-0.2", "sweep", 2 * K, "token", 0.2, "all"),
-    ("l70b-128k-page-0.05", "l70b", 128 * K, "page", 0.05, "all"),
-    ("batch-page-0.2", "batch", None, "page", 0.2, "extremes"),
-    ("l70b-1m-page-0.05", "l70b", 1024 * K, "page", 0.05, [(0, 0), (0, 7)]),
+    ("l8b-32k-page-0.3", "l8b", None, "page", 0.3, "all", 8),
+    ("l8b-32k-dense", "l8b", None, "page", 1.0, [(0, 0), (0, 5)], 0),
+    ("sweep-128k-token-0.3", "sweep", 128 * K, "token", 0.3, [(0, 0), (0, 3), (0, 7)], 1),
+    ("sweep-128k-token-0.2", "sweep", 128 * K, "token", 0.2, [(0, 1), (0, 6)], 0),
+    ("sweep-128k-dense", "sweep", 128 * K, "token", 1.0, [(0, 2)], 0),
+    ("sweep-64k-token-0.2", "sweep", 64 * K, "token", 0.2, [(0, 4)], 0),
+    ("sweep-32k-token-0.3", "sweep", 32 * K, "token", 0.3, "all", 2),
+    ("sweep-32k-token-0.2", "sweep", 32 * K, "token", 0.2, "all", 2),
+    ("sweep-8k-token-0.3", "sweep", 8 * K, "token", 0.3, "all", 8),
+    ("sweep-2k-token-0.2", "sweep", 2 * K, "token", 0.2, "all", 8),
+    ("l70b-128k-page-0.05", "l70b", 128 * K, "page", 0.05, "all", 8),
+    ("batch-page-0.2", "batch", None, "page", 0.2, "extremes", 4),
+    ("l70b-1m-page-0.05", "l70b", 1024 * K, "page", 0.05, [(0, 0), (0, 7)], 1),
 ]
 
 
-@pytest.mark.parametrize("cid,name,context,unit,r_kv,groups", CASES, ids=[c[0] for c in CASES])
-def test_full_size(cid, name, context, unit, r_kv, groups):
+@pytest.mark.parametrize("cid,name,context,unit,r_kv,groups,n_exact", CASES,
+                         ids=[c[0] for c in CASES])
+def test_full_size(cid, name, context, unit, r_kv, groups, n_exact):
     print(f"[fullsize] {cid}", flush=True)
     dev = _dev(name, context)
     s = dev.shape
@@ -107,8 +113,11 @@ def test_full_size(cid, name, context, unit, r_kv, groups):
         out, lse, sel, cnt = run_decode(dev, unit, r_kv)
         _finite(out, lse)
         _own_topk_property(dev, unit, r_kv, sel, cnt)
-    e_o, e_l = compare_step(dev, unit, r_kv, groups=groups)
-    print(f"[fullsize] {cid}: {len(groups)} instances vs oracle, max-abs out {e_o:.2e} "
+    counts = {}
+    e_o, e_l = compare_step(dev, unit, r_kv, groups=groups, counts=counts)
+    assert counts.get("exact", 0) == n_exact, counts
+    print(f"[fullsize] {cid}: {len(groups)} instances vs oracle ({counts.get('exact', 0)} as "
+          f"exact sets, {counts.get('fallback', 0)} under the gap rule), max-abs out {e_o:.2e} "
           f"lse {e_l:.2e}", flush=True)
 
 
