@@ -434,6 +434,29 @@ SD_API sd_status sd_dropped_mass(const sd_shape* shape, const int32_t* seq_lens,
                                  const int32_t* sel_idx, const int32_t* sel_count, int32_t k_max,
                                  float* delta, void* stream);
 
+/* ---- Allocation-free decode step -------------------------------------
+ * For callers that cannot allocate device memory or pass a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  The same work as sd_decode_step (same arguments without ws /
+ * ws_bytes, same kernels, same results), with its scratch space in a static
+ * device array of 32 MiB that the library holds on every device it runs on
+ * until the process ends.  The call allocates and frees nothing.
+ *   - Shapes whose sd_workspace_bytes exceeds 32 MiB are refused with
+ *     SD_E_WORKSPACE before anything is enqueued (every configuration of the
+ *     benchmark fits; 1M-token token-unit steps do not).
+ *   - Calls on one device share that device's array: calls that overlap in
+ *     time on one device (different streams, or several host threads) race
+ *     and give undefined results.  Enqueue them on one stream.  Nothing in
+ *     the array needs clearing between calls: every region is written before
+ *     it is read, as with a caller workspace.
+ *   - The first call on a device looks up the array's device address
+ *     (SD_E_DEVICE if that fails). */
+SD_API sd_status sd_decode_step_noalloc(const sd_shape* shape, const void* q, const void* k_pages,
+                                        const void* v_pages, const void* page_bounds,
+                                        const int32_t* block_table, const int32_t* seq_lens,
+                                        int32_t unit, double r_kv, float* out, float* lse,
+                                        int32_t* sel_idx, int32_t* sel_count, void* stream);
+
 /* Text of the last non-OK status on this thread ("" if none). */
 SD_API const char* sd_last_error(void);
 

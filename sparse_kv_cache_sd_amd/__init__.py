@@ -23,6 +23,7 @@ from ._lib import (  # noqa: F401
     bounds_shape,
     compressed_keys_shape,
     decode_step,
+    decode_step_noalloc,
     decode_step_entmax,
     decode_step_sel,
     dropped_mass,

@@ -104,6 +104,8 @@ _SIGS = {
                                              ctypes.c_size_t, _P]),
     "sd_dropped_mass": (ctypes.c_int, [ctypes.POINTER(SdShape), _P, _P, _P, _P, _P, _I32, _P,
                                        _P]),
+    "sd_decode_step_noalloc": (ctypes.c_int, [ctypes.POINTER(SdShape), _P, _P, _P, _P, _P, _P,
+                                              _I32, ctypes.c_double, _P, _P, _P, _P, _P]),
     "sd_last_error": (ctypes.c_char_p, []),
 }
 EXPORTS = tuple(_SIGS)
@@ -365,6 +367,31 @@ def decode_step(shape: Shape, q, k_pages, v_pages, page_bounds, block_table, seq
         _dev(sel_idx, "sel_idx", torch.int32, (s.batch, s.num_kv_heads, k_max), optional=True),
         _dev(sel_count, "sel_count", torch.int32, (s.batch, s.num_kv_heads), optional=True),
         wp, wn, _stream(stream)))
+
+
+def decode_step_noalloc(shape: Shape, q, k_pages, v_pages, page_bounds, block_table, seq_lens,
+                        unit, r_kv, out, lse, sel_idx=None, sel_count=None, stream=None):
+    """decode_step with the library's static device scratch instead of a
+    workspace (no allocation; calls on one device must not overlap)."""
+    s, u = shape, _unit(unit)
+    umax = s.max_pages_per_seq if u == UNIT_PAGE else s.max_seq_len
+    dense = r_kv >= 1.0
+    k_max = keep_count(r_kv, umax) if not (math.isnan(r_kv) or r_kv <= 0) else 0
+    _check(lib().sd_decode_step_noalloc(
+        ctypes.byref(s.c()),
+        _dev(q, "q", s.torch_dtype, (s.batch, s.num_q_heads, s.head_dim)),
+        _dev(k_pages, "k_pages", s.torch_dtype, _kv_shape(s)),
+        _dev(v_pages, "v_pages", s.torch_dtype, _kv_shape(s)),
+        _dev(page_bounds, "page_bounds", s.torch_dtype,
+             _bounds_shape(s), optional=dense or u == UNIT_TOKEN),
+        _dev(block_table, "block_table", torch.int32, (s.batch, s.max_pages_per_seq)),
+        _dev(seq_lens, "seq_lens", torch.int32, (s.batch,)),
+        u, float(r_kv),
+        _dev(out, "out", torch.float32, (s.batch, s.num_q_heads, s.head_dim)),
+        _dev(lse, "lse", torch.float32, (s.batch, s.num_q_heads)),
+        _dev(sel_idx, "sel_idx", torch.int32, (s.batch, s.num_kv_heads, k_max), optional=True),
+        _dev(sel_count, "sel_count", torch.int32, (s.batch, s.num_kv_heads), optional=True),
+        _stream(stream)))
 
 
 def select_attend(shape: Shape, q, k_pages, v_pages, block_table, seq_lens, unit_scores, r_kv,

@@ -1166,4 +1166,8 @@ sd_status sd_dropped_mass(const sd_shape* shape, const int32_t* seq_lens,
 
 const char* sd_last_error(void) { return g_err; }
 
+// For sd_decode_step_noalloc (noalloc.hip): a status with its message, as
+// sd_last_error() reports it.  Not exported.
+sd_status sdkv_fail_noalloc(sd_status st, const char* msg) { return fail(st, "%s", msg); }
+
 }  // extern "C"

@@ -184,3 +184,16 @@ def test_page_bounds_list_arguments():
     assert g(ctypes.byref(s.c()), p, p, p, p, 0, p, None) == 2
     assert g(ctypes.byref(s.c()), p, p, p, p, 32769, p, None) == 2
     assert g(ctypes.byref(s.c()), p, p, p, None, 1, p, None) == 1
+
+
+def test_noalloc_refuses_shapes_past_the_static_scratch():
+    """The allocation-free step refuses, before touching the device, a shape
+    whose scratch exceeds its static 32 MiB (1M tokens in token unit)."""
+    s = _shape(num_q_heads=64, max_pages_per_seq=16384, max_seq_len=1 << 20, num_pages=16384,
+               page_size=64)
+    assert sd.workspace_bytes(s, "token", 0.05) > 32 << 20
+    p = ctypes.c_void_p(16)     # never dereferenced: the call is refused on the host
+    st = sd.lib().sd_decode_step_noalloc(ctypes.byref(s.c()), p, p, p, None, p, p, 0,
+                                         ctypes.c_double(0.05), p, p, None, None, None)
+    assert st == 5
+    assert b"static scratch" in sd.lib().sd_last_error()
