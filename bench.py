@@ -4,20 +4,34 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload l8b]
                     [--selection topk|window|init_local_topk|mass_budget]
                     [--scorer bounds|compressed] [--attention softmax|entmax]
+                    [--no-points] [--blocks N]
 
 A step is one decode step of one attention layer: page-bound (or exact)
 scoring, top-k selection under r_KV and split-K attention over the kept
-units, merged by log-sum-exp.  Steps cycle over L distinct layer caches whose
-total size is at least 4x the 256 MB Infinity Cache, so the KV bytes come from
-HBM; the L-layer loop is captured in a HIP graph and replayed.  Inputs are
-resident in HBM before timing starts.
+units, merged by log-sum-exp.  Inputs are resident in HBM before timing
+starts.
 
-Prints ONE JSON line: the metric (microseconds per decode-step-layer, lower
-is better), effective HBM GB/s on the algorithmic bytes, the roofline of the
-dominant kernel (the split-K attention kernel, timed alone with HIP events on
-its stream), the same-kernel dense step for comparison, and the fp64 CPU
-oracle timed on a bounded sample on the host cores.  Token-unit lines also
-report the dropped softmax mass of layer 0's selection (computed on the GPU).
+Timing protocol, per workload:
+* L distinct layer caches, L chosen from the bytes the SPARSE step reads so
+  that between two reads of one layer the steps read at least 4x the 256 MB
+  Infinity Cache of other layers' data (layers past the first are device
+  copies of it at their own addresses);
+* W untimed warmup steps and one untimed pass over the L layers, then
+  exactly K step-layers (step i on layer i mod L) captured in one HIP graph
+  and replayed once, timed with HIP events on the launch stream;
+* the same for the dense step (every unit kept, same kernels) and for the
+  attention kernel alone.
+
+Prints ONE JSON line: the metric (microseconds per decode-step-layer of the
+main workload, lower is better), effective HBM GB/s on the algorithmic
+bytes, the roofline of the dominant kernel (the split-K attention kernel),
+the dense step, `points` (the other workloads of the 32K-1M range, each with
+its step time, GB/s, dense time, speedup, byte bound and attention-kernel
+fraction), and the fp64 CPU oracle timed on a bounded sample on the host
+cores (sparse and dense steps apart, one thread too, with the dropped mass
+delta).  Token-unit results also report the dropped softmax mass of layer
+0's selection, computed on the GPU.  --blocks N runs N fresh processes and
+reports paired dense/sparse ratios with an interval from resampling them.
 """
 
 from __future__ import annotations
@@ -50,6 +64,8 @@ WORKLOADS = {
                       "8B-shaped, batch 1, 128K, exact q.K token top-k r_KV=0.2"),
     "sweep32k-0.2": ("sweep", {"seq_len": 32768, "seed": 5}, "token", 0.2,
                      "8B-shaped, batch 1, 32K, exact q.K token top-k r_KV=0.2"),
+    "sweep32k-0.3": ("sweep", {"seq_len": 32768, "seed": 5}, "token", 0.3,
+                     "8B-shaped, batch 1, 32K, exact q.K token top-k r_KV=0.3"),
     "batch": ("batch", {}, "page", 0.2,
               "16 sequences x U(48K,64K) context, 8B-shaped, page-bound top-k r_KV=0.2"),
     "l70b-128k": ("l70b", {"seq_len": 131072, "seed": 5}, "page", 0.05,
@@ -240,45 +256,512 @@ def algorithmic_stats_bytes(seq_lens, H_kv, d, P, elem, scorer):
     return H_kv * int(np.sum([-(-int(n) // P) for n in seq_lens])) * 2 * d * elem
 
 
-def cpu_baseline(w, unit, r_kv, budget_s=12.0, selection=None, scorer="bounds", alpha=None):
-    from oracle import entmaxref, sdref
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        return int(max([p.get("num_threads", 1) for p in threadpool_info()] or [1]))
     except Exception:
-        cores = 1
+        return 1
+
+
+def oracle_instance(w, b, g):
+    """fp64 q of the group and the valid K, V of (sequence b, KV head g)."""
+    from oracle import sdref
     r = w.recipe
-    G = r.group
-    scale = 1.0 / math.sqrt(r.head_dim)
-    groups = [(b, g) for b in range(r.batch) for g in range(r.num_kv_heads)]
+    G, n = r.group, int(w.seq_lens[b])
+    return (sdref.widen(w.q[b, g * G:(g + 1) * G], r.dtype),
+            sdref.widen(w.K[b, g, :n], r.dtype), sdref.widen(w.V[b, g, :n], r.dtype))
+
+
+def oracle_sparse_step(qg, Kg, Vg, stats, unit, P, r_kv, scale):
+    """One (sequence, KV head) of the sparse decode step through the oracle's
+    own functions: unit scores (from the page bounds, which are setup, or
+    from the exact logits), keep count, top-k, softmax over the kept tokens.
+    In page unit only the kept pages' keys enter a logit."""
+    from oracle import sdref
+    n = Kg.shape[0]
+    if unit == "page":
+        sigma = sdref.page_scores(qg, stats[0], stats[1], scale)
+        kept, _ = sdref.select_topk(sigma, sdref.keep_count(r_kv, sigma.shape[0]))
+        tokens = sdref.unit_tokens(kept, unit, P, n)
+        s = sdref.group_logits(qg, Kg[tokens], scale)
+        Vt = Vg[tokens]
+        return [sdref.attention(s[i], Vt) for i in range(s.shape[0])]
+    s = sdref.group_logits(qg, Kg, scale)
+    sigma = sdref.token_scores(s)
+    kept, _ = sdref.select_topk(sigma, sdref.keep_count(r_kv, sigma.shape[0]))
+    tokens = sdref.unit_tokens(kept, unit, P, n)
+    return [sdref.attention(s[i], Vg, tokens) for i in range(s.shape[0])]
+
+
+def oracle_dense_step(qg, Kg, Vg, scale):
+    from oracle import sdref
+    s = sdref.group_logits(qg, Kg, scale)
+    return [sdref.attention(s[i], Vg) for i in range(s.shape[0])]
+
+
+def _timed_rounds(fn, n_inst, budget_s, max_rounds):
+    """Mean seconds per call of fn(i) over round-robin calls until budget_s
+    has passed (at least one call, at most max_rounds passes)."""
     t0 = time.perf_counter()
     done = 0
     while True:
-        b, g = groups[done % len(groups)]
-        n = int(w.seq_lens[b])
-        qg = sdref.widen(w.q[b, g * G:(g + 1) * G], r.dtype)
-        Kg = sdref.widen(w.K[b, g, :n], r.dtype)
-        Vg = sdref.widen(w.V[b, g, :n], r.dtype)
-        if alpha is None:
-            sdref.group_step(qg, Kg, Vg, unit=unit, page_size=r.page_size, r_kv=r_kv,
-                             scale=scale, selection=selection, scorer=scorer)
-        else:
-            entmaxref.group_step(qg, Kg, Vg, unit=unit, page_size=r.page_size, r_kv=r_kv,
-                                 scale=scale, alpha=alpha, selection=selection, scorer=scorer)
+        fn(done % n_inst)
         done += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or done >= 64 * len(groups):
-            break
-    per_group = el / done
-    us_per_step = per_group * len(groups) * 1e6
-    return {"value": round(us_per_step, 1), "unit": "us/step-layer", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"{done} runs over the step's {len(groups)} (sequence, KV head) selection "
-                      f"instances of layer 0 through "
-                      f"{'oracle.sdref' if alpha is None else 'oracle.entmaxref'}.group_step "
-                      f"(fp64 numpy: page statistics, scores, top-k, dense + sparse "
-                      f"{'softmax' if alpha is None else f'{alpha:g}-entmax'} attention, delta) in "
-                      f"{el:.1f} s; value = mean time per instance x {len(groups)}"}
+        if el >= budget_s or done >= max_rounds * n_inst:
+            return el / done, done, el
+
+
+def cpu_baseline(w, unit, r_kv, budget_s=12.0, selection=None, scorer="bounds", alpha=None,
+                 one_thread=True):
+    """The fp64 oracle timed on the host cores over a bounded sample of the
+    workload's (sequence, KV head) instances, scaled to microseconds per
+    decode-step-layer.  The plain top-k softmax step reports the sparse step
+    (value), the dense step and, at one thread, the sparse step again, plus
+    the dropped mass delta of the sampled instances; other kept sets and
+    alpha-entmax time the oracle's group step (dense and sparse together)."""
+    from oracle import entmaxref, sdref
+    r = w.recipe
+    scale = 1.0 / math.sqrt(r.head_dim)
+    groups = [(b, g) for b in range(r.batch) for g in range(r.num_kv_heads)]
+    cores = blas_threads()
+    base = {"unit": "us/step-layer", "cores": cores, "kind": "oracle", "cpu_model": cpu_model()}
+    n_inst = len(groups)
+    if selection is not None or alpha is not None or scorer != "bounds":
+        def step(i):
+            b, g = groups[i]
+            qg, Kg, Vg = oracle_instance(w, b, g)
+            if alpha is None:
+                sdref.group_step(qg, Kg, Vg, unit=unit, page_size=r.page_size, r_kv=r_kv,
+                                 scale=scale, selection=selection, scorer=scorer)
+            else:
+                entmaxref.group_step(qg, Kg, Vg, unit=unit, page_size=r.page_size, r_kv=r_kv,
+                                     scale=scale, alpha=alpha, selection=selection, scorer=scorer)
+        per, done, el = _timed_rounds(step, n_inst, budget_s, 10 ** 6)
+        return dict(base, value=round(per * n_inst * 1e6, 1), sample=(
+            f"{done} calls over the step's {n_inst} (sequence, KV head) instances through "
+            f"{'oracle.sdref' if alpha is None else 'oracle.entmaxref'}.group_step (fp64 numpy: "
+            f"scores, kept set, dense + sparse "
+            f"{'softmax' if alpha is None else f'{alpha:g}-entmax'} attention, delta) in "
+            f"{el:.1f} s; value = mean time per instance x {n_inst}"))
+    # the setup (page bounds) and the fp64 copies of the inputs are made
+    # outside the timed calls, as the GPU's page bounds are built beforehand
+    # and its inputs are resident before timing
+    sample = groups if n_inst <= 16 else groups[:: max(1, n_inst // 16)]
+    inst = []
+    for b, g in sample:
+        qg, Kg, Vg = oracle_instance(w, b, g)
+        stats = sdref.page_bounds(Kg, r.page_size) if unit == "page" else None
+        inst.append((qg, Kg, Vg, stats))
+    m = len(inst)
+    sparse = lambda i: oracle_sparse_step(*inst[i][:3], inst[i][3], unit, r.page_size, r_kv, scale)
+    dense = lambda i: oracle_dense_step(*inst[i][:3], scale)
+    t_sp, n_sp, e_sp = _timed_rounds(sparse, m, 0.4 * budget_s, 10 ** 6)
+    t_de, n_de, e_de = _timed_rounds(dense, m, 0.25 * budget_s, 10 ** 6)
+    out = dict(base, value=round(t_sp * n_inst * 1e6, 1),
+               dense_us_per_step_layer=round(t_de * n_inst * 1e6, 1))
+    if one_thread:
+        try:
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(limits=1):
+                t1, n1, e1 = _timed_rounds(sparse, m, 0.2 * budget_s, 10 ** 6)
+            out["one_thread_us_per_step_layer"] = round(t1 * n_inst * 1e6, 1)
+        except Exception as e:                       # threadpoolctl missing: say so
+            out["one_thread_us_per_step_layer"] = None
+            log(f"one-thread oracle timing skipped: {e}")
+    # dropped mass of the sampled instances (the oracle's group step)
+    deltas = []
+    for qg, Kg, Vg, _ in inst:
+        res = sdref.group_step(qg, Kg, Vg, unit=unit, page_size=r.page_size, r_kv=r_kv,
+                               scale=scale)
+        deltas.extend(res.delta.tolist())
+    out["dropped_mass"] = {"mean": round(float(np.mean(deltas)), 5),
+                           "max": round(float(np.max(deltas)), 5),
+                           "of": f"the oracle's fp64 delta, every query head of the {m} sampled "
+                                 f"(sequence, KV head) instances"}
+    out["sample"] = (f"{m} of the step's {n_inst} (sequence, KV head) instances of layer 0, "
+                     f"round-robin: sparse step (oracle page_scores / token logits, keep_count, "
+                     f"select_topk, attention over the kept tokens; page bounds built "
+                     f"beforehand) {n_sp} calls in {e_sp:.1f} s, dense step (logits + attention "
+                     f"over every token) {n_de} calls in {e_de:.1f} s; value and dense = mean "
+                     f"time per instance x {n_inst}")
+    return out
+
+
+# ----------------------------------------------------------------------------
+# GPU measurement of one workload
+# ----------------------------------------------------------------------------
+
+MALL_SAFE = 4   # Infinity Caches' worth of other data read between two reads of one layer
+
+# the other points of the metric's 32K-1M range, timed after the main workload
+POINTS = ["sweep32k-0.2", "sweep128k-0.3", "sweep128k-0.2", "batch", "l70b-128k", "l70b-1m"]
+
+
+def layers_for(step_bytes):
+    """Distinct layer caches so that between two reads of one layer the steps
+    read at least MALL_SAFE x the Infinity Cache of other layers' data."""
+    return max(2, math.ceil(MALL_SAFE * MALL_BYTES / max(1, step_bytes)) + 1)
+
+
+class Measure:
+    """Timing of one workload on the GPU: layer caches resident in HBM, the
+    sparse step, the dense step and the attention kernel alone, each timed
+    over exactly `steps` step-layers with HIP events on the launch stream."""
+
+    def __init__(self, torch, sd, stream, graph):
+        self.torch, self.sd, self.stream, self.graph = torch, sd, stream, graph
+
+    def timed(self, fn, steps, warmup, L):
+        """Microseconds per call of fn(layer) over exactly `steps` calls, layer
+        i mod L for call i.  Untimed first: `warmup` calls, then one pass over
+        all L layers, so that every timed call reads a layer last read L
+        calls earlier."""
+        torch, stream = self.torch, self.stream
+        with torch.cuda.stream(stream):
+            for i in range(warmup):
+                fn(i % L)
+            torch.cuda.synchronize()
+            if self.graph:
+                prime = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(prime, stream=stream):
+                    for i in range(L):
+                        fn(i)
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    for i in range(steps):
+                        fn(i % L)
+                prime.replay()
+            else:
+                for i in range(L):
+                    fn(i)
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            if self.graph:
+                g.replay()
+            else:
+                for i in range(steps):
+                    fn(i % L)
+            e1.record(stream)
+            torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / steps
+
+
+def measure_workload(name, args, torch, sd, kvsynth, stream, *, selection_kind="topk",
+                     scorer="bounds", entmax=False, main=False, w0=None):
+    """Times one workload; returns (result dict, the layer-0 workload)."""
+    rname, over, unit, r_kv, desc = WORKLOADS[name]
+    if main and args.r_kv > 0:
+        r_kv = args.r_kv
+        desc += f"; r_KV overridden to {r_kv:g}"
+    rec = kvsynth.RECIPES[rname].with_(**over)
+    P, d, H_q, H_kv = rec.page_size, rec.head_dim, rec.num_q_heads, rec.num_kv_heads
+    elem = 2 if rec.dtype == "bf16" else 4
+    dt = torch.bfloat16 if rec.dtype == "bf16" else torch.float32
+    t_gen = time.perf_counter()
+    if w0 is None:
+        w0 = kvsynth.generate(rec)
+
+    def dev(a):
+        if rec.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+                torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    pc = w0.paged()
+    bt_dev = torch.from_numpy(pc.block_table).cuda()
+    sl_dev = torch.from_numpy(w0.seq_lens).cuda()
+    shape = sd.Shape(rec.batch, H_q, H_kv, d, P, w0.max_pages(), w0.n_alloc, rec.dtype,
+                     pc.num_pages)
+    lay0 = dict(q=dev(w0.q), k=dev(pc.k_pool), v=dev(pc.v_pool))
+    del pc
+    if scorer == "compressed":
+        lay0["bounds"] = torch.empty(sd.compressed_keys_shape(shape), dtype=torch.float32,
+                                     device="cuda")
+        sd.update_compressed_keys(shape, lay0["k"], bt_dev, sl_dev, lay0["bounds"])
+    else:
+        lay0["bounds"] = torch.empty(sd.bounds_shape(shape), dtype=dt, device="cuda")
+        sd.update_page_bounds(shape, lay0["k"], bt_dev, sl_dev, lay0["bounds"])
+    torch.cuda.synchronize()
+    log(f"{name}: layer 0 resident ({time.perf_counter() - t_gen:.1f} s)")
+
+    structured = selection_kind != "topk" or scorer != "bounds"
+    local_units = args.local_units or (2048 // P if unit == "page" else 2048)
+    uni = selection_kind == "init_local_topk"
+    selection = sd.Selection(selection_kind, r_kv, args.init_units if uni else 0,
+                             local_units if uni else 0,
+                             args.max_dropped if selection_kind == "mass_budget" else 0.0, scorer)
+    config_sel = {}
+    if structured:
+        config_sel = {"selection": selection_kind, "init_units": selection.init_units,
+                      "local_units": selection.local_units,
+                      "max_dropped": selection.max_dropped, "scorer": scorer}
+        desc += f"; kept set: {selection_kind}" + {
+            "init_local_topk": f" ({selection.init_units} initial + {selection.local_units} "
+                               f"local units + top-k)",
+            "window": " (most recent units)",
+            "mass_budget": f" (at most {selection.max_dropped:g} of each head's mass dropped, "
+                           f"capped at r_KV)",
+            "topk": ""}[selection_kind]
+        if scorer == "compressed":
+            desc += "; pages scored from compressed keys (mean-pooled, kernel 32 stride 16)"
+    if entmax:
+        desc += f"; {args.alpha:g}-entmax attention over the kept set (dense: every unit)"
+    k_max = sd.selection_capacity(selection, shape.units_max(unit))
+    dense_sel = sd.Selection("topk", 1.0)
+    if entmax:
+        ws = sd.alloc_workspace_entmax(shape, unit, selection)
+        ws_dense = sd.alloc_workspace_entmax(shape, unit, dense_sel)
+        tau = torch.empty((rec.batch, H_q), dtype=torch.float32, device="cuda")
+    else:
+        ws = sd.alloc_workspace_sel(shape, unit, selection)
+        ws_dense = sd.alloc_workspace(shape, unit, 1.0)
+    out = torch.empty((rec.batch, H_q, d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((rec.batch, H_q), dtype=torch.float32, device="cuda")
+    layers = [lay0]
+    sels, cnts = [], []
+
+    def new_sel():
+        sels.append(torch.empty((rec.batch, H_kv, k_max), dtype=torch.int32, device="cuda"))
+        cnts.append(torch.empty((rec.batch, H_kv), dtype=torch.int32, device="cuda"))
+
+    def sparse_step(i):
+        lay = layers[i]
+        if entmax:
+            sd.decode_step_entmax(shape, lay["q"], lay["k"], lay["v"], lay["bounds"], bt_dev,
+                                  sl_dev, unit, selection, args.alpha, out, ws, tau=tau,
+                                  sel_idx=sels[i], sel_count=cnts[i], stream=stream)
+        elif structured:
+            sd.decode_step_sel(shape, lay["q"], lay["k"], lay["v"], lay["bounds"], bt_dev, sl_dev,
+                               unit, selection, out, lse, ws, sels[i], cnts[i], stream=stream)
+        else:
+            sd.decode_step(shape, lay["q"], lay["k"], lay["v"], lay["bounds"], bt_dev, sl_dev,
+                           unit, r_kv, out, lse, ws, sels[i], cnts[i], stream=stream)
+
+    def dense_step(i):
+        lay = layers[i]
+        if entmax:
+            sd.decode_step_entmax(shape, lay["q"], lay["k"], lay["v"], None, bt_dev, sl_dev,
+                                  unit, dense_sel, args.alpha, out, ws_dense, tau=tau,
+                                  stream=stream)
+        else:
+            sd.decode_step(shape, lay["q"], lay["k"], lay["v"], None, bt_dev, sl_dev, unit, 1.0,
+                           out, lse, ws_dense, stream=stream)
+
+    # one sparse step on layer 0 gives the bytes a step reads, which size the
+    # layer count
+    new_sel()
+    with torch.cuda.stream(stream):
+        sparse_step(0)
+    torch.cuda.synchronize()
+    kept = kept_token_count(sels[0].cpu().numpy(), cnts[0].cpu().numpy(), w0.seq_lens, unit, P)
+    window = selection_kind == "window"
+    b_sparse = algorithmic_bytes(w0.seq_lens, H_q, H_kv, d, P, elem, unit, r_kv, kept,
+                                 window=window)
+    if unit == "page" and scorer == "compressed" and not window:
+        b_sparse += (algorithmic_stats_bytes(w0.seq_lens, H_kv, d, P, elem, "compressed") -
+                     algorithmic_stats_bytes(w0.seq_lens, H_kv, d, P, elem, "bounds"))
+    b_dense = algorithmic_bytes(w0.seq_lens, H_q, H_kv, d, P, elem, unit, 1.0, 0)
+    L = args.layers if main and args.layers else layers_for(b_sparse)
+    # layers 1 .. L-1: device copies of layer 0 at their own addresses (the
+    # same values, so the same selections; only the addresses differ, which
+    # is what keeps a layer out of the caches until it is read again)
+    for i in range(1, L):
+        layers.append({key: t.clone() for key, t in lay0.items()})
+        new_sel()
+    torch.cuda.synchronize()
+    log(f"{name}: {L} layer caches ({L} x {b_sparse / 1e6:.1f} MB read by the sparse step, "
+        f"{L} x {b_dense / 1e6:.1f} MB by the dense step)")
+
+    # scores (and token logits) of every layer, for the attention kernel alone
+    umax = shape.units_max(unit)
+    scores = [torch.empty((rec.batch, H_kv, umax), dtype=torch.float32, device="cuda")
+              for _ in range(L)]
+    logits = [torch.empty((rec.batch, H_q, shape.max_seq_len), dtype=torch.float32,
+                          device="cuda") if unit == "token" else None for _ in range(L)]
+    with torch.cuda.stream(stream):
+        for i, lay in enumerate(layers):
+            sparse_step(i)
+            if scorer == "compressed":
+                sd.score_compressed(shape, lay["q"], lay["bounds"], sl_dev, scores[i],
+                                    stream=stream)
+            else:
+                sd.score_pages(shape, lay["q"], lay["k"], lay["bounds"], bt_dev, sl_dev, unit,
+                               scores[i], logits[i], stream=stream)
+    torch.cuda.synchronize()
+
+    def attend_only(i):
+        """The split-K attention kernel alone (one launch), as the decode step
+        runs it: page unit selects inside the attention kernel; token unit
+        attends the stored selection with the stored logits."""
+        lay = layers[i]
+        if structured:
+            sd.attend_partials(shape, lay["q"], lay["k"], lay["v"], bt_dev, sl_dev, unit, ws,
+                               sel_idx=sels[i], sel_count=cnts[i],
+                               token_logits=logits[i] if not window else None, stream=stream)
+        elif unit == "page":
+            sd.attend_partials(shape, lay["q"], lay["k"], lay["v"], bt_dev, sl_dev, unit, ws,
+                               unit_scores=scores[i], r_kv=r_kv, stream=stream)
+        else:
+            sd.attend_partials(shape, lay["q"], lay["k"], lay["v"], bt_dev, sl_dev, unit, ws,
+                               sel_idx=sels[i], sel_count=cnts[i], token_logits=logits[i],
+                               stream=stream)
+
+    M = Measure(torch, sd, stream, not args.no_graph)
+    K, W = args.steps, args.warmup
+    us_sparse = M.timed(sparse_step, K, W, L)
+    log(f"{name}: sparse step {us_sparse:.2f} us/step-layer over {K} steps")
+    us_dense = M.timed(dense_step, K, W, L)
+    log(f"{name}: dense step  {us_dense:.2f} us/step-layer")
+    us_attend = None
+    if not entmax:
+        us_attend = M.timed(attend_only, K, W, L)
+        log(f"{name}: attention kernel alone {us_attend:.2f} us/launch")
+    us_eager = None
+    if main and M.graph:
+        M.graph = False
+        us_eager = M.timed(sparse_step, min(K, 400), W, L)
+        M.graph = True
+        log(f"{name}: sparse step eager {us_eager:.2f} us/step-layer")
+
+    b_attend = attend_bytes(kept, d, elem, unit == "token" and not window)
+    if entmax:
+        # several launches behind one entry point: the roofline is the step's
+        us_attend, b_attend = us_sparse, b_sparse
+    gbps = b_sparse / (us_sparse * 1e-6) / 1e9
+    gbps_dense = b_dense / (us_dense * 1e-6) / 1e9
+    gbps_att = b_attend / (us_attend * 1e-6) / 1e9
+    res = {
+        "workload": name,
+        "desc": desc,
+        "shape": {"batch": rec.batch, "num_q_heads": H_q, "num_kv_heads": H_kv, "head_dim": d,
+                  "page_size": P, "context": int(w0.seq_lens.max()), "unit": unit,
+                  "r_kv": r_kv, "k_per_kv_head": k_max},
+        "layer_caches": L,
+        "sparse_footprint_bytes": int(L * b_sparse),
+        "us_per_step_layer": round(us_sparse, 3),
+        "kept_tokens_per_step": int(kept),
+        "effective_gbps": round(gbps, 1),
+        "pct_hbm_roofline": round(100 * gbps / HBM_PEAK_GBPS, 1),
+        "algorithmic_bytes_per_step": int(b_sparse),
+        "dense": {"us_per_step_layer": round(us_dense, 3), "effective_gbps": round(gbps_dense, 1),
+                  "pct_hbm_roofline": round(100 * gbps_dense / HBM_PEAK_GBPS, 1),
+                  "bytes_per_step": int(b_dense)},
+        "speedup_vs_dense": round(us_dense / us_sparse, 3),
+        "byte_bound_speedup": round(b_dense / b_sparse, 3),
+        "attend": {"us_per_launch": round(us_attend, 3), "bytes_per_launch": int(b_attend),
+                   "achieved_gbps": round(gbps_att, 1),
+                   "frac": round(gbps_att / HBM_PEAK_GBPS, 4)},
+        "structured": structured,
+        "config_sel": config_sel,
+    }
+    if us_eager is not None:
+        res["eager_us_per_step_layer"] = round(us_eager, 3)
+    if unit == "token" and not entmax and shape.max_seq_len <= 262144:
+        # dropped dense softmax mass of layer 0's kept lists (token unit: every
+        # logit is stored, so the library computes it on the GPU)
+        delta = torch.empty((rec.batch, H_q), dtype=torch.float32, device="cuda")
+        sd.dropped_mass(shape, sl_dev, bt_dev, logits[0], sels[0], cnts[0], delta, stream=stream)
+        torch.cuda.synchronize()
+        dl = delta.cpu().numpy()
+        res["dropped_mass"] = {"mean": round(float(dl.mean()), 5), "max": round(float(dl.max()), 5),
+                               "of": "layer 0, every query head (sd_dropped_mass)"}
+    del layers, lay0, scores, logits, sels, cnts, ws, ws_dense
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res, w0
+
+
+def point_summary(res):
+    """The compact form of a workload's result for the main line's points."""
+    a = res["attend"]
+    return {"workload": res["workload"], "desc": res["desc"], "unit": res["shape"]["unit"],
+            "r_kv": res["shape"]["r_kv"], "context": res["shape"]["context"],
+            "batch": res["shape"]["batch"], "us_per_step_layer": res["us_per_step_layer"],
+            "effective_gbps": res["effective_gbps"], "pct_hbm_roofline": res["pct_hbm_roofline"],
+            "dense_us_per_step_layer": res["dense"]["us_per_step_layer"],
+            "speedup_vs_dense": res["speedup_vs_dense"],
+            "byte_bound_speedup": res["byte_bound_speedup"],
+            "attend_us": a["us_per_launch"], "attend_frac": a["frac"],
+            "layer_caches": res["layer_caches"],
+            "sparse_footprint_bytes": res["sparse_footprint_bytes"],
+            **({"dropped_mass": res["dropped_mass"]} if "dropped_mass" in res else {})}
+
+
+# ----------------------------------------------------------------------------
+# fresh-process blocks (the parent never touches the GPU)
+# ----------------------------------------------------------------------------
+
+def child_args(argv):
+    """A block's arguments: ours without --blocks, and neither the points nor
+    the CPU baseline (the parent times the oracle once)."""
+    out, skip = [], False
+    for a in argv:
+        if skip:
+            skip = False
+            continue
+        if a == "--blocks":
+            skip = True
+            continue
+        if a.startswith("--blocks="):
+            continue
+        out.append(a)
+    return out + ["--no-cpu-baseline", "--no-points"]
+
+
+def run_blocks(args, argv):
+    """Runs `args.blocks` fresh child processes of this script one after
+    another (each a whole measurement of the main workload, no points, no
+    CPU baseline) and pairs the dense and sparse times within each block."""
+    import subprocess
+    child = [sys.executable, os.path.abspath(__file__), *child_args(argv)]
+    runs = []
+    for j in range(args.blocks):
+        log(f"block {j + 1}/{args.blocks}: {' '.join(child[1:])}")
+        r = subprocess.run(child, capture_output=True, text=True, timeout=900)
+        sys.stderr.write(r.stderr[-2000:])
+        if r.returncode != 0:
+            log(f"block {j + 1} failed with status {r.returncode}")
+            sys.exit(r.returncode)
+        runs.append(json.loads(r.stdout.strip().splitlines()[-1]))
+    sp = np.array([x["value"] for x in runs])
+    de = np.array([x["dense"]["us_per_step_layer"] for x in runs])
+    ratio = de / sp
+    rng = np.random.default_rng(0)
+    boot = np.median(ratio[rng.integers(0, len(ratio), size=(4000, len(ratio)))], axis=1)
+    boot_sp = np.median(sp[rng.integers(0, len(sp), size=(4000, len(sp)))], axis=1)
+    result = runs[int(np.argsort(sp)[len(sp) // 2])]
+    result["value"] = round(float(np.median(sp)), 3)
+    result["ms_per_step"] = round(result["value"] / 1e3, 6)
+    result["blocks"] = {
+        "n": len(runs),
+        "sparse_us": [round(float(x), 3) for x in sp],
+        "dense_us": [round(float(x), 3) for x in de],
+        "speedup_paired": [round(float(x), 3) for x in ratio],
+        "speedup_median": round(float(np.median(ratio)), 3),
+        "speedup_interval_95": [round(float(np.percentile(boot, 2.5)), 3),
+                                round(float(np.percentile(boot, 97.5)), 3)],
+        "sparse_us_interval_95": [round(float(np.percentile(boot_sp, 2.5)), 3),
+                                  round(float(np.percentile(boot_sp, 97.5)), 3)],
+        "note": "value = median over fresh-process blocks; intervals from resampling the blocks "
+                "(median of each resample), the speedup paired within each block",
+    }
+    return result
 
 
 # ----------------------------------------------------------------------------
@@ -291,8 +774,17 @@ def main():
     ap.add_argument("--steps", type=int, default=800, help="decode-step-layers timed")
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="l8b", choices=sorted(WORKLOADS))
-    ap.add_argument("--layers", type=int, default=0, help="distinct layer caches (0 = auto)")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="distinct layer caches (0 = enough that 4x the Infinity Cache of other "
+                         "layers is read between two reads of one layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-points", action="store_true",
+                    help="time only the main workload (not the other 32K-1M points)")
+    ap.add_argument("--points", default=",".join(POINTS),
+                    help="comma-separated workloads timed after the main one")
+    ap.add_argument("--blocks", type=int, default=1,
+                    help="N > 1: N fresh processes, paired dense/sparse ratios with a "
+                         "resampled interval")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead")
     ap.add_argument("--selection", default="topk",
                     choices=["topk", "window", "init_local_topk", "mass_budget"],
@@ -330,294 +822,102 @@ def main():
               "by sequence or by KV head with no exchange); use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    import torch
-    import kvsynth
-    import sparse_kv_cache_sd_amd as sd
-
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    torch.cuda.set_device(0)
-    sd.lib()  # fail loudly if the HIP library is missing
-    if args.copy_calibrate:
-        copy_calibration()
-
-    rname, over, unit, r_kv, desc = WORKLOADS[args.workload]
-    if args.r_kv > 0:
-        r_kv = args.r_kv
-        desc += f"; r_KV overridden to {r_kv:g}"
-    rec = kvsynth.RECIPES[rname].with_(**over)
-    P, d, H_q, H_kv = rec.page_size, rec.head_dim, rec.num_q_heads, rec.num_kv_heads
-    elem = 2 if rec.dtype == "bf16" else 4
-
-    # ---- layer caches
-    w0 = kvsynth.generate(rec)
-    dense_layer = H_kv * int(np.sum(w0.seq_lens)) * 2 * d * elem
-    L = args.layers or max(1, math.ceil(4 * MALL_BYTES / dense_layer))
-    L = min(L, 16)
-    log(f"workload {args.workload}: {desc}; {L} layer caches of {dense_layer / 1e6:.1f} MB")
-    dt = torch.bfloat16 if rec.dtype == "bf16" else torch.float32
-
-    def dev(a):
-        if rec.dtype == "bf16":
-            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
-        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
-
-    # Every layer has its own K/V pool and query; the sequences' block table
-    # and lengths are shared by all layers, as in a serving engine.
-    layers = []
-    bt_host = None
-    for i in range(L):
-        w = w0 if i == 0 else kvsynth.generate(rec.with_(seed=rec.seed + 100 * i),
-                                               seq_lens=w0.seq_lens)
-        pc = w.paged(block_table=bt_host)
-        if bt_host is None:
-            bt_host = pc.block_table
-            bt_dev = torch.from_numpy(bt_host).cuda()
-            sl_dev = torch.from_numpy(w0.seq_lens).cuda()
-        lay = dict(q=dev(w.q), k=dev(pc.k_pool), v=dev(pc.v_pool), bt=bt_dev, sl=sl_dev,
-                   num_pages=pc.num_pages)
-        del pc
-        if i > 0:
-            del w
-        layers.append(lay)
-        log(f"layer {i} resident")
-    num_pages = layers[0]["num_pages"]
-    shape = sd.Shape(rec.batch, H_q, H_kv, d, P, w0.max_pages(), w0.n_alloc, rec.dtype, num_pages)
-    for lay in layers:
-        if args.scorer == "compressed":
-            lay["bounds"] = torch.empty(sd.compressed_keys_shape(shape), dtype=torch.float32,
-                                        device="cuda")
-            sd.update_compressed_keys(shape, lay["k"], lay["bt"], lay["sl"], lay["bounds"])
-        else:
-            lay["bounds"] = torch.empty(sd.bounds_shape(shape), dtype=dt, device="cuda")
-            sd.update_page_bounds(shape, lay["k"], lay["bt"], lay["sl"], lay["bounds"])
-    torch.cuda.synchronize()
-
     structured = args.selection != "topk" or args.scorer != "bounds"
-    local_units = args.local_units or (2048 // P if unit == "page" else 2048)
-    selection = sd.Selection(args.selection, r_kv,
-                             args.init_units if args.selection == "init_local_topk" else 0,
-                             local_units if args.selection == "init_local_topk" else 0,
-                             args.max_dropped if args.selection == "mass_budget" else 0.0,
-                             args.scorer)
-    if structured:
-        config_sel = {"selection": args.selection, "init_units": selection.init_units,
-                      "local_units": selection.local_units,
-                      "max_dropped": selection.max_dropped, "scorer": args.scorer}
-        desc += f"; kept set: {args.selection}" + {
-            "init_local_topk": f" ({selection.init_units} initial + {selection.local_units} "
-                               f"local units + top-k)",
-            "window": " (most recent units)",
-            "mass_budget": f" (at most {selection.max_dropped:g} of each head's mass dropped, "
-                           f"capped at r_KV)",
-            "topk": ""}[args.selection]
-        if args.scorer == "compressed":
-            desc += "; pages scored from compressed keys (mean-pooled, kernel 32 stride 16)"
     entmax = args.attention == "entmax"
-    if entmax:
-        desc += f"; {args.alpha:g}-entmax attention over the kept set (dense: every unit)"
-    k_max = sd.selection_capacity(selection, shape.units_max(unit))
-    ws = sd.alloc_workspace_sel(shape, unit, selection)
-    ws_dense = sd.alloc_workspace(shape, unit, 1.0)
-    dense_sel = sd.Selection("topk", 1.0)
-    if entmax:
-        ws = sd.alloc_workspace_entmax(shape, unit, selection)
-        ws_dense = sd.alloc_workspace_entmax(shape, unit, dense_sel)
-        tau = torch.empty((rec.batch, H_q), dtype=torch.float32, device="cuda")
-    out = torch.empty((rec.batch, H_q, d), dtype=torch.float32, device="cuda")
-    lse = torch.empty((rec.batch, H_q), dtype=torch.float32, device="cuda")
-    sels = [torch.empty((rec.batch, H_kv, k_max), dtype=torch.int32, device="cuda") for _ in range(L)]
-    cnts = [torch.empty((rec.batch, H_kv), dtype=torch.int32, device="cuda") for _ in range(L)]
-    stream = torch.cuda.Stream()
+    if args.blocks > 1:
+        result = run_blocks(args, sys.argv[1:])
+        w0 = None
+    else:
+        import torch
+        import kvsynth
+        import sparse_kv_cache_sd_amd as sd
 
-    def sparse_step(i):
-        lay = layers[i]
+        assert torch.cuda.is_available(), "bench.py needs a GPU"
+        torch.cuda.set_device(0)
+        sd.lib()  # fail loudly if the HIP library is missing
+        if args.copy_calibrate:
+            copy_calibration()
+        stream = torch.cuda.Stream()
+        res, w0 = measure_workload(args.workload, args, torch, sd, kvsynth, stream,
+                                   selection_kind=args.selection, scorer=args.scorer,
+                                   entmax=entmax, main=True)
+        page_plain = res["shape"]["unit"] == "page" and not structured and not entmax
+        result = {
+            "metric": METRIC,
+            "value": res["us_per_step_layer"],
+            "unit": "us/step-layer",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": round(res["us_per_step_layer"] / 1e3, 6),
+            "higher_is_better": False,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": kvsynth.RECIPES[WORKLOADS[args.workload][0]].dtype,
+            "data": "synthetic",
+            "config": {"workload": res["desc"], **res["shape"],
+                       "layer_caches": res["layer_caches"],
+                       "sparse_footprint_bytes": res["sparse_footprint_bytes"],
+                       "timing": "eager" if args.no_graph else "hip-graph",
+                       **res["config_sel"]},
+            "kept_tokens_per_step": res["kept_tokens_per_step"],
+            "effective_gbps": res["effective_gbps"],
+            "pct_hbm_roofline": res["pct_hbm_roofline"],
+            "algorithmic_bytes_per_step": res["algorithmic_bytes_per_step"],
+            "dense": res["dense"],
+            "speedup_vs_dense": res["speedup_vs_dense"],
+            "byte_bound_speedup": res["byte_bound_speedup"],
+            "roofline": {
+                "kernel": ("whole alpha-entmax decode step (sd_decode_step_entmax)" if entmax else
+                           "attend_mfma_kernel: split-K attention partials over the stored kept "
+                           "lists" if structured else
+                           "attend_mfma_kernel: in-kernel top-k + split-K attention partials "
+                           "over the kept pages" if res["shape"]["unit"] == "page" else
+                           "attend_mfma_kernel: split-K attention partials over the kept tokens "
+                           "(stored logits)"),
+                "bound": "hbm", "achieved": res["attend"]["achieved_gbps"],
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": res["attend"]["frac"],
+                "traffic": read_traffic(args.workload) if page_plain else None,
+                "us_per_launch": res["attend"]["us_per_launch"],
+                "bytes_per_launch": res["attend"]["bytes_per_launch"],
+            },
+        }
+        if "eager_us_per_step_layer" in res:
+            result["eager_us_per_step_layer"] = res["eager_us_per_step_layer"]
+        if "dropped_mass" in res:
+            result["dropped_mass"] = res["dropped_mass"]
         if entmax:
-            sd.decode_step_entmax(shape, lay["q"], lay["k"], lay["v"], lay["bounds"], lay["bt"],
-                                  lay["sl"], unit, selection, args.alpha, out, ws, tau=tau,
-                                  sel_idx=sels[i], sel_count=cnts[i], stream=stream)
-        elif structured:
-            sd.decode_step_sel(shape, lay["q"], lay["k"], lay["v"], lay["bounds"], lay["bt"],
-                               lay["sl"], unit, selection, out, lse, ws, sels[i], cnts[i],
-                               stream=stream)
-        else:
-            sd.decode_step(shape, lay["q"], lay["k"], lay["v"], lay["bounds"], lay["bt"],
-                           lay["sl"], unit, r_kv, out, lse, ws, sels[i], cnts[i], stream=stream)
-
-    def dense_step(i):
-        lay = layers[i]
-        if entmax:
-            sd.decode_step_entmax(shape, lay["q"], lay["k"], lay["v"], None, lay["bt"], lay["sl"],
-                                  unit, dense_sel, args.alpha, out, ws_dense, tau=tau,
-                                  stream=stream)
-        else:
-            sd.decode_step(shape, lay["q"], lay["k"], lay["v"], None, lay["bt"], lay["sl"],
-                           unit, 1.0, out, lse, ws_dense, stream=stream)
-
-    # scores of every layer, for timing the attention stage on its own
-    umax = shape.units_max(unit)
-    scores = [torch.empty((rec.batch, H_kv, umax), dtype=torch.float32, device="cuda")
-              for _ in range(L)]
-    logits = [torch.empty((rec.batch, H_q, shape.max_seq_len), dtype=torch.float32, device="cuda")
-              if unit == "token" else None for _ in range(L)]
-    for i, lay in enumerate(layers):
-        if args.scorer == "compressed":
-            sd.score_compressed(shape, lay["q"], lay["bounds"], lay["sl"], scores[i], stream=stream)
-        else:
-            sd.score_pages(shape, lay["q"], lay["k"], lay["bounds"], lay["bt"], lay["sl"], unit,
-                           scores[i], logits[i], stream=stream)
-    torch.cuda.synchronize()
-
-    def attend_only(i):
-        """The split-K attention kernel alone (one launch), as the decode step
-        runs it: page unit selects inside the attention kernel; token unit
-        attends the stored selection with the stored logits."""
-        lay = layers[i]
-        if structured:
-            sd.attend_partials(shape, lay["q"], lay["k"], lay["v"], lay["bt"], lay["sl"], unit, ws,
-                               sel_idx=sels[i], sel_count=cnts[i],
-                               token_logits=logits[i] if args.selection != "window" else None,
-                               stream=stream)
-        elif unit == "page":
-            sd.attend_partials(shape, lay["q"], lay["k"], lay["v"], lay["bt"], lay["sl"], unit, ws,
-                               unit_scores=scores[i], r_kv=r_kv, stream=stream)
-        else:
-            sd.attend_partials(shape, lay["q"], lay["k"], lay["v"], lay["bt"], lay["sl"], unit, ws,
-                               sel_idx=sels[i], sel_count=cnts[i], token_logits=logits[i],
-                               stream=stream)
-
-    def timed(fn, steps, warmup, graph):
-        """Mean microseconds per call of fn(layer) over `steps` calls cycling layers."""
-        with torch.cuda.stream(stream):
-            for i in range(warmup):
-                fn(i % L)
-            torch.cuda.synchronize()
-            reps = max(1, steps // L)
-            if graph:
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=stream):
-                    for i in range(L):
-                        fn(i)
-                g.replay()
-                torch.cuda.synchronize()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            e0.record(stream)
-            for _ in range(reps):
-                if graph:
-                    g.replay()
-                else:
-                    for i in range(L):
-                        fn(i)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            return e0.elapsed_time(e1) * 1e3 / (reps * L), reps * L
-
-    graph = not args.no_graph
-    # warm selections so attend_only has valid inputs
-    with torch.cuda.stream(stream):
-        for i in range(L):
-            sparse_step(i)
-    torch.cuda.synchronize()
-
-    us_sparse, n_steps = timed(sparse_step, args.steps, args.warmup, graph)
-    log(f"sparse step: {us_sparse:.2f} us/step-layer over {n_steps} steps ({'graph' if graph else 'eager'})")
-    us_dense, _ = timed(dense_step, args.steps, args.warmup, graph)
-    log(f"dense step:  {us_dense:.2f} us/step-layer")
-    if not entmax:
-        us_attend, n_att = timed(attend_only, args.steps, args.warmup, graph)
-        log(f"attend alone (HIP events on its stream): {us_attend:.2f} us/launch")
-    us_sparse_eager, _ = timed(sparse_step, min(args.steps, 400), 10, False)
-    log(f"sparse step eager: {us_sparse_eager:.2f} us/step-layer")
-
-    # bytes from the actual selections
-    kept = []
-    for i in range(L):
-        kept.append(kept_token_count(sels[i].cpu().numpy(), cnts[i].cpu().numpy(),
-                                     w0.seq_lens, unit, P))
-    kept_mean = float(np.mean(kept))
-    window = args.selection == "window"
-    b_sparse = algorithmic_bytes(w0.seq_lens, H_q, H_kv, d, P, elem, unit, r_kv, kept_mean,
-                                 window=window)
-    if unit == "page" and args.scorer == "compressed" and not window:
-        b_sparse += (algorithmic_stats_bytes(w0.seq_lens, H_kv, d, P, elem, "compressed") -
-                     algorithmic_stats_bytes(w0.seq_lens, H_kv, d, P, elem, "bounds"))
-    b_dense = algorithmic_bytes(w0.seq_lens, H_q, H_kv, d, P, elem, unit, 1.0, 0)
-    b_attend = attend_bytes(kept_mean, d, elem, unit == "token" and not window)
-    gbps = b_sparse / (us_sparse * 1e-6) / 1e9
-    gbps_dense = b_dense / (us_dense * 1e-6) / 1e9
-    if entmax:
-        # The entmax step is several launches (scores, selection, logits of
-        # the kept tokens, thresholds, attention, merge) behind one entry
-        # point, so the roofline here is that of the whole step on its
-        # algorithmic bytes; per-kernel durations come from a kernel trace.
-        us_attend, b_attend = us_sparse, b_sparse
-    gbps_att = b_attend / (us_attend * 1e-6) / 1e9
-
-    result = {
-        "metric": METRIC,
-        "value": round(us_sparse, 3),
-        "unit": "us/step-layer",
-        "n_gpus": 1,
-        "steps": n_steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(us_sparse / 1e3, 6),
-        "higher_is_better": False,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": rec.dtype,
-        "data": "synthetic",
-        "config": {
-            "workload": desc,
-            "batch": rec.batch, "num_q_heads": H_q, "num_kv_heads": H_kv, "head_dim": d,
-            "page_size": P, "context": int(w0.seq_lens.max()), "unit": unit, "r_kv": r_kv,
-            "k_per_kv_head": k_max, "layer_caches": L, "timing": "hip-graph" if graph else "eager",
-        },
-        "kept_tokens_per_step": round(kept_mean, 1),
-        "effective_gbps": round(gbps, 1),
-        "pct_hbm_roofline": round(100 * gbps / HBM_PEAK_GBPS, 1),
-        "algorithmic_bytes_per_step": int(b_sparse),
-        "dense": {"us_per_step_layer": round(us_dense, 3), "effective_gbps": round(gbps_dense, 1),
-                  "pct_hbm_roofline": round(100 * gbps_dense / HBM_PEAK_GBPS, 1),
-                  "bytes_per_step": int(b_dense)},
-        "speedup_vs_dense": round(us_dense / us_sparse, 3),
-        "byte_bound_speedup": round(b_dense / b_sparse, 3),
-        "eager_us_per_step_layer": round(us_sparse_eager, 3),
-        "roofline": {
-            "kernel": ("whole alpha-entmax decode step (sd_decode_step_entmax)" if entmax else
-                       "attend_mfma_kernel: split-K attention partials over the stored kept "
-                       "lists" if structured else
-                       "attend_mfma_kernel: in-kernel top-k + split-K attention partials over "
-                       "the kept pages" if unit == "page" else
-                       "attend_mfma_kernel: split-K attention partials over the kept tokens "
-                       "(stored logits)"),
-            "bound": "hbm", "achieved": round(gbps_att, 1), "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s", "frac": round(gbps_att / HBM_PEAK_GBPS, 4),
-            "traffic": (read_traffic(args.workload)
-                        if unit == "page" and not structured and not entmax else None),
-            "us_per_launch": round(us_attend, 3), "bytes_per_launch": int(b_attend),
-        },
-    }
-    if unit == "token" and not entmax and shape.max_seq_len <= 262144:
-        # dropped dense softmax mass of layer 0's kept lists (token unit: every
-        # logit is stored, so the library computes it on the GPU)
-        delta = torch.empty((rec.batch, H_q), dtype=torch.float32, device="cuda")
-        sd.dropped_mass(shape, layers[0]["sl"], layers[0]["bt"], logits[0], sels[0], cnts[0],
-                        delta, stream=stream)
-        torch.cuda.synchronize()
-        dl = delta.cpu().numpy()
-        result["dropped_mass"] = {"mean": round(float(dl.mean()), 5),
-                                  "max": round(float(dl.max()), 5),
-                                  "of": "layer 0, every query head (sd_dropped_mass)"}
+            result["config"].update({"attention": "entmax", "alpha": args.alpha})
+        if not args.no_points and not structured and not entmax:
+            pts = []
+            cache = {}
+            for name in [p for p in args.points.split(",") if p and p != args.workload]:
+                key = (WORKLOADS[name][0], tuple(sorted(WORKLOADS[name][1].items())))
+                pres, wl = measure_workload(name, args, torch, sd, kvsynth, stream,
+                                            w0=cache.get(key))
+                cache = {key: wl}         # keep one drawn workload (the 128K pair shares it)
+                pts.append(point_summary(pres))
+            del cache
+            result["points"] = pts
     if not args.no_cpu_baseline:
+        import kvsynth
         log("timing the CPU oracle on a bounded sample ...")
-        result["cpu_baseline"] = cpu_baseline(
-            w0, unit, r_kv, selection=None if not structured else sdref_selection(selection),
-            scorer=args.scorer, alpha=args.alpha if entmax else None)
-    if structured:
-        result["config"].update(config_sel)
-    if entmax:
-        result["config"].update({"attention": "entmax", "alpha": args.alpha})
+        if w0 is None:
+            rname, over = WORKLOADS[args.workload][:2]
+            w0 = kvsynth.generate(kvsynth.RECIPES[rname].with_(**over))
+        unit, r_kv = WORKLOADS[args.workload][2], args.r_kv or WORKLOADS[args.workload][3]
+        sel = None
+        if structured:
+            import sparse_kv_cache_sd_amd as sd
+            P = w0.recipe.page_size
+            sel = sdref_selection(sd.Selection(
+                args.selection, r_kv,
+                args.init_units if args.selection == "init_local_topk" else 0,
+                (args.local_units or (2048 // P if unit == "page" else 2048))
+                if args.selection == "init_local_topk" else 0,
+                args.max_dropped if args.selection == "mass_budget" else 0.0, args.scorer))
+        result["cpu_baseline"] = cpu_baseline(w0, unit, r_kv, selection=sel, scorer=args.scorer,
+                                              alpha=args.alpha if entmax else None)
     print(json.dumps(result), flush=True)
 
 

@@ -131,3 +131,19 @@ def test_gpus_other_than_one_are_refused():
     r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+@pytest.mark.parametrize("step_mb", [35.4, 48.7, 80.6, 282.1, 349.0, 1021.6, 5000.0])
+def test_layer_count_keeps_a_layer_out_of_the_infinity_cache(step_mb):
+    """Between two reads of one layer the other L - 1 layers' sparse steps
+    read at least 4x the 256 MiB Infinity Cache."""
+    b = int(step_mb * 1e6)
+    L = bench.layers_for(b)
+    assert L >= 2 and (L - 1) * b >= 4 * bench.MALL_BYTES
+    assert (L - 2) * b < 4 * bench.MALL_BYTES or L == 2
+
+
+def test_block_children_drop_blocks_and_extras():
+    argv = ["--steps", "20", "--blocks", "5", "--workload", "l8b", "--blocks=3"]
+    assert bench.child_args(argv) == ["--steps", "20", "--workload", "l8b",
+                                      "--no-cpu-baseline", "--no-points"]
