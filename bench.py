@@ -131,7 +131,7 @@ def kept_token_count(sel, cnt, seq_lens, unit, P):
 # HBM traffic of the dominant kernel from committed rocprofv3 counter passes
 # ----------------------------------------------------------------------------
 
-KERNEL_SOURCES = ["attend.hip", "topk.h", "device.h", "kernels.h"]
+KERNEL_SOURCES = ["attend.hip", "score.hip", "topk.h", "device.h", "kernels.h"]
 COPY_BYTES = 1 << 30            # one plain copy: 1 GiB read + 1 GiB written
 
 
@@ -144,14 +144,16 @@ def kernel_sources_sha():
 
 
 def traffic_file(workload):
-    return os.path.join(ROOT, "profiles", f"attend_mfma_{workload}_traffic.txt")
+    return os.path.join(ROOT, "profiles", f"decode_step_{workload}_traffic.txt")
 
 
-def read_traffic(workload):
-    """HBM bytes per launch of the attention kernel: FETCH_SIZE and WRITE_SIZE
-    (KiB per dispatch, rocprofv3 --pmc, one pass each) scaled by what the same
-    counters read for a plain 1 GiB copy.  None when no summary exists or the
-    kernel sources changed since the counters were taken."""
+def read_traffic(workload, tag="attend"):
+    """HBM bytes per launch of one kernel of the workload's step ("attend":
+    the attention kernel as the step runs it; "score", "dense", "merge"):
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch, rocprofv3 --pmc, one pass
+    each) scaled by what the same counters read for a plain 1 GiB copy.
+    None when no summary exists, it lacks the kernel, or the kernel sources
+    changed since the counters were taken."""
     path = traffic_file(workload)
     if not os.path.exists(path):
         return None
@@ -163,9 +165,24 @@ def read_traffic(workload):
                 kv[k.strip()] = v.strip()
     if kv.get("kernel_sources_sha256_16") != kernel_sources_sha():
         return None
-    f = float(kv["attend_fetch_kib_per_dispatch"]) * 1024 * float(kv["fetch_scale"])
-    w = float(kv["attend_write_kib_per_dispatch"]) * 1024 * float(kv["write_scale"])
+    if f"{tag}_fetch_kib_per_dispatch" not in kv:
+        return None
+    f = float(kv[f"{tag}_fetch_kib_per_dispatch"]) * 1024 * float(kv["fetch_scale"])
+    w = float(kv[f"{tag}_write_kib_per_dispatch"]) * 1024 * float(kv["write_scale"])
     return int(f + w)
+
+
+# the kernels a traffic summary covers, by workload unit: (tag, name pattern)
+PMC_KERNELS = {
+    "page": [("attend", r"attend_mfma_kernel<\d+, \d+, false, (4|8|32), 0>"),
+             ("score", r"score_pages(_mfma)?_kernel<"),
+             ("dense", r"attend_mfma_kernel<\d+, \d+, false, 0, 0>"),
+             ("merge", r"merge_splits_kernel<")],
+    "token": [("attend", r"attend_mfma_kernel<\d+, \d+, true, 0, 0>"),
+              ("score", r"score_tokens_(mfma|f32)_kernel<"),
+              ("dense", r"attend_mfma_kernel<\d+, \d+, false, 0, 0>"),
+              ("merge", r"merge_splits_kernel<")],
+}
 
 
 def copy_calibration():
@@ -183,9 +200,11 @@ def copy_calibration():
 
 def summarize_pmc(fetch_dir, write_dir, workload, out_path, cmd_fetch, cmd_write):
     """Writes the traffic summary from the counter_collection.csv files of
-    the two passes (attention kernel of the page-unit step vs. the copy)."""
+    the two passes: for each kernel of PMC_KERNELS[unit] its mean FETCH_SIZE
+    and WRITE_SIZE per dispatch, and the scales from the plain copy."""
     import csv
     import glob
+    import re
 
     def rows(d):
         files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
@@ -193,47 +212,55 @@ def summarize_pmc(fetch_dir, write_dir, workload, out_path, cmd_fetch, cmd_write
         out = []
         for f in files:
             with open(f) as fh:
-                out += [(r["Kernel_Name"], r["Grid_Size"], float(r["Counter_Value"]))
+                out += [(r["Kernel_Name"], r["Dispatch_Id"], float(r["Counter_Value"]))
                         for r in csv.DictReader(fh)]
         return out
 
     def mean(rs, pred):
-        v = [x for n, gsz, x in rs if pred(n, gsz)]
-        assert v, "kernel not found in the counter pass"
-        return sum(v) / len(v), len(v)
+        v = [x for n, did, x in rs if pred(n, did)]
+        return (sum(v) / len(v), len(v)) if v else (None, 0)
 
     fr, wr = rows(fetch_dir), rows(write_dir)
-    # the in-kernel-selection attention instance: attend_mfma_kernel<D, G,
-    # LOGITS = false, SEL in {4, 8, 32}, softmax weights>
-    import re
-    sel_inst = re.compile(r"attend_mfma_kernel<\d+, \d+, false, (4|8|32), 0>")
-    att = lambda n, gsz: sel_inst.search(n) is not None
-    af, an = mean(fr, att)
-    aw, _ = mean(wr, att)
-    # the plain copy: the blit dispatches with the grid of the 1 GiB copy, whose
-    # write counter is the largest of the process
-    copy_grid = max((x, gsz) for n, gsz, x in wr if "copyBuffer" in n)[1]
-    cp = lambda n, gsz: "copyBuffer" in n and gsz == copy_grid
-    cf, _ = mean(fr, cp)
+    unit = WORKLOADS[workload][2] if workload in WORKLOADS else "page"
+    # the plain copy (--copy-calibrate): the blit dispatches that write exactly
+    # COPY_BYTES; the fetch pass runs the same program, so the same dispatch
+    # ids are the copy there (other device copies, e.g. of layer caches, write
+    # other amounts)
+    copy_ids = {did for n, did, x in wr
+                if "copyBuffer" in n and abs(x - COPY_BYTES / 1024) < 1.0}
+    assert copy_ids, "the calibration copy is not in the write pass"
+    cp = lambda n, did: "copyBuffer" in n and did in copy_ids
+    cf, nf = mean(fr, cp)
     cw, _ = mean(wr, cp)
-    anames = [n for n, _, _ in fr if att(n, None)]
+    assert nf == len(copy_ids), "the fetch pass's dispatch ids differ from the write pass's"
     lines = [
-        f"# HBM traffic of the in-kernel-selection attention kernel, workload {workload}",
+        f"# HBM traffic of the decode step's kernels, workload {workload}",
         "# FETCH_SIZE / WRITE_SIZE are KiB per dispatch (rocprofv3 --pmc, one counter per pass);",
         f"# the scales make a plain {COPY_BYTES} B device copy read and write exactly that.",
         f"# fetch pass: {cmd_fetch}",
         f"# write pass: {cmd_write}",
-        f"# kernels: {sorted(set(anames))[0][:120]}",
         f"kernel_sources_sha256_16 = {kernel_sources_sha()}",
-        f"attend_dispatches = {an}",
-        f"attend_fetch_kib_per_dispatch = {af:.1f}",
-        f"attend_write_kib_per_dispatch = {aw:.1f}",
         f"copy_bytes = {COPY_BYTES}",
         f"copy_fetch_kib_per_dispatch = {cf:.1f}",
         f"copy_write_kib_per_dispatch = {cw:.1f}",
         f"fetch_scale = {COPY_BYTES / (cf * 1024):.4f}",
         f"write_scale = {COPY_BYTES / (cw * 1024):.4f}",
     ]
+    found = 0
+    for tag, pat in PMC_KERNELS[unit]:
+        rx = re.compile(pat)
+        pred = lambda n, gsz, rx=rx: rx.search(n) is not None
+        af, an = mean(fr, pred)
+        aw, _ = mean(wr, pred)
+        if af is None or aw is None:
+            continue
+        names = sorted({n for n, _, _ in fr if pred(n, None)})
+        found += 1
+        lines += [f"# {tag}: {names[0][:120]}",
+                  f"{tag}_dispatches = {an}",
+                  f"{tag}_fetch_kib_per_dispatch = {af:.1f}",
+                  f"{tag}_write_kib_per_dispatch = {aw:.1f}"]
+    assert found, "none of the step's kernels is in the counter passes"
     with open(out_path, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -667,6 +694,7 @@ def measure_workload(name, args, torch, sd, kvsynth, stream, *, selection_kind="
         "attend": {"us_per_launch": round(us_attend, 3), "bytes_per_launch": int(b_attend),
                    "achieved_gbps": round(gbps_att, 1),
                    "frac": round(gbps_att / HBM_PEAK_GBPS, 4)},
+        "traffic": None if structured or entmax else read_traffic(name),
         "structured": structured,
         "config_sel": config_sel,
     }
@@ -698,6 +726,9 @@ def point_summary(res):
             "speedup_vs_dense": res["speedup_vs_dense"],
             "byte_bound_speedup": res["byte_bound_speedup"],
             "attend_us": a["us_per_launch"], "attend_frac": a["frac"],
+            "attend_traffic_bytes": res["traffic"],
+            "attend_traffic_ratio": (round(res["traffic"] / a["bytes_per_launch"], 3)
+                                     if res["traffic"] else None),
             "layer_caches": res["layer_caches"],
             "sparse_footprint_bytes": res["sparse_footprint_bytes"],
             **({"dropped_mass": res["dropped_mass"]} if "dropped_mass" in res else {})}
@@ -805,7 +836,7 @@ def main():
     ap.add_argument("--copy-calibrate", action="store_true",
                     help="run a plain 1 GiB copy first (for counter passes)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="write profiles/attend_mfma_<workload>_traffic.txt from two "
+                    help="write profiles/decode_step_<workload>_traffic.txt from two "
                          "rocprofv3 --pmc passes and exit")
     ap.add_argument("--pmc-commands", nargs=2, default=["?", "?"],
                     help="the two rocprofv3 command lines, recorded in the summary")
@@ -841,7 +872,6 @@ def main():
         res, w0 = measure_workload(args.workload, args, torch, sd, kvsynth, stream,
                                    selection_kind=args.selection, scorer=args.scorer,
                                    entmax=entmax, main=True)
-        page_plain = res["shape"]["unit"] == "page" and not structured and not entmax
         result = {
             "metric": METRIC,
             "value": res["us_per_step_layer"],
@@ -877,7 +907,7 @@ def main():
                            "(stored logits)"),
                 "bound": "hbm", "achieved": res["attend"]["achieved_gbps"],
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": res["attend"]["frac"],
-                "traffic": read_traffic(args.workload) if page_plain else None,
+                "traffic": res["traffic"],
                 "us_per_launch": res["attend"]["us_per_launch"],
                 "bytes_per_launch": res["attend"]["bytes_per_launch"],
             },

@@ -80,29 +80,30 @@ def test_kept_token_count_partial_last_page():
 
 
 def _write_pmc(path, rows):
+    """rows: dicts with Kernel_Name and Counter_Value; dispatch ids follow the
+    order of the list (the same program in both passes)."""
     os.makedirs(path, exist_ok=True)
     with open(os.path.join(path, "pmc_counter_collection.csv"), "w", newline="") as fh:
-        w = csv.DictWriter(fh, fieldnames=["Kernel_Name", "Grid_Size", "Counter_Value"])
+        w = csv.DictWriter(fh, fieldnames=["Kernel_Name", "Dispatch_Id", "Counter_Value"])
         w.writeheader()
-        for r in rows:
-            w.writerow(r)
+        for i, r in enumerate(rows):
+            w.writerow({"Kernel_Name": r["Kernel_Name"], "Dispatch_Id": str(i + 1),
+                        "Counter_Value": r["Counter_Value"]})
 
 
-def test_summarize_pmc_picks_the_selecting_instance(tmp_path, monkeypatch):
+def test_summarize_pmc_picks_the_step_kernels(tmp_path, monkeypatch):
     att = "void sdkv::attend_mfma_kernel<128, 4, false, 4, 0>(sdkv::AttendArgs)"
     dense = "void sdkv::attend_mfma_kernel<128, 4, false, 0, 0>(sdkv::AttendArgs)"
     ent = "void sdkv::attend_mfma_kernel<128, 4, false, 4, 2>(sdkv::AttendArgs)"
+    score = "void sdkv::score_pages_kernel<unsigned short, 128, 4>(unsigned short const*)"
     copy = "__amd_rocclr_copyBuffer"
     gib = bench.COPY_BYTES / 1024
-    fetch = [dict(Kernel_Name=att, Grid_Size=131072, Counter_Value=1000.0),
-             dict(Kernel_Name=att, Grid_Size=131072, Counter_Value=1200.0),
-             dict(Kernel_Name=dense, Grid_Size=131072, Counter_Value=9999.0),
-             dict(Kernel_Name=ent, Grid_Size=131072, Counter_Value=7777.0),
-             dict(Kernel_Name=copy, Grid_Size=4096, Counter_Value=gib / 2),
-             dict(Kernel_Name=copy, Grid_Size=64, Counter_Value=1.0)]
-    write = [dict(Kernel_Name=att, Grid_Size=131072, Counter_Value=50.0),
-             dict(Kernel_Name=copy, Grid_Size=4096, Counter_Value=gib),
-             dict(Kernel_Name=copy, Grid_Size=64, Counter_Value=1.0)]
+    # the same dispatch order in both passes: the 1 GiB calibration copy,
+    # a smaller copy (a layer cache), then the step's kernels
+    order = [(copy, gib / 2, gib), (copy, 1.0, 8.0), (att, 1000.0, 50.0), (att, 1200.0, 50.0),
+             (dense, 9999.0, 70.0), (ent, 7777.0, 1.0), (score, 300.0, 8.0)]
+    fetch = [dict(Kernel_Name=n, Counter_Value=f) for n, f, _ in order]
+    write = [dict(Kernel_Name=n, Counter_Value=w) for n, _, w in order]
     _write_pmc(str(tmp_path / "f"), fetch)
     _write_pmc(str(tmp_path / "w"), write)
     out = str(tmp_path / "summary.txt")
@@ -111,6 +112,9 @@ def test_summarize_pmc_picks_the_selecting_instance(tmp_path, monkeypatch):
               and not l.startswith("#"))
     assert float(kv["attend_fetch_kib_per_dispatch"]) == 1100.0   # mean of the selecting instance
     assert float(kv["attend_write_kib_per_dispatch"]) == 50.0
+    assert float(kv["dense_fetch_kib_per_dispatch"]) == 9999.0
+    assert float(kv["score_write_kib_per_dispatch"]) == 8.0
+    assert "merge_fetch_kib_per_dispatch" not in kv                # not in the passes
     assert abs(float(kv["fetch_scale"]) - 2.0) < 1e-3            # the copy's fetch reads half
     assert abs(float(kv["write_scale"]) - 1.0) < 1e-3
     # the summary is read back only while the kernel sources are unchanged
@@ -118,11 +122,30 @@ def test_summarize_pmc_picks_the_selecting_instance(tmp_path, monkeypatch):
     # FETCH and WRITE KiB per dispatch, each scaled by the copy's factor (the
     # scales are stored to four decimals)
     assert abs(bench.read_traffic("l8b") - (1100 * 1024 * 2.0 + 50 * 1024)) < 1024
+    assert abs(bench.read_traffic("l8b", "score") - (300 * 1024 * 2.0 + 8 * 1024)) < 1024
+    assert bench.read_traffic("l8b", "merge") is None
     stale = str(tmp_path / "stale.txt")
     with open(stale, "w") as fh:
         fh.write(open(out).read().replace(bench.kernel_sources_sha(), "0" * 16))
     monkeypatch.setattr(bench, "traffic_file", lambda wl: stale)
     assert bench.read_traffic("l8b") is None
+
+
+def test_summarize_pmc_token_attention_instance(tmp_path):
+    att = "void sdkv::attend_mfma_kernel<128, 4, true, 0, 0>(sdkv::AttendArgs)"
+    sel = "void sdkv::attend_mfma_kernel<128, 4, false, 4, 0>(sdkv::AttendArgs)"
+    copy = "__amd_rocclr_copyBuffer"
+    gib = bench.COPY_BYTES / 1024
+    rows = [dict(Kernel_Name=copy, Counter_Value=gib),
+            dict(Kernel_Name=att, Counter_Value=10.0),
+            dict(Kernel_Name=sel, Counter_Value=99.0)]
+    _write_pmc(str(tmp_path / "f"), rows)
+    _write_pmc(str(tmp_path / "w"), rows)
+    out = str(tmp_path / "s.txt")
+    bench.summarize_pmc(str(tmp_path / "f"), str(tmp_path / "w"), "sweep128k-0.3", out, "f", "w")
+    kv = dict(l.split(" = ", 1) for l in open(out).read().splitlines() if " = " in l
+              and not l.startswith("#"))
+    assert float(kv["attend_fetch_kib_per_dispatch"]) == 10.0
 
 
 def test_gpus_other_than_one_are_refused():
