@@ -321,8 +321,9 @@ char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 
 sd_status do_score(const sdkv::Dims& d, const void* q, const void* k_pages, const void* bounds,
                    const int32_t* bt, const int32_t* sl, int unit, float* scores, float* logits,
-                   hipStream_t st, uint32_t* score_mm = nullptr) {
+                   hipStream_t st, uint32_t* score_mm = nullptr, bool logits_tm = false) {
   sdkv::ScoreArgs a{d, unit, q, k_pages, bounds, bt, sl, scores, logits, score_mm};
+  a.logits_tm = logits_tm ? 1 : 0;
   return device_status(sdkv::launch_score(a, st), "score kernel launch");
 }
 
@@ -401,7 +402,8 @@ sd_status do_partials(const sdkv::Dims& d, const void* q, const void* kp, const 
                       const int32_t* sel_count, int k_max, const float* logits, void* ws,
                       hipStream_t st, const float* unit_scores = nullptr, int R_ppm = -1,
                       int32_t* sel_out = nullptr, int32_t* sel_count_out = nullptr,
-                      int* S_out = nullptr, ListMode lm = ListMode{}, Weights wt = Weights{}) {
+                      int* S_out = nullptr, ListMode lm = ListMode{}, Weights wt = Weights{},
+                      bool logits_tm = false) {
   const bool listed = sel_idx != nullptr || unit_scores != nullptr || lm.window;
   const int64_t kk = listed ? k_max : units_max(d, unit);
   const Split sp = plan_split(d, unit, kk);
@@ -418,6 +420,7 @@ sd_status do_partials(const sdkv::Dims& d, const void* q, const void* kp, const 
   a.sel_count = sel_count;
   a.k_max = listed ? k_max : 0;
   a.token_logits = logits;
+  a.logits_tm = logits_tm ? 1 : 0;
   a.E = sp.E;
   a.S = sp.S;
   a.part_o = reinterpret_cast<float*>(at(ws, L.part_o));
@@ -569,10 +572,15 @@ sd_status decode_impl(const sdkv::Dims& d, const void* q, const void* k_pages,
   uint32_t* smm = unit == SD_UNIT_TOKEN && multi_select(d, unit)
                       ? reinterpret_cast<uint32_t*>(at(ws, L.score_mm))
                       : nullptr;
+  // the logits stay inside this step unless the budget reads them: then
+  // they are laid out token-major (whole-line writes, one piece per kept
+  // token when the attention pass reads them)
+  const bool tm = unit == SD_UNIT_TOKEN && sel.kind != SD_SEL_MASS_BUDGET;
   if (unit == SD_UNIT_PAGE && sel.scorer == SD_SCORER_COMPRESSED)
     st = do_score_compressed(d, q, static_cast<const float*>(page_bounds), seq_lens, scores, s);
   else
-    st = do_score(d, q, k_pages, page_bounds, block_table, seq_lens, unit, scores, logits, s, smm);
+    st = do_score(d, q, k_pages, page_bounds, block_table, seq_lens, unit, scores, logits, s, smm,
+                  tm);
   if (st != SD_OK) return st;
   if (unit == SD_UNIT_PAGE)
     return do_select_attend(d, q, k_pages, v_pages, block_table, seq_lens, scores, sel, out, lse,
@@ -584,7 +592,8 @@ sd_status decode_impl(const sdkv::Dims& d, const void* q, const void* k_pages,
                            reinterpret_cast<int32_t*>(at(ws, L.topk_cnt)), s, smm)) != SD_OK)
     return st;
   if ((st = do_partials(d, q, k_pages, v_pages, block_table, seq_lens, unit, idx, cnt, k_max,
-                        logits, ws, s, nullptr, -1, nullptr, nullptr, &S)) != SD_OK)
+                        logits, ws, s, nullptr, -1, nullptr, nullptr, &S, ListMode{}, Weights{},
+                        tm)) != SD_OK)
     return st;
   return do_merge(d, out, lse, ws, s, S);
 }

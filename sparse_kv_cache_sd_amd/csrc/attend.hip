@@ -331,10 +331,14 @@ __global__ __launch_bounds__(kAttendWaves * 64) void attend_mfma_kernel(AttendAr
   const float qs = d.scale * kLog2e;
   // a valid row-sized address for loads of rows that are not attended
   const bf16_t* qrow0 = static_cast<const bf16_t*>(a.q) + ((int64_t)b * d.Hq + g * G) * D;
-  // stored logits of head `row` of the group (token unit)
+  // stored logits of head `row` of the group (token unit): token t's is
+  // logit_row[t * logit_st] (the public [B][Hq][max_seq] layout, or
+  // token-major [B][Hkv][max_seq][G] inside a decode step)
   const float* logit_row =
-      LOGITS ? a.token_logits + ((int64_t)b * d.Hq + g * G + min(row, G - 1)) * d.max_seq
-             : nullptr;
+      !LOGITS ? nullptr
+      : a.logits_tm ? a.token_logits + ((int64_t)b * d.Hkv + g) * d.max_seq * G + min(row, G - 1)
+                    : a.token_logits + ((int64_t)b * d.Hq + g * G + min(row, G - 1)) * d.max_seq;
+  const int logit_st = a.logits_tm ? G : 1;
 
   float4_t acc[CT];
 #pragma unroll
@@ -482,7 +486,7 @@ __global__ __launch_bounds__(kAttendWaves * 64) void attend_mfma_kernel(AttendAr
             int t = s_tok[TOK ? wave : 0][min(c, RW - 1)][4 * quad + r];
             t = t < 0 ? 0 : (t >= d.max_seq ? d.max_seq - 1 : t);
             tt[i][r] = t;
-            if constexpr (LOGITS) ll[i][r] = logit_row[t];
+            if constexpr (LOGITS) ll[i][r] = logit_row[(int64_t)t * logit_st];
             else ll[i][r] = 0.f;
           }
         }
@@ -610,7 +614,9 @@ __global__ __launch_bounds__(kAttendWaves * 64) void attend_f32_kernel(AttendArg
     if (use_logits) {
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float z = ok ? a.token_logits[((int64_t)b * d.Hq + g * G + h) * d.max_seq + t] : 0.f;
+        const int64_t at = a.logits_tm ? (((int64_t)b * d.Hkv + g) * d.max_seq + t) * G + h
+                                       : ((int64_t)b * d.Hq + g * G + h) * d.max_seq + t;
+        const float z = ok ? a.token_logits[at] : 0.f;
         s[h] = ent ? z : z * kLog2e;
       }
     } else {

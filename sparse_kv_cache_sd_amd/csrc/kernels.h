@@ -44,10 +44,14 @@ struct ScoreArgs {
   const int32_t* block_table;
   const int32_t* seq_lens;
   float* unit_scores;   // [B][Hkv][U_max]
-  float* token_logits;  // [B][Hq][max_seq] (token unit)
+  float* token_logits;  // [B][Hq][max_seq] (token unit), or token-major (below)
   // Optional (token unit): per scoring block, the min and max order keys of
   // its valid unit scores, [B*Hkv][ceil(max_seq / score_units_per_block)][2].
   uint32_t* score_mm;
+  // Token unit: logits_tm != 0 lays token_logits out token-major,
+  // [B][Hkv][max_seq][G] (the G logits of a token adjacent), for readers
+  // inside one decode step; 0 is the public [B][Hq][max_seq].
+  int logits_tm = 0;
 };
 
 // Units one token-scoring block covers (the stride of ScoreArgs::score_mm).
@@ -77,6 +81,7 @@ struct AttendArgs {
   const int32_t* sel_count;
   int k_max;
   const float* token_logits;  // token unit: read logits instead of q.K
+  int logits_tm;              // token_logits token-major (ScoreArgs::logits_tm)
   int E;                      // kept units per split
   int S;                      // splits per (sequence, KV head), <= kMaxSplits
   float* part_o;              // [B][Hq][S][D]  split outputs, normalised

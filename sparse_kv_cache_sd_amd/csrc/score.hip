@@ -217,7 +217,8 @@ template <int D, int G>
 __global__ __launch_bounds__(kScoreThreads) void score_tokens_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k_pages,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
-    float* __restrict__ scores, float* __restrict__ logits, uint32_t* __restrict__ mm, Dims d) {
+    float* __restrict__ scores, float* __restrict__ logits, uint32_t* __restrict__ mm, Dims d,
+    int tm) {
   constexpr int LPR = D / 8;
   constexpr int RPW = 64 / LPR;
   constexpr int IT = kScoreIters;
@@ -274,7 +275,11 @@ __global__ __launch_bounds__(kScoreThreads) void score_tokens_f32_kernel(
     const int t = tt[it];
     if (t < n) {
       if (!ok[it]) { best = -3.0e38f; mine = -3.0e38f; }
-      if (cl < G) logits[((int64_t)b * d.Hq + g * G + cl) * d.max_seq + t] = mine;
+      if (cl < G) {
+        const int64_t at = tm ? (((int64_t)b * d.Hkv + g) * d.max_seq + t) * G + cl
+                              : ((int64_t)b * d.Hq + g * G + cl) * d.max_seq + t;
+        logits[at] = mine;
+      }
       if (cl == 0) sc[t] = best;
       kmn = min(kmn, order_key(best));
       kmx = max(kmx, order_key(best));
@@ -290,7 +295,11 @@ template <int D, int G>
 __global__ __launch_bounds__(kScoreThreads) void score_tokens_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_pages,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
-    float* __restrict__ scores, float* __restrict__ logits, uint32_t* __restrict__ mm, Dims d) {
+    float* __restrict__ scores, float* __restrict__ logits, uint32_t* __restrict__ mm, Dims d,
+    int tm) {
+  // token-major logits: a chunk's 16 x G values go through LDS so that they
+  // leave as whole consecutive pieces (16 G floats per chunk)
+  __shared__ __align__(16) float s_lg[kScoreThreads / 64][16 * G];
   constexpr int KS = D / 32;
   constexpr int IT = kTokenIters;
   constexpr int NW = kScoreThreads / 64;
@@ -338,7 +347,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_tokens_mfma_kernel(
   }
   __builtin_amdgcn_sched_barrier(0);
   float* sc = scores + ((int64_t)b * d.Hkv + g) * d.max_seq;
-  float* lg = logits + ((int64_t)b * d.Hq + g * G + row) * d.max_seq;
+  float* lg = logits + ((int64_t)b * d.Hq + g * G + min(row, G - 1)) * d.max_seq;
+  float* lg_tm = logits + ((int64_t)b * d.Hkv + g) * d.max_seq * G;
   uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
@@ -361,7 +371,33 @@ __global__ __launch_bounds__(kScoreThreads) void score_tokens_mfma_kernel(
         kmx = max(kmx, order_key(bs[r]));
       }
     }
-    if ((d.max_seq & 3) == 0 && t4 + 3 < n) {  // rows are 16-byte aligned
+    if (tm) {
+      // lane (row = head, quad) holds tokens 4 quad + r: stage [token][head],
+      // then lane i writes floats 4i .. 4i + 3 of the chunk (G >= 4: part of
+      // one token's G logits) or float i (G < 4), tokens past n left out
+      float* st_w = s_lg[wave];
+      if (row < G) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st_w[(4 * quad + r) * G + row] = xs[r];
+      }
+      __builtin_amdgcn_wave_barrier();
+      if constexpr (G >= 4) {
+        if (lane < 4 * G && tc[it] + (4 * lane) / G < n)
+          *reinterpret_cast<float4_t*>(lg_tm + (int64_t)tc[it] * G + 4 * lane) =
+              *reinterpret_cast<const float4_t*>(st_w + 4 * lane);
+      } else {
+        if (lane < 16 * G && tc[it] + lane / G < n)
+          lg_tm[(int64_t)tc[it] * G + lane] = st_w[lane];
+      }
+      __builtin_amdgcn_wave_barrier();
+      if ((d.max_seq & 3) == 0 && t4 + 3 < n) {
+        if (row == 0) *reinterpret_cast<float4_t*>(sc + t4) = bs;
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (t4 + r < n && row == 0) sc[t4 + r] = bs[r];
+      }
+    } else if ((d.max_seq & 3) == 0 && t4 + 3 < n) {  // rows are 16-byte aligned
       if (row < G) *reinterpret_cast<float4_t*>(lg + t4) = xs;
       if (row == 0) *reinterpret_cast<float4_t*>(sc + t4) = bs;
     } else {
@@ -411,13 +447,13 @@ hipError_t launch_score(const ScoreArgs& a, hipStream_t st) {
       const dim3 grid((d.max_seq + R - 1) / R * d.Hkv * d.B);
       score_tokens_f32_kernel<D, G><<<grid, kScoreThreads, 0, st>>>(
           static_cast<const float*>(a.q), static_cast<const float*>(a.k_pages), a.block_table,
-          a.seq_lens, a.unit_scores, a.token_logits, a.score_mm, d);
+          a.seq_lens, a.unit_scores, a.token_logits, a.score_mm, d, a.logits_tm);
     } else {
       constexpr int R = (kScoreThreads / 64) * kTokenIters * 16;
       const dim3 grid((d.max_seq + R - 1) / R * d.Hkv * d.B);
       score_tokens_mfma_kernel<D, G><<<grid, kScoreThreads, 0, st>>>(
           static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k_pages), a.block_table,
-          a.seq_lens, a.unit_scores, a.token_logits, a.score_mm, d);
+          a.seq_lens, a.unit_scores, a.token_logits, a.score_mm, d, a.logits_tm);
     }
   });
   if (!ok) return hipErrorInvalidValue;
