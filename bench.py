@@ -715,6 +715,45 @@ def measure_workload(name, args, torch, sd, kvsynth, stream, *, selection_kind="
     return res, w0
 
 
+def bounds_update_times(name, args, torch, sd, kvsynth, stream):
+    """Microseconds per call of the three forms of the page-statistics
+    update on one workload (graph replays of `steps` calls): a full rebuild,
+    the listed pages (each sequence's last page) and the append of one token
+    per sequence (folded into its page's bounds)."""
+    rname, over = WORKLOADS[name][:2]
+    rec = kvsynth.RECIPES[rname].with_(**over)
+    w = kvsynth.generate(rec)
+    pc = w.paged()
+    dt = torch.bfloat16 if rec.dtype == "bf16" else torch.float32
+
+    def dev(a):
+        if rec.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+                torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    k = dev(pc.k_pool)
+    bt = torch.from_numpy(pc.block_table).cuda()
+    sl = torch.from_numpy(w.seq_lens).cuda()
+    shape = sd.Shape(rec.batch, rec.num_q_heads, rec.num_kv_heads, rec.head_dim, rec.page_size,
+                     w.max_pages(), w.n_alloc, rec.dtype, pc.num_pages)
+    bounds = torch.empty(sd.bounds_shape(shape), dtype=dt, device="cuda")
+    last = [(b, (int(n) - 1) // rec.page_size) for b, n in enumerate(w.seq_lens)]
+    pages = torch.tensor(last, dtype=torch.int32).cuda()
+    one = torch.ones(rec.batch, dtype=torch.int32, device="cuda")
+    M = Measure(torch, sd, stream, not args.no_graph)
+    full = lambda i: sd.update_page_bounds(shape, k, bt, sl, bounds, stream=stream)
+    listed = lambda i: sd.update_page_bounds(shape, k, bt, sl, bounds, pages=pages, stream=stream)
+    append = lambda i: sd.append_page_bounds(shape, k, bt, sl, one, 1, bounds, stream=stream)
+    out = {"workload": name, "batch": rec.batch, "num_kv_heads": rec.num_kv_heads,
+           "page_size": rec.page_size, "context_max": int(w.seq_lens.max())}
+    for key, fn in (("full_rebuild_us", full), ("last_page_list_us", listed),
+                    ("append_one_token_us", append)):
+        out[key] = round(M.timed(fn, args.steps, args.warmup, 1), 3)
+        log(f"bounds update {name}: {key} = {out[key]}")
+    return out
+
+
 def point_summary(res):
     """The compact form of a workload's result for the main line's points."""
     a = res["attend"]
@@ -817,6 +856,9 @@ def main():
                     help="N > 1: N fresh processes, paired dense/sparse ratios with a "
                          "resampled interval")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead")
+    ap.add_argument("--bounds-update", action="store_true",
+                    help="time only the page-statistics updates (full, listed last pages, "
+                         "append of one token per sequence) on --workload and exit")
     ap.add_argument("--selection", default="topk",
                     choices=["topk", "window", "init_local_topk", "mass_budget"],
                     help="kept set: top-k (default), the KV window, initial + local + top-k, or "
@@ -855,6 +897,16 @@ def main():
 
     structured = args.selection != "topk" or args.scorer != "bounds"
     entmax = args.attention == "entmax"
+    if args.bounds_update:
+        import torch
+        import kvsynth
+        import sparse_kv_cache_sd_amd as sd
+        assert torch.cuda.is_available(), "bench.py needs a GPU"
+        torch.cuda.set_device(0)
+        sd.lib()
+        print(json.dumps({"bounds_update": bounds_update_times(
+            args.workload, args, torch, sd, kvsynth, torch.cuda.Stream())}), flush=True)
+        return
     if args.blocks > 1:
         result = run_blocks(args, sys.argv[1:])
         w0 = None
