@@ -174,7 +174,7 @@ SD_API sd_status sd_score_pages(const sd_shape* shape, const void* q, const void
  * scores going to the lower unit id (-0.0 equals +0.0), and writes them in
  * ascending order to sel_idx[b][g][0 .. k_b - 1]; sel_count[b][g] = k_b.
  * Scores must be finite.  k_max = sd_keep_count(r_kv, U_max) is the row
- * length of sel_idx.  Up to 32768 units per sequence one block selects each
+ * length of sel_idx.  Up to 16384 units per sequence one block selects each
  * (b, g) and ws may be NULL; beyond that the selection is spread over many
  * blocks per (b, g), whose scratch lives in ws (sd_workspace_bytes for this
  * shape and unit suffices; contents need not be set; SD_E_NULL /

@@ -213,7 +213,7 @@ struct Layout {
 
 // Scratch of the many-block top-k (units beyond one block's registers).
 bool multi_select(const sdkv::Dims& d, int unit) {
-  return units_max(d, unit) > sdkv::kMaxSelectOne;
+  return units_max(d, unit) > sdkv::kOneBlockTopkMax;
 }
 
 size_t select_ws_bytes(const sdkv::Dims& d, int unit) {

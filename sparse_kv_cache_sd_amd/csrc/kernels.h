@@ -231,6 +231,10 @@ constexpr int kMaxSelectE = 2048;
 constexpr int kMaxSelectU = 16384;
 // Most units the one-block selection kernel takes (more: select_multi.hip).
 constexpr int kMaxSelectOne = 32768;
+// Most units the library gives the one-block top-k; past this the many-block
+// top-k runs (slices of 4096 units: measured faster at 32768 token units,
+// 54.4 against 56.8 us per step).
+constexpr int kOneBlockTopkMax = 16384;
 
 hipError_t launch_page_bounds(const BoundsArgs& a, hipStream_t st);
 hipError_t launch_score(const ScoreArgs& a, hipStream_t st);

@@ -32,7 +32,7 @@ namespace {
 
 constexpr int kMT = 512;               // threads per block
 constexpr int kMNW = kMT / 64;
-constexpr int kMK = 16;                // keys per thread
+constexpr int kMK = 8;                 // keys per thread
 constexpr int kMSlice = kMT * kMK;     // units per block
 constexpr int kMBins = 2048;           // 11-bit bins
 constexpr int kMPasses = 3;
