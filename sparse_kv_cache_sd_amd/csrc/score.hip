@@ -32,7 +32,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kScoreThreads = 256;
-constexpr int kScoreIters = 4;
+constexpr int kScoreIters = 2;
 constexpr int kTokenIters = 4;  // 16-token chunks per wave, bf16 token scorer
 
 template <typename T, int D>
@@ -115,7 +115,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_pages_kernel(
 // group needs at most one lane exchange (G = 8).  Each wave scores
 // kPageTiles tiles of 16 pages, all loads issued before the first product.
 // Used for bf16 groups of more than four heads.
-constexpr int kPageTiles = 2;
+constexpr int kPageTiles = 1;
 
 template <int D, int G>
 __global__ __launch_bounds__(kScoreThreads) void score_pages_mfma_kernel(
