@@ -174,13 +174,13 @@ def read_traffic(workload, tag="attend"):
 
 # the kernels a traffic summary covers, by workload unit: (tag, name pattern)
 PMC_KERNELS = {
-    "page": [("attend", r"attend_mfma_kernel<\d+, \d+, false, (4|8|32), 0>"),
+    "page": [("attend", r"attend_mfma_kernel<\d+, \d+, false, (4|8|32), 0(, \d+)?>"),
              ("score", r"score_pages(_mfma)?_kernel<"),
-             ("dense", r"attend_mfma_kernel<\d+, \d+, false, 0, 0>"),
+             ("dense", r"attend_mfma_kernel<\d+, \d+, false, 0, 0(, \d+)?>"),
              ("merge", r"merge_splits_kernel<")],
-    "token": [("attend", r"attend_mfma_kernel<\d+, \d+, true, 0, 0>"),
+    "token": [("attend", r"attend_mfma_kernel<\d+, \d+, true, 0, 0(, \d+)?>"),
               ("score", r"score_tokens_(mfma|f32)_kernel<"),
-              ("dense", r"attend_mfma_kernel<\d+, \d+, false, 0, 0>"),
+              ("dense", r"attend_mfma_kernel<\d+, \d+, false, 0, 0(, \d+)?>"),
               ("merge", r"merge_splits_kernel<")],
 }
 

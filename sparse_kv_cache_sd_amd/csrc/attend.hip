@@ -49,7 +49,11 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 
 
 constexpr int kAttendWaves = 8;     // waves per block
-constexpr int kResolveWindow = 8;   // chunks a wave resolves per round
+// Chunks a wave resolves per round (list entry, then block table): 8 when a
+// wave holds many chunks (fewer dependent rounds), 4 when it holds at most 4
+// (cfg2's 20-page splits: 25.6 -> 24.9 us per step; 8 is better for long
+// lists and dense, 75.9 against 78.0 us at 1M).
+constexpr int kResolveWide = 8, kResolveNarrow = 4;
 
 // What a block does with the attended tokens' logits.
 enum WeightMode : int {
@@ -225,9 +229,10 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(MergeArgs a) {
 // bf16: matrix-core kernel
 // ----------------------------------------------------------------------------
 
-template <int D, int G, bool LOGITS, int SEL, int WM>
+template <int D, int G, bool LOGITS, int SEL, int WM, int RW>
 __global__ __launch_bounds__(kAttendWaves * 64) void attend_mfma_kernel(AttendArgs a) {
-  constexpr int NW = kAttendWaves, NT = NW * 64, RW = kResolveWindow;
+  constexpr int NW = kAttendWaves, NT = NW * 64;
+  static_assert(RW == 4 || RW == 8, "resolve windows of 4 or 8 chunks");
   constexpr int KS = D / 32;        // 16x16x32 steps over the channels
   constexpr int CT = D / 16;        // 16-channel output tiles
   constexpr int VROW = D + 8;       // staged V row, bf16 elements (16-byte aligned rows)
@@ -727,6 +732,17 @@ static int select_mode(int max_pages) {
   return kBlock32;
 }
 
+// One launch of the matrix-core kernel with the resolve window for the
+// split's chunks per wave.
+template <int D, int G, bool LOGITS, int SEL, int WM>
+static void go_mfma(const AttendArgs& a, dim3 grid, hipStream_t st, bool narrow) {
+  constexpr int NT = kAttendWaves * 64;
+  if (narrow)
+    attend_mfma_kernel<D, G, LOGITS, SEL, WM, kResolveNarrow><<<grid, NT, 0, st>>>(a);
+  else
+    attend_mfma_kernel<D, G, LOGITS, SEL, WM, kResolveWide><<<grid, NT, 0, st>>>(a);
+}
+
 hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
   const Dims& d = a.d;
   if (a.S < 1 || a.S > kMaxSplits) return hipErrorInvalidValue;
@@ -742,6 +758,10 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
   if (ent && (!logits || wl || selects)) return hipErrorInvalidValue;
   if (wl && logits) return hipErrorInvalidValue;
   if (ent && !(a.alpha_m1 > 0.f && a.alpha_m1 <= 1.f && a.beta >= 1.f)) return hipErrorInvalidValue;
+  // chunks of 16 rows a wave holds in one split: E pages of P / 16 chunks,
+  // or E listed tokens / 16
+  const int64_t nch = a.unit == kPage ? (int64_t)a.E * (d.P / 16) : ((int64_t)a.E + 15) / 16;
+  const bool narrow = (nch + kAttendWaves - 1) / kAttendWaves <= kResolveNarrow;
   const bool ok = dispatch_tdg(d.dtype, d.D, d.G, [&](auto t, auto dd, auto gg) {
     using T = decltype(t);
     constexpr int D = decltype(dd)::value;
@@ -754,8 +774,8 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
       // kept tokens' logits that entmax attention later reads
       auto go = [&](auto sel) {
         constexpr int SEL = decltype(sel)::value;
-        if (wl) attend_mfma_kernel<D, G, false, SEL, kWLogits><<<grid, NT, 0, st>>>(a);
-        else attend_mfma_kernel<D, G, false, SEL, kWSoftmax><<<grid, NT, 0, st>>>(a);
+        if (wl) go_mfma<D, G, false, SEL, kWLogits>(a, grid, st, narrow);
+        else go_mfma<D, G, false, SEL, kWSoftmax>(a, grid, st, narrow);
       };
       switch (select_mode(d.max_pages)) {
         case kBlock4: go(std::integral_constant<int, kBlock4>{}); break;
@@ -763,13 +783,13 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
         default: go(std::integral_constant<int, kBlock32>{}); break;
       }
     } else if (wl) {
-      attend_mfma_kernel<D, G, false, kListed, kWLogits><<<grid, NT, 0, st>>>(a);
+      go_mfma<D, G, false, kListed, kWLogits>(a, grid, st, narrow);
     } else if (logits && ent) {
-      attend_mfma_kernel<D, G, true, kListed, kWEntmax><<<grid, NT, 0, st>>>(a);
+      go_mfma<D, G, true, kListed, kWEntmax>(a, grid, st, narrow);
     } else if (logits) {
-      attend_mfma_kernel<D, G, true, kListed, kWSoftmax><<<grid, NT, 0, st>>>(a);
+      go_mfma<D, G, true, kListed, kWSoftmax>(a, grid, st, narrow);
     } else {
-      attend_mfma_kernel<D, G, false, kListed, kWSoftmax><<<grid, NT, 0, st>>>(a);
+      go_mfma<D, G, false, kListed, kWSoftmax>(a, grid, st, narrow);
     }
   });
   if (!ok) return hipErrorInvalidValue;

@@ -33,7 +33,7 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kScoreThreads = 256;
 constexpr int kScoreIters = 2;
-constexpr int kTokenIters = 4;  // 16-token chunks per wave, bf16 token scorer
+constexpr int kTokenIters = 2;  // 16-token chunks per wave, bf16 token scorer
 
 template <typename T, int D>
 constexpr int score_rows_per_block() {
