@@ -51,8 +51,9 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 constexpr int kAttendWaves = 8;     // waves per block
 // Chunks a wave resolves per round (list entry, then block table): 8 when a
 // wave holds many chunks (fewer dependent rounds), 4 when it holds at most 4
-// (cfg2's 20-page splits: 25.6 -> 24.9 us per step; 8 is better for long
-// lists and dense, 75.9 against 78.0 us at 1M).
+// (the 13-page splits of a 32K-token sequence kept at 0.2 with 8 KV heads:
+// 25.6 -> 24.9 us per step; 8 is better for long lists and dense, 75.9
+// against 78.0 us at 1M tokens).
 constexpr int kResolveWide = 8, kResolveNarrow = 4;
 
 // What a block does with the attended tokens' logits.

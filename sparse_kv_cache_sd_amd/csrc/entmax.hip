@@ -24,7 +24,9 @@
 // (sequence, query head) holds the logits in registers (16 per thread),
 // finds their max, compacts the candidates into LDS in slot order (wave
 // ballots and prefix offsets) and lets one wave run the Newton steps with
-// wave-level sums only.  With more slots, chunks of kTauChunk slots go to
+// wave-level sums only (the values in registers up to 1024 of them, else in
+// LDS; the per-value arithmetic compiled for beta = 2, beta = 1 or any
+// other beta).  With more slots, chunks of kTauChunk slots go to
 // blocks of their own, which leave their max and the slots within
 // 1 / (alpha - 1) of it (a superset of the candidates, since a chunk's max
 // never exceeds the head's) in the workspace; a merge block per head keeps
@@ -34,6 +36,8 @@
 // (sequence, KV head) fastest, so all blocks of a KV head share the XCD of
 // its attention blocks.  Sums run in a fixed order, so tau does not depend
 // on timing.
+#include <type_traits>
+
 #include "device.h"
 
 namespace sdkv {
@@ -129,27 +133,52 @@ struct Slots {
   }
 };
 
+// Exponent classes of the weights, fixed per launch: beta = 2 (alpha = 1.5:
+// squares), beta = 1 (sparsemax: the positive parts themselves), any other
+// beta (exp2 / log2).  The Newton loops are compiled once per class so that
+// the per-value work has no branches.
+enum BetaKind : int { kBetaAny = 0, kBetaOne = 1, kBetaTwo = 2 };
+
 // The alpha-entmax arithmetic of one head.
 struct Newton {
   float am1, beta, e_sub;
   __device__ Newton(const TauArgs& a) : am1(a.alpha_m1), beta(a.beta), e_sub(1.f - a.alpha_m1) {}
-  // s0 = sum of weights, s1 = sum of weight / t (= -f'(tau) / beta)
+  // s0 = sum of weights max(t, 0)^beta, s1 = sum of max(t, 0)^(beta - 1)
+  // (= -f'(tau) / beta), t = (alpha - 1) z - tau
+  template <int K>
   __device__ __forceinline__ void accum(float z, float tau, float& s0, float& s1) const {
     const float t = fmaf(am1, z, -tau);
-    const float w = entmax_weight(t, beta);
-    s0 += w;
-    s1 += t > 0.f ? (beta == 2.f ? t : (beta == 1.f ? 1.f : w / t)) : 0.f;
+    if constexpr (K == kBetaTwo) {
+      const float p = fmaxf(t, 0.f);
+      s0 += p * p;
+      s1 += p;
+    } else if constexpr (K == kBetaOne) {
+      s0 += fmaxf(t, 0.f);
+      s1 += t > 0.f ? 1.f : 0.f;
+    } else {
+      const float lt = log2f(t);  // used only where t > 0
+      s0 += t > 0.f ? exp2f(beta * lt) : 0.f;
+      s1 += t > 0.f ? exp2f((beta - 1.f) * lt) : 0.f;
+    }
   }
   // Newton step on g from the sums; false when the iteration ends.
+  template <int K>
   __device__ __forceinline__ bool step(float s0, float s1, float& tau) const {
     if (!(s0 > 1.f)) return false;  // at the root, up to rounding
-    const float sub = beta == 1.f ? 1.f : (beta == 2.f ? sqrtf(s0) : exp2f(e_sub * log2f(s0)));
+    const float sub = K == kBetaOne ? 1.f : (K == kBetaTwo ? sqrtf(s0) : exp2f(e_sub * log2f(s0)));
     const float nt = tau + (s0 - sub) / s1;
     if (!(nt > tau)) return false;  // the step no longer moves tau
     tau = nt;
     return true;
   }
   __device__ __forceinline__ bool cand(float z, float lo) const { return fmaf(am1, z, -lo) > 0.f; }
+  // fn(integral_constant<int, K>) for this head's exponent class
+  template <typename Fn>
+  __device__ __forceinline__ float by_kind(Fn&& fn) const {
+    if (beta == 2.f) return fn(std::integral_constant<int, kBetaTwo>{});
+    if (beta == 1.f) return fn(std::integral_constant<int, kBetaOne>{});
+    return fn(std::integral_constant<int, kBetaAny>{});
+  }
 };
 
 // Block-wide max of a per-thread value (every thread gets it).
@@ -166,13 +195,34 @@ __device__ __forceinline__ float block_max(float v, float* s_max) {
 }
 
 // Newton steps by one wave over n values at s_c; returns tau.  Lane l owns
-// the values s_c[l + 64 k] and sums them in k order.  tau only grows, so a
-// value whose weight is zero at one step is zero at every later one: each
-// step keeps, in order and in place, only the lane's values still positive,
-// and later steps read fewer.  Dropped values add exactly 0 to both sums, so
-// the sums (and tau) are those of the full list.  The LDS reads go in
-// batches of eight, issued together.  s_c is overwritten.
-__device__ __forceinline__ float newton_wave(const Newton& nw, float* s_c, int n, float tau) {
+// the values s_c[l + 64 k] and sums them in k order.  Up to 64 R values stay
+// in registers (R per lane, -inf past n) for every step.
+template <int K, int R>
+__device__ __forceinline__ float newton_regs(const Newton& nw, const float* s_c, int n,
+                                             float tau) {
+  const int lane = threadIdx.x & 63;
+  float z[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) z[r] = lane + 64 * r < n ? s_c[lane + 64 * r] : -INFINITY;
+  for (int it = 0; it < 64; ++it) {
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) nw.accum<K>(z[r], tau, s0, s1);
+    s0 = wave_sum_dpp(s0);
+    s1 = wave_sum_dpp(s1);
+    if (!nw.step<K>(s0, s1, tau)) break;
+  }
+  return tau;
+}
+
+// More values: they stay in LDS.  tau only grows, so a value whose weight is
+// zero at one step is zero at every later one: each step keeps, in order and
+// in place, only the lane's values still positive, and later steps read
+// fewer.  Dropped values add exactly 0 to both sums, so the sums (and tau)
+// are those of the full list.  The LDS reads go in batches of eight, issued
+// together.  s_c is overwritten.
+template <int K>
+__device__ __forceinline__ float newton_lds(const Newton& nw, float* s_c, int n, float tau) {
   constexpr int R = 8;
   const int lane = threadIdx.x & 63;
   int m = lane < n ? (n - 1 - lane) / 64 + 1 : 0;  // this lane's values
@@ -184,20 +234,32 @@ __device__ __forceinline__ float newton_wave(const Newton& nw, float* s_c, int n
       // the values in order; writes land at or below the values read
       float z[R];
 #pragma unroll
-      for (int r = 0; r < R; ++r) z[r] = s_c[lane + 64 * min(k + r, m - 1)];
+      for (int r = 0; r < R; ++r) {
+        z[r] = s_c[lane + 64 * min(k + r, m - 1)];
+        if (k + r >= m) z[r] = -INFINITY;
+      }
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        if (k + r >= m) break;
-        nw.accum(z[r], tau, s0, s1);
+        nw.accum<K>(z[r], tau, s0, s1);
         if (fmaf(nw.am1, z[r], -tau) > 0.f) s_c[lane + 64 * keep++] = z[r];
       }
     }
     m = keep;
     s0 = wave_sum_dpp(s0);
     s1 = wave_sum_dpp(s1);
-    if (!nw.step(s0, s1, tau)) break;
+    if (!nw.step<K>(s0, s1, tau)) break;
   }
   return tau;
+}
+
+// The values' count picks registers (up to 1024) or LDS.
+__device__ __forceinline__ float newton_wave(const Newton& nw, float* s_c, int n, float tau) {
+  return nw.by_kind([&](auto kind) {
+    constexpr int K = decltype(kind)::value;
+    if (n <= 64 * 8) return newton_regs<K, 8>(nw, s_c, n, tau);
+    if (n <= 64 * 16) return newton_regs<K, 16>(nw, s_c, n, tau);
+    return newton_lds<K>(nw, s_c, n, tau);
+  });
 }
 
 // Newton steps by the whole block over every kept logit, re-read each step
@@ -205,21 +267,25 @@ __device__ __forceinline__ float newton_wave(const Newton& nw, float* s_c, int n
 template <int NW>
 __device__ __forceinline__ float newton_block(const Newton& nw, const Slots& sl, float tau,
                                               float (*s_red)[2][NW]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int it = 0; it < 64; ++it) {
-    float s0 = 0.f, s1 = 0.f;
-    sl.for_range(0, sl.slots, [&](float z) { nw.accum(z, tau, s0, s1); });
-    s0 = wave_sum_dpp(s0);
-    s1 = wave_sum_dpp(s1);
-    const int par = it & 1;
-    if (lane == 0) { s_red[par][0][wave] = s0; s_red[par][1][wave] = s1; }
-    __syncthreads();
-    s0 = 0.f; s1 = 0.f;
+  return nw.by_kind([&](auto kind) {
+    constexpr int K = decltype(kind)::value;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    float t = tau;
+    for (int it = 0; it < 64; ++it) {
+      float s0 = 0.f, s1 = 0.f;
+      sl.for_range(0, sl.slots, [&](float z) { nw.accum<K>(z, t, s0, s1); });
+      s0 = wave_sum_dpp(s0);
+      s1 = wave_sum_dpp(s1);
+      const int par = it & 1;
+      if (lane == 0) { s_red[par][0][wave] = s0; s_red[par][1][wave] = s1; }
+      __syncthreads();
+      s0 = 0.f; s1 = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) { s0 += s_red[par][0][w]; s1 += s_red[par][1][w]; }
-    if (!nw.step(s0, s1, tau)) break;
-  }
-  return tau;
+      for (int w = 0; w < NW; ++w) { s0 += s_red[par][0][w]; s1 += s_red[par][1][w]; }
+      if (!nw.step<K>(s0, s1, t)) break;
+    }
+    return t;
+  });
 }
 
 // One block per head, at most kTauChunk kept slots.

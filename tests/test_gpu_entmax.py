@@ -294,3 +294,28 @@ def test_entmax_token_ragged_batch():
     for r in (0.2, 1.0):
         sel = sd.Selection("topk", r)
         _compare(w, dev, "token", sel, 1.5, _run(dev, "token", sel, 1.5))
+
+
+@pytest.mark.parametrize("alpha", [1.5, 1.25])
+@pytest.mark.parametrize("seq_len", [6000, 65536], ids=["lds-newton", "block-fallback"])
+def test_entmax_flat_logits_bf16_pages(seq_len, alpha):
+    """q = 0 on bf16 pages: every logit is 0 and every kept token is a
+    candidate.  At 6000 tokens (1808 kept slots per head) the candidates are
+    too many for the Newton steps in registers and run in LDS; at 65536
+    tokens (19664 slots) the threshold is split into chunks whose candidate
+    lists overflow, so the whole block iterates over every kept logit."""
+    rec = R["l8b"].with_(seq_len=seq_len, num_q_heads=16, num_kv_heads=4)
+    w = kvsynth.generate(rec)
+    w.q[...] = 0
+    dev = upload(w)
+    sel = sd.Selection("topk", 0.3)
+    res = _run(dev, "page", sel, alpha)
+    _compare(w, dev, "page", sel, alpha, res)
+    _, tau, idx, cnt = res
+    P, G = rec.page_size, rec.group
+    for g in range(rec.num_kv_heads):
+        pages = idx[0, g, :int(cnt[0, g])].astype(np.int64)
+        n = int(np.minimum(P, seq_len - pages * P).sum())
+        # tau solves n * (-tau)^beta = 1
+        want = -(1.0 / n) ** (alpha - 1.0)
+        assert np.abs(tau[0, g * G:(g + 1) * G] - want).max() <= 1e-6
