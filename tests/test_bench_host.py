@@ -23,7 +23,7 @@ def _mb(x):
     return x / 1e6
 
 
-def test_dense_bytes_cfg2():
+def test_dense_bytes_8b_32k():
     # 8 KV heads x 32768 tokens x (K + V) x 128 x 2 B, plus q / out / lse
     b = bench.algorithmic_bytes(np.array([32 * K]), 32, 8, 128, 16, 2, "page", 1.0, 0)
     qo = 32 * (128 * 2 + 128 * 4 + 4)
@@ -31,7 +31,7 @@ def test_dense_bytes_cfg2():
     assert abs(_mb(b) - 134.2) < 0.1
 
 
-def test_page_bytes_cfg2():
+def test_page_bytes_8b_32k():
     # k = 615 of 2048 pages per KV head, all full: 615 * 16 tokens kept per head
     kept = 615 * 16 * 8
     b = bench.algorithmic_bytes(np.array([32 * K]), 32, 8, 128, 16, 2, "page", 0.3, kept)
@@ -43,7 +43,7 @@ def test_page_bytes_cfg2():
 
 
 @pytest.mark.parametrize("n,k,want_mb", [(128 * K, 103, 35.4), (1024 * K, 820, 282.1)])
-def test_page_bytes_cfg5(n, k, want_mb):
+def test_page_bytes_70b_page64(n, k, want_mb):
     U = n // 64
     kept = k * 64 * 8
     b = bench.algorithmic_bytes(np.array([n]), 64, 8, 128, 64, 2, "page", 0.05, kept)
@@ -52,7 +52,7 @@ def test_page_bytes_cfg5(n, k, want_mb):
 
 
 @pytest.mark.parametrize("r,k,want_mb", [(0.3, 39322, 349.0), (0.2, 26215, 322.1)])
-def test_token_bytes_cfg3(r, k, want_mb):
+def test_token_bytes_8b_128k_token(r, k, want_mb):
     n = 128 * K
     b = bench.algorithmic_bytes(np.array([n]), 32, 8, 128, 16, 2, "token", r, k * 8)
     # every K row once, V of the kept tokens only
