@@ -5,25 +5,35 @@
 // ascending order ("SparDA ..." summary, Section 3.1 and Appendix A: the
 // selected set).
 //
-// An MSD radix select on the order-preserving 32-bit keys:
-//   the key interval starts at [min, max] of the scores (per-block partial
-//   minima and maxima, written by the token scorer or by a small kernel);
-//   pass p (p = 0, 1, 2): every block first derives the interval [lo, hi] and
-//     the count `need` still to take from it (from its own copy of the
-//     previous pass's state and the per-block histograms, each block
-//     redundantly), records that state in its own copy, and writes the
-//     2048-bin histogram of its slice's keys inside [lo, hi] (bins of 2^shift
-//     keys) and its number of keys above hi;
-//   place: from the last histogram, the final state (a single key T, or a
-//     bin kept whole) and, summed over the slices before this block, the keys
-//     above T and equal to T; equal keys go to the lower id, so each block
-//     knows its quota of them and where its ids go, and writes them in
-//     ascending order.
-// Three passes of 11 bits cover any 32-bit interval; a pass whose interval is
-// settled returns at once.  Histograms are per block (no atomics), so the
-// result does not depend on timing.  Block ids are bg + B*Hkv*slice in every
-// kernel here (device.h, group_block): all blocks of one (sequence, KV head)
-// share an XCD, so the histograms and states they exchange stay in its L2.
+// Three launches, every block of one (sequence, KV head) working on its slice:
+//   hist: 2048 bins uniform in the score's value over [min, max] of the
+//     scores (from the per-block partial minima and maxima); each block
+//     writes the histogram of its slice.  Scores crowd a few exponents, so
+//     bins of the value leave far fewer keys beside the k-th largest than
+//     bins of the key's bits: about 200 of 131072 at 128K tokens, r 0.3, on
+//     the synthetic inputs, where 11 key bits leave thousands.
+//   collect: each block sums the slices' histograms, finds the bin b* that
+//     holds the k-th largest score, and writes the number of its slice's keys
+//     above b* and its keys in b* (key and unit: the candidates).
+//   place: each block loads every candidate of its (sequence, KV head) and
+//     ranks them (key descending, then unit ascending: equal scores go to the
+//     lower id).  That gives the last kept candidate (T, t) and the kept
+//     units of the slices before this one; the block keeps its units with
+//     key > T, or key == T and unit <= t, and writes them in ascending order.
+// The bin of a score is an fp32 subtract and multiply by the same constants
+// in every block, then a clamp: monotone in the score, so every key above b*
+// is above every candidate.  Where bins cannot be formed (k = 0 or U, all
+// scores equal, a range that is not finite) or the candidates do not fit
+// (kCapS per slice, kCapT per (sequence, KV head)), the place kernel finds
+// the k-th largest key itself: MSD radix passes of 11 bits over every key of
+// its (sequence, KV head), re-read from memory at each pass by every block of
+// the group, then one pass that counts the kept units before its slice.
+// Nothing here uses atomics outside LDS (counts only), so the result does not
+// depend on timing.  Block ids are bg + B*Hkv*slice in every kernel here
+// (device.h, group_block): all blocks of one (sequence, KV head) share an XCD,
+// so the histograms and candidates they exchange stay in its L2.
+#include <cfloat>
+
 #include "topk.h"
 
 namespace sdkv {
@@ -34,12 +44,13 @@ constexpr int kMT = 512;               // threads per block
 constexpr int kMNW = kMT / 64;
 constexpr int kMK = 8;                 // keys per thread
 constexpr int kMSlice = kMT * kMK;     // units per block
-constexpr int kMBins = 2048;           // 11-bit bins
-constexpr int kMPasses = 3;
-
-struct MState {
-  uint32_t lo, hi, need, whole, done, k, pad0, pad1;
-};
+constexpr int kMBins = 2048;           // value bins (collect, place); 11-bit bins (fallback)
+constexpr int kBPT = kMBins / kMT;     // bins per thread when a block scans them
+constexpr int kCapS = 64;              // candidates a slice hands on
+constexpr int kCapT = 1024;            // candidates of one (sequence, KV head)
+constexpr int kMaxSlices = 512;        // slices per (sequence, KV head) the binned path takes
+constexpr int kCR = 8;                 // candidate slots per thread read with the setup
+static_assert(kBPT == 4, "a thread scans four bins");
 
 struct MArgs {
   Dims d;
@@ -49,25 +60,74 @@ struct MArgs {
   int U_max, k_max, R_ppm, NB;
   const uint32_t* mm;        // [B*Hkv][mm_nb][2] partial min / max keys
   int mm_nb, mm_per;         // partials per (b, g); units per partial
-  MState* st;                // [kMPasses][B*Hkv][NB] state at the start of each pass,
-                             // one copy per block (read back by the same block id)
-  uint32_t* over;            // [kMPasses][B*Hkv][NB] keys above hi per slice
-  uint32_t* hist;            // [kMPasses][B*Hkv][NB][kMBins]
+  uint32_t* hist;            // [B*Hkv][NB][kMBins] value histogram of each slice
+  uint32_t* above;           // [B*Hkv][NB] keys above bin b* in each slice
+  uint32_t* ccount;          // [B*Hkv][NB] keys in bin b* in each slice
+  uint2* cand;               // [B*Hkv][NB][kCapS] (key, unit) of the first of them
   int32_t* sel_idx;          // [B][Hkv][k_max]
   int32_t* sel_count;        // [B][Hkv]
   const int32_t* k_of;       // [B*Hkv] counts to keep, or NULL: min(keep_count(U), k_max)
 };
 
 struct MShared {
-  RadixState rs;             // wa / wb: block scan scratch
-  uint32_t hist[kMBins + 64];
-  MState S;
-  uint32_t red[4 * kMNW];
+  uint32_t hist[kMBins + 64];  // + a sink word per lane for keys outside the range
+  uint32_t wa[kMNW], wb[kMNW], wc[kMNW], wd[kMNW];
+  uint32_t cnt[kMaxSlices], off[kMaxSlices + 1];
+  // candidates as key << 32 | ~unit: a larger value ranks first (larger key,
+  // then lower unit); zero past the last (never ranks above one)
+  uint64_t comp[kCapT + 8];
+  uint32_t rank[kCapT];
+  uint32_t sv[8];
 };
 
-__device__ __forceinline__ int units_of(const MArgs& a, int b) {
-  const int n = clamp_len(a.seq_lens[b], a.d.max_seq);
-  return min(a.unit == kPage ? (n + a.d.P - 1) / a.d.P : n, a.U_max);
+// inverse of order_key (+0 for the key of -0)
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// The (sequence, KV head) of this block and what every block of it derives
+// alike: its count to keep, the key range of its scores and the value bins.
+struct Group {
+  int64_t bg;
+  int blk, s0, U, k, nsl;
+  uint32_t kmin, kmax;
+  float vmin, inv;  // bin of value v: min((v - vmin) * inv, 2047)
+  bool binned;
+};
+
+__device__ __forceinline__ uint32_t vbin(const Group& g, uint32_t key) {
+  const float t = (key_value(key) - g.vmin) * g.inv;
+  return t >= (float)(kMBins - 1) ? (uint32_t)(kMBins - 1) : (uint32_t)t;
+}
+
+// Block sums of two counters (every thread gets them).
+__device__ __forceinline__ void block_sum2(MShared& sm, uint32_t& x, uint32_t& y) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  x = wave_sum(x);
+  y = wave_sum(y);
+  __syncthreads();  // wa / wb may still be read from a previous call
+  if (lane == 0) { sm.wa[wave] = x; sm.wb[wave] = y; }
+  __syncthreads();
+  x = y = 0u;
+#pragma unroll
+  for (int w = 0; w < kMNW; ++w) { x += sm.wa[w]; y += sm.wb[w]; }
+}
+
+// Exclusive block scan of one counter, in thread order; *total gets the sum.
+__device__ __forceinline__ uint32_t block_excl_scan(MShared& sm, uint32_t v, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t inc = wave_scan_dpp(v);
+  __syncthreads();
+  if (lane == 63) sm.wa[wave] = inc;
+  __syncthreads();
+  uint32_t before = 0u, all = 0u;
+#pragma unroll
+  for (int w = 0; w < kMNW; ++w) {
+    before += w < wave ? sm.wa[w] : 0u;
+    all += sm.wa[w];
+  }
+  *total = all;
+  return before + inc - v;
 }
 
 // Keys of this block's slice, interleaved (key[i] of thread t is slice unit
@@ -80,239 +140,395 @@ __device__ __forceinline__ void load_slice(const MArgs& a, int64_t bg, int s0,
     key[i] = order_key(sc[min(s0 + (int)threadIdx.x + kMT * i, a.U_max - 1)]);
 }
 
+// Partial minima and maxima a thread reads in the first round (more in a
+// loop after it).
+constexpr int kMMR = 4;
+
+// Every block starts with the same round of loads, none waiting for another:
+// the sequence length, the group's partial minima and maxima (all of them,
+// masked once the length is known) and the slice's keys.
+__device__ Group group_setup(const MArgs& a, MShared& sm, uint32_t (&key)[kMK]) {
+  const GroupBlock gbk = group_block(a.d.B * a.d.Hkv);
+  Group g;
+  g.bg = gbk.bg;
+  g.blk = gbk.j;
+  g.s0 = g.blk * kMSlice;
+  const int b = gbk.bg / a.d.Hkv;
+  const int tid = threadIdx.x;
+  const int n_raw = a.seq_lens[b];
+  const uint32_t* mm = a.mm + g.bg * a.mm_nb * 2;
+  uint2 part[kMMR];
+#pragma unroll
+  for (int r = 0; r < kMMR; ++r)
+    part[r] = *reinterpret_cast<const uint2*>(mm + 2 * min(tid + kMT * r, a.mm_nb - 1));
+  load_slice(a, g.bg, g.s0, key);
+  const int n = clamp_len(n_raw, a.d.max_seq);
+  g.U = min(a.unit == kPage ? (n + a.d.P - 1) / a.d.P : n, a.U_max);
+  g.k = a.k_of ? min(max(a.k_of[g.bg], 0), g.U) : min(keep_count_dev(g.U, a.R_ppm), a.k_max);
+  g.nsl = (g.U + kMSlice - 1) / kMSlice;
+  const int parts = min(a.mm_nb, (g.U + a.mm_per - 1) / a.mm_per);
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+  for (int r = 0; r < kMMR; ++r) {
+    if (tid + kMT * r < parts) {
+      mn = min(mn, part[r].x);
+      mx = max(mx, part[r].y);
+    }
+  }
+  for (int i = tid + kMT * kMMR; i < parts; i += kMT) {
+    mn = min(mn, mm[2 * i]);
+    mx = max(mx, mm[2 * i + 1]);
+  }
+  mn = wave_umin(mn);
+  mx = wave_umax(mx);
+  const int lane = tid & 63, wave = tid >> 6;
+  if (lane == 0) { sm.wa[wave] = mn; sm.wb[wave] = mx; }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kMNW; ++w) { mn = min(mn, sm.wa[w]); mx = max(mx, sm.wb[w]); }
+  g.kmin = mn;
+  g.kmax = mx;
+  g.vmin = key_value(mn);
+  const float w = key_value(mx) - g.vmin;
+  g.inv = (float)kMBins / w;
+  // w and inv finite and positive (false for NaN as well)
+  g.binned = g.k > 0 && g.k < g.U && mn < mx && w > 0.f && w <= FLT_MAX && g.inv > 0.f &&
+             g.inv <= FLT_MAX && g.nsl <= kMaxSlices;
+  return g;
+}
+
 __device__ __forceinline__ uint32_t shift_of(uint32_t lo, uint32_t hi) {
   const uint32_t span = hi - lo;
   const int bits = span == 0u ? 0 : 32 - __clz(span);
   return bits > 11 ? bits - 11 : 0;
 }
 
-// Block sum of two counters (result in every thread).
-__device__ __forceinline__ void block_sum2(MShared& sm, uint32_t& x, uint32_t& y) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  x = wave_sum(x);
-  y = wave_sum(y);
-  if (lane == 0) { sm.red[2 * wave] = x; sm.red[2 * wave + 1] = y; }
-  __syncthreads();
-  x = y = 0u;
-#pragma unroll
-  for (int w = 0; w < kMNW; ++w) { x += sm.red[2 * w]; y += sm.red[2 * w + 1]; }
-  __syncthreads();
-}
-
-// State at the start of pass 0: [min, max] of the keys, need = k.
-__device__ void initial_state(const MArgs& a, MShared& sm, int64_t bg, int U) {
-  const int parts = min(a.mm_nb, (U + a.mm_per - 1) / a.mm_per);
-  const uint32_t* mm = a.mm + bg * a.mm_nb * 2;
-  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-  for (int i = threadIdx.x; i < parts; i += kMT) {
-    mn = min(mn, mm[2 * i]);
-    mx = max(mx, mm[2 * i + 1]);
-  }
-  block_minmax<kMNW>(sm.rs, mn, mx);
-  if (threadIdx.x == 0) {
-    const int k = a.k_of ? min(max(a.k_of[bg], 0), U) : min(keep_count_dev(U, a.R_ppm), a.k_max);
-    MState S{};
-    S.lo = sm.rs.lo;
-    S.hi = sm.rs.hi;
-    S.need = (uint32_t)k;
-    S.k = (uint32_t)k;
-    S.whole = 0u;
-    S.done = (k == 0 || k == U || S.lo >= S.hi) ? 1u : 0u;
-    sm.S = S;
-  }
-  __syncthreads();
-}
-
-// Narrows `prev` with the histograms of pass p (summed over the NB slices):
-// the bin holding the need-th largest key becomes the interval.  With
-// blk >= 0 it also sums, over the slices before blk, the keys above the new
-// interval and inside it (*above_before, *inside_before; every thread).
-__device__ void narrow(const MArgs& a, MShared& sm, int64_t bg, int p, const MState prev,
-                       int blk, uint32_t* above_before, uint32_t* inside_before) {
-  const int tid = threadIdx.x;
-  const uint32_t* h = a.hist + ((int64_t)p * a.d.B * a.d.Hkv + bg) * a.NB * kMBins;
-  // thread t holds bins kMBins - 1 - BPT t - j (j < BPT): descending order;
-  // its BPT bins are one vector load per slice
-  constexpr int BPT = kMBins / kMT;
-  static_assert(BPT == 2 || BPT == 4 || BPT == 8, "2, 4 or 8 bins per thread");
-  typedef unsigned int vec_t __attribute__((ext_vector_type(BPT)));
-  uint32_t c[BPT] = {}, cb[BPT] = {};
-  for (int b0 = 0; b0 < a.NB; b0 += 8) {
-    vec_t v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int s = min(b0 + i, a.NB - 1);
-      v[i] = *reinterpret_cast<const vec_t*>(h + (int64_t)s * kMBins + (kMBins - BPT - BPT * tid));
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bool valid = b0 + i < a.NB, before = b0 + i < blk;
-#pragma unroll
-      for (int j = 0; j < BPT; ++j) {  // bin kMBins - 1 - BPT t - j is element BPT - 1 - j
-        c[j] += valid ? v[i][BPT - 1 - j] : 0u;
-        cb[j] += before ? v[i][BPT - 1 - j] : 0u;
-      }
-    }
-  }
+// The bin holding the need-th largest of the keys counted in c (thread t
+// holds bins kMBins - 1 - kBPT t - j, j < kBPT: descending order).  Sets
+// sm.sv[0] = bin, sm.sv[1] = keys in higher bins, sm.sv[2] = keys in it;
+// every thread reads them after the barrier.
+__device__ __forceinline__ void pick_bin(MShared& sm, const uint32_t (&c)[kBPT], uint32_t need) {
   uint32_t tot = 0u;
 #pragma unroll
-  for (int j = 0; j < BPT; ++j) tot += c[j];
-  uint32_t run, unused;
-  block_excl_scan2(sm.rs, tot, 0u, &run, &unused);  // keys in higher bins
-  const uint32_t shift = shift_of(prev.lo, prev.hi);
+  for (int j = 0; j < kBPT; ++j) tot += c[j];
+  uint32_t all;
+  uint32_t run = block_excl_scan(sm, tot, &all);  // keys in higher bins
 #pragma unroll
-  for (int j = 0; j < BPT; ++j) {
-    if (run < prev.need && run + c[j] >= prev.need) {
-      const uint32_t bin = (uint32_t)(kMBins - 1 - BPT * tid - j);
-      MState S = prev;
-      S.lo = prev.lo + (bin << shift);
-      const uint64_t top = (uint64_t)S.lo + ((1ull << shift) - 1ull);
-      S.hi = (uint32_t)(top < (uint64_t)prev.hi ? top : (uint64_t)prev.hi);
-      S.need = prev.need - run;
-      S.whole = c[j] == S.need ? 1u : 0u;
-      S.done = (S.whole || S.lo == S.hi) ? 1u : 0u;
-      sm.S = S;
-      sm.red[4 * kMNW - 1] = (uint32_t)(BPT * tid + j);  // rank of the bin from the top
+  for (int j = 0; j < kBPT; ++j) {
+    if (run < need && run + c[j] >= need) {
+      sm.sv[0] = (uint32_t)(kMBins - 1 - kBPT * (int)threadIdx.x - j);
+      sm.sv[1] = run;
+      sm.sv[2] = c[j];
     }
     run += c[j];
   }
   __syncthreads();
-  if (blk < 0) return;
-  // slices before blk: keys in bins above the chosen one, and in it
-  const uint32_t r = sm.red[4 * kMNW - 1];
-  uint32_t ab = 0u, in = 0u;
-#pragma unroll
-  for (int j = 0; j < BPT; ++j) {
-    const uint32_t rank = (uint32_t)(BPT * tid + j);
-    ab += rank < r ? cb[j] : 0u;
-    in += rank == r ? cb[j] : 0u;
-  }
-  __syncthreads();  // red[] is reused below
-  block_sum2(sm, ab, in);
-  *above_before = ab;
-  *inside_before = in;
 }
 
 __global__ __launch_bounds__(kMT) void msel_minmax_kernel(MArgs a, uint32_t* mm) {
-  __shared__ MShared sm;
+  __shared__ uint32_t s_w[2][kMNW];
   const GroupBlock gbk = group_block(a.d.B * a.d.Hkv);
   const int blk = gbk.j, b = gbk.bg / a.d.Hkv;
   const int64_t bg = gbk.bg;
   const int s0 = blk * kMSlice;
-  uint32_t key[kMK];
-  load_slice(a, bg, s0, key);
-  const int U = units_of(a, b);
+  const float* sc = a.scores + bg * a.U_max;
+  const int n = clamp_len(a.seq_lens[b], a.d.max_seq);
+  const int U = min(a.unit == kPage ? (n + a.d.P - 1) / a.d.P : n, a.U_max);
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
 #pragma unroll
-  for (int i = 0; i < kMK; ++i)
-    if (s0 + (int)threadIdx.x + kMT * i < U) { mn = min(mn, key[i]); mx = max(mx, key[i]); }
-  block_minmax<kMNW>(sm.rs, mn, mx);
+  for (int i = 0; i < kMK; ++i) {
+    const int u = s0 + (int)threadIdx.x + kMT * i;
+    const uint32_t key = order_key(sc[min(u, a.U_max - 1)]);
+    if (u < U) { mn = min(mn, key); mx = max(mx, key); }
+  }
+  mn = wave_umin(mn);
+  mx = wave_umax(mx);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) { s_w[0][wave] = mn; s_w[1][wave] = mx; }
+  __syncthreads();
   if (threadIdx.x == 0) {
-    mm[(bg * a.NB + blk) * 2] = sm.rs.lo;
-    mm[(bg * a.NB + blk) * 2 + 1] = sm.rs.hi;
+#pragma unroll
+    for (int w = 1; w < kMNW; ++w) { mn = min(mn, s_w[0][w]); mx = max(mx, s_w[1][w]); }
+    mm[(bg * a.NB + blk) * 2] = mn;
+    mm[(bg * a.NB + blk) * 2 + 1] = mx;
   }
 }
 
-__global__ __launch_bounds__(kMT) void msel_pass_kernel(MArgs a, int p) {
+// Value histogram of each slice.
+__global__ __launch_bounds__(kMT) void msel_hist_kernel(MArgs a) {
   __shared__ MShared sm;
-  const GroupBlock gbk = group_block(a.d.B * a.d.Hkv);
-  const int blk = gbk.j, b = gbk.bg / a.d.Hkv;
-  const int64_t bg = gbk.bg;
-  const int64_t BG = (int64_t)a.d.B * a.d.Hkv;
-  const int s0 = blk * kMSlice;
   uint32_t key[kMK];
-  load_slice(a, bg, s0, key);
-  const int U = units_of(a, b);
-  if (p == 0) {
-    initial_state(a, sm, bg, U);
-  } else {
-    const MState prev = a.st[((p - 1) * BG + bg) * a.NB + blk];
-    if (prev.done) {
-      if (threadIdx.x == 0) sm.S = prev;
-      __syncthreads();
-    } else {
-      narrow(a, sm, bg, p - 1, prev, -1, nullptr, nullptr);
-    }
-  }
-  const MState S = sm.S;
-  if (threadIdx.x == 0) a.st[(p * BG + bg) * a.NB + blk] = S;
-  if (S.done) return;
-  const uint32_t shift = shift_of(S.lo, S.hi);
-  for (int i = threadIdx.x; i < kMBins; i += kMT) sm.hist[i] = 0u;
+  const Group g = group_setup(a, sm, key);
+  if (!g.binned || g.s0 >= g.U) return;  // uniform per block
+  for (int i = threadIdx.x; i < kMBins + 64; i += kMT) sm.hist[i] = 0u;
   __syncthreads();
   const int lane = threadIdx.x & 63;
-  uint32_t above = 0u;
 #pragma unroll
   for (int i = 0; i < kMK; ++i) {
-    const bool v = s0 + (int)threadIdx.x + kMT * i < U;
-    const bool in = v && key[i] >= S.lo && key[i] <= S.hi;
-    above += (v && key[i] > S.hi) ? 1u : 0u;
-    atomicAdd(&sm.hist[in ? (key[i] - S.lo) >> shift : kMBins + lane], in ? 1u : 0u);
+    const bool v = g.s0 + (int)threadIdx.x + kMT * i < g.U;
+    atomicAdd(&sm.hist[v ? vbin(g, key[i]) : (uint32_t)(kMBins + lane)], v ? 1u : 0u);
   }
-  uint32_t unused = 0u;
-  block_sum2(sm, above, unused);  // includes a barrier: the histogram is complete
-  uint32_t* h = a.hist + ((p * BG + bg) * a.NB + blk) * kMBins;
+  __syncthreads();
+  uint32_t* h = a.hist + (g.bg * a.NB + g.blk) * kMBins;
   for (int i = threadIdx.x; i < kMBins; i += kMT) h[i] = sm.hist[i];
-  if (threadIdx.x == 0) a.over[(p * BG + bg) * a.NB + blk] = above;
+}
+
+// The bin b* of the k-th largest score; this slice's keys above it and in it.
+__global__ __launch_bounds__(kMT) void msel_collect_kernel(MArgs a) {
+  __shared__ MShared sm;
+  uint32_t key[kMK];
+  const Group g = group_setup(a, sm, key);
+  if (!g.binned || g.s0 >= g.U) return;  // uniform per block
+  // sum the slices' histograms, kBPT bins per thread (one vector load per
+  // slice), eight slices' loads issued together
+  typedef unsigned int vec_t __attribute__((ext_vector_type(kBPT)));
+  const int tid = threadIdx.x;
+  const uint32_t* h = a.hist + g.bg * a.NB * kMBins;
+  uint32_t c[kBPT] = {};
+  for (int s0 = 0; s0 < g.nsl; s0 += 8) {
+    vec_t v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int s = min(s0 + i, g.nsl - 1);
+      v[i] = *reinterpret_cast<const vec_t*>(h + (int64_t)s * kMBins + (kMBins - kBPT - kBPT * tid));
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bool valid = s0 + i < g.nsl;
+#pragma unroll
+      for (int j = 0; j < kBPT; ++j) c[j] += valid ? v[i][kBPT - 1 - j] : 0u;
+    }
+  }
+  pick_bin(sm, c, (uint32_t)g.k);
+  const uint32_t bstar = sm.sv[0];
+  // this slice: keys above b*, and its keys in b* in (i, wave, lane) order
+  const int lane = tid & 63, wave = tid >> 6;
+  const uint64_t below = (1ull << lane) - 1ull;
+  uint32_t above = 0u, inbin = 0u;
+  uint32_t vb[kMK];
+#pragma unroll
+  for (int i = 0; i < kMK; ++i) {
+    const bool v = g.s0 + tid + kMT * i < g.U;
+    vb[i] = v ? vbin(g, key[i]) : 0u;
+    above += (v && vb[i] > bstar) ? 1u : 0u;
+    const bool in = v && vb[i] == bstar;
+    inbin += in ? 1u : 0u;
+    const uint64_t m = __ballot(in);
+    if (lane == 0) sm.hist[i * kMNW + wave] = (uint32_t)__popcll(m);
+  }
+  __syncthreads();
+  // offsets of the (i, wave) groups: one wave scans the kMK * kMNW counts
+  if (wave == 0) {
+    const uint32_t x = lane < kMK * kMNW ? sm.hist[lane] : 0u;
+    const uint32_t inc = wave_scan_dpp(x);
+    if (lane < kMK * kMNW) sm.hist[64 + lane] = inc - x;
+  }
+  __syncthreads();
+  uint2* dst = a.cand + (g.bg * a.NB + g.blk) * kCapS;
+#pragma unroll
+  for (int i = 0; i < kMK; ++i) {
+    const bool in = g.s0 + tid + kMT * i < g.U && vb[i] == bstar;
+    const uint64_t m = __ballot(in);
+    const uint32_t pos = sm.hist[64 + i * kMNW + wave] + (uint32_t)__popcll(m & below);
+    if (in && pos < (uint32_t)kCapS) dst[pos] = make_uint2(key[i], (uint32_t)(g.s0 + tid + kMT * i));
+  }
+  block_sum2(sm, above, inbin);
+  if (tid == 0) {
+    a.above[g.bg * a.NB + g.blk] = above;
+    a.ccount[g.bg * a.NB + g.blk] = inbin;
+  }
+}
+
+// Without usable bins or candidates: the k-th largest key T of the group by
+// MSD radix passes over every key (re-read from memory), then the kept units
+// before this slice.  kept = key > T, plus the first `quota` keys equal to T
+// of this slice in unit order; whole: kept = key >= T.
+__device__ void select_all(const MArgs& a, MShared& sm, const Group& g, uint32_t* T,
+                           uint32_t* quota, bool* whole, uint32_t* base) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const float* sc = a.scores + g.bg * a.U_max;
+  uint32_t lo = g.kmin, hi = g.kmax, need = (uint32_t)g.k;
+  bool wh = false;
+  // 11 bits per pass: 32 -> 21 -> 10 -> 0 bits of span in at most three
+  for (int p = 0; p < 3 && lo < hi && !wh; ++p) {  // uniform
+    const uint32_t shift = shift_of(lo, hi);
+    __syncthreads();  // the previous pass's readers are done with hist
+    for (int i = tid; i < kMBins + 64; i += kMT) sm.hist[i] = 0u;
+    __syncthreads();
+    for (int u0 = 0; u0 < g.U; u0 += kMT * 8) {
+      uint32_t kk[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) kk[r] = order_key(sc[min(u0 + tid + kMT * r, g.U - 1)]);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const bool in = u0 + tid + kMT * r < g.U && kk[r] >= lo && kk[r] <= hi;
+        atomicAdd(&sm.hist[in ? (kk[r] - lo) >> shift : (uint32_t)(kMBins + lane)], in ? 1u : 0u);
+      }
+    }
+    __syncthreads();
+    uint32_t c[kBPT];
+#pragma unroll
+    for (int j = 0; j < kBPT; ++j) c[j] = sm.hist[kMBins - 1 - kBPT * tid - j];
+    pick_bin(sm, c, need);
+    const uint32_t bin = sm.sv[0], run = sm.sv[1], cnt = sm.sv[2];
+    const uint32_t nlo = lo + (bin << shift);
+    const uint64_t top = (uint64_t)nlo + ((1ull << shift) - 1ull);
+    hi = (uint32_t)(top < (uint64_t)hi ? top : (uint64_t)hi);
+    lo = nlo;
+    need -= run;
+    wh = cnt == need;
+  }
+  // kept units before this slice
+  uint32_t ab = 0u, eq = 0u;
+  for (int u0 = 0; u0 < g.s0; u0 += kMT * 8) {
+    uint32_t kk[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) kk[r] = order_key(sc[min(u0 + tid + kMT * r, g.s0 - 1)]);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const bool v = u0 + tid + kMT * r < g.s0;
+      ab += (v && (wh ? kk[r] >= lo : kk[r] > lo)) ? 1u : 0u;
+      eq += (v && !wh && kk[r] == lo) ? 1u : 0u;
+    }
+  }
+  block_sum2(sm, ab, eq);
+  *T = lo;
+  *whole = wh;
+  *quota = wh ? 0u : (uint32_t)max((int)need - (int)eq, 0);
+  *base = ab + (wh ? 0u : min(eq, need));
 }
 
 // Kept ids of each slice at their place in the ascending list.
 __global__ __launch_bounds__(kMT) void msel_place_kernel(MArgs a) {
   __shared__ MShared sm;
   __shared__ KeptScratch<kMK, kMNW> ks;
-  const GroupBlock gbk = group_block(a.d.B * a.d.Hkv);
-  const int blk = gbk.j, b = gbk.bg / a.d.Hkv;
-  const int64_t bg = gbk.bg;
-  const int64_t BG = (int64_t)a.d.B * a.d.Hkv;
-  const int s0 = blk * kMSlice;
+  // Loads issued with the group's setup, before anything is known: this
+  // thread's slice's counts and candidate slots (masked later; slots past
+  // the first round are read after the counts).
   const int tid = threadIdx.x;
+  const int64_t bg0 = group_block(a.d.B * a.d.Hkv).bg;
+  const int tsl = min(tid, a.NB - 1);
+  const uint32_t as_raw = a.above[bg0 * a.NB + tsl];
+  const uint32_t cs_raw = a.ccount[bg0 * a.NB + tsl];
+  const uint2* src = a.cand + bg0 * a.NB * kCapS;
+  const int nslots = a.NB * kCapS;
+  uint2 cv[kCR];
+#pragma unroll
+  for (int r = 0; r < kCR; ++r) cv[r] = src[min(tid + kMT * r, nslots - 1)];
   uint32_t key[kMK];
-  load_slice(a, bg, s0, key);
-  const int U = units_of(a, b);
-  // the last pass that built histograms
-  int L = -1;
-  MState prev = a.st[bg * a.NB + blk];
-  for (int p = 0; p < kMPasses; ++p) {
-    const MState s = a.st[(p * BG + bg) * a.NB + blk];
-    if (!s.done) { L = p; prev = s; }
-  }
-  int32_t* out = a.sel_idx + bg * a.k_max;
-  const uint32_t k = prev.k;
-  if (blk == 0 && tid == 0) a.sel_count[bg] = (int32_t)k;
-  if (k == 0u || s0 >= U) return;
-  if ((int)k == U) {
-    for (int i = tid; i < kMSlice && s0 + i < U; i += kMT) out[s0 + i] = s0 + i;
+  const Group g = group_setup(a, sm, key);
+  int32_t* out = a.sel_idx + g.bg * a.k_max;
+  if (g.blk == 0 && tid == 0) a.sel_count[g.bg] = g.k;
+  if (g.k == 0 || g.s0 >= g.U) return;  // uniform per block
+  if (g.k == g.U) {
+    for (int i = tid; i < kMSlice && g.s0 + i < g.U; i += kMT) out[g.s0 + i] = g.s0 + i;
     return;
   }
-  uint32_t above_before, equal_before;
-  MState S;
-  if (L < 0) {
-    // every key equals lo: all are ties, the first k by id are kept
-    S = prev;
-    S.whole = 0u;
-    above_before = 0u;
-    equal_before = (uint32_t)s0;
-  } else {
-    // keys above hi_L in the slices before this one (loaded before the
-    // narrowing so that the two reads overlap)
-    uint32_t ov = 0u;
-    for (int j = tid; j < blk; j += kMT) ov += a.over[(L * BG + bg) * a.NB + j];
-    uint32_t ab, inb;
-    narrow(a, sm, bg, L, prev, blk, &ab, &inb);
-    S = sm.S;
-    uint32_t unused = 0u;
-    block_sum2(sm, ov, unused);
-    above_before = ov + ab + (S.whole ? inb : 0u);
-    equal_before = S.whole ? 0u : inb;
+  bool fallback = !g.binned;
+  uint32_t T = 0u, quota = 0u, base = 0u;
+  bool whole = false;
+  if (g.binned) {
+    // every slice's counts (thread s reads slice s: nsl <= kMT): keys above
+    // b* before this slice and in all, slices over kCapS, and the offsets of
+    // the candidates in the gathered list -- one barrier pair for all four
+    static_assert(kMaxSlices <= kMT, "a thread per slice");
+    const int lane = tid & 63, wave = tid >> 6;
+    const bool mine = tid < g.nsl;
+    const uint32_t as = mine ? as_raw : 0u, cs = mine ? cs_raw : 0u;
+    const uint32_t cc = min(cs, (uint32_t)kCapS);
+    uint32_t ab = wave_sum(tid < g.blk ? as : 0u), atot = wave_sum(as);
+    const uint32_t over = wave_sum(cs > (uint32_t)kCapS ? 1u : 0u);
+    const uint32_t inc = wave_scan_dpp(cc);
+    __syncthreads();  // the setup's readers of wa / wb are done
+    if (lane == 63) { sm.wa[wave] = ab; sm.wb[wave] = atot; sm.wc[wave] = over; sm.wd[wave] = inc; }
+    __syncthreads();
+    ab = atot = 0u;
+    uint32_t ov = 0u, off = inc - cc, ctot = 0u;
+#pragma unroll
+    for (int w = 0; w < kMNW; ++w) {
+      ab += sm.wa[w];
+      atot += sm.wb[w];
+      ov += sm.wc[w];
+      off += w < wave ? sm.wd[w] : 0u;
+      ctot += sm.wd[w];
+    }
+    fallback = ov != 0u || ctot > (uint32_t)kCapT;
+    if (!fallback) {
+      if (mine) {
+        sm.cnt[tid] = cc;
+        sm.off[tid] = off;
+      }
+      const int nc = (int)ctot, nc8 = (nc + 7) & ~7;
+      if (tid < nc8 - nc) sm.comp[nc + tid] = 0ull;
+      for (int c = tid; c < nc; c += kMT) sm.rank[c] = 0u;
+      __syncthreads();
+      // gather the candidates: slot x = (slice x / kCapS, entry x % kCapS)
+      const int used = g.nsl * kCapS;
+      auto comp_of = [](uint2 v) { return ((uint64_t)v.x << 32) | (uint64_t)(~v.y); };
+#pragma unroll
+      for (int r = 0; r < kCR; ++r) {
+        const int x = tid + kMT * r, sl = x / kCapS, e = x - sl * kCapS;
+        if (x < used && (uint32_t)e < sm.cnt[sl]) sm.comp[sm.off[sl] + e] = comp_of(cv[r]);
+      }
+      for (int x = tid + kMT * kCR; x < used; x += kMT) {
+        const int sl = x / kCapS, e = x - sl * kCapS;
+        if ((uint32_t)e < sm.cnt[sl]) sm.comp[sm.off[sl] + e] = comp_of(src[x]);
+      }
+      __syncthreads();
+      // rank of each candidate = the candidates above it.  With fewer
+      // candidates than threads, P threads share one candidate's comparisons
+      // (an interval of the others each, eight read at a time) and add their
+      // counts in LDS.
+      const int P = nc >= kMT ? 1 : kMT / max(nc, 1);
+      const int span = ((nc8 + P - 1) / P + 7) & ~7;
+      for (int t = tid; t < nc * P; t += kMT) {
+        const int c = t % nc, part = t / nc;
+        const uint64_t me = sm.comp[c];
+        const int o1 = min((part + 1) * span, nc8);
+        uint32_t r = 0u;
+        for (int o = part * span; o < o1; o += 8) {
+          uint64_t x[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x[j] = sm.comp[o + j];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) r += x[j] > me ? 1u : 0u;
+        }
+        atomicAdd(&sm.rank[c], r);
+      }
+      __syncthreads();
+      const uint32_t need = (uint32_t)g.k - atot;  // >= 1: b* holds the k-th largest
+      uint32_t kb = 0u;  // kept candidates of the slices before this one
+      for (int c = tid; c < nc; c += kMT) {
+        const uint32_t r = sm.rank[c];
+        const uint64_t me = sm.comp[c];
+        const uint32_t unit = ~(uint32_t)me;
+        if (r + 1u == need) { sm.sv[4] = (uint32_t)(me >> 32); sm.sv[5] = unit; }
+        kb += (r < need && (int)unit < g.s0) ? 1u : 0u;
+      }
+      __syncthreads();
+      T = sm.sv[4];
+      const uint32_t t_unit = sm.sv[5];
+      // ties of this slice that are kept: equal to T with unit <= t
+      uint32_t q = 0u;
+      for (int c = tid; c < nc; c += kMT) {
+        const uint64_t x = sm.comp[c];
+        const uint32_t unit = ~(uint32_t)x;
+        q += ((uint32_t)(x >> 32) == T && (int)unit >= g.s0 && (int)unit < g.s0 + kMSlice &&
+              unit <= t_unit)
+                 ? 1u
+                 : 0u;
+      }
+      block_sum2(sm, kb, q);
+      quota = q;
+      base = ab + kb;
+    }
   }
-  // max(need - equal_before, 0), as a signed difference (see kept_words)
-  const uint32_t quota = (uint32_t)max((int)S.need - (int)equal_before, 0);
-  const uint32_t base = above_before + min(equal_before, S.need);
-  const int n_slice = min(kMSlice, U - s0);
-  kept_words<kMK, kMNW>(ks.mask, ks.tie, ks.base, key, n_slice, S.lo, quota, S.whole != 0u);
+  if (fallback) select_all(a, sm, g, &T, &quota, &whole, &base);
+  const int n_slice = min(kMSlice, g.U - g.s0);
+  kept_words<kMK, kMNW>(ks.mask, ks.tie, ks.base, key, n_slice, T, quota, whole);
   emit_kept<kMK, kMNW>(ks.mask, ks.base, 0u, (uint32_t)kMSlice, [&](int pos, int u) {
     const uint32_t gp = base + (uint32_t)pos;
-    if (gp < k) out[gp] = s0 + u;
+    if (gp < (uint32_t)g.k) out[gp] = g.s0 + u;
   });
 }
 
@@ -321,8 +537,8 @@ __global__ __launch_bounds__(kMT) void msel_place_kernel(MArgs a) {
 size_t msel_workspace_bytes(int B, int Hkv, int U_max) {
   const int64_t bg = (int64_t)B * Hkv;
   const int64_t NB = (U_max + kMSlice - 1) / kMSlice;
-  return sizeof(uint32_t) * 2 * bg * NB + sizeof(MState) * kMPasses * bg * NB +
-         sizeof(uint32_t) * kMPasses * bg * NB + sizeof(uint32_t) * kMPasses * bg * NB * kMBins;
+  return sizeof(uint32_t) * 2 * bg * NB + sizeof(uint32_t) * bg * NB * kMBins +
+         sizeof(uint32_t) * 2 * bg * NB + sizeof(uint2) * bg * NB * kCapS;
 }
 
 hipError_t launch_select_multi(const SelectArgs& sa, const uint32_t* mm, int mm_nb, int mm_per,
@@ -340,11 +556,13 @@ hipError_t launch_select_multi(const SelectArgs& sa, const uint32_t* mm, int mm_
   char* p = static_cast<char*>(ws);
   uint32_t* mm_own = reinterpret_cast<uint32_t*>(p);
   p += sizeof(uint32_t) * 2 * bg * a.NB;
-  a.st = reinterpret_cast<MState*>(p);
-  p += sizeof(MState) * kMPasses * bg * a.NB;
-  a.over = reinterpret_cast<uint32_t*>(p);
-  p += sizeof(uint32_t) * kMPasses * bg * a.NB;
   a.hist = reinterpret_cast<uint32_t*>(p);
+  p += sizeof(uint32_t) * bg * a.NB * kMBins;
+  a.above = reinterpret_cast<uint32_t*>(p);
+  p += sizeof(uint32_t) * bg * a.NB;
+  a.ccount = reinterpret_cast<uint32_t*>(p);
+  p += sizeof(uint32_t) * bg * a.NB;
+  a.cand = reinterpret_cast<uint2*>(p);
   a.sel_idx = sa.sel_idx;
   a.sel_count = sa.sel_count;
   a.k_of = k_of;
@@ -359,7 +577,8 @@ hipError_t launch_select_multi(const SelectArgs& sa, const uint32_t* mm, int mm_
     a.mm_nb = a.NB;
     a.mm_per = kMSlice;
   }
-  for (int pass = 0; pass < kMPasses; ++pass) msel_pass_kernel<<<grid, kMT, 0, stream>>>(a, pass);
+  msel_hist_kernel<<<grid, kMT, 0, stream>>>(a);
+  msel_collect_kernel<<<grid, kMT, 0, stream>>>(a);
   msel_place_kernel<<<grid, kMT, 0, stream>>>(a);
   return hipGetLastError();
 }

@@ -147,6 +147,33 @@ def test_select_bitexact_with_ties(seed, U, unit, r):
     _select_case(sc, seq_lens, unit, r, shape)
 
 
+@pytest.mark.parametrize("kind", ["duplicates", "far-outlier", "range-overflow", "two-clusters",
+                                  "k-one", "k-all-but-one"])
+def test_select_many_units_value_bins(kind):
+    """Past 16384 units the top-k bins the scores by value.  Score sets that
+    put many keys in the bin of the k-th largest, or whose range overflows
+    fp32, take the exact fallback; every case must give the oracle's set."""
+    rng = np.random.default_rng(11)
+    U, r = 40000, 0.3
+    shape = sd.Shape(2, 8, 2, 128, 16, -(-U // 16), U, "bf16", 1)
+    sc = rng.standard_normal((2, 2, U)).astype(np.float32)
+    if kind == "duplicates":      # many equal scores inside one value bin
+        sc = np.round(sc * 50) / 50
+    elif kind == "far-outlier":   # one huge score: every other one lands in the lowest bin
+        sc[:, :, 123] = 1e30
+    elif kind == "range-overflow":  # max - min is not finite in fp32
+        sc[:, :, 7] = 3e38
+        sc[:, :, 99] = -3e38
+    elif kind == "two-clusters":  # the k-th largest inside a dense cluster far from the other
+        sc[:, :, : U // 2] += 1e6
+    elif kind == "k-one":
+        r = 1e-6
+    elif kind == "k-all-but-one":
+        r = 1.0 - 1.0 / U
+    seq_lens = np.array([U, (U * 3) // 5], dtype=np.int32)
+    _select_case(sc, seq_lens, "token", r, shape)
+
+
 # ------------------------------------------------------------- attention over a given set
 
 @pytest.mark.parametrize("name,kw,unit,r", [
