@@ -393,6 +393,7 @@ struct Weights {
   const float* tau = nullptr;
   float alpha_m1 = 0.f, beta = 0.f;
   float* logits_out = nullptr;
+  bool logits_slots = false;  // AttendArgs::logits_slots
 };
 
 // Split-K attention partials.  Exactly one list source: sel_idx (list),
@@ -440,6 +441,7 @@ sd_status do_partials(const sdkv::Dims& d, const void* q, const void* kp, const 
   a.alpha_m1 = wt.alpha_m1;
   a.beta = wt.beta;
   a.logits_out = wt.logits_out;
+  a.logits_slots = wt.logits_slots ? 1 : 0;
   if (S_out) *S_out = sp.S;
   return device_status(sdkv::launch_attend(a, st), "attention kernel launch");
 }
@@ -669,6 +671,12 @@ sd_status entmax_impl(const sdkv::Dims& d, const void* q, const void* k_pages,
   const bool fused = !dense && unit == SD_UNIT_PAGE &&
                      (sel.kind == SD_SEL_TOPK || sel.kind == SD_SEL_INIT_LOCAL_TOPK) &&
                      fused_select(d, unit, k_max);
+  // Logits written by the logits-only attention pass (every case but the
+  // token scorer's) are laid out by kept slot on the matrix-core path: the
+  // threshold kernel then reads them without the list and the block table,
+  // and the entmax pass reads a split's logits as one run.
+  const bool scorer_logits = unit == SD_UNIT_TOKEN && !dense && sel.kind != SD_SEL_WINDOW;
+  const bool slots = d.dtype == SD_BF16 && !scorer_logits;
   if (!dense) {
     idx = sel_idx ? sel_idx : reinterpret_cast<int32_t*>(at(ws, L.sel_idx));
     cnt = sel_count ? sel_count : reinterpret_cast<int32_t*>(at(ws, L.sel_count));
@@ -685,6 +693,7 @@ sd_status entmax_impl(const sdkv::Dims& d, const void* q, const void* k_pages,
       lm.force_local = sel.local;
       Weights w;
       w.logits_out = logits;
+      w.logits_slots = slots;
       if ((st = do_partials(d, q, k_pages, v_pages, block_table, seq_lens, unit, nullptr, nullptr,
                             k_max, nullptr, ws, s, scores, ratio_ppm(sel.r), idx, cnt, nullptr,
                             lm, w)) != SD_OK)
@@ -715,6 +724,7 @@ sd_status entmax_impl(const sdkv::Dims& d, const void* q, const void* k_pages,
   if (!have_logits) {
     Weights w;
     w.logits_out = logits;
+    w.logits_slots = slots;
     if ((st = do_partials(d, q, k_pages, v_pages, block_table, seq_lens, unit, idx, cnt, k_max,
                           nullptr, ws, s, nullptr, -1, nullptr, nullptr, nullptr, ListMode{},
                           w)) != SD_OK)
@@ -724,6 +734,7 @@ sd_status entmax_impl(const sdkv::Dims& d, const void* q, const void* k_pages,
                    tau, E.nch, reinterpret_cast<float*>(at(ws, E.cand)),
                    reinterpret_cast<float*>(at(ws, E.cmax)),
                    reinterpret_cast<int32_t*>(at(ws, E.ccnt))};
+  ta.logits_slots = slots ? 1 : 0;
   if ((st = device_status(sdkv::launch_entmax_tau(ta, s), "entmax threshold kernel launch")) !=
       SD_OK)
     return st;
@@ -731,6 +742,7 @@ sd_status entmax_impl(const sdkv::Dims& d, const void* q, const void* k_pages,
   w.tau = tau;
   w.alpha_m1 = am1;
   w.beta = beta;
+  w.logits_slots = slots;
   int S = 0;
   if ((st = do_partials(d, q, k_pages, v_pages, block_table, seq_lens, unit, idx, cnt, k_max,
                         logits, ws, s, nullptr, -1, nullptr, nullptr, &S, ListMode{}, w)) !=

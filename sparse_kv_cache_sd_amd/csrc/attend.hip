@@ -345,6 +345,9 @@ __global__ __launch_bounds__(kAttendWaves * 64) void attend_mfma_kernel(AttendAr
       : a.logits_tm ? a.token_logits + ((int64_t)b * d.Hkv + g) * d.max_seq * G + min(row, G - 1)
                     : a.token_logits + ((int64_t)b * d.Hq + g * G + min(row, G - 1)) * d.max_seq;
   const int logit_st = a.logits_tm ? G : 1;
+  // slot of the split's first row (slot-indexed logits): chunk c of the
+  // split holds slots slot0 + 16 c .. + 15
+  const int slot0 = sp.e0 * (a.unit == kPage ? d.P : 1);
 
   float4_t acc[CT];
 #pragma unroll
@@ -362,7 +365,7 @@ __global__ __launch_bounds__(kAttendWaves * 64) void attend_mfma_kernel(AttendAr
   // chunk's stored logits (rows 4 quad + r of head `row`) when LOGITS; tk
   // holds those rows' token ids when logits are written out.
   auto process = [&](const u32x4_t (&kv)[KS], const u32x4_t (&vv)[KS], const float (&lg)[4],
-                     const int (&tk)[4], uint32_t vmask) {
+                     const int (&tk)[4], uint32_t vmask, int ci) {
     if constexpr (WM != kWLogits) {
 #pragma unroll
       for (int s = 0; s < KS; ++s)
@@ -377,9 +380,17 @@ __global__ __launch_bounds__(kAttendWaves * 64) void attend_mfma_kernel(AttendAr
     }
     if constexpr (WM == kWLogits) {
       if (row < G) {
+        if (a.logits_slots) {
+          // the chunk's 16 slots: attended rows get their logit, the rest -inf
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if ((vmask >> (4 * quad + r)) & 1u) logit_out_row[tk[r]] = st[r] * d.scale;
+          for (int r = 0; r < 4; ++r)
+            logit_out_row[slot0 + ci * 16 + 4 * quad + r] =
+                ((vmask >> (4 * quad + r)) & 1u) ? st[r] * d.scale : -INFINITY;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if ((vmask >> (4 * quad + r)) & 1u) logit_out_row[tk[r]] = st[r] * d.scale;
+        }
       }
       return;
     }
@@ -459,6 +470,36 @@ __global__ __launch_bounds__(kAttendWaves * 64) void attend_mfma_kernel(AttendAr
       }
     }
     __builtin_amdgcn_wave_barrier();
+    // Entmax weights are exactly zero below the threshold, and most kept
+    // chunks hold no token above it: the window's logits are read first
+    // (one round of loads), and a chunk whose every weight is zero is
+    // skipped -- its V is not read, and it would add nothing.
+    uint32_t live_chunks = 0xFFFFFFFFu;
+    if constexpr (WM == kWEntmax) {
+      float zl[RW][4];
+      bool rv[RW][4];
+#pragma unroll
+      for (int c = 0; c < RW; ++c) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          int t = s_tok[wave][c][4 * quad + r];
+          t = t < 0 ? 0 : (t >= d.max_seq ? d.max_seq - 1 : t);
+          rv[c][r] = s_rows[wave][c][4 * quad + r] >= 0;
+          zl[c][r] = a.logits_slots
+                         ? logit_row[min(slot0 + (r0 + c) * 16 + 4 * quad + r, d.max_seq - 1)]
+                         : logit_row[(int64_t)t * logit_st];
+        }
+      }
+      live_chunks = 0u;
+#pragma unroll
+      for (int c = 0; c < RW; ++c) {
+        bool any = false;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          any = any || (row < G && rv[c][r] && fmaf(a.alpha_m1, zl[c][r], -tau_row) > 0.f);
+        live_chunks |= (__ballot(any) != 0ull ? 1u : 0u) << c;
+      }
+    }
 
     // Two chunks per load batch, double-buffered: batch i+1 is in flight while
     // batch i is processed.  Every load is issued unconditionally (rows that
@@ -475,7 +516,7 @@ __global__ __launch_bounds__(kAttendWaves * 64) void attend_mfma_kernel(AttendAr
       for (int i = 0; i < 2; ++i) {
         const int c = c0 + i;
         int pr = s_rows[wave][min(c, RW - 1)][row];
-        if (c >= nc) pr = -1;
+        if (c >= nc || !((live_chunks >> min(c, 31)) & 1u)) pr = -1;
         mm[i] = (uint32_t)(__ballot(pr >= 0) & 0xFFFFull);
         const bf16_t* kr = pr >= 0 ? kp + (int64_t)pr * D : qrow0;
         const bf16_t* vr = pr >= 0 ? vp + (int64_t)pr * D : qrow0;
@@ -492,25 +533,31 @@ __global__ __launch_bounds__(kAttendWaves * 64) void attend_mfma_kernel(AttendAr
             int t = s_tok[TOK ? wave : 0][min(c, RW - 1)][4 * quad + r];
             t = t < 0 ? 0 : (t >= d.max_seq ? d.max_seq - 1 : t);
             tt[i][r] = t;
-            if constexpr (LOGITS) ll[i][r] = logit_row[(int64_t)t * logit_st];
+            if constexpr (LOGITS)
+              ll[i][r] = a.logits_slots
+                             ? logit_row[min(slot0 + (r0 + c) * 16 + 4 * quad + r, d.max_seq - 1)]
+                             : logit_row[(int64_t)t * logit_st];
             else ll[i][r] = 0.f;
           }
         }
       }
     };
+    // (slot-indexed logits only: the logits-only pass also visits the
+    // window's chunks that attend nothing, to write their -inf slots)
     auto run2 = [&](u32x4_t (&kk)[2][KS], u32x4_t (&vv)[2][KS], float (&ll)[2][4],
-                    int (&tt)[2][4], uint32_t (&mm)[2]) {
+                    int (&tt)[2][4], uint32_t (&mm)[2], int c0) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        if (mm[i] != 0u) process(kk[i], vv[i], ll[i], tt[i], mm[i]);
+        if (mm[i] != 0u || (WM == kWLogits && a.logits_slots && c0 + i < nc))
+          process(kk[i], vv[i], ll[i], tt[i], mm[i], r0 + c0 + i);
     };
     load2(kA, vA, lA, tA, mA, 0);
     for (int c = 0;; c += 4) {
       load2(kB, vB, lB, tB, mB, c + 2);
-      run2(kA, vA, lA, tA, mA);
+      run2(kA, vA, lA, tA, mA, c);
       if (c + 2 >= nc) break;
       load2(kA, vA, lA, tA, mA, c + 4);
-      run2(kB, vB, lB, tB, mB);
+      run2(kB, vB, lB, tB, mB, c + 2);
       if (c + 4 >= nc) break;
     }
   }
@@ -758,6 +805,8 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
   const bool ent = a.tau != nullptr, wl = a.logits_out != nullptr;
   if (ent && (!logits || wl || selects)) return hipErrorInvalidValue;
   if (wl && logits) return hipErrorInvalidValue;
+  if (a.logits_slots && (d.dtype != kBF16 || a.logits_tm || (!wl && !logits) || a.window))
+    return hipErrorInvalidValue;
   if (ent && !(a.alpha_m1 > 0.f && a.alpha_m1 <= 1.f && a.beta >= 1.f)) return hipErrorInvalidValue;
   // chunks of 16 rows a wave holds in one split: E pages of P / 16 chunks,
   // or E listed tokens / 16

@@ -73,9 +73,9 @@ struct Slots {
   const int32_t* list;
   const int32_t* bt;
   const float* row;
-  int k_max, n, U, slots, lp, P, max_pages;
+  int k_max, n, U, slots, lp, P, max_pages, last;
   int64_t num_pages;
-  bool pg;
+  bool pg, by_slot;
 
   __device__ Slots(const TauArgs& a, int b, int bg, int h) {
     const Dims& d = a.d;
@@ -90,14 +90,23 @@ struct Slots {
     slots = pg ? cnt * d.P : cnt;
     row = a.logits + ((int64_t)b * d.Hq + h) * d.max_seq;
     bt = a.block_table + (int64_t)b * d.max_pages;
+    by_slot = a.logits_slots != 0;
+    // the last slot the logits pass wrote: its splits cover the list's k_max
+    // entries, or every unit without a list
+    last = (list ? (pg ? k_max * d.P : k_max) : d.max_seq) - 1;
     max_pages = d.max_pages;
     num_pages = d.num_pages;
   }
   __device__ __forceinline__ int unit_of(int i) const {
+    if (by_slot) return 0;  // not needed
     const int e = pg ? i >> lp : i;
     return list ? list[min(e, k_max - 1)] : e;
   }
   __device__ __forceinline__ float logit_of(int i, int u) const {
+    if (by_slot) {  // slot i directly (its writer put -inf where nothing is attended)
+      const float z = row[min(max(i, 0), last)];  // a bound known without the count
+      return i < slots ? z : -INFINITY;
+    }
     const int t = pg ? (u << lp) + (i & (P - 1)) : u;
     const int tc = t < 0 ? 0 : (t >= n ? max(n - 1, 0) : t);
     const int ph = bt[min(tc >> lp, max_pages - 1)];

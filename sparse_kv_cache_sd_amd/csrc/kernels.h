@@ -109,6 +109,12 @@ struct AttendArgs {
   // logits_out != NULL: no attention; the logits scale * q.K of every
   // attended token are written to logits_out [B][Hq][max_seq] (V not read).
   float* logits_out;
+  // bf16 only: logits_out, and token_logits when read, are indexed by kept
+  // slot instead of token: slot e * P + r for row r of the page at list
+  // entry e (page unit), e for list entry e (token unit), so a split's slots
+  // are one contiguous run.  The logits-only pass then also writes -inf to
+  // the slots of its list range that it does not attend.
+  int logits_slots;
 };
 
 // alpha-entmax threshold of every (sequence, query head) over the logits of
@@ -135,6 +141,10 @@ struct TauArgs {
   float* cand;
   float* cmax;
   int32_t* ccnt;
+  // logits indexed by kept slot (AttendArgs::logits_slots): slot i's logit is
+  // logits[(b*Hq + h)*max_seq + i], -inf where nothing is attended; the list
+  // and block table are then not read
+  int logits_slots;
 };
 constexpr int kTauChunk = 16384;     // kept slots per threshold block
 constexpr int kTauChunkCap = 2048;   // candidates a chunk hands on
