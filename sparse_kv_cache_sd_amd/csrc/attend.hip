@@ -53,8 +53,11 @@ constexpr int kAttendWaves = 8;     // waves per block
 // wave holds many chunks (fewer dependent rounds), 4 when it holds at most 4
 // (the 13-page splits of a 32K-token sequence kept at 0.2 with 8 KV heads:
 // 25.6 -> 24.9 us per step; 8 is better for long lists and dense, 75.9
-// against 78.0 us at 1M tokens).
-constexpr int kResolveWide = 8, kResolveNarrow = 4;
+// against 78.0 us at 1M tokens).  Softmax attention over 9 to 16 chunks per
+// wave resolves them all at once, so no wave stalls on a second round for
+// its last few chunks: the V gather at 128K tokens kept at 0.3 (10 chunks a
+// wave) 27.5 -> 25.9 us, the 1M-token page attention (13) 58.0 -> 57.2 us.
+constexpr int kResolveWide = 8, kResolveNarrow = 4, kResolveLong = 16;
 
 // What a block does with the attended tokens' logits.
 enum WeightMode : int {
@@ -233,7 +236,7 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(MergeArgs a) {
 template <int D, int G, bool LOGITS, int SEL, int WM, int RW>
 __global__ __launch_bounds__(kAttendWaves * 64) void attend_mfma_kernel(AttendArgs a) {
   constexpr int NW = kAttendWaves, NT = NW * 64;
-  static_assert(RW == 4 || RW == 8, "resolve windows of 4 or 8 chunks");
+  static_assert(RW == 4 || RW == 8 || RW == 16, "resolve windows of 4, 8 or 16 chunks");
   constexpr int KS = D / 32;        // 16x16x32 steps over the channels
   constexpr int CT = D / 16;        // 16-channel output tiles
   constexpr int VROW = D + 8;       // staged V row, bf16 elements (16-byte aligned rows)
@@ -781,14 +784,21 @@ static int select_mode(int max_pages) {
 }
 
 // One launch of the matrix-core kernel with the resolve window for the
-// split's chunks per wave.
+// split's chunks per wave (cpw).
 template <int D, int G, bool LOGITS, int SEL, int WM>
-static void go_mfma(const AttendArgs& a, dim3 grid, hipStream_t st, bool narrow) {
+static void go_mfma(const AttendArgs& a, dim3 grid, hipStream_t st, int64_t cpw) {
   constexpr int NT = kAttendWaves * 64;
-  if (narrow)
+  if (cpw <= kResolveNarrow) {
     attend_mfma_kernel<D, G, LOGITS, SEL, WM, kResolveNarrow><<<grid, NT, 0, st>>>(a);
-  else
-    attend_mfma_kernel<D, G, LOGITS, SEL, WM, kResolveWide><<<grid, NT, 0, st>>>(a);
+    return;
+  }
+  if constexpr (WM == kWSoftmax) {
+    if (cpw > kResolveWide && cpw <= kResolveLong) {
+      attend_mfma_kernel<D, G, LOGITS, SEL, WM, kResolveLong><<<grid, NT, 0, st>>>(a);
+      return;
+    }
+  }
+  attend_mfma_kernel<D, G, LOGITS, SEL, WM, kResolveWide><<<grid, NT, 0, st>>>(a);
 }
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
@@ -811,7 +821,7 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
   // chunks of 16 rows a wave holds in one split: E pages of P / 16 chunks,
   // or E listed tokens / 16
   const int64_t nch = a.unit == kPage ? (int64_t)a.E * (d.P / 16) : ((int64_t)a.E + 15) / 16;
-  const bool narrow = (nch + kAttendWaves - 1) / kAttendWaves <= kResolveNarrow;
+  const int64_t cpw = (nch + kAttendWaves - 1) / kAttendWaves;
   const bool ok = dispatch_tdg(d.dtype, d.D, d.G, [&](auto t, auto dd, auto gg) {
     using T = decltype(t);
     constexpr int D = decltype(dd)::value;
@@ -824,8 +834,8 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
       // kept tokens' logits that entmax attention later reads
       auto go = [&](auto sel) {
         constexpr int SEL = decltype(sel)::value;
-        if (wl) go_mfma<D, G, false, SEL, kWLogits>(a, grid, st, narrow);
-        else go_mfma<D, G, false, SEL, kWSoftmax>(a, grid, st, narrow);
+        if (wl) go_mfma<D, G, false, SEL, kWLogits>(a, grid, st, cpw);
+        else go_mfma<D, G, false, SEL, kWSoftmax>(a, grid, st, cpw);
       };
       switch (select_mode(d.max_pages)) {
         case kBlock4: go(std::integral_constant<int, kBlock4>{}); break;
@@ -833,13 +843,13 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
         default: go(std::integral_constant<int, kBlock32>{}); break;
       }
     } else if (wl) {
-      go_mfma<D, G, false, kListed, kWLogits>(a, grid, st, narrow);
+      go_mfma<D, G, false, kListed, kWLogits>(a, grid, st, cpw);
     } else if (logits && ent) {
-      go_mfma<D, G, true, kListed, kWEntmax>(a, grid, st, narrow);
+      go_mfma<D, G, true, kListed, kWEntmax>(a, grid, st, cpw);
     } else if (logits) {
-      go_mfma<D, G, true, kListed, kWSoftmax>(a, grid, st, narrow);
+      go_mfma<D, G, true, kListed, kWSoftmax>(a, grid, st, cpw);
     } else {
-      go_mfma<D, G, false, kListed, kWSoftmax>(a, grid, st, narrow);
+      go_mfma<D, G, false, kListed, kWSoftmax>(a, grid, st, cpw);
     }
   });
   if (!ok) return hipErrorInvalidValue;

@@ -233,6 +233,21 @@ def test_decode_step(name, kw, unit, r):
     compare_step(dev, unit, r)
 
 
+@pytest.mark.parametrize("unit", ["page", "token"])
+@pytest.mark.parametrize("r", [0.1, 0.2, 0.39, 1.0])
+def test_resolve_windows(unit, r):
+    """32 sequences x 8 KV heads fill the 256 CUs with one split each, so a
+    wave of the attention kernel holds about k / 128 chunks of 16 rows: at
+    4096 tokens (256 pages) r 0.1, 0.2, 0.39 and 1 give about 4, 7, 13 and 32
+    chunks per wave -- one narrow, one wide and one long resolve window, and
+    several wide ones.  Lengths are ragged (1000 to 4096 tokens), so many
+    splits end early and their last chunks are masked."""
+    rec = R["batch"].with_(batch=32, seq_len=4096, seq_len_min=1000, num_q_heads=32,
+                           num_kv_heads=8)
+    dev = upload(kvsynth.generate(rec))
+    compare_step(dev, unit, r)
+
+
 @pytest.mark.parametrize("G,d,dtype", [(1, 128, "bf16"), (2, 64, "bf16"), (8, 64, "f32"),
                                        (4, 64, "bf16"), (1, 64, "f32")])
 def test_group_and_head_dim_variants(G, d, dtype):
