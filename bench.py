@@ -131,7 +131,7 @@ def kept_token_count(sel, cnt, seq_lens, unit, P):
 # HBM traffic of the dominant kernel from committed rocprofv3 counter passes
 # ----------------------------------------------------------------------------
 
-KERNEL_SOURCES = ["attend.hip", "score.hip", "topk.h", "device.h", "kernels.h"]
+KERNEL_SOURCES = ["attend.hip", "score.hip", "topk.h", "msel.h", "device.h", "kernels.h"]
 COPY_BYTES = 1 << 30            # one plain copy: 1 GiB read + 1 GiB written
 
 
@@ -179,6 +179,7 @@ PMC_KERNELS = {
              ("dense", r"attend_mfma_kernel<\d+, \d+, false, 0, 0(, \d+)?>"),
              ("merge", r"merge_splits_kernel<")],
     "token": [("attend", r"attend_mfma_kernel<\d+, \d+, true, 0, 0(, \d+)?>"),
+              ("step_attend", r"attend_mfma_kernel<\d+, \d+, true, 1, 0(, \d+)?>"),
               ("score", r"score_tokens_(mfma|f32)_kernel<"),
               ("dense", r"attend_mfma_kernel<\d+, \d+, false, 0, 0(, \d+)?>"),
               ("merge", r"merge_splits_kernel<")],

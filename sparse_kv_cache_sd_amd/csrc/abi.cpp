@@ -463,6 +463,70 @@ sd_status do_merge(const sdkv::Dims& d, float* out, float* lse, void* ws, hipStr
   return device_status(sdkv::launch_merge(a, st), "merge kernel launch");
 }
 
+// The plain top-k in token unit past one block's selection (bf16): the
+// many-block top-k's placement runs inside the attention kernel, whose split
+// j of (b, g) is then a range of kSliceUnits >> l units (l returned, the
+// largest up to 3 that keeps NB << l within the splits the partials hold).
+// -1: not this path (more slices than splits, or another selection).
+int sliced_sub_log2(const sdkv::Dims& d, int unit, const Sel& sel) {
+  if (unit != SD_UNIT_TOKEN || d.dtype != SD_BF16 || sel.kind != SD_SEL_TOPK || sel.r >= 1.0 ||
+      !multi_select(d, unit))
+    return -1;
+  const int64_t NB = ceil_div(units_max(d, unit), sdkv::kSliceUnits);
+  const int64_t S = max_splits(d);
+  if (NB > S) return -1;
+  int l = 0;
+  while (l < 3 && (NB << (l + 1)) <= S) ++l;
+  return l;
+}
+
+// Top-k selection and attention of that path: the histogram and candidate
+// launches of the many-block top-k, then the attention with the placement
+// (it writes the kept list to idx / cnt).
+sd_status do_sliced_attend(const sdkv::Dims& d, const void* q, const void* kp, const void* vp,
+                           const int32_t* bt, const int32_t* sl, double r_kv, int sub_log2,
+                           const float* scores, const float* logits, const uint32_t* score_mm,
+                           int32_t* idx, int32_t* cnt, void* msel_ws, void* ws, hipStream_t st,
+                           int* S_out) {
+  const int U = units_max(d, SD_UNIT_TOKEN);
+  const int R = ratio_ppm(r_kv);
+  const int k = static_cast<int>(keep_count_ppm(R, U));
+  sdkv::SelectArgs sa{d, SD_UNIT_TOKEN, sl, scores, U, k, R, idx, cnt};
+  sdkv::SliceSel ss;
+  sd_status s;
+  if ((s = device_status(sdkv::launch_select_multi_bins(sa, score_mm, score_mm_parts(d),
+                                                         sdkv::score_units_per_block(d.dtype, d.D),
+                                                         msel_ws, st, &ss),
+                         "select kernels launch")) != SD_OK)
+    return s;
+  const Layout L = layout(d, SD_UNIT_TOKEN, 1.0);
+  sdkv::AttendArgs a{};
+  a.d = d;
+  a.unit = SD_UNIT_TOKEN;
+  a.q = q;
+  a.k_pages = kp;
+  a.v_pages = vp;
+  a.block_table = bt;
+  a.seq_lens = sl;
+  a.k_max = k;
+  a.R_ppm = R;
+  a.token_logits = logits;
+  a.logits_tm = 1;
+  a.sl = ss;
+  a.sub_log2 = sub_log2;
+  a.S = ss.NB << sub_log2;
+  // the expected kept units of a range (the resolve window only)
+  const int64_t range = sdkv::kSliceUnits >> sub_log2;
+  a.E = static_cast<int>(ceil_div(ceil_div(static_cast<int64_t>(k) * range, U), 16) * 16);
+  a.part_o = reinterpret_cast<float*>(at(ws, L.part_o));
+  a.part_lse = reinterpret_cast<float*>(at(ws, L.part_lse));
+  a.split_count = reinterpret_cast<int32_t*>(at(ws, L.split_count));
+  a.sel_out = idx;
+  a.sel_count_out = cnt;
+  *S_out = a.S;
+  return device_status(sdkv::launch_attend(a, st), "attention kernel launch");
+}
+
 // Whether the top-k can run inside the attention kernel: page unit, bf16, at
 // most kMaxSelectU pages per sequence, and a split slice that fits the
 // kernel's LDS list.
@@ -589,6 +653,13 @@ sd_status decode_impl(const sdkv::Dims& d, const void* q, const void* k_pages,
                             sel_idx, sel_count, ws, s);
   int32_t* idx = sel_idx ? sel_idx : reinterpret_cast<int32_t*>(at(ws, L.sel_idx));
   int32_t* cnt = sel_count ? sel_count : reinterpret_cast<int32_t*>(at(ws, L.sel_count));
+  const int sub = tm ? sliced_sub_log2(d, unit, sel) : -1;
+  if (sub >= 0) {
+    if ((st = do_sliced_attend(d, q, k_pages, v_pages, block_table, seq_lens, sel.r, sub, scores,
+                               logits, smm, idx, cnt, at(ws, L.msel), ws, s, &S)) != SD_OK)
+      return st;
+    return do_merge(d, out, lse, ws, s, S);
+  }
   if ((st = do_select_list(d, unit, seq_lens, scores, logits, sel, idx, cnt, at(ws, L.msel),
                            reinterpret_cast<int32_t*>(at(ws, L.topk_tmp)),
                            reinterpret_cast<int32_t*>(at(ws, L.topk_cnt)), s, smm)) != SD_OK)

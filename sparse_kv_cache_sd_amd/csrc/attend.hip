@@ -39,7 +39,7 @@
 // then block table) into LDS, then K/V loads run two chunks at a time,
 // double-buffered.  The fp32 kernel keeps the same split structure with
 // vector FMAs.
-#include "topk.h"
+#include "msel.h"
 
 namespace sdkv {
 
@@ -69,6 +69,7 @@ enum WeightMode : int {
 // How a block obtains its kept list.
 enum SelMode : int {
   kListed = 0,     // from memory (sel_idx) or the identity
+  kSliced = 1,     // token unit: placed in the kernel from the many-block top-k's candidates
   kBlock4 = 4,     // in-kernel top-k by the whole block, 4 / 8 / 32 keys per thread
   kBlock8 = 8,
   kBlock32 = 32
@@ -240,8 +241,13 @@ __global__ __launch_bounds__(kAttendWaves * 64) void attend_mfma_kernel(AttendAr
   constexpr int KS = D / 32;        // 16x16x32 steps over the channels
   constexpr int CT = D / 16;        // 16-channel output tiles
   constexpr int VROW = D + 8;       // staged V row, bf16 elements (16-byte aligned rows)
-  constexpr bool SELECTS = SEL != kListed;
+  constexpr bool SLICED = SEL == kSliced;
+  constexpr bool SELECTS = SEL != kListed && !SLICED;  // page top-k in the kernel
+  constexpr bool LOCAL = SELECTS || SLICED;            // the list is built in LDS
   constexpr int KEYS = SELECTS ? SEL : 1;
+  constexpr int KK = SLICED ? msel::kMK : KEYS;        // keys per thread of the kept bitmap
+  static_assert(!SLICED || (LOGITS && WM == kWSoftmax && NW == msel::kMNW),
+                "placement: softmax over stored logits, one placement block");
   constexpr bool TOK = LOGITS || WM == kWLogits;  // rows' token ids are kept
   static_assert(WM != kWEntmax || LOGITS, "entmax weights read stored logits");
   static_assert(WM != kWLogits || !LOGITS, "logits are computed from K");
@@ -254,9 +260,10 @@ __global__ __launch_bounds__(kAttendWaves * 64) void attend_mfma_kernel(AttendAr
   __shared__ float s_m[NW][16], s_l[NW][16];
   __shared__ __align__(16) float s_po[G * D];
   __shared__ float s_plse[G];
-  __shared__ int s_list[SELECTS ? kMaxSelectE : 1];
+  __shared__ int s_list[SLICED ? kSliceUnits : (SELECTS ? kMaxSelectE : 1)];
   __shared__ RadixState s_rs;
-  __shared__ KeptScratch<SELECTS ? KEYS : 1, NW> s_kept;
+  __shared__ msel::MShared s_ms;
+  __shared__ KeptScratch<LOCAL ? KK : 1, NW> s_kept;
   auto s_v = reinterpret_cast<bf16_t(*)[16 * VROW]>(s_raw);
   auto s_o = reinterpret_cast<float(*)[G][D]>(s_raw);
 
@@ -270,10 +277,7 @@ __global__ __launch_bounds__(kAttendWaves * 64) void attend_mfma_kernel(AttendAr
   const bf16_t* vp = static_cast<const bf16_t*>(a.v_pages);
   const int32_t* list = a.sel_idx ? a.sel_idx + bg * a.k_max : nullptr;
   const int units_cap = a.unit == kPage ? d.max_pages : d.max_seq;
-  const Span sp = span_of(a, j, (list || SELECTS || a.window) ? a.k_max : units_cap);
-  // chunks [w_lo, w_hi) of this block belong to this wave
-  const int cpw = (sp.nch + NW - 1) / NW;
-  const int w_lo = min(sp.nch, wave * cpw), w_hi = min(sp.nch, w_lo + cpw);
+  Span sp = span_of(a, j, (list || LOCAL || a.window) ? a.k_max : units_cap);
 
   // In-kernel selection: the scores of (b, g) are read before the sequence
   // length is known (a row holds max_pages of them).
@@ -312,12 +316,75 @@ __global__ __launch_bounds__(kAttendWaves * 64) void attend_mfma_kernel(AttendAr
     if (j == 0 && a.sel_count_out && threadIdx.x == 0) a.sel_count_out[bg] = kept;
     cnt = kept;
     __syncthreads();
+  } else if constexpr (SLICED) {
+    // The placement of the many-block top-k for slice j >> sub_log2 (every
+    // block of the slice alike), then the kept units of this split's range
+    // into the LDS list, in unit order, and to sel_out at their place.
+    msel::MArgs ma{};
+    ma.d = d;
+    ma.unit = a.unit;
+    ma.seq_lens = a.seq_lens;
+    ma.scores = a.sl.scores;
+    ma.U_max = units_cap;
+    ma.k_max = a.k_max;
+    ma.R_ppm = a.R_ppm;
+    ma.NB = a.sl.NB;
+    ma.mm = a.sl.mm;
+    ma.mm_nb = a.sl.mm_nb;
+    ma.mm_per = a.sl.mm_per;
+    ma.above = const_cast<uint32_t*>(a.sl.above);
+    ma.ccount = const_cast<uint32_t*>(a.sl.ccount);
+    ma.cand = const_cast<uint2*>(a.sl.cand);
+    const int slice = j >> a.sub_log2, sub = j - (slice << a.sub_log2);
+    const msel::PlaceLoads pl = msel::place_loads(ma, bg);
+    uint32_t mkey[msel::kMK];
+    const msel::Group gr = msel::group_setup(ma, s_ms, mkey, bg, slice);
+    const int R = kSliceUnits >> a.sub_log2;  // units of this split
+    constexpr int W = msel::kMK * NW;         // bitmap words of a slice
+    const int wd0 = (sub * R) >> 6, wd1 = ((sub + 1) * R) >> 6;
+    int32_t* full = a.sel_out ? a.sel_out + bg * a.k_max : nullptr;
+    if (j == 0 && a.sel_count_out && threadIdx.x == 0) a.sel_count_out[bg] = gr.k;
+    int kept = 0;
+    if (gr.k > 0 && gr.s0 < gr.U) {  // uniform
+      const int u_lo = gr.s0 + sub * R;
+      if (gr.k == gr.U) {
+        kept = max(0, min(R, gr.U - u_lo));
+        for (int e = threadIdx.x; e < kept; e += NT) {
+          s_list[e] = u_lo + e;
+          if (full) full[u_lo + e] = u_lo + e;
+        }
+      } else {
+        uint32_t T, quota, base;
+        bool whole;
+        msel::place_bounds(ma, s_ms, gr, pl, &T, &quota, &whole, &base);
+        kept_words<msel::kMK, NW>(s_kept.mask, s_kept.tie, s_kept.base, mkey,
+                                  min(kSliceUnits, gr.U - gr.s0), T, quota, whole, 0,
+                                  0x7FFFFFFF, &s_kept.total);
+        // ranks in the slice of the range's first and last kept units
+        const uint32_t r_lo = wd0 < W ? s_kept.base[wd0] : s_kept.total;
+        const uint32_t r_hi = wd1 < W ? s_kept.base[wd1] : s_kept.total;
+        kept = (int)(r_hi - r_lo);
+        emit_kept<msel::kMK, NW>(s_kept.mask, s_kept.base, r_lo, r_hi, [&](int pos, int u) {
+          s_list[pos - (int)r_lo] = gr.s0 + u;
+          const uint32_t gp = base + (uint32_t)pos;
+          if (full && gp < (uint32_t)gr.k) full[gp] = gr.s0 + u;
+        });
+      }
+    }
+    cnt = kept;
+    sp.e0 = 0;
+    sp.e_hi = kept;
+    sp.nch = (kept + 15) / 16;
+    __syncthreads();
   } else {
     w0 = window_start(a, U);
     cnt = list ? min(a.sel_count[bg], a.k_max) : U - w0;
   }
+  // chunks [w_lo, w_hi) of this block belong to this wave
+  const int cpw = (sp.nch + NW - 1) / NW;
+  const int w_lo = min(sp.nch, wave * cpw), w_hi = min(sp.nch, w_lo + cpw);
   auto unit_at = [&](int e) -> int {
-    if constexpr (SELECTS) return e < cnt ? s_list[e - sp.e0] : -1;
+    if constexpr (LOCAL) return e < cnt ? s_list[e - sp.e0] : -1;
     else {
       // one unconditional load (a valid dummy address in identity mode)
       const int v = *(list ? list + e : a.seq_lens + b);
@@ -818,8 +885,14 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
   if (a.logits_slots && (d.dtype != kBF16 || a.logits_tm || (!wl && !logits) || a.window))
     return hipErrorInvalidValue;
   if (ent && !(a.alpha_m1 > 0.f && a.alpha_m1 <= 1.f && a.beta >= 1.f)) return hipErrorInvalidValue;
+  const bool sliced = a.sl.NB > 0;
+  if (sliced && (a.unit != kToken || d.dtype != kBF16 || selects || a.sel_idx || a.window || ent ||
+                 wl || !logits || !a.logits_tm || a.logits_slots || a.sub_log2 < 0 ||
+                 a.sub_log2 > 3 || a.S != (a.sl.NB << a.sub_log2) || !a.sl.scores || !a.sl.mm ||
+                 !a.sl.above || !a.sl.ccount || !a.sl.cand))
+    return hipErrorInvalidValue;
   // chunks of 16 rows a wave holds in one split: E pages of P / 16 chunks,
-  // or E listed tokens / 16
+  // or E listed tokens / 16 (sliced: the expected kept units of a range)
   const int64_t nch = a.unit == kPage ? (int64_t)a.E * (d.P / 16) : ((int64_t)a.E + 15) / 16;
   const int64_t cpw = (nch + kAttendWaves - 1) / kAttendWaves;
   const bool ok = dispatch_tdg(d.dtype, d.D, d.G, [&](auto t, auto dd, auto gg) {
@@ -842,6 +915,8 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
         case kBlock8: go(std::integral_constant<int, kBlock8>{}); break;
         default: go(std::integral_constant<int, kBlock32>{}); break;
       }
+    } else if (sliced) {
+      go_mfma<D, G, true, kSliced, kWSoftmax>(a, grid, st, cpw);
     } else if (wl) {
       go_mfma<D, G, false, kListed, kWLogits>(a, grid, st, cpw);
     } else if (logits && ent) {

@@ -69,6 +69,22 @@ struct SelectArgs {
   int32_t* sel_count;  // [B][Hkv]
 };
 
+// Units per slice of the many-block top-k (select_multi.hip).
+constexpr int kSliceUnits = 4096;
+
+// Where the many-block top-k's first two launches (value histograms, then
+// the bin of the k-th largest score and its candidates) leave their results,
+// for a placement of the kept units that another kernel runs.
+struct SliceSel {
+  int NB = 0;                     // slices per (sequence, KV head); 0: none
+  const float* scores = nullptr;  // [B][Hkv][U_max] unit scores
+  const uint32_t* mm = nullptr;   // [B*Hkv][mm_nb][2] partial min / max keys
+  int mm_nb = 0, mm_per = 0;
+  const uint32_t* above = nullptr;   // [B*Hkv][NB] keys above the bin, per slice
+  const uint32_t* ccount = nullptr;  // [B*Hkv][NB] keys in the bin, per slice
+  const uint2* cand = nullptr;       // [B*Hkv][NB][64] (key, unit) candidates
+};
+
 struct AttendArgs {
   Dims d;
   int unit;
@@ -115,6 +131,16 @@ struct AttendArgs {
   // are one contiguous run.  The logits-only pass then also writes -inf to
   // the slots of its list range that it does not attend.
   int logits_slots;
+  // Token unit, bf16, with sl.NB > 0: the kept list is placed inside the
+  // kernel from the many-block top-k's candidates (sel_idx, unit_scores
+  // NULL; softmax over token_logits, token-major).  Split j of (b, g) covers
+  // units [j R, (j + 1) R), R = kSliceUnits >> sub_log2 (S = NB << sub_log2):
+  // every block finds the kept units of its slice as the placement launch
+  // would (keep count min(keep_count(U, R_ppm), k_max)), attends those in
+  // its range and writes them to sel_out [B][Hkv][k_max] at their place in
+  // the group's list (split 0 writes sel_count_out).
+  SliceSel sl;
+  int sub_log2;
 };
 
 // alpha-entmax threshold of every (sequence, query head) over the logits of
@@ -259,6 +285,10 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t st);
 size_t msel_workspace_bytes(int B, int Hkv, int U_max);
 hipError_t launch_select_multi(const SelectArgs& a, const uint32_t* mm, int mm_nb, int mm_per,
                                void* ws, hipStream_t st, const int32_t* k_of = nullptr);
+// The first two launches only (mm given, k_of NULL); *out receives where
+// their results live, for the attention kernel's placement (AttendArgs::sl).
+hipError_t launch_select_multi_bins(const SelectArgs& a, const uint32_t* mm, int mm_nb,
+                                    int mm_per, void* ws, hipStream_t st, SliceSel* out);
 // Log-sum-exp merge of the split partials written by an attention launch.
 struct MergeArgs {
   Dims d;

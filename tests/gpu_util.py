@@ -149,3 +149,27 @@ def compare_step(dev: Dev, unit: str, r_kv: float, groups=None, report=None, cou
     if report is not None:
         report.append((unit, r_kv, err_o, err_l))
     return err_o, err_l
+
+
+def own_topk_property(dev, unit: str, r_kv: float, sel: np.ndarray, cnt: np.ndarray):
+    """The kept set of every (b, g) is the top-k of the library's own unit
+    scores, ties to the lower id, in ascending order."""
+    s = dev.shape
+    umax = s.units_max(unit)
+    scores = torch.empty((s.batch, s.num_kv_heads, umax), dtype=torch.float32, device="cuda")
+    logits = (torch.empty((s.batch, s.num_q_heads, s.max_seq_len), dtype=torch.float32,
+                          device="cuda") if unit == "token" else None)
+    sd.score_pages(s, dev.q, dev.k, dev.bounds, dev.bt, dev.sl, unit, scores, logits)
+    torch.cuda.synchronize()
+    sc = scores.cpu().numpy()
+    P = s.page_size
+    for b in range(s.batch):
+        n = int(dev.w.seq_lens[b])
+        U = -(-n // P) if unit == "page" else n
+        k = sdref.keep_count(r_kv, U)
+        assert int(cnt[b].min()) == k and int(cnt[b].max()) == k, f"b={b}: count != {k}"
+        for g in range(s.num_kv_heads):
+            x = sc[b, g, :U].astype(np.float64)
+            assert np.all(np.isfinite(x))
+            ref = np.sort(np.lexsort((np.arange(U), -x))[:k])
+            np.testing.assert_array_equal(sel[b, g, :k], ref, err_msg=f"(b={b}, g={g})")

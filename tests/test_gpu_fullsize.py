@@ -26,7 +26,7 @@ import kvsynth
 import sparse_kv_cache_sd_amd as sd
 from oracle import sdref
 
-from gpu_util import compare_step, run_decode, upload
+from gpu_util import compare_step, own_topk_property, run_decode, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -47,30 +47,6 @@ def _dev(name: str, context: int | None):
         raise ValueError(name)
     print(f"[fullsize] generating {name} context={context}", flush=True)
     return upload(kvsynth.generate(rec))
-
-
-def _own_topk_property(dev, unit: str, r_kv: float, sel: np.ndarray, cnt: np.ndarray):
-    """The kept set of every (b, g) is the top-k of the library's own unit
-    scores, ties to the lower id, in ascending order."""
-    s = dev.shape
-    umax = s.units_max(unit)
-    scores = torch.empty((s.batch, s.num_kv_heads, umax), dtype=torch.float32, device="cuda")
-    logits = (torch.empty((s.batch, s.num_q_heads, s.max_seq_len), dtype=torch.float32,
-                          device="cuda") if unit == "token" else None)
-    sd.score_pages(s, dev.q, dev.k, dev.bounds, dev.bt, dev.sl, unit, scores, logits)
-    torch.cuda.synchronize()
-    sc = scores.cpu().numpy()
-    P = s.page_size
-    for b in range(s.batch):
-        n = int(dev.w.seq_lens[b])
-        U = -(-n // P) if unit == "page" else n
-        k = sdref.keep_count(r_kv, U)
-        assert int(cnt[b].min()) == k and int(cnt[b].max()) == k, f"b={b}: count != {k}"
-        for g in range(s.num_kv_heads):
-            x = sc[b, g, :U].astype(np.float64)
-            assert np.all(np.isfinite(x))
-            ref = np.sort(np.lexsort((np.arange(U), -x))[:k])
-            np.testing.assert_array_equal(sel[b, g, :k], ref, err_msg=f"(b={b}, g={g})")
 
 
 def _finite(out, lse):
@@ -112,7 +88,7 @@ def test_full_size(cid, name, context, unit, r_kv, groups, n_exact):
     if r_kv < 1.0:
         out, lse, sel, cnt = run_decode(dev, unit, r_kv)
         _finite(out, lse)
-        _own_topk_property(dev, unit, r_kv, sel, cnt)
+        own_topk_property(dev, unit, r_kv, sel, cnt)
     counts = {}
     e_o, e_l = compare_step(dev, unit, r_kv, groups=groups, counts=counts)
     assert counts.get("exact", 0) == n_exact, counts
@@ -162,7 +138,7 @@ def test_full_size_entmax(cid, name, context, unit, r_kv, groups):
     s, w = dev.shape, dev.w
     out, tau, idx, cnt = _entmax_step(dev, unit, r_kv, alpha)
     assert np.all(np.isfinite(out)) and np.all(np.isfinite(tau))
-    _own_topk_property(dev, unit, r_kv, idx, cnt)
+    own_topk_property(dev, unit, r_kv, idx, cnt)
     if groups == "all":
         groups = [(b, g) for b in range(s.batch) for g in range(s.num_kv_heads)]
     elif groups == "extremes":

@@ -12,7 +12,8 @@ import kvsynth
 import sparse_kv_cache_sd_amd as sd
 from oracle import sdref
 
-from gpu_util import GAP, compare_step, host_f64, oracle_group, t_dev, upload
+from gpu_util import (GAP, compare_step, host_f64, oracle_group, own_topk_property,
+                      run_decode, t_dev, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -246,6 +247,63 @@ def test_resolve_windows(unit, r):
                            num_kv_heads=8)
     dev = upload(kvsynth.generate(rec))
     compare_step(dev, unit, r)
+
+
+# Token unit past 16384 units with the plain top-k: the many-block top-k's
+# histogram and candidate launches run, then the attention kernel places the
+# kept units itself, each split a range of 4096 >> l units of one slice.  The
+# shapes reach l = 0, 2 and 3, the listed path (more slices than splits), a
+# keep ratio that keeps every unit, and ragged batches with short sequences.
+PLACE_CASES = [
+    ("b1-h8-20k", "sweep", dict(seq_len=20000), 0.2),
+    ("b2-h2-ragged", "batch", dict(batch=2, seq_len=41000, seq_len_min=17000, num_q_heads=8,
+                                   num_kv_heads=2), 0.3),
+    ("b1-h1-30k", "sweep", dict(seq_len=30000, num_q_heads=4, num_kv_heads=1), 0.3),
+    ("b4-h8-ragged", "batch", dict(batch=4, seq_len=24000, seq_len_min=100), 0.25),
+    ("b8-h8-listed", "batch", dict(batch=8, seq_len=20000, seq_len_min=16000), 0.3),
+    ("keep-all", "sweep", dict(seq_len=20000, num_q_heads=8, num_kv_heads=2), 0.99999),
+]
+
+
+@pytest.mark.parametrize("cid,name,kw,r", PLACE_CASES, ids=[c[0] for c in PLACE_CASES])
+def test_token_topk_placed_in_attention(cid, name, kw, r):
+    dev = upload(kvsynth.generate(_recipe(name, **kw)))
+    compare_step(dev, "token", r)
+    _, _, sel, cnt = run_decode(dev, "token", r)
+    own_topk_property(dev, "token", r, sel, cnt)
+
+
+def test_token_placement_flat_scores():
+    """q = 0: every score is 0, so no value bins form and the placement takes
+    the radix fallback inside the attention kernel; equal scores go to the
+    lower ids, so the kept list is 0 .. k - 1."""
+    w = kvsynth.generate(_recipe("sweep", seq_len=20000, num_q_heads=8, num_kv_heads=2))
+    w.q[...] = 0
+    dev = upload(w)
+    compare_step(dev, "token", 0.3)
+    _, _, sel, cnt = run_decode(dev, "token", 0.3)
+    k = sdref.keep_count(0.3, 20000)
+    for g in range(2):
+        assert int(cnt[0, g]) == k
+        np.testing.assert_array_equal(sel[0, g, :k], np.arange(k))
+
+
+def test_token_placement_tied_run():
+    """8000 tokens of each KV head share the key of its highest score, so the
+    k-th largest (k = 4800) lies inside a run of ties that spans slices: more
+    candidates than a slice hands on, the radix fallback, and each slice's
+    quota of ties (the lowest ids first)."""
+    rec = _recipe("sweep", seq_len=24000, num_q_heads=8, num_kv_heads=2)
+    w = kvsynth.generate(rec)
+    G = rec.num_q_heads // rec.num_kv_heads
+    for g in range(rec.num_kv_heads):
+        sig = (w.K[0, g, :24000].astype(np.float64) @
+               w.q[0, g * G:(g + 1) * G].astype(np.float64).T).max(axis=1)
+        w.K[0, g, 3000:11000] = w.K[0, g, int(np.argmax(sig))]
+    dev = upload(w)
+    compare_step(dev, "token", 0.2)
+    _, _, sel, cnt = run_decode(dev, "token", 0.2)
+    own_topk_property(dev, "token", 0.2, sel, cnt)
 
 
 @pytest.mark.parametrize("G,d,dtype", [(1, 128, "bf16"), (2, 64, "bf16"), (8, 64, "f32"),
