@@ -20,7 +20,9 @@
 // identity (dense), or is computed by the block itself from the page scores:
 // every split of (b, g) runs the same exact top-k (topk.h, all eight waves)
 // and keeps its slice, which saves a kernel launch and a round trip through
-// memory.
+// memory.  In token unit past one block's selection the block instead places
+// the kept units of its range of one slice from the many-block top-k's
+// candidates (msel.h), the last step of that top-k.
 //
 // bf16 kernel (matrix cores).  Per chunk and wave:
 //   S^T[t][h] = sum_c K[t][c] Q[h][c]   4 x mfma 16x16x32 bf16 (d = 128): K rows
