@@ -253,7 +253,8 @@ def test_resolve_windows(unit, r):
 # histogram and candidate launches run, then the attention kernel places the
 # kept units itself, each split a range of 4096 >> l units of one slice.  The
 # shapes reach l = 0, 2 and 3, the listed path (more slices than splits), a
-# keep ratio that keeps every unit, and ragged batches with short sequences.
+# keep ratio that keeps every unit, ragged batches with short sequences,
+# groups of 1, 2, 4 and 8 query heads, d = 64 and 64-token pages.
 PLACE_CASES = [
     ("b1-h8-20k", "sweep", dict(seq_len=20000), 0.2),
     ("b2-h2-ragged", "batch", dict(batch=2, seq_len=41000, seq_len_min=17000, num_q_heads=8,
@@ -262,6 +263,10 @@ PLACE_CASES = [
     ("b4-h8-ragged", "batch", dict(batch=4, seq_len=24000, seq_len_min=100), 0.25),
     ("b8-h8-listed", "batch", dict(batch=8, seq_len=20000, seq_len_min=16000), 0.3),
     ("keep-all", "sweep", dict(seq_len=20000, num_q_heads=8, num_kv_heads=2), 0.99999),
+    ("g8", "sweep", dict(seq_len=20000, num_q_heads=64, num_kv_heads=8), 0.3),
+    ("g1-d64", "sweep", dict(seq_len=20000, num_q_heads=2, num_kv_heads=2, head_dim=64), 0.3),
+    ("g2-page64", "batch", dict(batch=2, seq_len=30000, seq_len_min=17000, num_q_heads=8,
+                                num_kv_heads=4, page_size=64), 0.2),
 ]
 
 
