@@ -114,6 +114,15 @@ def attend_bytes(kept_tokens, d, elem, token_unit):
     return kept_tokens * (1 if token_unit else 2) * d * elem
 
 
+def fixed_cost_us(us_sparse, us_dense, b_sparse, b_dense):
+    """The sparse step's time beyond its bytes at the dense step's rate:
+    us_sparse - us_dense * b_sparse / b_dense ("Where Activation Sparsity and
+    KV-Cache Sparsity Cross in LLM Decoding", list view, Table 10: the
+    selection's cost beyond byte time).  Positive: fixed costs (launches,
+    selection, latency chains) the byte account does not see."""
+    return us_sparse - us_dense * b_sparse / b_dense
+
+
 def kept_token_count(sel, cnt, seq_lens, unit, P):
     total = 0
     for b in range(sel.shape[0]):
@@ -692,6 +701,7 @@ def measure_workload(name, args, torch, sd, kvsynth, stream, *, selection_kind="
                   "bytes_per_step": int(b_dense)},
         "speedup_vs_dense": round(us_dense / us_sparse, 3),
         "byte_bound_speedup": round(b_dense / b_sparse, 3),
+        "fixed_cost_us": round(fixed_cost_us(us_sparse, us_dense, b_sparse, b_dense), 3),
         "attend": {"us_per_launch": round(us_attend, 3), "bytes_per_launch": int(b_attend),
                    "achieved_gbps": round(gbps_att, 1),
                    "frac": round(gbps_att / HBM_PEAK_GBPS, 4)},
@@ -765,6 +775,7 @@ def point_summary(res):
             "dense_us_per_step_layer": res["dense"]["us_per_step_layer"],
             "speedup_vs_dense": res["speedup_vs_dense"],
             "byte_bound_speedup": res["byte_bound_speedup"],
+            "fixed_cost_us": res["fixed_cost_us"],
             "attend_us": a["us_per_launch"], "attend_frac": a["frac"],
             "attend_traffic_bytes": res["traffic"],
             "attend_traffic_ratio": (round(res["traffic"] / a["bytes_per_launch"], 3)
@@ -950,6 +961,7 @@ def main():
             "dense": res["dense"],
             "speedup_vs_dense": res["speedup_vs_dense"],
             "byte_bound_speedup": res["byte_bound_speedup"],
+            "fixed_cost_us": res["fixed_cost_us"],
             "roofline": {
                 "kernel": ("whole alpha-entmax decode step (sd_decode_step_entmax)" if entmax else
                            "attend_mfma_kernel: split-K attention partials over the stored kept "

@@ -71,6 +71,14 @@ def test_attend_bytes():
     assert bench.attend_bytes(100, 128, 2, token_unit=True) == 100 * 128 * 2
 
 
+def test_fixed_cost_is_time_beyond_bytes_at_dense_rate():
+    # a step that moves a third of the dense bytes in half the dense time
+    # spends 50 - 100 / 3 us beyond its byte time
+    assert abs(bench.fixed_cost_us(50.0, 100.0, 1.0e6, 3.0e6) - (50.0 - 100.0 / 3)) < 1e-9
+    # exactly byte-bound at the dense rate: no fixed cost
+    assert bench.fixed_cost_us(25.0, 100.0, 1.0, 4.0) == 0.0
+
+
 def test_kept_token_count_partial_last_page():
     # one sequence of 40 tokens, pages of 16: pages 0, 1, 2 hold 16, 16, 8 tokens
     sel = np.array([[[0, 2], [1, 2]]], dtype=np.int32)
