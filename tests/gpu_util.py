@@ -125,8 +125,15 @@ def compare_step(dev: Dev, unit: str, r_kv: float, groups=None, report=None, cou
         groups = [(b, g) for b in range(s.batch) for g in range(s.num_kv_heads)]
     err_o = err_l = 0.0
     for b, g in groups:
-        orc = oracle_group(w, b, g, unit, r_kv, scale)
         heads = slice(g * G, (g + 1) * G)
+        if int(w.seq_lens[b]) == 0:
+            # an empty sequence keeps nothing and gives out = 0, lse = -inf
+            # (the oracle takes no empty instance)
+            assert np.all(out[b, heads] == 0) and np.all(np.isneginf(lse[b, heads]))
+            if r_kv < 1.0:
+                assert int(cnt[b, g]) == 0
+            continue
+        orc = oracle_group(w, b, g, unit, r_kv, scale)
         if r_kv >= 1.0:
             ref_o, ref_l = orc.out_dense, orc.lse_dense
         else:
