@@ -180,3 +180,32 @@ def own_topk_property(dev, unit: str, r_kv: float, sel: np.ndarray, cnt: np.ndar
             assert np.all(np.isfinite(x))
             ref = np.sort(np.lexsort((np.arange(U), -x))[:k])
             np.testing.assert_array_equal(sel[b, g, :k], ref, err_msg=f"(b={b}, g={g})")
+
+
+def random_shapes(n, seed, allow_empty=True, max_len=36000):
+    """n seeded random decode-step shapes the library accepts: (id, recipe
+    keyword arguments for the "batch" recipe, unit, r_kv, empty) with batch
+    1-4, G and H_kv in {1, 2, 4, 8}, d in {64, 128}, pages of 16 or 64 tokens,
+    bf16 or fp32, ragged lengths up to max_len, and (empty) the last sequence
+    of a batch to be emptied by the caller."""
+    rng = np.random.default_rng(seed)
+    lens = [x for x in (300, 2000, 9000, 20000, 36000) if x <= max_len]
+    out = []
+    for i in range(n):
+        G = int(rng.choice([1, 2, 4, 8]))
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        d = int(rng.choice([64, 128]))
+        P = int(rng.choice([16, 64]))
+        dtype = "f32" if rng.random() < 0.25 else "bf16"
+        B = int(rng.integers(1, 5))
+        unit = "token" if rng.random() < 0.5 else "page"
+        n_max = int(rng.choice(lens))
+        n_min = int(rng.integers(1, n_max + 1)) if B > 1 else n_max
+        r = float(rng.choice([0.02, 0.1, 0.3, 0.5, 0.9, 1.0]))
+        empty = allow_empty and B > 1 and rng.random() < 0.3
+        out.append((f"{i:02d}-B{B}-G{G}-H{Hkv}-d{d}-P{P}-{dtype}-{unit}-n{n_max}-r{r}"
+                    + ("-empty" if empty else ""),
+                    dict(batch=B, num_q_heads=G * Hkv, num_kv_heads=Hkv, head_dim=d,
+                         page_size=P, dtype=dtype, seq_len=n_max, seq_len_min=n_min,
+                         seed=seed + i), unit, r, empty))
+    return out

@@ -26,7 +26,7 @@ import kvsynth
 import sparse_kv_cache_sd_amd as sd
 from oracle import entmaxref, sdref
 
-from gpu_util import GAP, TOL, check_selection, upload
+from gpu_util import GAP, TOL, check_selection, random_shapes, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -319,3 +319,35 @@ def test_entmax_flat_logits_bf16_pages(seq_len, alpha):
         # tau solves n * (-tau)^beta = 1
         want = -(1.0 / n) ** (alpha - 1.0)
         assert np.abs(tau[0, g * G:(g + 1) * G] - want).max() <= 1e-6
+
+
+def _random_entmax(n, seed):
+    """Seeded random shapes (gpu_util.random_shapes) with a random alpha and a
+    top-k, window or union selection."""
+    rng = np.random.default_rng(seed + 1)
+    out = []
+    for cid, kw, unit, r, empty in random_shapes(n, seed, max_len=20000):
+        kind = str(rng.choice(["topk", "window", "init_local_topk"]))
+        alpha = float(rng.choice([1.25, 1.5, 2.0]))
+        if kind == "init_local_topk":
+            sel = sd.Selection(kind, min(r, 0.9), int(rng.integers(0, 5)),
+                               int(rng.integers(0, 65)))
+        else:
+            sel = sd.Selection(kind, r)
+        out.append((f"{cid}-{kind}-a{alpha}", kw, unit, sel, alpha, empty))
+    return out
+
+
+RANDOM_CASES = _random_entmax(12, 4040)
+
+
+@pytest.mark.parametrize("cid,kw,unit,sel,alpha,empty", RANDOM_CASES,
+                         ids=[c[0] for c in RANDOM_CASES])
+def test_entmax_random_shapes(cid, kw, unit, sel, alpha, empty):
+    print(f"[entmax] {cid}", flush=True)
+    w = kvsynth.generate(R["batch"].with_(**kw))
+    dev = upload(w)
+    if empty:  # the oracle and the library both see length 0
+        w.seq_lens[-1] = 0
+        dev.sl[-1] = 0
+    _compare(w, dev, unit, sel, alpha, _run(dev, unit, sel, alpha))

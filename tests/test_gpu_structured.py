@@ -34,7 +34,7 @@ import kvsynth
 import sparse_kv_cache_sd_amd as sd
 from oracle import sdref
 
-from gpu_util import GAP, TOL, oracle_group, upload
+from gpu_util import GAP, TOL, oracle_group, random_shapes, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -158,6 +158,32 @@ def test_structured_matches_oracle(cid, rec, unit, sel):
     dev = upload(kvsynth.generate(rec))
     worst = _check(dev, unit, sel)
     print(f"[structured] {cid}: max-abs {worst:.2e}", flush=True)
+
+
+def _random_structured(n, seed):
+    """Seeded random shapes (gpu_util.random_shapes, no empty sequences) with
+    a window, a union of random forced ranges, or the plain top-k."""
+    rng = np.random.default_rng(seed + 1)
+    out = []
+    for cid, kw, unit, r, _ in random_shapes(n, seed, allow_empty=False, max_len=20000):
+        kind = str(rng.choice(["window", "init_local_topk", "topk"]))
+        r = min(r, 0.9)
+        if kind == "init_local_topk":
+            sel = SEL(kind, r, int(rng.integers(0, 5)), int(rng.integers(0, 65)))
+        else:
+            sel = SEL(kind, r)
+        out.append((f"{cid}-{kind}", kw, unit, sel))
+    return out
+
+
+RANDOM_CASES = _random_structured(12, 3030)
+
+
+@pytest.mark.parametrize("cid,kw,unit,sel", RANDOM_CASES, ids=[c[0] for c in RANDOM_CASES])
+def test_structured_random_shapes(cid, kw, unit, sel):
+    print(f"[structured] {cid}", flush=True)
+    dev = upload(kvsynth.generate(R["batch"].with_(**kw)))
+    _check(dev, unit, sel)
 
 
 @pytest.mark.parametrize("unit,P", [("page", 16), ("page", 64), ("token", 16)])
