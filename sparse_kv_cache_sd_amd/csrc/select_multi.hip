@@ -20,6 +20,8 @@
 //     lower id).  That gives the last kept candidate (T, t) and the kept
 //     units of the slices before this one; the block keeps its units with
 //     key > T, or key == T and unit <= t, and writes them in ascending order.
+//     (In the token decode step the attention kernel runs this placement in
+//     its own prologue instead: launch_select_multi_bins runs the first two.)
 // The bin of a score is an fp32 subtract and multiply by the same constants
 // in every block, then a clamp: monotone in the score, so every key above b*
 // is above every candidate.  Where bins cannot be formed (k = 0 or U, all
