@@ -33,7 +33,7 @@ struct MArgs {
   int U_max, k_max, R_ppm, NB;
   const uint32_t* mm;        // [B*Hkv][mm_nb][2] partial min / max keys
   int mm_nb, mm_per;         // partials per (b, g); units per partial
-  uint32_t* hist;            // [B*Hkv][NB][kMBins] value histogram of each slice
+  uint16_t* hist;            // [B*Hkv][NB][kMBins] value histogram of each slice (<= 4096 a bin)
   uint32_t* above;           // [B*Hkv][NB] keys above bin b* in each slice
   uint32_t* ccount;          // [B*Hkv][NB] keys in bin b* in each slice
   uint2* cand;               // [B*Hkv][NB][kCapS] (key, unit) of the first of them

@@ -89,8 +89,13 @@ __global__ __launch_bounds__(kMT) void msel_hist_kernel(MArgs a) {
     atomicAdd(&sm.hist[v ? vbin(g, key[i]) : (uint32_t)(kMBins + lane)], v ? 1u : 0u);
   }
   __syncthreads();
-  uint32_t* h = a.hist + (g.bg * a.NB + g.blk) * kMBins;
-  for (int i = threadIdx.x; i < kMBins; i += kMT) h[i] = sm.hist[i];
+  // 16-bit counts (a slice holds kMSlice keys), four bins per thread in one
+  // 8-byte store: half the bytes every collect block reads back
+  static_assert(kMBins == 4 * kMT && kMSlice < 65536, "four 16-bit bins per thread");
+  const int t4 = 4 * threadIdx.x;
+  const uint2 packed = make_uint2(sm.hist[t4] | (sm.hist[t4 + 1] << 16),
+                                  sm.hist[t4 + 2] | (sm.hist[t4 + 3] << 16));
+  *reinterpret_cast<uint2*>(a.hist + (g.bg * a.NB + g.blk) * kMBins + t4) = packed;
 }
 
 // The bin b* of the k-th largest score; this slice's keys above it and in it.
@@ -100,24 +105,26 @@ __global__ __launch_bounds__(kMT) void msel_collect_kernel(MArgs a) {
   const GroupBlock gbk = group_block(a.d.B * a.d.Hkv);
   const Group g = group_setup(a, sm, key, gbk.bg, gbk.j);
   if (!g.binned || g.s0 >= g.U) return;  // uniform per block
-  // sum the slices' histograms, kBPT bins per thread (one vector load per
-  // slice), eight slices' loads issued together
-  typedef unsigned int vec_t __attribute__((ext_vector_type(kBPT)));
+  // sum the slices' histograms, kBPT bins per thread (one 8-byte load of
+  // four 16-bit counts per slice), eight slices' loads issued together
   const int tid = threadIdx.x;
-  const uint32_t* h = a.hist + g.bg * a.NB * kMBins;
+  const uint16_t* h = a.hist + g.bg * a.NB * kMBins;
   uint32_t c[kBPT] = {};
   for (int s0 = 0; s0 < g.nsl; s0 += 8) {
-    vec_t v[8];
+    uint2 v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int s = min(s0 + i, g.nsl - 1);
-      v[i] = *reinterpret_cast<const vec_t*>(h + (int64_t)s * kMBins + (kMBins - kBPT - kBPT * tid));
+      v[i] = *reinterpret_cast<const uint2*>(h + (int64_t)s * kMBins + (kMBins - kBPT - kBPT * tid));
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const bool valid = s0 + i < g.nsl;
-#pragma unroll
-      for (int j = 0; j < kBPT; ++j) c[j] += valid ? v[i][kBPT - 1 - j] : 0u;
+      const uint32_t m = s0 + i < g.nsl ? 0xFFFFu : 0u;
+      // bins kMBins - 1 - kBPT tid - j, j = 0 .. 3: the last count first
+      c[0] += (v[i].y >> 16) & m;
+      c[1] += v[i].y & m;
+      c[2] += (v[i].x >> 16) & m;
+      c[3] += v[i].x & m;
     }
   }
   pick_bin(sm, c, (uint32_t)g.k);
@@ -193,7 +200,7 @@ __global__ __launch_bounds__(kMT) void msel_place_kernel(MArgs a) {
 size_t msel_workspace_bytes(int B, int Hkv, int U_max) {
   const int64_t bg = (int64_t)B * Hkv;
   const int64_t NB = (U_max + kMSlice - 1) / kMSlice;
-  return sizeof(uint32_t) * 2 * bg * NB + sizeof(uint32_t) * bg * NB * kMBins +
+  return sizeof(uint32_t) * 2 * bg * NB + sizeof(uint16_t) * bg * NB * kMBins +
          sizeof(uint32_t) * 2 * bg * NB + sizeof(uint2) * bg * NB * kCapS;
 }
 
@@ -215,8 +222,8 @@ MArgs make_args(const SelectArgs& sa, void* ws, const int32_t* k_of, uint32_t** 
   char* p = static_cast<char*>(ws);
   *mm_own = reinterpret_cast<uint32_t*>(p);
   p += sizeof(uint32_t) * 2 * bg * a.NB;
-  a.hist = reinterpret_cast<uint32_t*>(p);
-  p += sizeof(uint32_t) * bg * a.NB * kMBins;
+  a.hist = reinterpret_cast<uint16_t*>(p);
+  p += sizeof(uint16_t) * bg * a.NB * kMBins;
   a.above = reinterpret_cast<uint32_t*>(p);
   p += sizeof(uint32_t) * bg * a.NB;
   a.ccount = reinterpret_cast<uint32_t*>(p);
